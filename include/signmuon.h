@@ -1,0 +1,178 @@
+/*
+ * signmuon.h -- C ABI of the MI355X (gfx950) Sign-Muon optimizer step.
+ *
+ * The method is the one summarised in "SignMuon: Communication-Efficient
+ * Distributed Muon Optimization" (gist.science, paper 2605.16311, technical
+ * summary; citations below name its sections). Each of Mw workers updates its
+ * own momentum, takes an approximate polar factor of it with Newton-Schulz
+ * iterations, and keeps only the entrywise signs, packed one bit per entry;
+ * all workers then take the majority vote of the Mw sign matrices and move
+ * the weights by eta times the vote.
+ *
+ * On one GPU the Mw workers' buffers sit side by side in device memory: the
+ * vote reads the Mw packed buffers that every worker would hold after the
+ * all-gather of the summary's 1-bit variant. No collective is called here.
+ *
+ * Conventions shared by every entry point
+ *  - A matrix is R x C, row-major and contiguous; n = R * C >= 1.
+ *  - Per-worker arrays are stacked: [Mw][R][C], worker m at offset m * n.
+ *  - All data pointers are DEVICE pointers owned by the caller. The library
+ *    allocates no memory, frees nothing and keeps no state between calls;
+ *    every call may be made from any host thread.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ *    the call returns without waiting for it. The library never synchronises.
+ *  - Pointers to device arrays must be 16-byte aligned (SIGNMUON_EALIGN).
+ *  - Every argument is checked before anything is enqueued: a call that
+ *    returns an error has enqueued no work. A launch failure returns
+ *    SIGNMUON_EHIP (signmuon_strerror names the HIP error); a device fault
+ *    shows up at the caller's next synchronisation of the stream.
+ *  - Buffers written by a call must not overlap any other buffer of the
+ *    same call, except where an entry point says "in place".
+ *  - bf16 is stored as its 16-bit pattern; fp32 -> bf16 rounds to nearest
+ *    even (NaN becomes a quiet NaN of the same sign).
+ *
+ * Packed signs (summary §2 "Algorithmic flow", step 3, 1-bit variant): one
+ * uint64 word per 64 entries, signmuon_packed_words(n) = ceil(n/64) words per
+ * worker. Bit j of word w is entry 64*w + j of the row-major flat index; bit
+ * 1 means +1, chosen when the value is >= 0 (so +0 and -0 give +1 and NaN
+ * gives -1); bits past n are zero.
+ */
+#ifndef SIGNMUON_H
+#define SIGNMUON_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SIGNMUON_ABI_VERSION 1
+
+/* Status codes. */
+enum {
+    SIGNMUON_OK = 0,
+    SIGNMUON_EINVAL = -1,     /* null pointer, size <= 0, workers < 1, bad count */
+    SIGNMUON_EDTYPE = -2,     /* dtype code not accepted by this entry point */
+    SIGNMUON_EALIGN = -3,     /* a device pointer is not 16-byte aligned */
+    SIGNMUON_EWORKSPACE = -4, /* workspace missing or smaller than required */
+    SIGNMUON_EHIP = -5,       /* a HIP call failed */
+    SIGNMUON_ERANGE = -6      /* a size exceeds what the kernels index */
+};
+
+typedef enum { SIGNMUON_F32 = 0, SIGNMUON_BF16 = 1 } signmuon_dtype;
+
+/* A hipStream_t, passed as an opaque pointer so that this header needs no
+ * HIP header. */
+typedef void *signmuon_stream;
+
+/* One weight matrix and its per-worker buffers. */
+typedef struct {
+    int64_t rows, cols;  /* R, C >= 1 */
+    const void *grad;    /* [Mw][R][C] of params.grad_dtype: each worker's stochastic
+                            gradient G (summary §2 "Algorithmic flow", step 1) */
+    void *momentum;      /* [Mw][R][C] of params.mom_dtype, in place: each worker's
+                            momentum M, the only persistent optimizer state (summary
+                            §4 "Memory"); start it at zero */
+    float *polar_out;    /* [Mw][R][C] fp32 or NULL: the Newton-Schulz output U of each
+                            worker. signmuon_momentum_ns requires it; signmuon_step
+                            writes it when non-NULL */
+    uint64_t *packed;    /* [Mw][signmuon_packed_words(R*C)]: each worker's packed
+                            signs S = sign(U) (required by signmuon_step) */
+    float *weight;       /* [R][C] fp32, in place: the weights W (required by
+                            signmuon_step) */
+    int8_t *vote_out;    /* [R][C] or NULL: the vote S-bar in {-1, 0, +1} */
+} signmuon_matrix;
+
+/* Hyper-parameters of one step (summary §2 "Algorithmic flow"). */
+typedef struct {
+    int32_t workers;          /* Mw >= 1 */
+    float beta;               /* momentum coefficient: M <- beta*M + G (finite) */
+    float eta;                /* step size eta_t of W <- W - eta_t * S-bar (finite) */
+    int32_t ns_iters;         /* k >= 0 Newton-Schulz iterations (k = 0: U = M/||M||_F) */
+    int32_t post_polar_iters; /* 0 = off; > 0: the optional local polar step on S-bar
+                                 (summary §2 "Algorithmic flow", step 5) with this many
+                                 iterations, which then replaces the sign update */
+    signmuon_dtype grad_dtype; /* G storage: F32 or BF16 */
+    signmuon_dtype mom_dtype;  /* M storage: F32 or BF16 */
+    signmuon_dtype ns_dtype;   /* Newton-Schulz operand storage: F32 or BF16 */
+} signmuon_params;
+
+/* Largest number of matrices one call accepts. */
+#define SIGNMUON_MAX_MATRICES 4096
+
+/*
+ * signmuon_momentum_ns -- each worker's local computation up to the polar
+ * factor (summary §2 "Core mechanism" and "Algorithmic flow" step 1):
+ *   M <- store_M(fmaf(beta, M, G))            (one fp32 fused multiply-add)
+ *   X0 = M / ||M||_F                          (Frobenius scaling; X0 = 0 if M = 0)
+ *   k times: A = X X^T, X <- 1.5 X - 0.5 A X  (R <= C)
+ *            A = X^T X, X <- 1.5 X - 0.5 X A  (R > C)
+ *   U = X_k written to polar_out as fp32.
+ * The Gram matrix A and every iterate before the last are stored in
+ * ns_dtype; products accumulate in fp32 on the matrix cores. The summary
+ * prints neither the momentum form nor the Newton-Schulz coefficients; the
+ * heavy-ball form and the cubic 1.5 / -0.5 are the readings taken.
+ * mats[i].grad, .momentum and .polar_out are used; the other fields are
+ * ignored. workspace: signmuon_workspace_bytes(mats, n_mats, p) bytes.
+ */
+int signmuon_momentum_ns(const signmuon_matrix *mats, int32_t n_mats, const signmuon_params *p,
+                         void *workspace, size_t workspace_bytes, signmuon_stream stream);
+
+/*
+ * signmuon_sign_pack -- entrywise sign and 1-bit packing (summary §2 "Core
+ * mechanism" and "Algorithmic flow" steps 2-3): u is [workers][n] of u_dtype
+ * (F32 or BF16); packed receives [workers][signmuon_packed_words(n)] words in
+ * the packed-sign layout above.
+ */
+int signmuon_sign_pack(const void *u, signmuon_dtype u_dtype, int64_t n, int32_t workers,
+                       uint64_t *packed, signmuon_stream stream);
+
+/*
+ * signmuon_vote_update -- majority vote and update (summary §2 "Core
+ * mechanism", and "Algorithmic flow" step 4):
+ *   c_i = number of workers whose bit i is 1,  S-bar_i = sign(2 c_i - workers)
+ *   W_i <- W_i - eta (S-bar_i = +1),  W_i + eta (S-bar_i = -1),  unchanged (0)
+ * Each add is one fp32 operation rounded to nearest even. A tie (even worker
+ * count only) votes 0 -- the summary does not say; this is the reading taken.
+ * packed is [workers][signmuon_packed_words(n)]; weight [n] fp32 is updated in
+ * place (NULL: vote only); vote_out [n] int8 or NULL. At least one of weight
+ * and vote_out must be non-NULL.
+ */
+int signmuon_vote_update(const uint64_t *packed, int32_t workers, int64_t n, float *weight,
+                         float eta, int8_t *vote_out, signmuon_stream stream);
+
+/*
+ * signmuon_step -- one whole optimizer step for every matrix (summary §2
+ * "Algorithmic flow", steps 1-5 with the collective of step 3 replaced by the
+ * workers' packed buffers being local): signmuon_momentum_ns, the sign and
+ * packing of U fused into the last Newton-Schulz product, then the vote and
+ * the update of W. With post_polar_iters > 0 the vote S-bar is not applied
+ * directly: W <- fmaf(-eta, Y, W) with Y the post_polar_iters-step
+ * Newton-Schulz factor of S-bar / ||S-bar||_F (W unchanged if S-bar = 0).
+ * mats[i].grad, .momentum, .packed and .weight are required; .polar_out and
+ * .vote_out are written when non-NULL.
+ */
+int signmuon_step(const signmuon_matrix *mats, int32_t n_mats, const signmuon_params *p,
+                  void *workspace, size_t workspace_bytes, signmuon_stream stream);
+
+/* ceil(n / 64): packed words per worker for n entries (0 for n <= 0). */
+size_t signmuon_packed_words(int64_t n);
+
+/* Device workspace, in bytes, that signmuon_step and signmuon_momentum_ns
+ * need for these matrices and parameters (0 on invalid arguments). The same
+ * workspace serves both entry points. */
+size_t signmuon_workspace_bytes(const signmuon_matrix *mats, int32_t n_mats,
+                                const signmuon_params *p);
+
+/* Text for a status code; for SIGNMUON_EHIP it names the HIP error of the
+ * calling thread's last failure. Never NULL. */
+const char *signmuon_strerror(int status);
+
+/* SIGNMUON_ABI_VERSION of the loaded library. */
+int signmuon_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,210 @@
+"""Python binding of the MI355X Sign-Muon step library (``libsignmuon.so``).
+
+Argument marshalling only: torch tensors are passed to the C ABI of
+``include/signmuon.h`` as device pointers, with the current torch stream.
+Every step of the optimizer runs in the library's HIP kernels. If the
+library is not built, every call raises: there is no other code path.
+
+The function names are those of the C ABI. ``Matrix`` describes one weight
+matrix with its per-worker buffers; ``Params`` the step's hyper-parameters.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional, Sequence
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libsignmuon.so")
+
+F32, BF16 = 0, 1
+ABI_VERSION = 1
+
+STATUS = {0: "SIGNMUON_OK", -1: "SIGNMUON_EINVAL", -2: "SIGNMUON_EDTYPE", -3: "SIGNMUON_EALIGN",
+          -4: "SIGNMUON_EWORKSPACE", -5: "SIGNMUON_EHIP", -6: "SIGNMUON_ERANGE"}
+
+
+class SignmuonError(RuntimeError):
+    def __init__(self, status: int, text: str):
+        super().__init__(f"{STATUS.get(status, status)}: {text}")
+        self.status = status
+
+
+class _Matrix(ctypes.Structure):
+    _fields_ = [("rows", ctypes.c_int64), ("cols", ctypes.c_int64), ("grad", ctypes.c_void_p),
+                ("momentum", ctypes.c_void_p), ("polar_out", ctypes.c_void_p),
+                ("packed", ctypes.c_void_p), ("weight", ctypes.c_void_p),
+                ("vote_out", ctypes.c_void_p)]
+
+
+class _Params(ctypes.Structure):
+    _fields_ = [("workers", ctypes.c_int32), ("beta", ctypes.c_float), ("eta", ctypes.c_float),
+                ("ns_iters", ctypes.c_int32), ("post_polar_iters", ctypes.c_int32),
+                ("grad_dtype", ctypes.c_int), ("mom_dtype", ctypes.c_int),
+                ("ns_dtype", ctypes.c_int)]
+
+
+_lib = None
+
+
+def library() -> ctypes.CDLL:
+    """Load ``libsignmuon.so`` (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built: run sign_muon_step_amd/build.py "
+                           "(or __graft_entry__.build()) first")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    mp, pp = ctypes.POINTER(_Matrix), ctypes.POINTER(_Params)
+    lib.signmuon_momentum_ns.restype = ctypes.c_int
+    lib.signmuon_momentum_ns.argtypes = [mp, i32, pp, vp, ctypes.c_size_t, vp]
+    lib.signmuon_step.restype = ctypes.c_int
+    lib.signmuon_step.argtypes = [mp, i32, pp, vp, ctypes.c_size_t, vp]
+    lib.signmuon_sign_pack.restype = ctypes.c_int
+    lib.signmuon_sign_pack.argtypes = [vp, ctypes.c_int, i64, i32, vp, vp]
+    lib.signmuon_vote_update.restype = ctypes.c_int
+    lib.signmuon_vote_update.argtypes = [vp, i32, i64, vp, ctypes.c_float, vp, vp]
+    lib.signmuon_packed_words.restype = ctypes.c_size_t
+    lib.signmuon_packed_words.argtypes = [i64]
+    lib.signmuon_workspace_bytes.restype = ctypes.c_size_t
+    lib.signmuon_workspace_bytes.argtypes = [mp, i32, pp]
+    lib.signmuon_strerror.restype = ctypes.c_char_p
+    lib.signmuon_strerror.argtypes = [ctypes.c_int]
+    lib.signmuon_abi_version.restype = ctypes.c_int
+    lib.signmuon_abi_version.argtypes = []
+    if lib.signmuon_abi_version() != ABI_VERSION:
+        raise RuntimeError("libsignmuon.so ABI version mismatch")
+    _lib = lib
+    return lib
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise SignmuonError(status, library().signmuon_strerror(status).decode())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to the library must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+@dataclass
+class Matrix:
+    """One R x C weight matrix and its buffers (see signmuon_matrix).
+
+    grad, momentum, polar_out: [Mw][R][C]; packed: [Mw][packed_words] int64
+    (bit pattern of the uint64 words); weight: [R][C] fp32; vote_out: [R][C]
+    int8. Optional fields may be None.
+    """
+    grad: torch.Tensor
+    momentum: torch.Tensor
+    packed: Optional[torch.Tensor] = None
+    weight: Optional[torch.Tensor] = None
+    polar_out: Optional[torch.Tensor] = None
+    vote_out: Optional[torch.Tensor] = None
+
+    @property
+    def shape(self):
+        return tuple(self.grad.shape[-2:])
+
+
+@dataclass
+class Params:
+    workers: int
+    beta: float = 0.9
+    eta: float = 1e-3
+    ns_iters: int = 1
+    post_polar_iters: int = 0
+    grad_dtype: int = F32
+    mom_dtype: int = F32
+    ns_dtype: int = F32
+
+
+def _marshal(mats: Sequence[Matrix], params: Params):
+    arr = (_Matrix * len(mats))()
+    for i, m in enumerate(mats):
+        R, C = m.shape
+        arr[i] = _Matrix(R, C, _ptr(m.grad), _ptr(m.momentum), _ptr(m.polar_out), _ptr(m.packed),
+                         _ptr(m.weight), _ptr(m.vote_out))
+    p = _Params(params.workers, params.beta, params.eta, params.ns_iters,
+                params.post_polar_iters, params.grad_dtype, params.mom_dtype, params.ns_dtype)
+    return arr, p
+
+
+def signmuon_packed_words(n: int) -> int:
+    return int(library().signmuon_packed_words(n))
+
+
+def signmuon_workspace_bytes(mats: Sequence[Matrix], params: Params) -> int:
+    arr, p = _marshal(mats, params)
+    return int(library().signmuon_workspace_bytes(arr, len(mats), ctypes.byref(p)))
+
+
+def signmuon_strerror(status: int) -> str:
+    return library().signmuon_strerror(status).decode()
+
+
+def signmuon_abi_version() -> int:
+    return int(library().signmuon_abi_version())
+
+
+def signmuon_momentum_ns(mats: Sequence[Matrix], params: Params, workspace: Optional[torch.Tensor],
+                         stream=None) -> None:
+    arr, p = _marshal(mats, params)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(library().signmuon_momentum_ns(arr, len(mats), ctypes.byref(p), _ptr(workspace), nbytes,
+                                          _stream(stream)))
+
+
+def signmuon_step(mats: Sequence[Matrix], params: Params, workspace: Optional[torch.Tensor],
+                  stream=None) -> None:
+    arr, p = _marshal(mats, params)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(library().signmuon_step(arr, len(mats), ctypes.byref(p), _ptr(workspace), nbytes,
+                                   _stream(stream)))
+
+
+def signmuon_sign_pack(u: torch.Tensor, n: int, workers: int, packed: torch.Tensor,
+                       stream=None) -> None:
+    _check(library().signmuon_sign_pack(_ptr(u), _dtype_code(u), n, workers, _ptr(packed),
+                                        _stream(stream)))
+
+
+def signmuon_vote_update(packed: torch.Tensor, workers: int, n: int, weight: Optional[torch.Tensor],
+                         eta: float, vote_out: Optional[torch.Tensor] = None, stream=None) -> None:
+    _check(library().signmuon_vote_update(_ptr(packed), workers, n, _ptr(weight), eta,
+                                          _ptr(vote_out), _stream(stream)))
+
+
+def dtype_code(t: torch.dtype) -> int:
+    return {torch.float32: F32, torch.bfloat16: BF16}[t]
+
+
+def workspace_tensor(mats: Sequence[Matrix], params: Params, device) -> Optional[torch.Tensor]:
+    """Allocate (with torch) the device workspace the library asks for."""
+    nbytes = signmuon_workspace_bytes(mats, params)
+    if nbytes == 0:
+        return None
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)

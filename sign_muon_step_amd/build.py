@@ -1,0 +1,53 @@
+"""Compile the gfx950 HIP library ``libsignmuon.so`` in-tree with hipcc.
+
+All HIP sources are built for gfx950 only, with packed fp32 instructions
+disabled (``-packed-fp32-ops``: a hipcc device feature; the host pass prints
+a harmless warning that it does not know it).
+"""
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+LIB = os.path.join(HERE, "libsignmuon.so")
+SOURCES = [os.path.join(HERE, "csrc", f) for f in ("api.hip", "elementwise.hip", "ns_gemm.hip")]
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+ARCH = "gfx950"
+
+
+def flags():
+    return ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall",
+            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc")]
+
+
+def build(verbose: bool = False, jobs: int = 3) -> str:
+    """Compile each source to an object in parallel, then link the library."""
+    objdir = os.path.join(HERE, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    procs = []
+    objs = []
+    for src in SOURCES:
+        obj = os.path.join(objdir, os.path.basename(src) + ".o")
+        objs.append(obj)
+        cmd = [HIPCC] + flags() + ["-c", src, "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append((subprocess.Popen(cmd), src))
+        while len([p for p, _ in procs if p.poll() is None]) >= jobs:
+            procs[0][0].wait()
+    for p, src in procs:
+        if p.wait() != 0:
+            raise RuntimeError(f"hipcc failed on {src}")
+    tmp = LIB + ".tmp"
+    cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.check_call(cmd)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-q" not in sys.argv))

@@ -1,0 +1,492 @@
+// api.hip -- host side of the C ABI declared in include/signmuon.h: argument
+// checks, workspace layout and the launch sequence of the Sign-Muon step.
+//
+// Method: "SignMuon: Communication-Efficient Distributed Muon Optimization"
+// (gist.science, paper 2605.16311, technical summary), §2 "Algorithmic flow".
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <vector>
+
+#include "signmuon.h"
+#include "sm_internal.h"
+
+namespace {
+
+thread_local char g_hip_err[192] = "";
+
+constexpr int64_t kMaxDim = (int64_t)1 << 20;   // rows or cols
+constexpr int64_t kMaxN = ((int64_t)1 << 31) - 1;  // entries per matrix
+constexpr int32_t kMaxWorkers = 255;             // vote counters are 8 bit-planes
+constexpr int32_t kMaxIters = 1000;
+constexpr size_t kSectionAlign = 256;
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+inline bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+inline bool dtype_ok(int d) { return d == SIGNMUON_F32 || d == SIGNMUON_BF16; }
+inline size_t esize(signmuon_dtype d) { return d == SIGNMUON_BF16 ? 2 : 4; }
+
+int hip_status(hipError_t e) {
+    if (e == hipSuccess) return SIGNMUON_OK;
+    std::snprintf(g_hip_err, sizeof g_hip_err, "HIP error %d: %s", (int)e, hipGetErrorString(e));
+    return SIGNMUON_EHIP;
+}
+
+inline int last_launch() { return hip_status(hipGetLastError()); }
+
+struct MatPlan {
+    int64_t R, C, n, r, nw;
+    int32_t mom_bpw;        // momentum blocks per worker
+    int32_t partial_begin;  // first partial of (matrix, worker 0)
+    int32_t unit_begin;     // scales index of (matrix, worker 0)
+    size_t gram_off;        // bytes from the Gram section: [Mw][r][r]
+    size_t iter_off;        // bytes from each iterate section: [Mw][n]
+    size_t post_gram_off;   // post-vote step: [r][r]
+    size_t post_iter_off;   // post-vote step: [n]
+    size_t vns_off;         // vote in NS storage: [n]
+    size_t u_off;           // fp32 U scratch [Mw][n] (unfused pack only)
+    bool fused_pack;        // the last product packs the signs itself
+    bool u_scratch;         // U goes through workspace scratch
+};
+
+struct Plan {
+    std::vector<MatPlan> m;
+    int32_t units = 0, post_unit_base = 0, partials = 0;
+    size_t off_partials = 0, off_scales = 0, off_nnz = 0, off_gram = 0, off_iter[2] = {0, 0};
+    size_t off_vns = 0, off_u = 0, total = 0;
+};
+
+// Shapes, counts and dtypes (not pointers). Fills the plan.
+int make_plan(const signmuon_matrix *mats, int32_t n_mats, const signmuon_params *p, bool step,
+              Plan &pl) {
+    if (!mats || !p || n_mats < 1 || n_mats > SIGNMUON_MAX_MATRICES) return SIGNMUON_EINVAL;
+    if (p->workers < 1 || p->ns_iters < 0 || p->post_polar_iters < 0) return SIGNMUON_EINVAL;
+    if (p->ns_iters > kMaxIters || p->post_polar_iters > kMaxIters) return SIGNMUON_ERANGE;
+    if (p->workers > kMaxWorkers) return SIGNMUON_ERANGE;
+    if (!std::isfinite(p->beta) || !std::isfinite(p->eta)) return SIGNMUON_EINVAL;
+    if (!dtype_ok(p->grad_dtype) || !dtype_ok(p->mom_dtype) || !dtype_ok(p->ns_dtype))
+        return SIGNMUON_EDTYPE;
+    if (p->mom_dtype != p->ns_dtype) return SIGNMUON_EDTYPE;  // X0 is read in place from M
+    const int64_t mw = p->workers;
+    const size_t ns = esize(p->ns_dtype);
+    const bool post = step && p->post_polar_iters > 0;
+    pl.m.assign(n_mats, MatPlan{});
+    size_t gram = 0, iter = 0, post_gram = 0, post_iter = 0, vns = 0, u = 0;
+    int64_t partials = 0;
+    for (int32_t i = 0; i < n_mats; ++i) {
+        const signmuon_matrix &s = mats[i];
+        if (s.rows < 1 || s.cols < 1) return SIGNMUON_EINVAL;
+        if (s.rows > kMaxDim || s.cols > kMaxDim || s.rows * s.cols > kMaxN) return SIGNMUON_ERANGE;
+        MatPlan &q = pl.m[i];
+        q.R = s.rows;
+        q.C = s.cols;
+        q.n = q.R * q.C;
+        q.r = q.R < q.C ? q.R : q.C;
+        q.nw = (q.n + 63) / 64;
+        q.mom_bpw = (int32_t)((q.n + sm::kMomChunk - 1) / sm::kMomChunk);
+        q.partial_begin = (int32_t)partials;
+        partials += mw * q.mom_bpw;
+        q.unit_begin = pl.units;
+        pl.units += (int32_t)mw;
+        q.gram_off = gram;
+        gram += align_up((size_t)(mw * q.r * q.r) * ns, kSectionAlign);
+        q.iter_off = iter;
+        iter += align_up((size_t)(mw * q.n) * ns, kSectionAlign);
+        q.post_gram_off = post_gram;
+        post_gram += align_up((size_t)(q.r * q.r) * ns, kSectionAlign);
+        q.post_iter_off = post_iter;
+        post_iter += align_up((size_t)q.n * ns, kSectionAlign);
+        q.vns_off = vns;
+        if (post) vns += align_up((size_t)q.n * ns, kSectionAlign);
+        q.fused_pack = step && p->ns_iters > 0 && (q.C % 64) == 0;
+        q.u_scratch = step && p->ns_iters > 0 && !q.fused_pack && s.polar_out == nullptr;
+        q.u_off = u;
+        if (q.u_scratch) u += align_up((size_t)(mw * q.n) * 4, kSectionAlign);
+    }
+    if (partials > INT32_MAX / 2) return SIGNMUON_ERANGE;
+    pl.partials = (int32_t)partials;
+    pl.post_unit_base = pl.units;
+    const int32_t scale_count = pl.units + n_mats;
+
+    size_t off = 0;
+    pl.off_partials = off;
+    off += align_up((size_t)partials * sizeof(double), kSectionAlign);
+    pl.off_scales = off;
+    off += align_up((size_t)scale_count * sizeof(float2), kSectionAlign);
+    pl.off_nnz = off;
+    off += align_up((size_t)n_mats * sizeof(uint32_t), kSectionAlign);
+    pl.off_gram = off;
+    const bool need_gram = p->ns_iters > 0 || post;
+    off += need_gram ? (gram > post_gram ? gram : post_gram) : 0;
+    size_t iter_need = 0;
+    if (p->ns_iters >= 2) iter_need = iter;
+    if (post && p->post_polar_iters >= 2 && post_iter > iter_need) iter_need = post_iter;
+    pl.off_iter[0] = off;
+    off += iter_need;
+    pl.off_iter[1] = off;
+    off += iter_need;
+    pl.off_vns = off;
+    off += vns;
+    pl.off_u = off;
+    off += u;
+    pl.total = off;
+    return SIGNMUON_OK;
+}
+
+int check_step_pointers(const signmuon_matrix *mats, int32_t n_mats, bool step) {
+    for (int32_t i = 0; i < n_mats; ++i) {
+        const signmuon_matrix &s = mats[i];
+        if (!s.grad || !s.momentum) return SIGNMUON_EINVAL;
+        if (step && (!s.packed || !s.weight)) return SIGNMUON_EINVAL;
+        if (!step && !s.polar_out) return SIGNMUON_EINVAL;
+        const void *ptrs[6] = {s.grad, s.momentum, s.polar_out, s.packed, s.weight, s.vote_out};
+        for (const void *q : ptrs)
+            if (q && !aligned16(q)) return SIGNMUON_EALIGN;
+    }
+    return SIGNMUON_OK;
+}
+
+template <typename T>
+T *ws_at(void *ws, size_t off) {
+    return reinterpret_cast<T *>(static_cast<char *>(ws) + off);
+}
+
+// ---------------------------------------------------------------------------
+// Launch sequence shared by signmuon_momentum_ns and signmuon_step.
+// ---------------------------------------------------------------------------
+int run_momentum(const signmuon_matrix *mats, int32_t n_mats, const signmuon_params *p,
+                 const Plan &pl, void *ws, hipStream_t st) {
+    for (int32_t c0 = 0; c0 < n_mats; c0 += sm::kMaxMatsPerLaunch) {
+        const int32_t cn = n_mats - c0 < sm::kMaxMatsPerLaunch ? n_mats - c0 : sm::kMaxMatsPerLaunch;
+        sm::MomBatch b{};
+        b.nmat = cn;
+        b.workers = p->workers;
+        b.beta = p->beta;
+        b.g_bf16 = p->grad_dtype == SIGNMUON_BF16;
+        b.m_bf16 = p->mom_dtype == SIGNMUON_BF16;
+        b.partials = ws_at<double>(ws, pl.off_partials);
+        b.scales = ws_at<float2>(ws, pl.off_scales);
+        int64_t blocks = 0;
+        for (int32_t j = 0; j < cn; ++j) {
+            const MatPlan &q = pl.m[c0 + j];
+            sm::MomMat &d = b.mat[j];
+            d.g = mats[c0 + j].grad;
+            d.m = mats[c0 + j].momentum;
+            d.n = q.n;
+            d.block_begin = (int32_t)blocks;
+            d.blocks_per_worker = q.mom_bpw;
+            d.partial_begin = q.partial_begin;
+            d.unit_begin = q.unit_begin;
+            blocks += (int64_t)p->workers * q.mom_bpw;
+        }
+        if (blocks > INT32_MAX) return SIGNMUON_ERANGE;
+        b.total_blocks = (int32_t)blocks;
+        sm::launch_momentum(b, st);
+        if (int rc = last_launch()) return rc;
+        sm::launch_finalize_scales(b, st);
+        if (int rc = last_launch()) return rc;
+    }
+    return SIGNMUON_OK;
+}
+
+// Newton-Schulz iterations of every (matrix, worker). final_epi selects the
+// last product's epilogue: EPI_FINAL writes U (polar_out or scratch) and, for
+// step, the fused packed signs.
+int run_newton_schulz(const signmuon_matrix *mats, int32_t n_mats, const signmuon_params *p,
+                      const Plan &pl, void *ws, bool step, hipStream_t st) {
+    const int k = p->ns_iters;
+    const bool bf16 = p->ns_dtype == SIGNMUON_BF16;
+    const float2 *scales = ws_at<float2>(ws, pl.off_scales);
+    for (int j = 0; j < k; ++j) {
+        const bool last = j == k - 1;
+        for (int pass = 0; pass < 2; ++pass) {  // 0 = Gram, 1 = product
+            for (int32_t c0 = 0; c0 < n_mats; c0 += sm::kMaxMatsPerLaunch) {
+                const int32_t cn =
+                    n_mats - c0 < sm::kMaxMatsPerLaunch ? n_mats - c0 : sm::kMaxMatsPerLaunch;
+                sm::NsBatch b{};
+                b.nmat = cn;
+                b.workers = p->workers;
+                b.use_scales = j == 0;
+                b.scales = scales;
+                int64_t tiles = 0;
+                for (int32_t i = 0; i < cn; ++i) {
+                    const MatPlan &q = pl.m[c0 + i];
+                    const signmuon_matrix &s = mats[c0 + i];
+                    sm::NsMat &d = b.mat[i];
+                    d.R = (int32_t)q.R;
+                    d.C = (int32_t)q.C;
+                    d.unit_begin = q.unit_begin;
+                    d.x = j == 0 ? s.momentum : ws_at<const char>(ws, pl.off_iter[(j - 1) & 1] + q.iter_off);
+                    d.a = ws_at<char>(ws, pl.off_gram + q.gram_off);
+                    if (!last) {
+                        d.out = ws_at<char>(ws, pl.off_iter[j & 1] + q.iter_off);
+                    } else if (s.polar_out) {
+                        d.out = s.polar_out;
+                    } else if (q.u_scratch) {
+                        d.out = ws_at<char>(ws, pl.off_u + q.u_off);
+                    } else {
+                        d.out = nullptr;
+                    }
+                    d.packed = (last && step && q.fused_pack) ? s.packed : nullptr;
+                    d.tiles_per_worker = pass == 0 ? sm::ns_gram_tiles(q.R, q.C) : sm::ns_product_tiles(q.R, q.C);
+                    d.tile_begin = (int32_t)tiles;
+                    tiles += (int64_t)p->workers * d.tiles_per_worker;
+                }
+                if (tiles > INT32_MAX) return SIGNMUON_ERANGE;
+                b.total_tiles = (int32_t)tiles;
+                if (pass == 0)
+                    sm::launch_ns_gram(b, bf16, st);
+                else
+                    sm::launch_ns_product(b, bf16, last ? sm::EPI_FINAL : sm::EPI_ITER, st);
+                if (int rc = last_launch()) return rc;
+            }
+        }
+    }
+    return SIGNMUON_OK;
+}
+
+// Sign + pack from a stored value: the scaled momentum (k = 0) or a U that the
+// last product could not pack itself.
+int run_pack(const signmuon_matrix *mats, int32_t n_mats, const signmuon_params *p, const Plan &pl,
+             void *ws, bool step, hipStream_t st) {
+    const bool k0 = p->ns_iters == 0;
+    std::vector<int32_t> sel;
+    for (int32_t i = 0; i < n_mats; ++i)
+        if (k0 || (step && !pl.m[i].fused_pack)) sel.push_back(i);
+    for (size_t c0 = 0; c0 < sel.size(); c0 += sm::kMaxMatsPerLaunch) {
+        const size_t cn = sel.size() - c0 < (size_t)sm::kMaxMatsPerLaunch ? sel.size() - c0
+                                                                          : (size_t)sm::kMaxMatsPerLaunch;
+        sm::PackBatch b{};
+        b.nmat = (int32_t)cn;
+        b.workers = p->workers;
+        b.u_bf16 = k0 ? p->mom_dtype == SIGNMUON_BF16 : 0;
+        b.scales = k0 ? ws_at<float2>(ws, pl.off_scales) : nullptr;
+        int64_t blocks = 0;
+        for (size_t i = 0; i < cn; ++i) {
+            const int32_t mi = sel[c0 + i];
+            const MatPlan &q = pl.m[mi];
+            const signmuon_matrix &s = mats[mi];
+            sm::PackMat &d = b.mat[i];
+            if (k0) {
+                d.u = s.momentum;
+                d.u_out = s.polar_out;
+            } else {
+                d.u = s.polar_out ? (const void *)s.polar_out : ws_at<const char>(ws, pl.off_u + q.u_off);
+                d.u_out = nullptr;
+            }
+            d.packed = step ? s.packed : nullptr;
+            d.n = q.n;
+            d.unit_begin = q.unit_begin;
+            d.blocks_per_worker = (int32_t)((q.nw + sm::kPackWordsPerBlock - 1) / sm::kPackWordsPerBlock);
+            d.block_begin = (int32_t)blocks;
+            blocks += (int64_t)p->workers * d.blocks_per_worker;
+        }
+        if (blocks > INT32_MAX) return SIGNMUON_ERANGE;
+        b.total_blocks = (int32_t)blocks;
+        sm::launch_sign_pack(b, st);
+        if (int rc = last_launch()) return rc;
+    }
+    return SIGNMUON_OK;
+}
+
+int run_vote(const signmuon_matrix *mats, int32_t n_mats, const signmuon_params *p, const Plan &pl,
+             void *ws, hipStream_t st) {
+    const bool post = p->post_polar_iters > 0;
+    uint32_t *nnz = ws_at<uint32_t>(ws, pl.off_nnz);
+    if (post) {
+        sm::launch_zero_u32(nnz, n_mats, st);
+        if (int rc = last_launch()) return rc;
+    }
+    for (int32_t c0 = 0; c0 < n_mats; c0 += sm::kMaxMatsPerLaunch) {
+        const int32_t cn = n_mats - c0 < sm::kMaxMatsPerLaunch ? n_mats - c0 : sm::kMaxMatsPerLaunch;
+        sm::VoteBatch b{};
+        b.nmat = cn;
+        b.workers = p->workers;
+        b.eta = p->eta;
+        b.v_ns_bf16 = p->ns_dtype == SIGNMUON_BF16;
+        int64_t blocks = 0;
+        for (int32_t i = 0; i < cn; ++i) {
+            const MatPlan &q = pl.m[c0 + i];
+            const signmuon_matrix &s = mats[c0 + i];
+            sm::VoteMat &d = b.mat[i];
+            d.packed = s.packed;
+            d.w = post ? nullptr : s.weight;
+            d.vote = s.vote_out;
+            d.v_ns = post ? ws_at<char>(ws, pl.off_vns + q.vns_off) : nullptr;
+            d.nnz = post ? nnz + c0 + i : nullptr;
+            d.n = q.n;
+            d.block_begin = (int32_t)blocks;
+            blocks += (q.nw + sm::kVoteWordsPerBlock - 1) / sm::kVoteWordsPerBlock;
+        }
+        if (blocks > INT32_MAX) return SIGNMUON_ERANGE;
+        b.total_blocks = (int32_t)blocks;
+        sm::launch_vote_update(b, st);
+        if (int rc = last_launch()) return rc;
+    }
+    return SIGNMUON_OK;
+}
+
+// Optional local polar step on the vote (summary §2 "Algorithmic flow", step
+// 5): Frobenius-scaled Newton-Schulz on S-bar, then W <- fmaf(-eta, Y, W).
+int run_post_polar(const signmuon_matrix *mats, int32_t n_mats, const signmuon_params *p,
+                   const Plan &pl, void *ws, hipStream_t st) {
+    const int k = p->post_polar_iters;
+    const bool bf16 = p->ns_dtype == SIGNMUON_BF16;
+    float2 *scales = ws_at<float2>(ws, pl.off_scales);
+    sm::launch_nnz_scales(ws_at<uint32_t>(ws, pl.off_nnz), n_mats, scales + pl.post_unit_base, st);
+    if (int rc = last_launch()) return rc;
+    for (int j = 0; j < k; ++j) {
+        const bool last = j == k - 1;
+        for (int pass = 0; pass < 2; ++pass) {
+            for (int32_t c0 = 0; c0 < n_mats; c0 += sm::kMaxMatsPerLaunch) {
+                const int32_t cn =
+                    n_mats - c0 < sm::kMaxMatsPerLaunch ? n_mats - c0 : sm::kMaxMatsPerLaunch;
+                sm::NsBatch b{};
+                b.nmat = cn;
+                b.workers = 1;
+                b.use_scales = j == 0;
+                b.scales = scales;
+                b.eta = p->eta;
+                int64_t tiles = 0;
+                for (int32_t i = 0; i < cn; ++i) {
+                    const MatPlan &q = pl.m[c0 + i];
+                    sm::NsMat &d = b.mat[i];
+                    d.R = (int32_t)q.R;
+                    d.C = (int32_t)q.C;
+                    d.unit_begin = pl.post_unit_base + c0 + i;
+                    d.x = j == 0 ? ws_at<const char>(ws, pl.off_vns + q.vns_off)
+                                 : ws_at<const char>(ws, pl.off_iter[(j - 1) & 1] + q.post_iter_off);
+                    d.a = ws_at<char>(ws, pl.off_gram + q.post_gram_off);
+                    d.out = last ? (void *)mats[c0 + i].weight
+                                 : ws_at<char>(ws, pl.off_iter[j & 1] + q.post_iter_off);
+                    d.packed = nullptr;
+                    d.tiles_per_worker = pass == 0 ? sm::ns_gram_tiles(q.R, q.C) : sm::ns_product_tiles(q.R, q.C);
+                    d.tile_begin = (int32_t)tiles;
+                    tiles += d.tiles_per_worker;
+                }
+                b.total_tiles = (int32_t)tiles;
+                if (pass == 0)
+                    sm::launch_ns_gram(b, bf16, st);
+                else
+                    sm::launch_ns_product(b, bf16, last ? sm::EPI_WUPD : sm::EPI_ITER, st);
+                if (int rc = last_launch()) return rc;
+            }
+        }
+    }
+    return SIGNMUON_OK;
+}
+
+int check_workspace(const Plan &pl, void *ws, size_t ws_bytes) {
+    if (pl.total == 0) return SIGNMUON_OK;
+    if (!ws || ws_bytes < pl.total) return SIGNMUON_EWORKSPACE;
+    if (!aligned16(ws)) return SIGNMUON_EALIGN;
+    return SIGNMUON_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t signmuon_packed_words(int64_t n) { return n <= 0 ? 0 : (size_t)((n + 63) / 64); }
+
+int signmuon_abi_version(void) { return SIGNMUON_ABI_VERSION; }
+
+const char *signmuon_strerror(int status) {
+    switch (status) {
+    case SIGNMUON_OK: return "ok";
+    case SIGNMUON_EINVAL: return "invalid argument (null pointer, size or count out of range)";
+    case SIGNMUON_EDTYPE: return "dtype not accepted (momentum and Newton-Schulz storage must match)";
+    case SIGNMUON_EALIGN: return "device pointer not 16-byte aligned";
+    case SIGNMUON_EWORKSPACE: return "workspace missing or too small";
+    case SIGNMUON_EHIP: return g_hip_err[0] ? g_hip_err : "HIP error";
+    case SIGNMUON_ERANGE: return "size beyond the kernels' limits";
+    default: return "unknown status";
+    }
+}
+
+size_t signmuon_workspace_bytes(const signmuon_matrix *mats, int32_t n_mats, const signmuon_params *p) {
+    Plan pl;
+    if (make_plan(mats, n_mats, p, true, pl) != SIGNMUON_OK) return 0;
+    return pl.total;
+}
+
+int signmuon_momentum_ns(const signmuon_matrix *mats, int32_t n_mats, const signmuon_params *p,
+                         void *workspace, size_t workspace_bytes, signmuon_stream stream) {
+    Plan pl;
+    if (int rc = make_plan(mats, n_mats, p, false, pl)) return rc;
+    if (int rc = check_step_pointers(mats, n_mats, false)) return rc;
+    if (int rc = check_workspace(pl, workspace, workspace_bytes)) return rc;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (int rc = run_momentum(mats, n_mats, p, pl, workspace, st)) return rc;
+    if (p->ns_iters == 0) return run_pack(mats, n_mats, p, pl, workspace, false, st);
+    return run_newton_schulz(mats, n_mats, p, pl, workspace, false, st);
+}
+
+int signmuon_step(const signmuon_matrix *mats, int32_t n_mats, const signmuon_params *p,
+                  void *workspace, size_t workspace_bytes, signmuon_stream stream) {
+    Plan pl;
+    if (int rc = make_plan(mats, n_mats, p, true, pl)) return rc;
+    if (int rc = check_step_pointers(mats, n_mats, true)) return rc;
+    if (int rc = check_workspace(pl, workspace, workspace_bytes)) return rc;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (int rc = run_momentum(mats, n_mats, p, pl, workspace, st)) return rc;
+    if (p->ns_iters > 0)
+        if (int rc = run_newton_schulz(mats, n_mats, p, pl, workspace, true, st)) return rc;
+    if (int rc = run_pack(mats, n_mats, p, pl, workspace, true, st)) return rc;
+    if (int rc = run_vote(mats, n_mats, p, pl, workspace, st)) return rc;
+    if (p->post_polar_iters > 0)
+        if (int rc = run_post_polar(mats, n_mats, p, pl, workspace, st)) return rc;
+    return SIGNMUON_OK;
+}
+
+int signmuon_sign_pack(const void *u, signmuon_dtype u_dtype, int64_t n, int32_t workers,
+                       uint64_t *packed, signmuon_stream stream) {
+    if (!u || !packed || n < 1 || workers < 1) return SIGNMUON_EINVAL;
+    if (!dtype_ok(u_dtype)) return SIGNMUON_EDTYPE;
+    if (!aligned16(u) || !aligned16(packed)) return SIGNMUON_EALIGN;
+    if (n > kMaxN) return SIGNMUON_ERANGE;
+    const int64_t nw = (n + 63) / 64;
+    const int64_t bpw = (nw + sm::kPackWordsPerBlock - 1) / sm::kPackWordsPerBlock;
+    if (bpw * workers > INT32_MAX) return SIGNMUON_ERANGE;
+    sm::PackBatch b{};
+    b.nmat = 1;
+    b.workers = workers;
+    b.u_bf16 = u_dtype == SIGNMUON_BF16;
+    b.scales = nullptr;
+    b.mat[0].u = u;
+    b.mat[0].packed = packed;
+    b.mat[0].u_out = nullptr;
+    b.mat[0].n = n;
+    b.mat[0].block_begin = 0;
+    b.mat[0].blocks_per_worker = (int32_t)bpw;
+    b.mat[0].unit_begin = 0;
+    b.total_blocks = (int32_t)(bpw * workers);
+    sm::launch_sign_pack(b, static_cast<hipStream_t>(stream));
+    return last_launch();
+}
+
+int signmuon_vote_update(const uint64_t *packed, int32_t workers, int64_t n, float *weight, float eta,
+                         int8_t *vote_out, signmuon_stream stream) {
+    if (!packed || n < 1 || workers < 1 || (!weight && !vote_out)) return SIGNMUON_EINVAL;
+    if (!std::isfinite(eta)) return SIGNMUON_EINVAL;
+    if (workers > kMaxWorkers || n > kMaxN) return SIGNMUON_ERANGE;
+    if (!aligned16(packed) || (weight && !aligned16(weight)) || (vote_out && !aligned16(vote_out)))
+        return SIGNMUON_EALIGN;
+    const int64_t nw = (n + 63) / 64;
+    sm::VoteBatch b{};
+    b.nmat = 1;
+    b.workers = workers;
+    b.eta = eta;
+    b.mat[0].packed = packed;
+    b.mat[0].w = weight;
+    b.mat[0].vote = vote_out;
+    b.mat[0].v_ns = nullptr;
+    b.mat[0].nnz = nullptr;
+    b.mat[0].n = n;
+    b.mat[0].block_begin = 0;
+    b.total_blocks = (int32_t)((nw + sm::kVoteWordsPerBlock - 1) / sm::kVoteWordsPerBlock);
+    sm::launch_vote_update(b, static_cast<hipStream_t>(stream));
+    return last_launch();
+}
+
+}  // extern "C"

@@ -1,0 +1,422 @@
+// elementwise.hip -- HBM-bound kernels of the Sign-Muon step for gfx950:
+// momentum update with Frobenius partial sums, sign + 1-bit pack, majority
+// vote + weight update, and the small helpers of the post-vote polar step.
+//
+// Method: "SignMuon: Communication-Efficient Distributed Muon Optimization"
+// (gist.science, paper 2605.16311, technical summary), cited by section.
+#include "sm_internal.h"
+
+namespace sm {
+namespace {
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+
+// Round-to-nearest-even fp32 -> bf16 pattern; NaN stays a quiet NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float x) {
+    uint32_t u = __float_as_uint(x);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+__device__ __forceinline__ double wave_sum(double v) {
+    for (int off = kWave / 2; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
+    return v;
+}
+
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
+    for (int off = kWave / 2; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
+    return v;
+}
+
+// Matrix of a flat block index: the descriptors are sorted by block_begin.
+template <typename Batch>
+__device__ __forceinline__ int find_mat(const Batch &b, int blk) {
+    int mi = 0;
+    while (mi + 1 < b.nmat && blk >= b.mat[mi + 1].block_begin) ++mi;
+    return mi;
+}
+
+// ---------------------------------------------------------------------------
+// Momentum: M <- store(fmaf(beta, M, G)) in place, one fp32 fused multiply-
+// add per entry (summary §2 "Algorithmic flow", step 1; heavy-ball form is
+// the reading taken), plus the sum of squares of the stored M per block for
+// the Frobenius normalisation (summary §4 "nanoGPT": Frobenius scaling).
+// ---------------------------------------------------------------------------
+template <bool GB, bool MB>
+__device__ __forceinline__ double momentum_vec8(const MomBatch &b, const void *gp, void *mp,
+                                                int64_t e) {
+    float g[8], m[8];
+    if (GB) {
+        uint4 v = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(gp) + e);
+        uint32_t wds[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            g[2 * i] = bf16_bits_to_f32(wds[i] & 0xffffu);
+            g[2 * i + 1] = bf16_bits_to_f32(wds[i] >> 16);
+        }
+    } else {
+        const float4 *p = reinterpret_cast<const float4 *>(static_cast<const float *>(gp) + e);
+        float4 a = p[0], c = p[1];
+        g[0] = a.x; g[1] = a.y; g[2] = a.z; g[3] = a.w;
+        g[4] = c.x; g[5] = c.y; g[6] = c.z; g[7] = c.w;
+    }
+    double ss = 0.0;
+    if (MB) {
+        uint4 *p = reinterpret_cast<uint4 *>(static_cast<uint16_t *>(mp) + e);
+        uint4 v = *p;
+        uint32_t wds[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            m[2 * i] = bf16_bits_to_f32(wds[i] & 0xffffu);
+            m[2 * i + 1] = bf16_bits_to_f32(wds[i] >> 16);
+        }
+        uint32_t out[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            uint32_t lo = f32_to_bf16_bits(__builtin_fmaf(b.beta, m[2 * i], g[2 * i]));
+            uint32_t hi = f32_to_bf16_bits(__builtin_fmaf(b.beta, m[2 * i + 1], g[2 * i + 1]));
+            out[i] = lo | (hi << 16);
+            double s0 = bf16_bits_to_f32(lo), s1 = bf16_bits_to_f32(hi);
+            ss += s0 * s0;
+            ss += s1 * s1;
+        }
+        *p = make_uint4(out[0], out[1], out[2], out[3]);
+    } else {
+        float4 *p = reinterpret_cast<float4 *>(static_cast<float *>(mp) + e);
+        float4 a = p[0], c = p[1];
+        m[0] = a.x; m[1] = a.y; m[2] = a.z; m[3] = a.w;
+        m[4] = c.x; m[5] = c.y; m[6] = c.z; m[7] = c.w;
+        float y[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            y[i] = __builtin_fmaf(b.beta, m[i], g[i]);
+            double d = y[i];
+            ss += d * d;
+        }
+        p[0] = make_float4(y[0], y[1], y[2], y[3]);
+        p[1] = make_float4(y[4], y[5], y[6], y[7]);
+    }
+    return ss;
+}
+
+template <bool GB, bool MB>
+__device__ __forceinline__ double momentum_one(const MomBatch &b, const void *gp, void *mp,
+                                               int64_t e) {
+    float g = GB ? bf16_bits_to_f32(static_cast<const uint16_t *>(gp)[e])
+                 : static_cast<const float *>(gp)[e];
+    float y;
+    if (MB) {
+        uint16_t *p = static_cast<uint16_t *>(mp) + e;
+        uint32_t bits = f32_to_bf16_bits(__builtin_fmaf(b.beta, bf16_bits_to_f32(*p), g));
+        *p = (uint16_t)bits;
+        y = bf16_bits_to_f32(bits);
+    } else {
+        float *p = static_cast<float *>(mp) + e;
+        y = __builtin_fmaf(b.beta, *p, g);
+        *p = y;
+    }
+    double d = y;
+    return d * d;
+}
+
+template <bool GB, bool MB>
+__global__ __launch_bounds__(kMomThreads) void momentum_kernel(MomBatch b) {
+    const int blk = blockIdx.x;
+    const MomMat &M = b.mat[find_mat(b, blk)];
+    const int local = blk - M.block_begin;
+    const int w = local / M.blocks_per_worker;
+    const int chunk = local - w * M.blocks_per_worker;
+    const int64_t n = M.n;
+    const size_t gsz = GB ? 2 : 4, msz = MB ? 2 : 4;
+    const void *gp = static_cast<const char *>(M.g) + (size_t)w * (size_t)n * gsz;
+    void *mp = static_cast<char *>(M.m) + (size_t)w * (size_t)n * msz;
+    const int64_t begin = (int64_t)chunk * kMomChunk;
+    double ss = 0.0;
+    if ((n & 7) == 0) {
+        // 8 consecutive entries per thread and round; n % 8 == 0 keeps every
+        // worker's slice 16-byte aligned and every 8-group inside the matrix.
+#pragma unroll
+        for (int r = 0; r < kMomElemsPerThread / 8; ++r) {
+            int64_t e = begin + (int64_t)(r * kMomThreads + (int)threadIdx.x) * 8;
+            if (e < n) ss += momentum_vec8<GB, MB>(b, gp, mp, e);
+        }
+    } else {
+        for (int r = 0; r < kMomElemsPerThread; ++r) {
+            int64_t e = begin + (int64_t)r * kMomThreads + threadIdx.x;
+            if (e < n) ss += momentum_one<GB, MB>(b, gp, mp, e);
+        }
+    }
+    // Deterministic block sum: waves by shuffle, then the 4 wave sums in order.
+    __shared__ double wsum[kMomThreads / kWave];
+    ss = wave_sum(ss);
+    if ((threadIdx.x & (kWave - 1)) == 0) wsum[threadIdx.x / kWave] = ss;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        double t = 0.0;
+        for (int i = 0; i < kMomThreads / kWave; ++i) t += wsum[i];
+        b.partials[M.partial_begin + local] = t;
+    }
+}
+
+// s = 1/||M||_F and s^2 per (matrix, worker), from the block partial sums
+// added in block order (summary §2 "Communication efficiency": the
+// normalisation is local to each worker).
+__global__ void finalize_scales_kernel(MomBatch b) {
+    int u = blockIdx.x * blockDim.x + threadIdx.x;
+    if (u >= b.nmat * b.workers) return;
+    const MomMat &M = b.mat[u / b.workers];
+    const int w = u % b.workers;
+    const double *p = b.partials + M.partial_begin + (int64_t)w * M.blocks_per_worker;
+    double ss = 0.0;
+    for (int i = 0; i < M.blocks_per_worker; ++i) ss += p[i];
+    float s = 0.f, s2 = 0.f;
+    if (ss > 0.0) {
+        s = (float)(1.0 / sqrt(ss));
+        s2 = (float)(1.0 / ss);
+    }
+    b.scales[M.unit_begin + w] = make_float2(s, s2);
+}
+
+// ---------------------------------------------------------------------------
+// Sign + 1-bit pack (summary §2 "Core mechanism"; "Algorithmic flow" steps
+// 2-3): word w of a worker holds entries 64w..64w+63, bit j = (u >= 0) for
+// entry 64w + j, exactly the wave64 ballot of lane j. Each wave packs 8 words.
+// ---------------------------------------------------------------------------
+template <bool UB>
+__global__ __launch_bounds__(256) void sign_pack_kernel(PackBatch b) {
+    const int blk = blockIdx.x;
+    const PackMat &M = b.mat[find_mat(b, blk)];
+    const int local = blk - M.block_begin;
+    const int w = local / M.blocks_per_worker;
+    const int wb = local - w * M.blocks_per_worker;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int64_t n = M.n;
+    const int64_t nw = (n + 63) >> 6;
+    const int64_t word0 = (int64_t)wb * kPackWordsPerBlock + wave * kPackWordsPerWave;
+    const float s = b.scales ? b.scales[M.unit_begin + w].x : 1.0f;
+    const size_t usz = UB ? 2 : 4;
+    const char *u = static_cast<const char *>(M.u) + (size_t)w * (size_t)n * usz;
+    float vals[kPackWordsPerWave];
+#pragma unroll
+    for (int j = 0; j < kPackWordsPerWave; ++j) {
+        int64_t e = (word0 + j) * 64 + lane;
+        float v = -1.0f;  // entries past n pack as 0
+        if (e < n) {
+            v = UB ? bf16_bits_to_f32(reinterpret_cast<const uint16_t *>(u)[e])
+                   : reinterpret_cast<const float *>(u)[e];
+            if (b.scales) v = s * v;
+            if (M.u_out) M.u_out[(size_t)w * (size_t)n + e] = v;
+        }
+        vals[j] = v;
+    }
+    uint64_t mine = 0;
+#pragma unroll
+    for (int j = 0; j < kPackWordsPerWave; ++j) {
+        uint64_t bal = __ballot(vals[j] >= 0.0f);
+        if (lane == j) mine = bal;
+    }
+    if (M.packed && lane < kPackWordsPerWave && word0 + lane < nw)
+        M.packed[(size_t)w * nw + word0 + lane] = mine;
+}
+
+// ---------------------------------------------------------------------------
+// Majority vote + update (summary §2 "Core mechanism": the vote is the sign
+// of the integer sum of the workers' signs; "Algorithmic flow" step 4:
+// W <- W - eta * S-bar). With c the number of +1 bits over Mw workers the
+// sum is 2c - Mw; a tie votes 0 and leaves the entry unchanged.
+//
+// Each wave counts 64 words (4096 entries): lane l holds word l of the group
+// for every worker and adds them into NB bit-sliced counters (one counter bit
+// per plane, 64 entries per plane word), then compares the counters with the
+// two thresholds to get a plus-mask and a minus-mask per word. The masks go
+// through LDS so that W is then read and written 16 bytes per lane in
+// coalesced order.
+// ---------------------------------------------------------------------------
+template <int NB>
+__device__ __forceinline__ uint64_t counter_gt(const uint64_t (&c)[NB], int t) {
+    uint64_t gt = 0, eq = ~0ull;
+#pragma unroll
+    for (int bit = NB - 1; bit >= 0; --bit) {
+        if ((t >> bit) & 1) {
+            eq &= c[bit];
+        } else {
+            gt |= eq & c[bit];
+            eq &= ~c[bit];
+        }
+    }
+    return gt;
+}
+
+template <int NB>
+__global__ __launch_bounds__(256) void vote_update_kernel(VoteBatch b) {
+    __shared__ uint64_t plus_s[4][kVoteWordsPerWave];
+    __shared__ uint64_t minus_s[4][kVoteWordsPerWave];
+    const int blk = blockIdx.x;
+    const VoteMat &M = b.mat[find_mat(b, blk)];
+    const int local = blk - M.block_begin;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int64_t n = M.n;
+    const int64_t nw = (n + 63) >> 6;
+    const int64_t group = (int64_t)local * 4 + wave;
+    const int64_t word = group * kVoteWordsPerWave + lane;
+    const int mw = b.workers;
+
+    uint64_t c[NB];
+#pragma unroll
+    for (int i = 0; i < NB; ++i) c[i] = 0;
+    if (word < nw) {
+        const uint64_t *p = M.packed + word;
+        for (int m = 0; m < mw; ++m) {
+            uint64_t carry = p[(size_t)m * nw];
+#pragma unroll
+            for (int i = 0; i < NB; ++i) {
+                uint64_t t = c[i] & carry;
+                c[i] ^= carry;
+                carry = t;
+            }
+        }
+    }
+    // plus: 2c > mw  <=>  c > floor(mw/2);  minus: 2c < mw  <=>  !(c > ceil(mw/2) - 1)
+    uint64_t plus = counter_gt<NB>(c, mw >> 1);
+    uint64_t minus = ~counter_gt<NB>(c, ((mw + 1) >> 1) - 1);
+    if (word >= nw) {
+        plus = 0;
+        minus = 0;
+    } else if ((word + 1) * 64 > n) {
+        uint64_t valid = (1ull << (n & 63)) - 1;
+        plus &= valid;
+        minus &= valid;
+    }
+    if (M.nnz) {
+        uint32_t cnt = wave_sum_u32((uint32_t)__popcll(plus | minus));
+        if (lane == 0 && cnt) atomicAdd(M.nnz, cnt);
+    }
+    plus_s[wave][lane] = plus;
+    minus_s[wave][lane] = minus;
+    __syncthreads();
+
+    const float eta = b.eta;
+    const int64_t ebase = group * (kVoteWordsPerWave * 64);
+#pragma unroll 4
+    for (int it = 0; it < kVoteWordsPerWave / 4; ++it) {
+        const int64_t e = ebase + it * 256 + lane * 4;
+        if (e >= n) break;
+        const int wi = it * 4 + (lane >> 4);
+        const int sh = (lane & 15) * 4;
+        const uint32_t p4 = (uint32_t)(plus_s[wave][wi] >> sh) & 0xfu;
+        const uint32_t m4 = (uint32_t)(minus_s[wave][wi] >> sh) & 0xfu;
+        int v[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[j] = (int)((p4 >> j) & 1u) - (int)((m4 >> j) & 1u);
+        const bool full = e + 4 <= n;
+        if (M.w) {
+            if (full) {
+                float4 *wp = reinterpret_cast<float4 *>(M.w + e);
+                float4 x = *wp;
+                float xs[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    xs[j] = v[j] > 0 ? xs[j] - eta : (v[j] < 0 ? xs[j] + eta : xs[j]);
+                *wp = make_float4(xs[0], xs[1], xs[2], xs[3]);
+            } else {
+                for (int j = 0; j < 4 && e + j < n; ++j) {
+                    float x = M.w[e + j];
+                    M.w[e + j] = v[j] > 0 ? x - eta : (v[j] < 0 ? x + eta : x);
+                }
+            }
+        }
+        if (M.vote) {
+            if (full) {
+                uint32_t packed4 = (uint32_t)(uint8_t)(int8_t)v[0] | ((uint32_t)(uint8_t)(int8_t)v[1] << 8) |
+                                   ((uint32_t)(uint8_t)(int8_t)v[2] << 16) |
+                                   ((uint32_t)(uint8_t)(int8_t)v[3] << 24);
+                *reinterpret_cast<uint32_t *>(M.vote + e) = packed4;
+            } else {
+                for (int j = 0; j < 4 && e + j < n; ++j) M.vote[e + j] = (int8_t)v[j];
+            }
+        }
+        if (M.v_ns) {
+            if (b.v_ns_bf16) {
+                uint16_t *vp = static_cast<uint16_t *>(M.v_ns) + e;
+                for (int j = 0; j < 4 && e + j < n; ++j)
+                    vp[j] = v[j] > 0 ? 0x3f80u : (v[j] < 0 ? 0xbf80u : 0u);
+            } else {
+                float *vp = static_cast<float *>(M.v_ns) + e;
+                for (int j = 0; j < 4 && e + j < n; ++j) vp[j] = (float)v[j];
+            }
+        }
+    }
+}
+
+__global__ void zero_u32_kernel(uint32_t *p, int32_t count) {
+    int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < count) p[i] = 0;
+}
+
+// Frobenius scale of the vote: ||S-bar||_F = sqrt(nnz) exactly.
+__global__ void nnz_scales_kernel(const uint32_t *nnz, int32_t count, float2 *scales) {
+    int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= count) return;
+    double c = (double)nnz[i];
+    scales[i] = c > 0.0 ? make_float2((float)(1.0 / sqrt(c)), (float)(1.0 / c)) : make_float2(0.f, 0.f);
+}
+
+}  // namespace
+
+void launch_momentum(const MomBatch &b, hipStream_t s) {
+    dim3 grid(b.total_blocks), block(kMomThreads);
+    if (b.g_bf16 && b.m_bf16)
+        hipLaunchKernelGGL((momentum_kernel<true, true>), grid, block, 0, s, b);
+    else if (b.g_bf16)
+        hipLaunchKernelGGL((momentum_kernel<true, false>), grid, block, 0, s, b);
+    else if (b.m_bf16)
+        hipLaunchKernelGGL((momentum_kernel<false, true>), grid, block, 0, s, b);
+    else
+        hipLaunchKernelGGL((momentum_kernel<false, false>), grid, block, 0, s, b);
+}
+
+void launch_finalize_scales(const MomBatch &b, hipStream_t s) {
+    int units = b.nmat * b.workers;
+    hipLaunchKernelGGL(finalize_scales_kernel, dim3((units + 255) / 256), dim3(256), 0, s, b);
+}
+
+void launch_sign_pack(const PackBatch &b, hipStream_t s) {
+    dim3 grid(b.total_blocks), block(256);
+    if (b.u_bf16)
+        hipLaunchKernelGGL(sign_pack_kernel<true>, grid, block, 0, s, b);
+    else
+        hipLaunchKernelGGL(sign_pack_kernel<false>, grid, block, 0, s, b);
+}
+
+void launch_vote_update(const VoteBatch &b, hipStream_t s) {
+    dim3 grid(b.total_blocks), block(256);
+    const int mw = b.workers;
+#define SM_VOTE(NBITS) hipLaunchKernelGGL(vote_update_kernel<NBITS>, grid, block, 0, s, b)
+    if (mw <= 1) SM_VOTE(1);
+    else if (mw <= 3) SM_VOTE(2);
+    else if (mw <= 7) SM_VOTE(3);
+    else if (mw <= 15) SM_VOTE(4);
+    else if (mw <= 31) SM_VOTE(5);
+    else if (mw <= 63) SM_VOTE(6);
+    else if (mw <= 127) SM_VOTE(7);
+    else SM_VOTE(8);
+#undef SM_VOTE
+}
+
+void launch_zero_u32(uint32_t *p, int32_t count, hipStream_t s) {
+    if (count <= 0) return;
+    hipLaunchKernelGGL(zero_u32_kernel, dim3((count + 255) / 256), dim3(256), 0, s, p, count);
+}
+
+void launch_nnz_scales(const uint32_t *nnz, int32_t count, float2 *scales, hipStream_t s) {
+    if (count <= 0) return;
+    hipLaunchKernelGGL(nnz_scales_kernel, dim3((count + 255) / 256), dim3(256), 0, s, nnz, count,
+                       scales);
+}
+
+}  // namespace sm

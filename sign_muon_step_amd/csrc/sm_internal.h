@@ -1,0 +1,156 @@
+// sm_internal.h -- launch descriptors shared by the host API and the gfx950
+// kernels of the Sign-Muon step. Not part of the public C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sm {
+
+// Matrices per kernel launch: the descriptors travel by value in the kernel
+// arguments, which must stay well under the 4 KiB argument limit.
+constexpr int kMaxMatsPerLaunch = 48;
+
+// ---------------------------------------------------------------------------
+// Momentum + Frobenius partial sums.
+// ---------------------------------------------------------------------------
+constexpr int kMomThreads = 256;
+constexpr int kMomElemsPerThread = 32;  // 4 rounds of 8
+constexpr int kMomChunk = kMomThreads * kMomElemsPerThread;
+
+struct MomMat {
+    const void *g;          // [Mw][n] gradient
+    void *m;                // [Mw][n] momentum, in place
+    int64_t n;
+    int32_t block_begin;    // first block of this matrix within the launch
+    int32_t blocks_per_worker;
+    int32_t partial_begin;  // index of (this matrix, worker 0, chunk 0) in partials
+    int32_t unit_begin;     // index of (this matrix, worker 0) in the unit arrays
+};
+
+struct MomBatch {
+    MomMat mat[kMaxMatsPerLaunch];
+    int32_t nmat;
+    int32_t workers;
+    int32_t total_blocks;
+    float beta;
+    int32_t g_bf16;
+    int32_t m_bf16;
+    double *partials;       // sum of squares of the stored momentum, per block
+    float2 *scales;         // per unit: {s = 1/||M||_F, s^2} (0 when ||M|| = 0)
+};
+
+void launch_momentum(const MomBatch &b, hipStream_t s);
+void launch_finalize_scales(const MomBatch &b, hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// Newton-Schulz GEMMs (matrix cores).
+// ---------------------------------------------------------------------------
+enum NsEpilogue { EPI_GRAM = 0, EPI_ITER = 1, EPI_FINAL = 2, EPI_WUPD = 3 };
+
+struct NsMat {
+    const void *x;      // current iterate, worker 0; worker stride n (ns dtype)
+    void *a;            // Gram buffer, worker 0; worker stride r*r (ns dtype)
+    void *out;          // EPI_ITER: next iterate (ns dtype); EPI_FINAL: U fp32 or
+                        // nullptr; EPI_WUPD: W fp32 (no worker stride)
+    uint64_t *packed;   // EPI_FINAL fused sign+pack target or nullptr
+    int32_t R, C;
+    int32_t tile_begin;  // first tile of this matrix in the launch
+    int32_t tiles_per_worker;
+    int32_t unit_begin;  // index of (this matrix, worker 0) in scales
+    int32_t pad_;
+};
+
+struct NsBatch {
+    NsMat mat[kMaxMatsPerLaunch];
+    int32_t nmat;
+    int32_t workers;
+    int32_t total_tiles;
+    int32_t use_scales;   // iteration 0: fold s^2 (Gram) and s (product) in
+    const float2 *scales;
+    float eta;            // EPI_WUPD step size
+    int32_t pad_;
+};
+
+// Output tile of every Newton-Schulz GEMM.
+constexpr int kNsTileM = 256;
+constexpr int kNsTileN = 256;
+
+// Tiles one worker of an R x C matrix needs.
+inline int32_t ns_gram_tiles(int64_t R, int64_t C) {
+    int64_t r = R < C ? R : C;
+    int64_t t = (r + kNsTileM - 1) / kNsTileM;
+    return (int32_t)(t * (t + 1) / 2);
+}
+inline int32_t ns_product_tiles(int64_t R, int64_t C) {
+    // output rows = R, cols = C in both orientations
+    return (int32_t)(((R + kNsTileM - 1) / kNsTileM) * ((C + kNsTileN - 1) / kNsTileN));
+}
+
+// ns_bf16 selects the operand storage type; epi the epilogue.
+void launch_ns_gram(const NsBatch &b, bool ns_bf16, hipStream_t s);
+void launch_ns_product(const NsBatch &b, bool ns_bf16, NsEpilogue epi, hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// Sign + pack of a stored U, and scale + sign + pack for k = 0.
+// ---------------------------------------------------------------------------
+struct PackMat {
+    const void *u;       // [Mw][n]
+    uint64_t *packed;    // [Mw][words]
+    float *u_out;        // optional fp32 copy of the scaled value (k = 0 path)
+    int64_t n;
+    int32_t block_begin;
+    int32_t blocks_per_worker;
+    int32_t unit_begin;
+    int32_t pad_;
+};
+
+struct PackBatch {
+    PackMat mat[kMaxMatsPerLaunch];
+    int32_t nmat;
+    int32_t workers;
+    int32_t total_blocks;
+    int32_t u_bf16;
+    const float2 *scales;  // nullptr: plain sign of u; else sign of s*u
+};
+
+constexpr int kPackWordsPerWave = 8;
+constexpr int kPackWordsPerBlock = 4 * kPackWordsPerWave;  // 256 threads
+
+void launch_sign_pack(const PackBatch &b, hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// Majority vote + update.
+// ---------------------------------------------------------------------------
+constexpr int kVoteWordsPerWave = 64;                     // 4096 entries
+constexpr int kVoteWordsPerBlock = 4 * kVoteWordsPerWave;  // 256 threads
+
+struct VoteMat {
+    const uint64_t *packed;  // [Mw][words]
+    float *w;                // [n] or nullptr
+    int8_t *vote;            // [n] or nullptr
+    void *v_ns;              // [n] vote written in the NS storage type, or nullptr
+    uint32_t *nnz;           // nonzero count of the vote (added to), or nullptr
+    int64_t n;
+    int32_t block_begin;
+    int32_t pad_;
+};
+
+struct VoteBatch {
+    VoteMat mat[kMaxMatsPerLaunch];
+    int32_t nmat;
+    int32_t workers;
+    int32_t total_blocks;
+    int32_t v_ns_bf16;
+    float eta;
+    int32_t pad_;
+};
+
+void launch_vote_update(const VoteBatch &b, hipStream_t s);
+
+// Post-vote polar step helpers.
+void launch_zero_u32(uint32_t *p, int32_t count, hipStream_t s);
+// scales[unit_begin + i] = {1/sqrt(nnz[i]), 1/nnz[i]} (0 when nnz = 0)
+void launch_nnz_scales(const uint32_t *nnz, int32_t count, float2 *scales, hipStream_t s);
+
+}  // namespace sm

@@ -1,0 +1,400 @@
+"""GPU parity of the HIP path (through the C ABI) against the CPU oracle on the
+same seeded inputs.
+
+Bar: momentum, pack, vote and update bit-exact (pack/vote/update given the
+same sign inputs); the Newton-Schulz factor within 1e-5 (fp32) / 2e-2 (bf16)
+relative Frobenius error; signs agree on >= 99.9% of the entries with
+|U| >= 1e-6 max|U|, every residual disagreement reported.
+"""
+import json
+import os
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sign_muon_step_amd as sm
+import synthetic
+from gpu_util import (DEV, announce, dtype_of, make_matrix, rel_fro, run, sign_stats, to_dev,
+                      to_host)
+
+pytestmark = pytest.mark.gpu
+
+NS_TOL = {"f32": 1e-5, "bf16": 2e-2}
+ORC_DT = {"f32": oracle.F32, "bf16": oracle.BF16}
+POOL = ThreadPoolExecutor(max_workers=12)
+
+
+@pytest.fixture(autouse=True)
+def _name_the_case(request):
+    announce(f"[gpu-test] {request.node.nodeid}")
+    yield
+    torch.cuda.synchronize()
+
+
+def grads(seed, mw, R, C, scale=1.0, dist="normal"):
+    return np.stack([synthetic.random_matrix(seed * 1000 + i, (R, C), scale, dist)
+                     for i in range(mw)])
+
+
+def zeros_m(mw, R, C, mom):
+    return np.zeros((mw, R, C), np.float32 if mom == "f32" else np.uint16)
+
+
+def oracle_u(m_after, k, ns):
+    """fp64 U of each worker from the stored momentum (oracle O2 + O3)."""
+    def one(mm):
+        _, x0 = oracle.normalise(mm)
+        return oracle.newton_schulz(x0, k, ORC_DT[ns])
+    return np.stack(list(POOL.map(one, list(m_after))))
+
+
+# ---------------------------------------------------------------------------
+# momentum (bit-exact) and the k = 0 polar output U = M / ||M||_F
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("gdt,mom", [("f32", "f32"), ("f32", "bf16"), ("bf16", "bf16"),
+                                     ("bf16", "f32")])
+@pytest.mark.parametrize("shape", [(37, 53), (256, 256), (1, 9), (700, 300)])
+def test_momentum_bitexact_two_steps(gdt, mom, shape):
+    R, C = shape
+    mw = 3
+    m_host = zeros_m(mw, R, C, mom)
+    m_dev = to_dev(m_host)
+    for step in range(2):
+        g = grads(10 + step, mw, R, C)
+        if gdt == "bf16":
+            g = oracle.bf16_from_f32(g)
+        mat = sm.Matrix(grad=to_dev(g), momentum=m_dev,
+                        polar_out=torch.zeros((mw, R, C), dtype=torch.float32, device=DEV))
+        run("signmuon_momentum_ns", [mat],
+            sm.Params(workers=mw, beta=0.9, ns_iters=0, grad_dtype=dtype_of(gdt)[2],
+                      mom_dtype=dtype_of(mom)[2], ns_dtype=dtype_of(mom)[2]))
+        oracle.momentum(g, m_host, 0.9)
+        np.testing.assert_array_equal(to_host(m_dev), m_host)
+        u = to_host(mat.polar_out)
+        for w in range(mw):
+            _, x0 = oracle.normalise(m_host[w])
+            assert rel_fro(u[w], x0) < 1e-6
+
+
+def test_zero_gradient_gives_all_plus_signs():
+    """M = 0 has no direction: U = 0 and every packed bit is 1 (+1)."""
+    mw, R, C = 2, 64, 128
+    g = np.zeros((mw, R, C), np.float32)
+    for k in (0, 1, 3):
+        mat = make_matrix(g, zeros_m(mw, R, C, "f32"), np.zeros((R, C), np.float32))
+        run("signmuon_step", [mat], sm.Params(workers=mw, ns_iters=k))
+        assert not to_host(mat.polar_out).any()
+        assert (to_host(mat.packed) == np.uint64(0xFFFFFFFFFFFFFFFF)).all()
+        assert (to_host(mat.vote_out) == 1).all()
+
+
+# ---------------------------------------------------------------------------
+# sign + pack (bit-exact)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("udt", ["f32", "bf16"])
+@pytest.mark.parametrize("n,workers", [(1, 1), (63, 2), (64, 1), (65, 3), (4097, 2), (100003, 5),
+                                       (2048 * 33 + 7, 1)])
+def test_sign_pack_bitexact(udt, n, workers):
+    rng = np.random.default_rng(n)
+    u = rng.standard_normal((workers, n)).astype(np.float32)
+    u.ravel()[rng.integers(0, u.size, max(1, u.size // 50))] = 0.0
+    u.ravel()[rng.integers(0, u.size, max(1, u.size // 50))] = -0.0
+    u.ravel()[rng.integers(0, u.size, max(1, u.size // 97))] = np.nan
+    if udt == "bf16":
+        u = oracle.bf16_from_f32(u)
+    nw = sm.signmuon_packed_words(n)
+    packed = torch.full((workers, nw), -1, dtype=torch.int64, device=DEV)
+    sm.signmuon_sign_pack(to_dev(u), n, workers, packed)
+    torch.cuda.synchronize()
+    got = to_host(packed)
+    for w in range(workers):
+        np.testing.assert_array_equal(got[w], oracle.sign_pack(u[w]))
+
+
+def test_sign_pack_golden_vectors(golden_dir):
+    spec = json.load(open(os.path.join(golden_dir, "pack_vectors.json")))
+    for case in spec["cases"]:
+        vals = []
+        for v, cnt in case["runs"]:
+            x = {"nan": np.nan, "-0": -0.0}.get(v, v) if isinstance(v, str) else float(v)
+            vals += [x] * cnt
+        u = np.array(vals, np.float32)[None, :]
+        packed = torch.zeros((1, sm.signmuon_packed_words(u.size)), dtype=torch.int64, device=DEV)
+        sm.signmuon_sign_pack(to_dev(u), u.size, 1, packed)
+        torch.cuda.synchronize()
+        expect = np.array([int(h, 16) for h in case["expected_words_hex"]], np.uint64)
+        np.testing.assert_array_equal(to_host(packed)[0], expect, err_msg=case["name"])
+
+
+# ---------------------------------------------------------------------------
+# vote + update (bit-exact)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("mw", [1, 2, 3, 4, 5, 8, 10, 15, 16, 17, 31, 64, 255])
+@pytest.mark.parametrize("n", [1, 100, 4096, 4096 * 4 + 37, 300001])
+def test_vote_update_bitexact(mw, n):
+    rng = np.random.default_rng(mw * 7 + n)
+    nw = (n + 63) // 64
+    bits = rng.integers(0, 2, (mw, nw * 64), dtype=np.uint8)
+    bits[:, n:] = 0
+    packed = np.packbits(bits, axis=1, bitorder="little").view(np.uint64).reshape(mw, nw)
+    w0 = rng.standard_normal(n).astype(np.float32) * np.float32(0.02)
+    eta = 1e-3
+    w_dev = to_dev(w0)
+    vote_dev = torch.zeros(n, dtype=torch.int8, device=DEV)
+    sm.signmuon_vote_update(to_dev(packed), mw, n, w_dev, eta, vote_dev)
+    torch.cuda.synchronize()
+    w_ref = w0.copy()
+    vote_ref = oracle.vote_update(packed, w_ref, eta)
+    np.testing.assert_array_equal(to_host(vote_dev), vote_ref)
+    np.testing.assert_array_equal(to_host(w_dev), w_ref)
+
+
+def test_vote_only_and_update_only():
+    rng = np.random.default_rng(5)
+    mw, n = 6, 5000
+    nw = (n + 63) // 64
+    bits = rng.integers(0, 2, (mw, nw * 64), dtype=np.uint8)
+    bits[:, n:] = 0
+    packed = np.packbits(bits, axis=1, bitorder="little").view(np.uint64).reshape(mw, nw)
+    w0 = rng.standard_normal(n).astype(np.float32)
+    w_ref = w0.copy()
+    vote_ref = oracle.vote_update(packed, w_ref, 0.5)
+    vote_dev = torch.zeros(n, dtype=torch.int8, device=DEV)
+    sm.signmuon_vote_update(to_dev(packed), mw, n, None, 0.5, vote_dev)
+    w_dev = to_dev(w0)
+    sm.signmuon_vote_update(to_dev(packed), mw, n, w_dev, 0.5, None)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(to_host(vote_dev), vote_ref)
+    np.testing.assert_array_equal(to_host(w_dev), w_ref)
+
+
+def test_vote_worked_example_from_pages(golden_dir):
+    spec = json.load(open(os.path.join(golden_dir, "vote_worked_example.json")))
+    for case in spec["cases"]:
+        mw, plus = case["workers"], case["plus_votes"]
+        packed = np.zeros((mw, 1), np.uint64)
+        packed[:plus, 0] = 1
+        w = to_dev(np.zeros(1, np.float32))
+        vote = torch.zeros(1, dtype=torch.int8, device=DEV)
+        sm.signmuon_vote_update(to_dev(packed), mw, 1, w, 1.0, vote)
+        torch.cuda.synchronize()
+        assert int(to_host(vote)[0]) == case["expected_vote"]
+        assert float(to_host(w)[0]) == -float(case["expected_vote"])
+
+
+# ---------------------------------------------------------------------------
+# Newton-Schulz factor (tolerance + sign agreement)
+# ---------------------------------------------------------------------------
+NS_CASES = ([("f32", s, k) for s in [(256, 256), (300, 700), (700, 300), (64, 576), (513, 260),
+                                      (130, 258), (1, 300), (300, 1), (1, 1)] for k in (1, 2, 5)]
+            + [("bf16", s, k) for s in [(768, 768), (384, 1024), (1024, 384), (300, 704),
+                                       (704, 300), (256, 520), (200, 333)] for k in (1, 2, 5)])
+
+
+@pytest.mark.parametrize("ns,shape,k", NS_CASES)
+def test_newton_schulz_parity(ns, shape, k):
+    R, C = shape
+    mw = 2
+    g = grads(77 + R + C, mw, R, C, 1e-3)
+    m_host = zeros_m(mw, R, C, ns)
+    mat = sm.Matrix(grad=to_dev(g), momentum=to_dev(m_host),
+                    polar_out=torch.zeros((mw, R, C), dtype=torch.float32, device=DEV))
+    run("signmuon_momentum_ns", [mat],
+        sm.Params(workers=mw, ns_iters=k, mom_dtype=dtype_of(ns)[2], ns_dtype=dtype_of(ns)[2]))
+    oracle.momentum(g, m_host, 0.9)
+    np.testing.assert_array_equal(to_host(mat.momentum), m_host)
+    u_ref = oracle_u(m_host, k, ns)
+    u = to_host(mat.polar_out)
+    for w in range(mw):
+        err = rel_fro(u[w], u_ref[w])
+        agree, bad, cnt = sign_stats(u[w], u_ref[w])
+        announce(f"  {ns} {shape} k={k} worker {w}: rel_fro={err:.3e} sign agreement "
+                 f"{agree:.6f} ({bad} of {cnt} differ)")
+        assert err <= NS_TOL[ns]
+        assert agree >= 0.999
+
+
+@pytest.mark.parametrize("ns", ["f32", "bf16"])
+def test_newton_schulz_grouped_launch_matches_single(ns):
+    """Several matrices and workers in one call give the same bits as each
+    matrix alone (no cross-talk between the tiles of a grouped launch)."""
+    shapes = [(256, 512), (512, 256), (96, 96), (300, 704)]
+    mw, k = 3, 2
+    gs = [grads(200 + i, mw, R, C, 1e-3) for i, (R, C) in enumerate(shapes)]
+    params = sm.Params(workers=mw, ns_iters=k, mom_dtype=dtype_of(ns)[2], ns_dtype=dtype_of(ns)[2])
+    together = [make_matrix(g, zeros_m(mw, *g.shape[1:], ns), np.zeros(g.shape[1:], np.float32))
+                for g in gs]
+    run("signmuon_step", together, params)
+    for g, t in zip(gs, together):
+        alone = make_matrix(g, zeros_m(mw, *g.shape[1:], ns), np.zeros(g.shape[1:], np.float32))
+        run("signmuon_step", [alone], params)
+        np.testing.assert_array_equal(to_host(alone.polar_out), to_host(t.polar_out))
+        np.testing.assert_array_equal(to_host(alone.packed), to_host(t.packed))
+        np.testing.assert_array_equal(to_host(alone.weight), to_host(t.weight))
+
+
+# ---------------------------------------------------------------------------
+# whole step on the small workloads
+# ---------------------------------------------------------------------------
+def check_step(wl: synthetic.Workload, steps=1, matrices=None, label=""):
+    idx = list(range(len(wl.shapes))) if matrices is None else matrices
+    mom_np, _, mom_code = dtype_of(wl.mom_dtype)
+    ns_code = dtype_of(wl.ns_dtype)[2]
+    params = sm.Params(workers=wl.workers, beta=wl.beta, eta=wl.eta, ns_iters=wl.ns_iters,
+                       post_polar_iters=wl.post_polar_iters, mom_dtype=mom_code, ns_dtype=ns_code)
+    host = {j: (np.zeros((wl.workers,) + wl.shapes[j], mom_np), synthetic.initial_weight(wl, j))
+            for j in idx}
+    dev = {j: (to_dev(host[j][0]), to_dev(host[j][1])) for j in idx}
+    for t in range(steps):
+        gs = dict(zip(idx, POOL.map(lambda j: synthetic.gradients(wl, j, t), idx)))
+        mats = []
+        for j in idx:
+            R, C = wl.shapes[j]
+            mats.append(sm.Matrix(
+                grad=to_dev(gs[j]), momentum=dev[j][0], weight=dev[j][1],
+                packed=torch.zeros((wl.workers, sm.signmuon_packed_words(R * C)), dtype=torch.int64,
+                                   device=DEV),
+                polar_out=torch.zeros((wl.workers, R, C), dtype=torch.float32, device=DEV),
+                vote_out=torch.zeros((R, C), dtype=torch.int8, device=DEV)))
+        run("signmuon_step", mats, params)
+        for j, mat in zip(idx, mats):
+            m_host, w_host = host[j]
+            oracle.momentum(gs[j], m_host, wl.beta)
+            np.testing.assert_array_equal(to_host(mat.momentum), m_host, err_msg=f"M {j} step {t}")
+            u = to_host(mat.polar_out)
+            u_ref = oracle_u(m_host, wl.ns_iters, wl.ns_dtype)
+            packed = to_host(mat.packed)
+            for w in range(wl.workers):
+                np.testing.assert_array_equal(packed[w], oracle.sign_pack(u[w]),
+                                              err_msg=f"pack {j} worker {w}")
+                err = rel_fro(u[w], u_ref[w])
+                agree, bad, cnt = sign_stats(u[w], u_ref[w])
+                announce(f"  {label} step {t} matrix {j} {wl.shapes[j]} worker {w}: rel_fro={err:.3e}"
+                         f" sign agreement {agree:.6f} ({bad} of {cnt} differ)")
+                assert err <= NS_TOL[wl.ns_dtype]
+                assert agree >= 0.999
+            # vote + update given the GPU's packed signs: bit-exact
+            vote = oracle.vote_update(packed, w_host, wl.eta)
+            np.testing.assert_array_equal(to_host(mat.vote_out), vote, err_msg=f"vote {j}")
+            np.testing.assert_array_equal(to_host(mat.weight), w_host, err_msg=f"W {j}")
+
+
+def test_step_square256_workload():
+    check_step(synthetic.WORKLOADS["square256_mw4_k1"], steps=3, label="square256")
+
+
+def test_step_resnet50_four_shapes_k1():
+    check_step(synthetic.WORKLOADS["resnet50_4shapes_mw4_k1"], steps=2, label="resnet50 k1")
+
+
+def test_step_resnet50_k5_small_shapes():
+    check_step(synthetic.WORKLOADS["resnet50_4shapes_mw4_k5"], steps=1, matrices=[0, 1],
+               label="resnet50 k5")
+
+
+def test_step_resnet50_all_convs_subset():
+    """Ragged shapes (64 x 147: no fused pack) next to regular ones."""
+    check_step(synthetic.WORKLOADS["resnet50_all_convs_mw4_k1"], steps=1,
+               matrices=[0, 1, 2, 3, 5, 8], label="resnet50 all")
+
+
+def test_step_gpt2_shapes_mw16_k5_one_layer():
+    """Student-t gradients, 16 workers (ties), 5 iterations, bf16: one layer."""
+    check_step(synthetic.WORKLOADS["gpt2s_mw16_k5_t3"].with_(workers=4), steps=1,
+               matrices=[1], label="gpt2 k5")
+
+
+def test_step_is_deterministic():
+    wl = synthetic.WORKLOADS["gpt2s_mw8_k1"]
+    shapes = [(768, 768), (3072, 768)]
+    outs = []
+    for _ in range(2):
+        mats = []
+        for j, (R, C) in enumerate(shapes):
+            g = grads(300 + j, 4, R, C, 1e-3)
+            mats.append(make_matrix(g, zeros_m(4, R, C, "bf16"), np.zeros((R, C), np.float32)))
+        run("signmuon_step", mats, sm.Params(workers=4, ns_iters=2, mom_dtype=sm.BF16,
+                                             ns_dtype=sm.BF16))
+        outs.append([(to_host(m.polar_out), to_host(m.packed), to_host(m.weight)) for m in mats])
+    for a, b in zip(*outs):
+        for x, y in zip(a, b):
+            np.testing.assert_array_equal(x, y)
+    del wl
+
+
+# ---------------------------------------------------------------------------
+# optional post-vote polar step
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("ns", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", [(256, 512), (512, 256), (100, 130)])
+def test_post_polar_step(ns, shape):
+    R, C = shape
+    mw, k, kp, eta = 4, 1, 2, 1e-3
+    g = grads(400 + R, mw, R, C, 1e-3, "student_t3")
+    w0 = synthetic.random_matrix(401, (R, C), 0.02)
+    mat = make_matrix(g, zeros_m(mw, R, C, ns), w0)
+    run("signmuon_step", [mat], sm.Params(workers=mw, ns_iters=k, post_polar_iters=kp,
+                                          mom_dtype=dtype_of(ns)[2], ns_dtype=dtype_of(ns)[2]))
+    packed = to_host(mat.packed)
+    w_tmp = w0.copy()
+    vote = oracle.vote_update(packed, w_tmp, eta)  # the vote of the GPU's own signs
+    np.testing.assert_array_equal(to_host(mat.vote_out), vote)
+    w_ref = w0.copy()
+    nnz = oracle.post_polar(vote, w_ref, eta, kp, ORC_DT[ns])
+    assert nnz > 0
+    y_gpu = (to_host(mat.weight).astype(np.float64) - w0) / -eta
+    y_ref = (w_ref.astype(np.float64) - w0) / -eta
+    err = rel_fro(y_gpu, y_ref)
+    announce(f"  post-polar {ns} {shape}: rel_fro(Y) = {err:.3e}")
+    assert err <= NS_TOL[ns] + 1e-4  # W's own fp32 rounding adds ~|W| ulp / eta
+
+
+# ---------------------------------------------------------------------------
+# the GPT-2 small workload at full size (84.9M parameters, 8 workers)
+# ---------------------------------------------------------------------------
+def test_gpt2_small_full_size_sampled():
+    wl = synthetic.WORKLOADS["gpt2s_mw8_k1"]
+    mw = wl.workers
+    idx = list(range(len(wl.shapes)))
+    gs = list(POOL.map(lambda j: synthetic.gradients(wl, j, 0), idx))
+    ws_host = [synthetic.initial_weight(wl, j) for j in idx]
+    mats = []
+    for j, (R, C) in enumerate(wl.shapes):
+        mats.append(sm.Matrix(
+            grad=to_dev(gs[j]), momentum=torch.zeros((mw, R, C), dtype=torch.bfloat16, device=DEV),
+            weight=to_dev(ws_host[j]),
+            packed=torch.zeros((mw, sm.signmuon_packed_words(R * C)), dtype=torch.int64, device=DEV),
+            polar_out=torch.zeros((mw, R, C), dtype=torch.float32, device=DEV) if j < 4 else None,
+            vote_out=None))
+    announce("  full-size step: launching")
+    run("signmuon_step", mats, sm.Params(workers=mw, beta=wl.beta, eta=wl.eta, ns_iters=1,
+                                         mom_dtype=sm.BF16, ns_dtype=sm.BF16))
+    rng = np.random.default_rng(0)
+    for j, mat in enumerate(mats):
+        R, C = wl.shapes[j]
+        m_ref = np.zeros((mw, R, C), np.uint16)
+        oracle.momentum(gs[j], m_ref, wl.beta)
+        m_gpu = to_host(mat.momentum)
+        np.testing.assert_array_equal(m_gpu, m_ref, err_msg=f"momentum {j}")
+        packed = to_host(mat.packed)
+        if j < 4:  # the first layer's four shapes: sampled U entries and the fused pack
+            u = to_host(mat.polar_out)
+            for w in (0, mw - 1):
+                np.testing.assert_array_equal(packed[w], oracle.sign_pack(u[w]))
+                _, x0 = oracle.normalise(m_ref[w])
+                ri = rng.integers(0, R, 96)
+                ci = rng.integers(0, C, 96)
+                ref = oracle.ns1_entries(x0, oracle.BF16, ri, ci)
+                got = u[w][ri, ci].astype(np.float64)
+                scale = np.sqrt(np.mean(u[w].astype(np.float64) ** 2))
+                dev_rel = np.abs(got - ref).max() / scale
+                agree = np.mean((got >= 0) == (ref >= 0))
+                announce(f"  gpt2 full matrix {j} {wl.shapes[j]} worker {w}: max|dU|/rms(U) = "
+                         f"{dev_rel:.3e}, sampled sign agreement {agree:.4f}")
+                assert dev_rel <= 2e-2
+        w_ref = ws_host[j].copy()
+        oracle.vote_update(packed, w_ref, wl.eta, want_vote=False)
+        np.testing.assert_array_equal(to_host(mat.weight), w_ref, err_msg=f"W {j}")
