@@ -1,0 +1,260 @@
+#!/usr/bin/env python3
+"""Throughput of the Sign-Muon optimizer step on one MI355X.
+
+A step is one call of signmuon_step: every worker's momentum update,
+Frobenius normalisation, Newton-Schulz iterations, sign and 1-bit packing,
+then the majority vote and the weight update, for every matrix of the
+workload. Inputs are seeded synthetic gradients already resident in HBM.
+
+Default workload: GPT-2 small (nanoGPT, 124M) weight matrices -- 12 layers of
+768x2304, 768x768, 768x3072, 3072x768 (84.9M parameters) -- with 8 workers,
+bf16 momentum and Newton-Schulz operands, fp32 weights, 1 iteration.
+
+Prints one JSON line: params/s (each parameter counted once per step), the
+per-kernel timing measured with HIP events between the library's launches
+inside the timed region, the dominant kernel's roofline, and the CPU oracle
+timed on a bounded sample of the same workload on this host.
+"""
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+from concurrent.futures import ThreadPoolExecutor
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "Sign-Muon params/s per step at 1 GPU; NS MFMA util %; vote+update HBM GB/s"
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+PEAK_BF16_TFLOPS = 2500.0      # dense MFMA
+PEAK_FP32_TFLOPS = 157.3
+
+
+def log(msg):
+    sys.stderr.write(msg + "\n")
+    sys.stderr.flush()
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="gpt2s_mw8_k1")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="run one plain copy kernel of this size first (counter calibration)")
+    return ap.parse_args()
+
+
+class Hip:
+    """Event calls of the HIP runtime (events must live on the library's stream)."""
+
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def event(self):
+        e = ctypes.c_void_p()
+        if self.lib.hipEventCreate(ctypes.byref(e)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        return e.value
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        if self.lib.hipEventElapsedTime(ctypes.byref(ms), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def destroy(self, e):
+        self.lib.hipEventDestroy(e)
+
+
+def work_per_kind(wl):
+    """Algorithmic work of each kernel kind in one step: flops for the
+    Newton-Schulz GEMMs, HBM bytes for the streaming kernels."""
+    s_g = 4 if wl.grad_dtype == "f32" else 2
+    s_m = 4 if wl.mom_dtype == "f32" else 2
+    mw, k = wl.workers, wl.ns_iters
+    n = wl.params
+    gram = sum(mw * min(R, C) ** 2 * max(R, C) for R, C in wl.shapes) * k
+    prod = sum(mw * 2 * min(R, C) ** 2 * max(R, C) for R, C in wl.shapes) * k
+    unfused = sum(R * C for R, C in wl.shapes if C % 64 != 0) if k > 0 else n
+    return {
+        "momentum": ("hbm", mw * n * (s_g + 2 * s_m)),
+        "ns_gram": ("mfma", gram),
+        "ns_product": ("mfma", prod),
+        "sign_pack": ("hbm", mw * unfused * (4 + 1 / 8)),
+        "vote_update": ("hbm", n * (mw / 8 + 8)),
+    }
+
+
+def cpu_baseline(wl, j=1):
+    """The oracle, single-threaded, on one matrix of the workload with all
+    workers: one full step (momentum, normalisation, Newton-Schulz, sign/pack,
+    vote, update)."""
+    import numpy as np
+
+    import oracle
+    import synthetic
+    R, C = wl.shapes[j]
+    g = synthetic.gradients(wl, j, 0)
+    m = np.zeros((wl.workers, R, C), np.uint16 if wl.mom_dtype == "bf16" else np.float32)
+    w = synthetic.initial_weight(wl, j)
+    ns = oracle.BF16 if wl.ns_dtype == "bf16" else oracle.F32
+    t0 = time.perf_counter()
+    oracle.step_matrix(g, m, w, wl.beta, wl.eta, wl.ns_iters, ns, post_k=wl.post_polar_iters)
+    dt = time.perf_counter() - t0
+    return {"value": R * C / dt, "unit": "params/s", "cores": 1, "kind": "oracle",
+            "sample": f"{wl.name} matrix {j} ({R}x{C}), all {wl.workers} workers, one full step; "
+                      f"{dt:.2f} s single-threaded on this host's CPU"}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE {world}).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import sign_muon_step_amd as sm
+    import synthetic
+
+    wl = synthetic.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    code = {"f32": sm.F32, "bf16": sm.BF16}
+    mom_t = torch.bfloat16 if wl.mom_dtype == "bf16" else torch.float32
+
+    log(f"[bench] generating {wl.name}: {len(wl.shapes)} matrices, {wl.params} params, "
+        f"{wl.workers} workers")
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(max_workers=16) as ex:
+        grads = list(ex.map(lambda j: synthetic.gradients(wl, j, 0), range(len(wl.shapes))))
+    mats = []
+    for j, (R, C) in enumerate(wl.shapes):
+        mats.append(sm.Matrix(
+            grad=torch.from_numpy(grads[j]).to(dev),
+            momentum=torch.zeros((wl.workers, R, C), dtype=mom_t, device=dev),
+            packed=torch.zeros((wl.workers, sm.signmuon_packed_words(R * C)), dtype=torch.int64,
+                               device=dev),
+            weight=torch.from_numpy(synthetic.initial_weight(wl, j)).to(dev)))
+        grads[j] = None
+    params = sm.Params(workers=wl.workers, beta=wl.beta, eta=wl.eta, ns_iters=wl.ns_iters,
+                       post_polar_iters=wl.post_polar_iters, grad_dtype=code[wl.grad_dtype],
+                       mom_dtype=code[wl.mom_dtype], ns_dtype=code[wl.ns_dtype])
+    ws = sm.workspace_tensor(mats, params, dev)
+    torch.cuda.synchronize()
+    log(f"[bench] inputs resident in HBM after {time.perf_counter() - t0:.1f} s; workspace "
+        f"{0 if ws is None else ws.numel() / 2**20:.0f} MiB")
+
+    if args.calibrate_copy_mib:
+        src = torch.ones(args.calibrate_copy_mib << 18, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        log(f"[bench] calibration copy kernel: {args.calibrate_copy_mib} MiB read, "
+            f"{args.calibrate_copy_mib} MiB written")
+        del src, dst
+
+    hip = Hip()
+    cap = 64
+    traces = [sm.Trace([hip.event() for _ in range(cap)]) for _ in range(args.steps)]
+
+    for _ in range(args.warmup):
+        sm.signmuon_step(mats, params, ws)
+    torch.cuda.synchronize()
+    log(f"[bench] warmup {args.warmup} steps done; timing {args.steps} steps")
+
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        sm.signmuon_step_traced(mats, params, ws, traces[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = 1e3 * wall / args.steps
+
+    # per-kernel time per step, from the events around each launch
+    per_kind_ms = {}
+    for tr in traces:
+        kinds = tr.kinds()
+        if tr.launches + 1 > cap:
+            raise RuntimeError("trace capacity too small")
+        evs = list(tr._events)
+        for i, kd in enumerate(kinds):
+            name = sm.KERNEL_KINDS[kd]
+            per_kind_ms[name] = per_kind_ms.get(name, 0.0) + hip.elapsed_ms(evs[i], evs[i + 1])
+    per_kind_ms = {k: v / args.steps for k, v in per_kind_ms.items()}
+    launches = traces[0].launches
+    for tr in traces:
+        for e in list(tr._events):
+            hip.destroy(e)
+
+    work = work_per_kind(wl)
+    mfma_peak = PEAK_BF16_TFLOPS if wl.ns_dtype == "bf16" else PEAK_FP32_TFLOPS
+    kernels = {}
+    for name, ms in per_kind_ms.items():
+        entry = {"ms": round(ms, 5)}
+        if name in work and work[name][1] > 0:
+            bound, amount = work[name]
+            if bound == "hbm":
+                ach = amount / (ms * 1e-3) / 1e9
+                entry.update(bound="hbm", achieved=round(ach, 1), unit="GB/s",
+                             frac=round(ach / PEAK_HBM_GBS, 4), algorithmic_bytes=int(amount))
+            else:
+                ach = amount / (ms * 1e-3) / 1e12
+                entry.update(bound="mfma", achieved=round(ach, 1), unit="TFLOP/s",
+                             frac=round(ach / mfma_peak, 4), algorithmic_flops=int(amount))
+        kernels[name] = entry
+    dominant = max((k for k in kernels if "bound" in kernels[k]), key=lambda k: kernels[k]["ms"])
+    d = kernels[dominant]
+    roofline = {"bound": d["bound"], "achieved": d["achieved"],
+                "peak": PEAK_HBM_GBS if d["bound"] == "hbm" else mfma_peak, "unit": d["unit"],
+                "frac": d["frac"], "traffic": None, "kernel": dominant}
+    ns_ms = per_kind_ms.get("ns_gram", 0.0) + per_kind_ms.get("ns_product", 0.0)
+    ns_flops = work["ns_gram"][1] + work["ns_product"][1]
+    ns_util = 100.0 * ns_flops / (ns_ms * 1e-3) / (mfma_peak * 1e12) if ns_ms > 0 else None
+    vote_gbs = kernels.get("vote_update", {}).get("achieved")
+
+    base = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a bounded sample")
+        base = cpu_baseline(wl)
+
+    params_per_s = wl.params / (ms_per_step * 1e-3)
+    out = {
+        "metric": METRIC, "value": round(params_per_s, 1), "unit": "params/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": wl.ns_dtype, "data": "synthetic",
+        "config": {"workload": wl.name, "description": wl.description,
+                   "matrices": len(wl.shapes), "params": wl.params, "workers": wl.workers,
+                   "ns_iters": wl.ns_iters, "post_polar_iters": wl.post_polar_iters,
+                   "grad_dtype": wl.grad_dtype, "momentum_dtype": wl.mom_dtype,
+                   "ns_dtype": wl.ns_dtype, "weight_dtype": "f32"},
+        "steps_per_s": round(1e3 / ms_per_step, 2),
+        "worker_params_per_s": round(params_per_s * wl.workers, 1),
+        "ns_mfma_util_pct": None if ns_util is None else round(ns_util, 2),
+        "vote_update_hbm_gbs": vote_gbs,
+        "kernels_ms_per_step": kernels,
+        "launches_per_step": launches,
+        "roofline": roofline,
+        "cpu_baseline": base,
+    }
+    log("[bench] " + ", ".join(f"{k} {v['ms']:.3f} ms" + (f" ({v['frac'] * 100:.1f}% of "
+                                                          f"{v['bound']})" if "frac" in v else "")
+                               for k, v in kernels.items()))
+    print(json.dumps(out), flush=True)
+    del np
+
+
+if __name__ == "__main__":
+    main()

@@ -156,6 +156,34 @@ int signmuon_vote_update(const uint64_t *packed, int32_t workers, int64_t n, flo
 int signmuon_step(const signmuon_matrix *mats, int32_t n_mats, const signmuon_params *p,
                   void *workspace, size_t workspace_bytes, signmuon_stream stream);
 
+/* Kernel kinds reported by signmuon_step_traced, one per launch. */
+enum {
+    SIGNMUON_K_MOMENTUM = 1, /* momentum update + Frobenius partial sums */
+    SIGNMUON_K_SCALES = 2,   /* 1/||M||_F per (matrix, worker) */
+    SIGNMUON_K_GRAM = 3,     /* Newton-Schulz Gram matrix */
+    SIGNMUON_K_PRODUCT = 4,  /* Newton-Schulz product (+ fused sign/pack on the last) */
+    SIGNMUON_K_PACK = 5,     /* standalone sign + pack */
+    SIGNMUON_K_VOTE = 6,     /* majority vote + update */
+    SIGNMUON_K_AUX = 7       /* post-vote polar step bookkeeping */
+};
+
+/* Instrumentation for stage timing: events[0] (a hipEvent_t created by the
+ * caller) is recorded on the stream before the first launch and events[i+1]
+ * after launch i, while i + 1 < capacity; kinds[i] receives launch i's kind.
+ * launches receives the number of launches the call made. */
+typedef struct {
+    void **events;      /* hipEvent_t[capacity] */
+    int32_t capacity;
+    int32_t *kinds;     /* [capacity - 1] */
+    int32_t launches;   /* out */
+} signmuon_trace;
+
+/* signmuon_step with every kernel launch bracketed by trace events (same
+ * arguments, same results). trace may be NULL. */
+int signmuon_step_traced(const signmuon_matrix *mats, int32_t n_mats, const signmuon_params *p,
+                         void *workspace, size_t workspace_bytes, signmuon_stream stream,
+                         signmuon_trace *trace);
+
 /* ceil(n / 64): packed words per worker for n entries (0 for n <= 0). */
 size_t signmuon_packed_words(int64_t n);
 

@@ -47,6 +47,14 @@ class _Params(ctypes.Structure):
                 ("ns_dtype", ctypes.c_int)]
 
 
+class _Trace(ctypes.Structure):
+    _fields_ = [("events", ctypes.POINTER(ctypes.c_void_p)), ("capacity", ctypes.c_int32),
+                ("kinds", ctypes.POINTER(ctypes.c_int32)), ("launches", ctypes.c_int32)]
+
+
+KERNEL_KINDS = {1: "momentum", 2: "scales", 3: "ns_gram", 4: "ns_product", 5: "sign_pack",
+                6: "vote_update", 7: "aux"}
+
 _lib = None
 
 
@@ -65,6 +73,8 @@ def library() -> ctypes.CDLL:
     lib.signmuon_momentum_ns.argtypes = [mp, i32, pp, vp, ctypes.c_size_t, vp]
     lib.signmuon_step.restype = ctypes.c_int
     lib.signmuon_step.argtypes = [mp, i32, pp, vp, ctypes.c_size_t, vp]
+    lib.signmuon_step_traced.restype = ctypes.c_int
+    lib.signmuon_step_traced.argtypes = [mp, i32, pp, vp, ctypes.c_size_t, vp, ctypes.POINTER(_Trace)]
     lib.signmuon_sign_pack.restype = ctypes.c_int
     lib.signmuon_sign_pack.argtypes = [vp, ctypes.c_int, i64, i32, vp, vp]
     lib.signmuon_vote_update.restype = ctypes.c_int
@@ -184,6 +194,34 @@ def signmuon_step(mats: Sequence[Matrix], params: Params, workspace: Optional[to
     nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(library().signmuon_step(arr, len(mats), ctypes.byref(p), _ptr(workspace), nbytes,
                                    _stream(stream)))
+
+
+class Trace:
+    """Per-launch timing events for signmuon_step_traced. ``events`` are raw
+    hipEvent_t handles created by the caller (capacity = len(events))."""
+
+    def __init__(self, events: Sequence[int]):
+        self.capacity = len(events)
+        self._events = (ctypes.c_void_p * self.capacity)(*events)
+        self._kinds = (ctypes.c_int32 * max(1, self.capacity - 1))()
+        self.struct = _Trace(self._events, self.capacity, self._kinds, 0)
+
+    @property
+    def launches(self) -> int:
+        return int(self.struct.launches)
+
+    def kinds(self):
+        n = min(self.launches, self.capacity - 1)
+        return [int(self._kinds[i]) for i in range(n)]
+
+
+def signmuon_step_traced(mats: Sequence[Matrix], params: Params, workspace: Optional[torch.Tensor],
+                         trace: Optional[Trace], stream=None) -> None:
+    arr, p = _marshal(mats, params)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(library().signmuon_step_traced(arr, len(mats), ctypes.byref(p), _ptr(workspace), nbytes,
+                                          _stream(stream),
+                                          ctypes.byref(trace.struct) if trace else None))
 
 
 def signmuon_sign_pack(u: torch.Tensor, n: int, workers: int, packed: torch.Tensor,

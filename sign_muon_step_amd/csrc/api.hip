@@ -34,6 +34,30 @@ int hip_status(hipError_t e) {
 
 inline int last_launch() { return hip_status(hipGetLastError()); }
 
+// Optional per-launch event recording (signmuon_step_traced).
+struct Tracer {
+    signmuon_trace *t = nullptr;
+    hipStream_t st = nullptr;
+    int begin() {
+        if (!t) return SIGNMUON_OK;
+        t->launches = 0;
+        if (t->events && t->capacity > 0)
+            return hip_status(hipEventRecord(static_cast<hipEvent_t>(t->events[0]), st));
+        return SIGNMUON_OK;
+    }
+    // Check the launch just made, then record its event.
+    int after(int kind) {
+        if (int rc = last_launch()) return rc;
+        if (!t) return SIGNMUON_OK;
+        const int32_t i = t->launches++;
+        if (t->events && i + 1 < t->capacity) {
+            if (t->kinds) t->kinds[i] = kind;
+            return hip_status(hipEventRecord(static_cast<hipEvent_t>(t->events[i + 1]), st));
+        }
+        return SIGNMUON_OK;
+    }
+};
+
 struct MatPlan {
     int64_t R, C, n, r, nw;
     int32_t mom_bpw;        // momentum blocks per worker
@@ -155,7 +179,7 @@ T *ws_at(void *ws, size_t off) {
 // Launch sequence shared by signmuon_momentum_ns and signmuon_step.
 // ---------------------------------------------------------------------------
 int run_momentum(const signmuon_matrix *mats, int32_t n_mats, const signmuon_params *p,
-                 const Plan &pl, void *ws, hipStream_t st) {
+                 const Plan &pl, void *ws, hipStream_t st, Tracer &tr) {
     for (int32_t c0 = 0; c0 < n_mats; c0 += sm::kMaxMatsPerLaunch) {
         const int32_t cn = n_mats - c0 < sm::kMaxMatsPerLaunch ? n_mats - c0 : sm::kMaxMatsPerLaunch;
         sm::MomBatch b{};
@@ -182,9 +206,9 @@ int run_momentum(const signmuon_matrix *mats, int32_t n_mats, const signmuon_par
         if (blocks > INT32_MAX) return SIGNMUON_ERANGE;
         b.total_blocks = (int32_t)blocks;
         sm::launch_momentum(b, st);
-        if (int rc = last_launch()) return rc;
+        if (int rc = tr.after(SIGNMUON_K_MOMENTUM)) return rc;
         sm::launch_finalize_scales(b, st);
-        if (int rc = last_launch()) return rc;
+        if (int rc = tr.after(SIGNMUON_K_SCALES)) return rc;
     }
     return SIGNMUON_OK;
 }
@@ -193,7 +217,7 @@ int run_momentum(const signmuon_matrix *mats, int32_t n_mats, const signmuon_par
 // last product's epilogue: EPI_FINAL writes U (polar_out or scratch) and, for
 // step, the fused packed signs.
 int run_newton_schulz(const signmuon_matrix *mats, int32_t n_mats, const signmuon_params *p,
-                      const Plan &pl, void *ws, bool step, hipStream_t st) {
+                      const Plan &pl, void *ws, bool step, hipStream_t st, Tracer &tr) {
     const int k = p->ns_iters;
     const bool bf16 = p->ns_dtype == SIGNMUON_BF16;
     const float2 *scales = ws_at<float2>(ws, pl.off_scales);
@@ -238,7 +262,7 @@ int run_newton_schulz(const signmuon_matrix *mats, int32_t n_mats, const signmuo
                     sm::launch_ns_gram(b, bf16, st);
                 else
                     sm::launch_ns_product(b, bf16, last ? sm::EPI_FINAL : sm::EPI_ITER, st);
-                if (int rc = last_launch()) return rc;
+                if (int rc = tr.after(pass == 0 ? SIGNMUON_K_GRAM : SIGNMUON_K_PRODUCT)) return rc;
             }
         }
     }
@@ -248,7 +272,7 @@ int run_newton_schulz(const signmuon_matrix *mats, int32_t n_mats, const signmuo
 // Sign + pack from a stored value: the scaled momentum (k = 0) or a U that the
 // last product could not pack itself.
 int run_pack(const signmuon_matrix *mats, int32_t n_mats, const signmuon_params *p, const Plan &pl,
-             void *ws, bool step, hipStream_t st) {
+             void *ws, bool step, hipStream_t st, Tracer &tr) {
     const bool k0 = p->ns_iters == 0;
     std::vector<int32_t> sel;
     for (int32_t i = 0; i < n_mats; ++i)
@@ -284,18 +308,18 @@ int run_pack(const signmuon_matrix *mats, int32_t n_mats, const signmuon_params 
         if (blocks > INT32_MAX) return SIGNMUON_ERANGE;
         b.total_blocks = (int32_t)blocks;
         sm::launch_sign_pack(b, st);
-        if (int rc = last_launch()) return rc;
+        if (int rc = tr.after(SIGNMUON_K_PACK)) return rc;
     }
     return SIGNMUON_OK;
 }
 
 int run_vote(const signmuon_matrix *mats, int32_t n_mats, const signmuon_params *p, const Plan &pl,
-             void *ws, hipStream_t st) {
+             void *ws, hipStream_t st, Tracer &tr) {
     const bool post = p->post_polar_iters > 0;
     uint32_t *nnz = ws_at<uint32_t>(ws, pl.off_nnz);
     if (post) {
         sm::launch_zero_u32(nnz, n_mats, st);
-        if (int rc = last_launch()) return rc;
+        if (int rc = tr.after(SIGNMUON_K_AUX)) return rc;
     }
     for (int32_t c0 = 0; c0 < n_mats; c0 += sm::kMaxMatsPerLaunch) {
         const int32_t cn = n_mats - c0 < sm::kMaxMatsPerLaunch ? n_mats - c0 : sm::kMaxMatsPerLaunch;
@@ -321,7 +345,7 @@ int run_vote(const signmuon_matrix *mats, int32_t n_mats, const signmuon_params 
         if (blocks > INT32_MAX) return SIGNMUON_ERANGE;
         b.total_blocks = (int32_t)blocks;
         sm::launch_vote_update(b, st);
-        if (int rc = last_launch()) return rc;
+        if (int rc = tr.after(SIGNMUON_K_VOTE)) return rc;
     }
     return SIGNMUON_OK;
 }
@@ -329,12 +353,12 @@ int run_vote(const signmuon_matrix *mats, int32_t n_mats, const signmuon_params 
 // Optional local polar step on the vote (summary §2 "Algorithmic flow", step
 // 5): Frobenius-scaled Newton-Schulz on S-bar, then W <- fmaf(-eta, Y, W).
 int run_post_polar(const signmuon_matrix *mats, int32_t n_mats, const signmuon_params *p,
-                   const Plan &pl, void *ws, hipStream_t st) {
+                   const Plan &pl, void *ws, hipStream_t st, Tracer &tr) {
     const int k = p->post_polar_iters;
     const bool bf16 = p->ns_dtype == SIGNMUON_BF16;
     float2 *scales = ws_at<float2>(ws, pl.off_scales);
     sm::launch_nnz_scales(ws_at<uint32_t>(ws, pl.off_nnz), n_mats, scales + pl.post_unit_base, st);
-    if (int rc = last_launch()) return rc;
+    if (int rc = tr.after(SIGNMUON_K_AUX)) return rc;
     for (int j = 0; j < k; ++j) {
         const bool last = j == k - 1;
         for (int pass = 0; pass < 2; ++pass) {
@@ -369,7 +393,7 @@ int run_post_polar(const signmuon_matrix *mats, int32_t n_mats, const signmuon_p
                     sm::launch_ns_gram(b, bf16, st);
                 else
                     sm::launch_ns_product(b, bf16, last ? sm::EPI_WUPD : sm::EPI_ITER, st);
-                if (int rc = last_launch()) return rc;
+                if (int rc = tr.after(pass == 0 ? SIGNMUON_K_GRAM : SIGNMUON_K_PRODUCT)) return rc;
             }
         }
     }
@@ -417,26 +441,38 @@ int signmuon_momentum_ns(const signmuon_matrix *mats, int32_t n_mats, const sign
     if (int rc = check_step_pointers(mats, n_mats, false)) return rc;
     if (int rc = check_workspace(pl, workspace, workspace_bytes)) return rc;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    if (int rc = run_momentum(mats, n_mats, p, pl, workspace, st)) return rc;
-    if (p->ns_iters == 0) return run_pack(mats, n_mats, p, pl, workspace, false, st);
-    return run_newton_schulz(mats, n_mats, p, pl, workspace, false, st);
+    Tracer tr;
+    if (int rc = run_momentum(mats, n_mats, p, pl, workspace, st, tr)) return rc;
+    if (p->ns_iters == 0) return run_pack(mats, n_mats, p, pl, workspace, false, st, tr);
+    return run_newton_schulz(mats, n_mats, p, pl, workspace, false, st, tr);
 }
 
-int signmuon_step(const signmuon_matrix *mats, int32_t n_mats, const signmuon_params *p,
-                  void *workspace, size_t workspace_bytes, signmuon_stream stream) {
+int signmuon_step_traced(const signmuon_matrix *mats, int32_t n_mats, const signmuon_params *p,
+                         void *workspace, size_t workspace_bytes, signmuon_stream stream,
+                         signmuon_trace *trace) {
     Plan pl;
     if (int rc = make_plan(mats, n_mats, p, true, pl)) return rc;
     if (int rc = check_step_pointers(mats, n_mats, true)) return rc;
     if (int rc = check_workspace(pl, workspace, workspace_bytes)) return rc;
+    if (trace && trace->capacity > 0 && !trace->events) return SIGNMUON_EINVAL;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    if (int rc = run_momentum(mats, n_mats, p, pl, workspace, st)) return rc;
+    Tracer tr;
+    tr.t = trace;
+    tr.st = st;
+    if (int rc = tr.begin()) return rc;
+    if (int rc = run_momentum(mats, n_mats, p, pl, workspace, st, tr)) return rc;
     if (p->ns_iters > 0)
-        if (int rc = run_newton_schulz(mats, n_mats, p, pl, workspace, true, st)) return rc;
-    if (int rc = run_pack(mats, n_mats, p, pl, workspace, true, st)) return rc;
-    if (int rc = run_vote(mats, n_mats, p, pl, workspace, st)) return rc;
+        if (int rc = run_newton_schulz(mats, n_mats, p, pl, workspace, true, st, tr)) return rc;
+    if (int rc = run_pack(mats, n_mats, p, pl, workspace, true, st, tr)) return rc;
+    if (int rc = run_vote(mats, n_mats, p, pl, workspace, st, tr)) return rc;
     if (p->post_polar_iters > 0)
-        if (int rc = run_post_polar(mats, n_mats, p, pl, workspace, st)) return rc;
+        if (int rc = run_post_polar(mats, n_mats, p, pl, workspace, st, tr)) return rc;
     return SIGNMUON_OK;
+}
+
+int signmuon_step(const signmuon_matrix *mats, int32_t n_mats, const signmuon_params *p,
+                  void *workspace, size_t workspace_bytes, signmuon_stream stream) {
+    return signmuon_step_traced(mats, n_mats, p, workspace, workspace_bytes, stream, nullptr);
 }
 
 int signmuon_sign_pack(const void *u, signmuon_dtype u_dtype, int64_t n, int32_t workers,

@@ -101,85 +101,85 @@ struct Operand {
     int64_t ld;
     int rows;  // valid rows from the tile origin (may exceed 256)
     int K;
-    bool vec;  // 16-byte loads allowed (ld and base keep chunk alignment)
+    bool vec;  // 16-byte chunks: every chunk lies wholly inside or outside the operand
 };
 
+// Buffer offset beyond every extent: a load there returns zeros.
+constexpr uint32_t kOOB = 0x80000000u;
+
+template <bool BF16, bool KC>
+__device__ __forceinline__ int64_t operand_extent(const Operand &op) {
+    const int64_t sz = sizeof(typename Elem<BF16>::T);
+    return KC ? ((int64_t)(op.rows - 1) * op.ld + op.K) * sz : ((int64_t)(op.K - 1) * op.ld + op.rows) * sz;
+}
+
+// Stages one operand's BK-wide k-slice (256 rows) from global memory to LDS.
+// Loads go through a buffer resource spanning the operand: a chunk outside it
+// reads the out-of-bounds offset and comes back as zeros, so edge tiles need
+// no branches. KC: k-contiguous rows, 8 chunks of 16 bytes per 128-byte LDS
+// row. !KC: 8 x 8 (bf16) or 4 x 4 (fp32) blocks transposed in registers.
 template <bool BF16, bool KC>
 struct Stager {
     using E = Elem<BF16>;
     using T = typename E::T;
+    __amdgpu_buffer_rsrc_t rsrc;
+    uint32_t off[8];   // byte offset of each chunk at k = 0
+    int kofs[8];       // k of each chunk relative to the slice start
+    uint32_t valid;    // bit i: chunk i's rows lie inside the operand
+    uint32_t kstep;    // bytes per BK of k
+    int K;
     uint4 st[8];
 
-    __device__ __forceinline__ static uint4 gather(const Operand &op, int mn, int k0, bool kc_row) {
-        // One chunk element by element with bounds: kc_row means the chunk
-        // runs along k at fixed mn, otherwise along mn at fixed k.
-        const T *p = reinterpret_cast<const T *>(op.base);
-        T v[E::EPC];
-#pragma unroll
-        for (int e = 0; e < E::EPC; ++e) {
-            int r = kc_row ? mn : mn + e;
-            int k = kc_row ? k0 + e : k0;
-            bool ok = r < op.rows && k < op.K;
-            v[e] = ok ? (KC ? p[(int64_t)r * op.ld + k] : p[(int64_t)k * op.ld + r]) : (T)0;
-        }
-        uint4 out;
-        __builtin_memcpy(&out, v, 16);
-        return out;
-    }
-
-    __device__ __forceinline__ void load(const Operand &op, int k0) {
-        // Interior tiles and k-steps take plain 16-byte loads; edges go
-        // through the checked path.
-        if (op.vec && op.rows >= kNsTileM && k0 + E::BK <= op.K)
-            load_impl<false>(op, k0);
-        else
-            load_impl<true>(op, k0);
-    }
-
-    template <bool CHECK>
-    __device__ __forceinline__ void load_impl(const Operand &op, int k0) {
+    __device__ __forceinline__ void init(const Operand &op) {
         const int tid = threadIdx.x;
+        rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(op.base), (short)0,
+                                                 (int)operand_extent<BF16, KC>(op), 0x00020000);
+        K = op.K;
+        valid = 0;
+        const uint32_t sz = sizeof(T);
         if (KC) {
-            // 256 rows x 8 chunks; lanes 0-7 cover one 128-byte row segment.
+            const int c = tid & 7;
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                const int q = tid + kThreads * i;
-                const int row = q >> 3, c = q & 7;
-                const int gk = k0 + c * E::EPC;
-                if (!CHECK || (op.vec && row < op.rows && gk + E::EPC <= op.K))
-                    st[i] = *reinterpret_cast<const uint4 *>(
-                        op.base + ((int64_t)row * op.ld + gk) * (int64_t)sizeof(T));
-                else
-                    st[i] = gather(op, row, gk, true);
+                const int row = (tid >> 3) + 32 * i;
+                off[i] = (uint32_t)(row * op.ld + c * E::EPC) * sz;
+                kofs[i] = c * E::EPC;
+                valid |= (uint32_t)(row < op.rows) << i;
             }
+            kstep = E::BK * sz;
         } else if (BF16) {
-            // 8 x 8 blocks: kb = k block (8 of them), mb = mn block (32).
             const int kb = tid >> 5, mb = tid & 31;
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                const int gk = k0 + kb * 8 + j, gm = mb * 8;
-                if (!CHECK || (op.vec && gk < op.K && gm + 8 <= op.rows))
-                    st[j] = *reinterpret_cast<const uint4 *>(
-                        op.base + ((int64_t)gk * op.ld + gm) * (int64_t)sizeof(T));
-                else
-                    st[j] = gather(op, gm, gk, false);
+                off[j] = (uint32_t)((kb * 8 + j) * op.ld + mb * 8) * sz;
+                kofs[j] = kb * 8 + j;
+                valid |= (uint32_t)(mb * 8 < op.rows) << j;
             }
+            kstep = (uint32_t)(E::BK * op.ld) * sz;
         } else {
-            // fp32: 4 x 4 blocks, two per thread: kb (8), mb (64).
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
                 const int q = tid + kThreads * i;
                 const int kb = q >> 6, mb = q & 63;
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const int gk = k0 + kb * 4 + j, gm = mb * 4;
-                    if (!CHECK || (op.vec && gk < op.K && gm + 4 <= op.rows))
-                        st[4 * i + j] = *reinterpret_cast<const uint4 *>(
-                            op.base + ((int64_t)gk * op.ld + gm) * (int64_t)sizeof(T));
-                    else
-                        st[4 * i + j] = gather(op, gm, gk, false);
+                    off[4 * i + j] = (uint32_t)((kb * 4 + j) * op.ld + mb * 4) * sz;
+                    kofs[4 * i + j] = kb * 4 + j;
+                    valid |= (uint32_t)(mb * 4 < op.rows) << (4 * i + j);
                 }
             }
+            kstep = (uint32_t)(E::BK * op.ld) * sz;
+        }
+    }
+
+    __device__ __forceinline__ void load(int kt) {
+        const int k0 = kt * E::BK;
+        const uint32_t kb = (uint32_t)kt * kstep;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const bool ok = ((valid >> i) & 1u) && k0 + kofs[i] < K;
+            const uint32_t o = ok ? off[i] + kb : kOOB;
+            st[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)o, 0, 0));
         }
     }
 
@@ -226,59 +226,121 @@ struct Stager {
     }
 };
 
+// Slow staging for shapes whose rows break 16-byte chunk alignment: element
+// by element with bounds, written to LDS in the same layout.
+template <bool BF16, bool KC>
+struct SlowStager {
+    using E = Elem<BF16>;
+    using T = typename E::T;
+    const T *p;
+    int64_t ld;
+    int rows, K;
+
+    __device__ __forceinline__ void init(const Operand &op) {
+        p = reinterpret_cast<const T *>(op.base);
+        ld = op.ld;
+        rows = op.rows;
+        K = op.K;
+    }
+
+    __device__ __forceinline__ T at(int mn, int k) const {
+        if (mn >= rows || k >= K) return (T)0;
+        return KC ? p[(int64_t)mn * ld + k] : p[(int64_t)k * ld + mn];
+    }
+
+    // Load straight into LDS: thread t fills rows t (and chunks of all k).
+    __device__ __forceinline__ void load_store(int kt, char *lds) const {
+        const int k0 = kt * E::BK;
+        for (int q = threadIdx.x; q < kNsTileM * 8; q += kThreads) {
+            const int row = q >> 3, c = q & 7;
+            T v[E::EPC];
+#pragma unroll
+            for (int e = 0; e < E::EPC; ++e) v[e] = at(row, k0 + c * E::EPC + e);
+            uint4 u;
+            __builtin_memcpy(&u, v, 16);
+            *reinterpret_cast<uint4 *>(lds + lds_off(row, c)) = u;
+        }
+    }
+};
+
 // acc[f][g]: 32 x 32 block (f along m, g along n) of the wave's 128 x 128.
 // MFMA 32x32 layout: lane l holds column (l & 31) and, in register r, row
-// 8*(r/4) + 4*(l/32) + (r%4) of the block.
+// 8*(r/4) + 4*(l/32) + (r%4) of the block. The fragments of the next k16
+// step are read from LDS while the current step's 16 MFMAs run.
 template <bool BF16>
 __device__ __forceinline__ void mma_stage(const char *lds_p, const char *lds_q, int wm0, int wn0,
                                           f32x16_t (&acc)[4][4]) {
     const int lane = threadIdx.x & (kWave - 1);
     const int lrow = lane & 31, half = lane >> 5;
     if (BF16) {
+        bf16x8_t pa[2][4], qa[2][4];
+#pragma unroll
+        for (int f = 0; f < 4; ++f) {
+            pa[0][f] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(lds_p + lds_off(wm0 + f * 32 + lrow, half)));
+            qa[0][f] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(lds_q + lds_off(wn0 + f * 32 + lrow, half)));
+        }
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
-            bf16x8_t pa[4], qa[4];
+            const int cb = kk & 1, nb = cb ^ 1;
+            if (kk < 3) {
 #pragma unroll
-            for (int f = 0; f < 4; ++f) {
-                uint4 v = *reinterpret_cast<const uint4 *>(lds_p + lds_off(wm0 + f * 32 + lrow, 2 * kk + half));
-                pa[f] = __builtin_bit_cast(bf16x8_t, v);
-            }
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                uint4 v = *reinterpret_cast<const uint4 *>(lds_q + lds_off(wn0 + g * 32 + lrow, 2 * kk + half));
-                qa[g] = __builtin_bit_cast(bf16x8_t, v);
+                for (int f = 0; f < 4; ++f) {
+                    pa[nb][f] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(lds_p + lds_off(wm0 + f * 32 + lrow, 2 * (kk + 1) + half)));
+                    qa[nb][f] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(lds_q + lds_off(wn0 + f * 32 + lrow, 2 * (kk + 1) + half)));
+                }
             }
 #pragma unroll
             for (int f = 0; f < 4; ++f)
 #pragma unroll
                 for (int g = 0; g < 4; ++g)
-                    acc[f][g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[f], qa[g], acc[f][g], 0, 0, 0);
+                    acc[f][g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[cb][f], qa[cb][g], acc[f][g], 0, 0, 0);
         }
+        // Schedule: the first step's 8 reads, then each step's 16 MFMAs with
+        // the next step's 8 reads slotted between them.
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+        for (int kk = 0; kk < 3; ++kk) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
     } else {
         // fp32: each lane reads 4 consecutive k of a chunk; MFMA step s uses
         // element s, so one instruction contracts k = 8c + s (lanes 0-31) and
         // 8c + 4 + s (lanes 32-63). Both operands use the same mapping.
+        f32x4_t pa[2][4], qa[2][4];
+#pragma unroll
+        for (int f = 0; f < 4; ++f) {
+            pa[0][f] = *reinterpret_cast<const f32x4_t *>(lds_p + lds_off(wm0 + f * 32 + lrow, half));
+            qa[0][f] = *reinterpret_cast<const f32x4_t *>(lds_q + lds_off(wn0 + f * 32 + lrow, half));
+        }
 #pragma unroll
         for (int cp = 0; cp < 4; ++cp) {
-            f32x4_t pa[4], qa[4];
+            const int cb = cp & 1, nb = cb ^ 1;
+            if (cp < 3) {
 #pragma unroll
-            for (int f = 0; f < 4; ++f)
-                pa[f] = *reinterpret_cast<const f32x4_t *>(lds_p + lds_off(wm0 + f * 32 + lrow, 2 * cp + half));
-#pragma unroll
-            for (int g = 0; g < 4; ++g)
-                qa[g] = *reinterpret_cast<const f32x4_t *>(lds_q + lds_off(wn0 + g * 32 + lrow, 2 * cp + half));
+                for (int f = 0; f < 4; ++f) {
+                    pa[nb][f] = *reinterpret_cast<const f32x4_t *>(lds_p + lds_off(wm0 + f * 32 + lrow, 2 * (cp + 1) + half));
+                    qa[nb][f] = *reinterpret_cast<const f32x4_t *>(lds_q + lds_off(wn0 + f * 32 + lrow, 2 * (cp + 1) + half));
+                }
+            }
 #pragma unroll
             for (int s = 0; s < 4; ++s)
 #pragma unroll
                 for (int f = 0; f < 4; ++f)
 #pragma unroll
                     for (int g = 0; g < 4; ++g)
-                        acc[f][g] = __builtin_amdgcn_mfma_f32_32x32x2f32(pa[f][s], qa[g][s], acc[f][g], 0, 0, 0);
+                        acc[f][g] = __builtin_amdgcn_mfma_f32_32x32x2f32(pa[cb][f][s], qa[cb][g][s], acc[f][g], 0, 0, 0);
         }
     }
 }
 
-// Full K loop of one tile, double-buffered through LDS.
+// Full K loop of one tile, double-buffered through LDS: the next slice's
+// global loads are in flight while the current slice's MFMAs run.
 template <bool BF16, bool PKC, bool QKC>
 __device__ __forceinline__ void tile_mainloop(const Operand &P, const Operand &Q, char *smem,
                                               f32x16_t (&acc)[4][4]) {
@@ -291,29 +353,44 @@ __device__ __forceinline__ void tile_mainloop(const Operand &P, const Operand &Q
         for (int g = 0; g < 4; ++g)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[f][g][r] = 0.f;
-
-    Stager<BF16, PKC> sp;
-    Stager<BF16, QKC> sq;
     const int kt_n = (P.K + E::BK - 1) / E::BK;
-    sp.load(P, 0);
-    sq.load(Q, 0);
-    sp.store(smem);
-    sq.store(smem + kOpBytes);
-    __syncthreads();
-    for (int kt = 0; kt < kt_n; ++kt) {
-        char *cur = smem + (kt & 1) * kStageBytes;
-        char *nxt = smem + ((kt + 1) & 1) * kStageBytes;
-        const bool more = kt + 1 < kt_n;
-        if (more) {
-            sp.load(P, (kt + 1) * E::BK);
-            sq.load(Q, (kt + 1) * E::BK);
-        }
-        mma_stage<BF16>(cur, cur + kOpBytes, wm0, wn0, acc);
-        if (more) {
-            sp.store(nxt);
-            sq.store(nxt + kOpBytes);
-        }
+    if (P.vec && Q.vec) {
+        Stager<BF16, PKC> sp;
+        Stager<BF16, QKC> sq;
+        sp.init(P);
+        sq.init(Q);
+        sp.load(0);
+        sq.load(0);
+        sp.store(smem);
+        sq.store(smem + kOpBytes);
         __syncthreads();
+        for (int kt = 0; kt < kt_n; ++kt) {
+            char *cur = smem + (kt & 1) * kStageBytes;
+            char *nxt = smem + ((kt + 1) & 1) * kStageBytes;
+            const bool more = kt + 1 < kt_n;
+            if (more) {
+                sp.load(kt + 1);
+                sq.load(kt + 1);
+            }
+            mma_stage<BF16>(cur, cur + kOpBytes, wm0, wn0, acc);
+            if (more) {
+                sp.store(nxt);
+                sq.store(nxt + kOpBytes);
+            }
+            __syncthreads();
+        }
+    } else {
+        SlowStager<BF16, PKC> sp;
+        SlowStager<BF16, QKC> sq;
+        sp.init(P);
+        sq.init(Q);
+        for (int kt = 0; kt < kt_n; ++kt) {
+            sp.load_store(kt, smem);
+            sq.load_store(kt, smem + kOpBytes);
+            __syncthreads();
+            mma_stage<BF16>(smem, smem + kOpBytes, wm0, wn0, acc);
+            __syncthreads();
+        }
     }
 }
 
@@ -443,7 +520,8 @@ __device__ __forceinline__ void gram_tile(const Operand &P, const Operand &Q, ch
 }
 
 template <bool BF16>
-__global__ __launch_bounds__(kThreads) void ns_gram_kernel(NsBatch b) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void ns_gram_kernel(NsBatch b) {
     using T = typename Elem<BF16>::T;
     __shared__ __attribute__((aligned(16))) char smem[kLdsBytes];
     const int lt = xcd_remap(blockIdx.x, gridDim.x);
@@ -462,7 +540,8 @@ __global__ __launch_bounds__(kThreads) void ns_gram_kernel(NsBatch b) {
     const int tj = ti + t;
     const int64_t n = (int64_t)M.R * M.C;
     const char *y = static_cast<const char *>(M.x) + (int64_t)w * n * (int64_t)sizeof(T);
-    const bool vec = (M.C % Elem<BF16>::EPC) == 0;
+    // Buffer offsets are 32-bit: the 16-byte path needs the matrix under 2 GiB.
+    const bool vec = (M.C % Elem<BF16>::EPC) == 0 && n * (int64_t)sizeof(T) < ((int64_t)1 << 31);
     const float scale = b.use_scales ? b.scales[M.unit_begin + w].y : 1.0f;
     void *a = static_cast<char *>(M.a) + (int64_t)w * r * r * (int64_t)sizeof(T);
     if (wide) {
@@ -566,7 +645,8 @@ __device__ __forceinline__ void product_tile(const Operand &P, const Operand &Q,
 }
 
 template <bool BF16, int EPI>
-__global__ __launch_bounds__(kThreads) void ns_product_kernel(NsBatch b) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void ns_product_kernel(NsBatch b) {
     using T = typename Elem<BF16>::T;
     __shared__ __attribute__((aligned(16))) char smem[kLdsBytes];
     const int lt = xcd_remap(blockIdx.x, gridDim.x);
@@ -582,7 +662,9 @@ __global__ __launch_bounds__(kThreads) void ns_product_kernel(NsBatch b) {
     const int64_t n = (int64_t)R * C;
     const char *x = static_cast<const char *>(M.x) + (int64_t)w * n * (int64_t)sizeof(T);
     const char *a = static_cast<const char *>(M.a) + (int64_t)w * r * r * (int64_t)sizeof(T);
-    const bool vec = (C % Elem<BF16>::EPC) == 0 && (r % Elem<BF16>::EPC) == 0;
+    // Buffer offsets are 32-bit: the 16-byte path needs the matrix under 2 GiB.
+    const bool vec = (C % Elem<BF16>::EPC) == 0 && (r % Elem<BF16>::EPC) == 0 &&
+                     n * (int64_t)sizeof(T) < ((int64_t)1 << 31);
 
     ProductArgs pa;
     pa.x = x;
