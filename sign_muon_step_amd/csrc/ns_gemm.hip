@@ -13,10 +13,11 @@
 //   gram:    A = s2 * Y Y^T  (Y = X, or X^T for a tall X), r x r, symmetric:
 //            only tiles on or above the diagonal are computed and each is
 //            stored twice (itself and its mirror).
-//   product: X' = alpha X + gamma * (A X)   (wide)   or
-//            X' = alpha X + gamma * (X A)   (tall),
-//            alpha = 1.5 s, gamma = -0.5 s; s folds the Frobenius scaling of
-//            the first iteration in (s = 1 afterwards).
+//   product: X' = -0.5 s * (A X - 3 X)   (wide)   or
+//            X' = -0.5 s * (X A - 3 X)   (tall),
+//            i.e. s (1.5 X - 0.5 A X); the -3 X term is accumulated on the
+//            matrix cores with a -3 I fragment, and s folds the Frobenius
+//            scaling of the first iteration in (s = 1 afterwards).
 // The last product's epilogue either stores fp32 U and/or takes the sign of
 // each entry and packs 64 signs per uint64 word straight from the wave64
 // ballot of the accumulator registers (summary §2 "Algorithmic flow", steps
@@ -41,20 +42,20 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
 constexpr int kWave = 64;
-constexpr int kRowBytes = 128;
-constexpr int kOpBytes = kNsTileM * kRowBytes;  // 32 KiB per operand per stage
+constexpr int kStages = 4;                        // LDS pipeline depth
+constexpr int kOpBytes = 16 * 1024;               // one operand's k-slice
 constexpr int kStageBytes = 2 * kOpBytes;
-constexpr int kLdsBytes = 2 * kStageBytes;      // double-buffered: 128 KiB
+constexpr int kLdsBytes = kStages * kStageBytes;  // 128 KiB
 
 template <bool BF16> struct Elem;
 template <> struct Elem<true> {
     using T = uint16_t;
-    static constexpr int BK = 64;   // k per LDS row
+    static constexpr int BK = 32;   // k per stage
     static constexpr int EPC = 8;   // elements per 16-byte chunk
 };
 template <> struct Elem<false> {
     using T = float;
-    static constexpr int BK = 32;
+    static constexpr int BK = 16;
     static constexpr int EPC = 4;
 };
 
@@ -65,6 +66,37 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float x) {
     if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
     u += 0x7fffu + ((u >> 16) & 1u);
     return u >> 16;
+}
+
+// LDS layouts of one operand's k-slice (16 KiB):
+//  k-contiguous ("KL"): 256 rows x 64 bytes (BK of k), 16-byte chunk c of row
+//    r stored at chunk c ^ ((r >> 2) & 3): the MFMA reads of 16 consecutive
+//    rows then hit 16 distinct 16-byte bank groups.
+//  mn-contiguous bf16 ("ML"): 4 (k) x 16 (mn) blocks of 128 bytes, block
+//    (k/4, mn/16) at ((k/4) * 16 + mn/16) * 128: one LDS transpose read of a
+//    16-lane group covers exactly one block.
+//  mn-contiguous fp32: plain rows of 256 mn (1 KiB) per k.
+__device__ __forceinline__ uint32_t kl_off(int row, int chunk) {
+    return (uint32_t)(row * 64 + ((chunk ^ ((row >> 2) & 3)) << 4));
+}
+__device__ __forceinline__ uint32_t ml_off_bf16(int k, int mn) {
+    return (uint32_t)((((k >> 2) * 16 + (mn >> 4)) << 7) + ((k & 3) << 5) + ((mn & 15) << 1));
+}
+__device__ __forceinline__ uint32_t ml_off_f32(int k, int mn) { return (uint32_t)(k * 1024 + mn * 4); }
+
+// s_waitcnt with vmcnt = N, lgkmcnt = 0 (expcnt untouched).
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | ((N >> 4) << 14));
+}
+
+// Workgroup barrier that orders LDS accesses without waiting for the
+// direct-to-LDS loads still in flight (the caller waits for what it needs).
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
 }
 
 template <bool BF16>
@@ -79,11 +111,6 @@ __device__ __forceinline__ void store_val(void *p, int64_t i, float v) {
         static_cast<uint16_t *>(p)[i] = (uint16_t)f32_to_bf16_bits(v);
     else
         static_cast<float *>(p)[i] = v;
-}
-
-// Byte offset of (row, 16-byte chunk) inside one operand's LDS stage.
-__device__ __forceinline__ uint32_t lds_off(int row, int chunk) {
-    return (uint32_t)(row * kRowBytes + ((chunk ^ ((row ^ (row >> 3)) & 7)) << 4));
 }
 
 // Blocks go to the 8 XCDs round-robin; give each XCD a contiguous run of
@@ -113,123 +140,94 @@ __device__ __forceinline__ int64_t operand_extent(const Operand &op) {
     return KC ? ((int64_t)(op.rows - 1) * op.ld + op.K) * sz : ((int64_t)(op.K - 1) * op.ld + op.rows) * sz;
 }
 
-// Stages one operand's BK-wide k-slice (256 rows) from global memory to LDS.
-// Loads go through a buffer resource spanning the operand: a chunk outside it
-// reads the out-of-bounds offset and comes back as zeros, so edge tiles need
-// no branches. KC: k-contiguous rows, 8 chunks of 16 bytes per 128-byte LDS
-// row. !KC: 8 x 8 (bf16) or 4 x 4 (fp32) blocks transposed in registers.
+typedef uint32_t v4u32 __attribute__((ext_vector_type(4)));
+
+// One 16-byte-per-lane load from a buffer straight into LDS: lane L's 16
+// bytes land at LDS address lds + 16 L. Written as asm so that the compiler
+// does not order later LDS reads behind every load still in flight; the
+// caller waits with explicit vmcnt counts. The asm has no outputs: address
+// and descriptor are consumed at issue. M0 (the LDS base of the load) is a
+// register the compiler reserves and cannot take as a clobber; no code the
+// compiler generates for these kernels reads M0, so writing it here is safe.
+__device__ __forceinline__ void dma16(uint32_t lds, uint32_t voffset, v4u32 rsrc) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :
+                 : "s"(lds), "v"(voffset), "s"(rsrc)
+                 : "memory");
+}
+
+// Direct-to-LDS loader of one operand: each wave instruction moves 1 KiB (16
+// bytes per lane) from global memory straight into LDS, so a k-slice costs no
+// registers and several slices can be in flight. The LDS destination of lane
+// L is fixed (base + 16 L); the lane therefore fetches whichever global chunk
+// the layout puts there. Chunks outside the operand read the out-of-bounds
+// buffer offset and land as zeros. Each thread issues 4 loads per slice.
 template <bool BF16, bool KC>
-struct Stager {
+struct DmaLoader {
     using E = Elem<BF16>;
     using T = typename E::T;
-    __amdgpu_buffer_rsrc_t rsrc;
-    uint32_t off[8];   // byte offset of each chunk at k = 0
-    int kofs[8];       // k of each chunk relative to the slice start
+    v4u32 rsrc;
+    uint32_t off[4];   // byte offset of each of the thread's chunks in slice 0
+    int kofs[4];       // k of the chunk relative to the slice start
     uint32_t valid;    // bit i: chunk i's rows lie inside the operand
-    uint32_t kstep;    // bytes per BK of k
+    uint32_t kstep;    // bytes per slice
     int K;
-    uint4 st[8];
+    int wid;
 
     __device__ __forceinline__ void init(const Operand &op) {
-        const int tid = threadIdx.x;
-        rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(op.base), (short)0,
-                                                 (int)operand_extent<BF16, KC>(op), 0x00020000);
+        const int lane = threadIdx.x & (kWave - 1);
+        wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+        // Buffer descriptor: 48-bit base, stride 0, num_records = extent in
+        // bytes, raw 32-bit dword format (0x00020000 on this family).
+        const uint64_t base = reinterpret_cast<uint64_t>(op.base);
+        rsrc = v4u32{(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)base),
+                     (uint32_t)__builtin_amdgcn_readfirstlane((int)((uint32_t)(base >> 32) & 0xffffu)),
+                     (uint32_t)__builtin_amdgcn_readfirstlane((int)operand_extent<BF16, KC>(op)),
+                     0x00020000u};
         K = op.K;
         valid = 0;
         const uint32_t sz = sizeof(T);
-        if (KC) {
-            const int c = tid & 7;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int row = (tid >> 3) + 32 * i;
-                off[i] = (uint32_t)(row * op.ld + c * E::EPC) * sz;
-                kofs[i] = c * E::EPC;
-                valid |= (uint32_t)(row < op.rows) << i;
+        for (int i = 0; i < 4; ++i) {
+            const int b = i * 4 + wid;          // 1 KiB block of the slice
+            int mn, k;
+            if (KC) {                           // 16 rows of 64 bytes
+                const int row = b * 16 + (lane >> 2);
+                const int c = (lane & 3) ^ ((row >> 2) & 3);
+                mn = row;
+                k = c * E::EPC;
+            } else if (BF16) {                  // 8 blocks of 4 (k) x 16 (mn)
+                const int blk = b * 8 + (lane >> 3), w = lane & 7;
+                k = (blk >> 4) * 4 + (w >> 1);
+                mn = (blk & 15) * 16 + (w & 1) * 8;
+            } else {                            // one k row of 256 fp32
+                k = b;
+                mn = lane * 4;
             }
-            kstep = E::BK * sz;
-        } else if (BF16) {
-            const int kb = tid >> 5, mb = tid & 31;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                off[j] = (uint32_t)((kb * 8 + j) * op.ld + mb * 8) * sz;
-                kofs[j] = kb * 8 + j;
-                valid |= (uint32_t)(mb * 8 < op.rows) << j;
-            }
-            kstep = (uint32_t)(E::BK * op.ld) * sz;
-        } else {
-#pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const int q = tid + kThreads * i;
-                const int kb = q >> 6, mb = q & 63;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    off[4 * i + j] = (uint32_t)((kb * 4 + j) * op.ld + mb * 4) * sz;
-                    kofs[4 * i + j] = kb * 4 + j;
-                    valid |= (uint32_t)(mb * 4 < op.rows) << (4 * i + j);
-                }
-            }
-            kstep = (uint32_t)(E::BK * op.ld) * sz;
+            off[i] = KC ? (uint32_t)(mn * op.ld + k) * sz : (uint32_t)(k * op.ld + mn) * sz;
+            kofs[i] = k;
+            valid |= (uint32_t)(mn < op.rows) << i;
         }
+        kstep = KC ? (uint32_t)E::BK * sz : (uint32_t)(E::BK * op.ld) * sz;
     }
 
-    __device__ __forceinline__ void load(int kt) {
+    // lds: LDS byte address of this operand's slice buffer.
+    __device__ __forceinline__ void issue(int kt, uint32_t lds) const {
         const int k0 = kt * E::BK;
         const uint32_t kb = (uint32_t)kt * kstep;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < 4; ++i) {
             const bool ok = ((valid >> i) & 1u) && k0 + kofs[i] < K;
             const uint32_t o = ok ? off[i] + kb : kOOB;
-            st[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)o, 0, 0));
-        }
-    }
-
-    __device__ __forceinline__ void store(char *lds) const {
-        const int tid = threadIdx.x;
-        if (KC) {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int q = tid + kThreads * i;
-                *reinterpret_cast<uint4 *>(lds + lds_off(q >> 3, q & 7)) = st[i];
-            }
-        } else if (BF16) {
-            // Transpose the 8 (k) x 8 (mn) block of 16-bit values: output row
-            // e (mn = 8 mb + e) gathers element e of each of the 8 k rows.
-            const int kb = tid >> 5, mb = tid & 31;
-            uint32_t in[8][4];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                in[j][0] = st[j].x; in[j][1] = st[j].y; in[j][2] = st[j].z; in[j][3] = st[j].w;
-            }
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                uint32_t o[4];
-#pragma unroll
-                for (int d = 0; d < 4; ++d) {
-                    const uint32_t lo = in[2 * d][e >> 1], hi = in[2 * d + 1][e >> 1];
-                    o[d] = (e & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
-                }
-                *reinterpret_cast<uint4 *>(lds + lds_off(mb * 8 + e, kb)) =
-                    make_uint4(o[0], o[1], o[2], o[3]);
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const int q = tid + kThreads * i;
-                const int kb = q >> 6, mb = q & 63;
-                const uint4 *r = &st[4 * i];
-                *reinterpret_cast<uint4 *>(lds + lds_off(mb * 4 + 0, kb)) = make_uint4(r[0].x, r[1].x, r[2].x, r[3].x);
-                *reinterpret_cast<uint4 *>(lds + lds_off(mb * 4 + 1, kb)) = make_uint4(r[0].y, r[1].y, r[2].y, r[3].y);
-                *reinterpret_cast<uint4 *>(lds + lds_off(mb * 4 + 2, kb)) = make_uint4(r[0].z, r[1].z, r[2].z, r[3].z);
-                *reinterpret_cast<uint4 *>(lds + lds_off(mb * 4 + 3, kb)) = make_uint4(r[0].w, r[1].w, r[2].w, r[3].w);
-            }
+            dma16(lds + (uint32_t)(i * 4 + wid) * 1024u, o, rsrc);
         }
     }
 };
 
-// Slow staging for shapes whose rows break 16-byte chunk alignment: element
-// by element with bounds, written to LDS in the same layout.
+// Element-by-element loader for shapes whose rows break 16-byte alignment:
+// writes the same LDS layouts with plain loads and stores (synchronous).
 template <bool BF16, bool KC>
-struct SlowStager {
+struct SlowLoader {
     using E = Elem<BF16>;
     using T = typename E::T;
     const T *p;
@@ -243,110 +241,200 @@ struct SlowStager {
         K = op.K;
     }
 
-    __device__ __forceinline__ T at(int mn, int k) const {
-        if (mn >= rows || k >= K) return (T)0;
-        return KC ? p[(int64_t)mn * ld + k] : p[(int64_t)k * ld + mn];
-    }
-
-    // Load straight into LDS: thread t fills rows t (and chunks of all k).
     __device__ __forceinline__ void load_store(int kt, char *lds) const {
         const int k0 = kt * E::BK;
-        for (int q = threadIdx.x; q < kNsTileM * 8; q += kThreads) {
-            const int row = q >> 3, c = q & 7;
-            T v[E::EPC];
-#pragma unroll
-            for (int e = 0; e < E::EPC; ++e) v[e] = at(row, k0 + c * E::EPC + e);
-            uint4 u;
-            __builtin_memcpy(&u, v, 16);
-            *reinterpret_cast<uint4 *>(lds + lds_off(row, c)) = u;
+        for (int e = threadIdx.x; e < kNsTileM * E::BK; e += kThreads) {
+            const int mn = e / E::BK, k = e % E::BK;
+            T v = (T)0;
+            if (mn < rows && k0 + k < K) v = KC ? p[(int64_t)mn * ld + k0 + k] : p[(int64_t)(k0 + k) * ld + mn];
+            uint32_t o;
+            if (KC)
+                o = kl_off(mn, k / E::EPC) + (k % E::EPC) * sizeof(T);
+            else
+                o = BF16 ? ml_off_bf16(k, mn) : ml_off_f32(k, mn);
+            *reinterpret_cast<T *>(lds + o) = v;
         }
     }
 };
 
-// acc[f][g]: 32 x 32 block (f along m, g along n) of the wave's 128 x 128.
-// MFMA 32x32 layout: lane l holds column (l & 31) and, in register r, row
-// 8*(r/4) + 4*(l/32) + (r%4) of the block. The fragments of the next k16
-// step are read from LDS while the current step's 16 MFMAs run.
-template <bool BF16>
-__device__ __forceinline__ void mma_stage(const char *lds_p, const char *lds_q, int wm0, int wn0,
-                                          f32x16_t (&acc)[4][4]) {
+// MFMA fragments of one 32-row (m or n) block for k16 step kk (bf16): lane l
+// holds row (l & 31) and k = 16 kk + 8 (l / 32) .. + 7.
+template <bool KC>
+__device__ __forceinline__ bf16x8_t frag_bf16(const char *lds, int row0, int kk) {
     const int lane = threadIdx.x & (kWave - 1);
-    const int lrow = lane & 31, half = lane >> 5;
-    if (BF16) {
-        bf16x8_t pa[2][4], qa[2][4];
-#pragma unroll
-        for (int f = 0; f < 4; ++f) {
-            pa[0][f] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(lds_p + lds_off(wm0 + f * 32 + lrow, half)));
-            qa[0][f] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(lds_q + lds_off(wn0 + f * 32 + lrow, half)));
-        }
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            const int cb = kk & 1, nb = cb ^ 1;
-            if (kk < 3) {
-#pragma unroll
-                for (int f = 0; f < 4; ++f) {
-                    pa[nb][f] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(lds_p + lds_off(wm0 + f * 32 + lrow, 2 * (kk + 1) + half)));
-                    qa[nb][f] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(lds_q + lds_off(wn0 + f * 32 + lrow, 2 * (kk + 1) + half)));
-                }
-            }
-#pragma unroll
-            for (int f = 0; f < 4; ++f)
-#pragma unroll
-                for (int g = 0; g < 4; ++g)
-                    acc[f][g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[cb][f], qa[cb][g], acc[f][g], 0, 0, 0);
-        }
-        // Schedule: the first step's 8 reads, then each step's 16 MFMAs with
-        // the next step's 8 reads slotted between them.
-        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
-#pragma unroll
-        for (int kk = 0; kk < 3; ++kk) {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            }
-            __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
+    if (KC) {
+        const uint4 v = *reinterpret_cast<const uint4 *>(lds + kl_off(row0 + (lane & 31), 2 * kk + (lane >> 5)));
+        return __builtin_bit_cast(bf16x8_t, v);
     } else {
-        // fp32: each lane reads 4 consecutive k of a chunk; MFMA step s uses
-        // element s, so one instruction contracts k = 8c + s (lanes 0-31) and
-        // 8c + 4 + s (lanes 32-63). Both operands use the same mapping.
-        f32x4_t pa[2][4], qa[2][4];
+        // Two LDS transpose reads: in each 16-lane group g, lane 4j + q points
+        // at 4 mn-consecutive values of k row j; lane i gets mn column i of
+        // the 4 rows, i.e. 4 k-consecutive values of its own mn.
+        typedef short v4i16 __attribute__((ext_vector_type(4)));
+        typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+        const int g = lane >> 4, i = lane & 15;
+        const int mn = row0 + 16 * (g & 1) + 4 * (i & 3);
+        const int k = 16 * kk + 8 * (g >> 1) + (i >> 2);
+        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(lds + ml_off_bf16(k, mn)));
+        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(lds + ml_off_bf16(k + 4, mn)));
+        typedef short v8i16 __attribute__((ext_vector_type(8)));
+        const v8i16 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        return __builtin_bit_cast(bf16x8_t, both);
+    }
+}
+
+// fp32 fragments for chunk pair cp: lane l holds 4 consecutive k
+// (k = 8 cp + 4 (l / 32) .. + 3) of row (l & 31); MFMA step s uses element s.
+template <bool KC>
+__device__ __forceinline__ f32x4_t frag_f32(const char *lds, int row0, int cp) {
+    const int lane = threadIdx.x & (kWave - 1);
+    if (KC) return *reinterpret_cast<const f32x4_t *>(lds + kl_off(row0 + (lane & 31), 2 * cp + (lane >> 5)));
+    const int mn = row0 + (lane & 31), k = 8 * cp + 4 * (lane >> 5);
+    f32x4_t v;
 #pragma unroll
-        for (int f = 0; f < 4; ++f) {
-            pa[0][f] = *reinterpret_cast<const f32x4_t *>(lds_p + lds_off(wm0 + f * 32 + lrow, half));
-            qa[0][f] = *reinterpret_cast<const f32x4_t *>(lds_q + lds_off(wn0 + f * 32 + lrow, half));
-        }
+    for (int s = 0; s < 4; ++s) v[s] = *reinterpret_cast<const float *>(lds + ml_off_f32(k + s, mn));
+    return v;
+}
+
+// Fragments of one half of a k-slice (bf16: one k16 step; fp32: one pair of
+// 16-byte chunks) for the wave's 4 m-blocks and 4 n-blocks.
+template <bool BF16> struct Frags;
+template <> struct Frags<true> { bf16x8_t p[4], q[4]; };
+template <> struct Frags<false> { f32x4_t p[4], q[4]; };
+
+template <bool BF16, bool PKC, bool QKC>
+__device__ __forceinline__ void read_frags(Frags<BF16> &fr, const char *lds_p, const char *lds_q,
+                                           int wm0, int wn0, int half) {
 #pragma unroll
-        for (int cp = 0; cp < 4; ++cp) {
-            const int cb = cp & 1, nb = cb ^ 1;
-            if (cp < 3) {
-#pragma unroll
-                for (int f = 0; f < 4; ++f) {
-                    pa[nb][f] = *reinterpret_cast<const f32x4_t *>(lds_p + lds_off(wm0 + f * 32 + lrow, 2 * (cp + 1) + half));
-                    qa[nb][f] = *reinterpret_cast<const f32x4_t *>(lds_q + lds_off(wn0 + f * 32 + lrow, 2 * (cp + 1) + half));
-                }
-            }
-#pragma unroll
-            for (int s = 0; s < 4; ++s)
-#pragma unroll
-                for (int f = 0; f < 4; ++f)
-#pragma unroll
-                    for (int g = 0; g < 4; ++g)
-                        acc[f][g] = __builtin_amdgcn_mfma_f32_32x32x2f32(pa[cb][f][s], qa[cb][g][s], acc[f][g], 0, 0, 0);
+    for (int f = 0; f < 4; ++f) {
+        if constexpr (BF16) {
+            fr.p[f] = frag_bf16<PKC>(lds_p, wm0 + f * 32, half);
+            fr.q[f] = frag_bf16<QKC>(lds_q, wn0 + f * 32, half);
+        } else {
+            fr.p[f] = frag_f32<PKC>(lds_p, wm0 + f * 32, half);
+            fr.q[f] = frag_f32<QKC>(lds_q, wn0 + f * 32, half);
         }
     }
 }
 
-// Full K loop of one tile, double-buffered through LDS: the next slice's
-// global loads are in flight while the current slice's MFMAs run.
-template <bool BF16, bool PKC, bool QKC>
+// acc[f][g]: 32 x 32 block (f along m, g along n) of the wave's 128 x 128.
+// MFMA 32x32 layout: lane l holds column (l & 31) and, in register r, row
+// 8*(r/4) + 4*(l/32) + (r%4) of the block.
+template <bool BF16>
+__device__ __forceinline__ void mma_half(const Frags<BF16> &fr, f32x16_t (&acc)[4][4]) {
+    if constexpr (BF16) {
+#pragma unroll
+        for (int f = 0; f < 4; ++f)
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+                acc[f][g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr.p[f], fr.q[g], acc[f][g], 0, 0, 0);
+    } else {
+        // fp32: MFMA step s contracts element s of each lane's 4 k values.
+#pragma unroll
+        for (int st = 0; st < 4; ++st)
+#pragma unroll
+            for (int f = 0; f < 4; ++f)
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+                    acc[f][g] = __builtin_amdgcn_mfma_f32_32x32x2f32(fr.p[f][st], fr.q[g][st], acc[f][g], 0, 0, 0);
+    }
+}
+
+// The product adds -3 X to the accumulators, so that the epilogue's
+// -0.5 s * acc is s (1.5 X - 0.5 A X) without reading X again: -3 X is the
+// product of -3 I with the X fragments already in registers, issued at the
+// slices whose k range holds the output rows (wide: A X, identity on the P
+// side) or columns (tall: X A, identity on the Q side). -3 is exact in bf16
+// and the products are exact in fp32.
+enum IdSide { ID_NONE = 0, ID_P = 1, ID_Q = 2 };
+
+// One-hot -3 fragment: lane l, k index kl (within the 32-row block) holds -3
+// where kl equals the lane's row (l & 31).
+__device__ __forceinline__ bf16x8_t id_frag_bf16(int roff, int kk) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int j = (lane & 31) - roff - 16 * kk - 8 * (lane >> 5);  // element holding -3
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        w[e] = (j == 2 * e ? 0xc040u : 0u) | (j == 2 * e + 1 ? 0xc0400000u : 0u);
+    return __builtin_bit_cast(bf16x8_t, make_uint4(w[0], w[1], w[2], w[3]));
+}
+
+__device__ __forceinline__ f32x4_t id_frag_f32(int roff, int cp) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int j = (lane & 31) - roff - 8 * cp - 4 * (lane >> 5);
+    f32x4_t v;
+#pragma unroll
+    for (int st = 0; st < 4; ++st) v[st] = j == st ? -3.0f : 0.0f;
+    return v;
+}
+
+// d = slice index minus the wave's first identity slice.
+template <bool BF16, int SIDE>
+__device__ __forceinline__ void mma_identity(const Frags<BF16> &fr, f32x16_t (&acc)[4][4], int d,
+                                             int half) {
+    constexpr int RS = Elem<BF16>::BK;  // k rows per slice
+    if (SIDE == ID_NONE || d < 0 || d >= 128 / RS) return;
+    const int blk = d * RS / 32, roff = (d * RS) % 32;
+    if constexpr (BF16) {
+        const bf16x8_t id = id_frag_bf16(roff, half);
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+            if (b == blk)
+#pragma unroll
+                for (int o = 0; o < 4; ++o) {
+                    if (SIDE == ID_P)
+                        acc[b][o] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(id, fr.q[o], acc[b][o], 0, 0, 0);
+                    else
+                        acc[o][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr.p[o], id, acc[o][b], 0, 0, 0);
+                }
+    } else {
+        const f32x4_t id = id_frag_f32(roff, half);
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+            if (b == blk)
+#pragma unroll
+                for (int st = 0; st < 4; ++st)
+#pragma unroll
+                    for (int o = 0; o < 4; ++o) {
+                        if (SIDE == ID_P)
+                            acc[b][o] = __builtin_amdgcn_mfma_f32_32x32x2f32(id[st], fr.q[o][st], acc[b][o], 0, 0, 0);
+                        else
+                            acc[o][b] = __builtin_amdgcn_mfma_f32_32x32x2f32(fr.p[o][st], id[st], acc[o][b], 0, 0, 0);
+                    }
+    }
+}
+
+__device__ __forceinline__ void wait_slices(int n) {
+    // vmcnt = 8 loads per slice (4 per operand) times the slices allowed in flight
+    if (n >= 3)
+        wait_vm_lgkm0<24>();
+    else if (n == 2)
+        wait_vm_lgkm0<16>();
+    else if (n == 1)
+        wait_vm_lgkm0<8>();
+    else
+        wait_vm_lgkm0<0>();
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const char *p) {
+    return (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) char *)p);
+}
+
+// Full K loop of one tile. kStages LDS buffers hold k-slices kt .. kt + 3;
+// the direct-to-LDS loads run up to four slices ahead of the MFMAs. Each
+// slice is consumed in two halves; the barrier that hands over slice kt + 1
+// (and frees slice kt's buffer for slice kt + 4) sits between them, and the
+// first fragments of slice kt + 1 are read while the second half of slice kt
+// is still in the MFMA pipe.
+// id_origin: tile origin (rows for ID_P, columns for ID_Q) of the identity
+// term; unused for ID_NONE.
+template <bool BF16, bool PKC, bool QKC, int SIDE = ID_NONE>
 __device__ __forceinline__ void tile_mainloop(const Operand &P, const Operand &Q, char *smem,
-                                              f32x16_t (&acc)[4][4]) {
+                                              f32x16_t (&acc)[4][4], int id_origin = 0) {
     using E = Elem<BF16>;
     const int wid = threadIdx.x / kWave;
     const int wm0 = (wid >> 1) * 128, wn0 = (wid & 1) * 128;
+    const int id0 = (id_origin + (SIDE == ID_P ? wm0 : wn0)) / E::BK;  // first identity slice
 #pragma unroll
     for (int f = 0; f < 4; ++f)
 #pragma unroll
@@ -355,43 +443,62 @@ __device__ __forceinline__ void tile_mainloop(const Operand &P, const Operand &Q
             for (int r = 0; r < 16; ++r) acc[f][g][r] = 0.f;
     const int kt_n = (P.K + E::BK - 1) / E::BK;
     if (P.vec && Q.vec) {
-        Stager<BF16, PKC> sp;
-        Stager<BF16, QKC> sq;
-        sp.init(P);
-        sq.init(Q);
-        sp.load(0);
-        sq.load(0);
-        sp.store(smem);
-        sq.store(smem + kOpBytes);
-        __syncthreads();
+        DmaLoader<BF16, PKC> lp;
+        DmaLoader<BF16, QKC> lq;
+        lp.init(P);
+        lq.init(Q);
+        const uint32_t lds0 = lds_addr(smem);
+#pragma unroll
+        for (int s = 0; s < kStages; ++s)
+            if (s < kt_n) {
+                lp.issue(s, lds0 + s * kStageBytes);
+                lq.issue(s, lds0 + s * kStageBytes + kOpBytes);
+            }
+        const int pre = kt_n - 1 < kStages - 1 ? kt_n - 1 : kStages - 1;
+        wait_slices(pre);
+        lds_barrier();
+        Frags<BF16> fa, fb;
+        read_frags<BF16, PKC, QKC>(fa, smem, smem + kOpBytes, wm0, wn0, 0);
         for (int kt = 0; kt < kt_n; ++kt) {
-            char *cur = smem + (kt & 1) * kStageBytes;
-            char *nxt = smem + ((kt + 1) & 1) * kStageBytes;
-            const bool more = kt + 1 < kt_n;
-            if (more) {
-                sp.load(kt + 1);
-                sq.load(kt + 1);
+            const char *cur = smem + (kt % kStages) * kStageBytes;
+            read_frags<BF16, PKC, QKC>(fb, cur, cur + kOpBytes, wm0, wn0, 1);
+            mma_half<BF16>(fa, acc);
+            mma_identity<BF16, SIDE>(fa, acc, kt - id0, 0);
+            if (kt + 1 < kt_n) {
+                const int after = kt_n - 2 - kt;  // slices issued after kt + 1
+                wait_slices(after < 2 ? after : 2);
+                lds_barrier();
+                if (kt + kStages < kt_n) {
+                    const uint32_t dst = lds0 + (kt % kStages) * kStageBytes;
+                    lp.issue(kt + kStages, dst);
+                    lq.issue(kt + kStages, dst + kOpBytes);
+                }
+                const char *nxt = smem + ((kt + 1) % kStages) * kStageBytes;
+                read_frags<BF16, PKC, QKC>(fa, nxt, nxt + kOpBytes, wm0, wn0, 0);
             }
-            mma_stage<BF16>(cur, cur + kOpBytes, wm0, wn0, acc);
-            if (more) {
-                sp.store(nxt);
-                sq.store(nxt + kOpBytes);
-            }
-            __syncthreads();
+            mma_half<BF16>(fb, acc);
+            mma_identity<BF16, SIDE>(fb, acc, kt - id0, 1);
         }
     } else {
-        SlowStager<BF16, PKC> sp;
-        SlowStager<BF16, QKC> sq;
-        sp.init(P);
-        sq.init(Q);
+        SlowLoader<BF16, PKC> lp;
+        SlowLoader<BF16, QKC> lq;
+        lp.init(P);
+        lq.init(Q);
         for (int kt = 0; kt < kt_n; ++kt) {
-            sp.load_store(kt, smem);
-            sq.load_store(kt, smem + kOpBytes);
+            lp.load_store(kt, smem);
+            lq.load_store(kt, smem + kOpBytes);
             __syncthreads();
-            mma_stage<BF16>(smem, smem + kOpBytes, wm0, wn0, acc);
+            Frags<BF16> fa;
+            read_frags<BF16, PKC, QKC>(fa, smem, smem + kOpBytes, wm0, wn0, 0);
+            mma_half<BF16>(fa, acc);
+            mma_identity<BF16, SIDE>(fa, acc, kt - id0, 0);
+            read_frags<BF16, PKC, QKC>(fa, smem, smem + kOpBytes, wm0, wn0, 1);
+            mma_half<BF16>(fa, acc);
+            mma_identity<BF16, SIDE>(fa, acc, kt - id0, 1);
             __syncthreads();
         }
     }
+    __syncthreads();  // every wave is done with the slices before LDS is reused
 }
 
 __device__ __forceinline__ int find_ns_mat(const NsBatch &b, int t) {
@@ -558,18 +665,17 @@ void ns_gram_kernel(NsBatch b) {
 }
 
 // ---------------------------------------------------------------------------
-// Product tile: X' = alpha X + gamma (A X) or (X A), with the epilogue EPI.
+// Product tile: X' = gamma (A X - 3 X) or (X A - 3 X), with the epilogue EPI.
 // ---------------------------------------------------------------------------
 struct ProductArgs {
-    const char *x;   // this worker's iterate
     void *out;       // this worker's output (U / next iterate) or W
     uint64_t *pk;    // this worker's packed words or nullptr
     int R, C, ti, tj;
-    float alpha, gamma, eta;
+    float gamma, eta;
 };
 
 // Epilogue of the product, 32 rows of the wave's 128 x 128 at a time through
-// LDS: u = alpha * X + gamma * acc row-major (4 columns per lane), stored as
+// LDS: u = gamma * acc row-major (4 columns per lane), stored as
 // EPI asks; for the fused sign + pack, u goes back to LDS and each packed word
 // is the ballot of 64 consecutive columns of one row (needs C % 64 == 0).
 template <bool BF16, int EPI, bool FAST>
@@ -593,13 +699,11 @@ __device__ __forceinline__ void product_epilogue(const ProductArgs &pa, f32x16_t
             float *sp = stage + row * kStageStride + c4;
             const float4 v4 = *reinterpret_cast<const float4 *>(sp);
             const float v[4] = {v4.x, v4.y, v4.z, v4.w};
-            float xv[4];
-            load4<BF16, FAST>(pa.x, idx, xv, gm < R, C - gn);
             float u[4];
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
                 const bool ok = FAST || (gm < R && gn + t < C);
-                u[t] = ok ? __builtin_fmaf(pa.gamma, v[t], pa.alpha * xv[t]) : 0.f;
+                u[t] = ok ? pa.gamma * v[t] : 0.f;
             }
             if (want_out) {
                 if (EPI == EPI_ITER) {
@@ -632,11 +736,66 @@ __device__ __forceinline__ void product_epilogue(const ProductArgs &pa, f32x16_t
     }
 }
 
+// Sign + pack straight from the accumulators (final iteration, no U output):
+// u = gamma * acc, bit = (u >= 0). With the MFMA 32x32 layout, the ballot of
+// register rr of block (f, g) holds row R0 (lanes 0-31) and row R0 + 4
+// (lanes 32-63) over the block's 32 columns; blocks 2 gp and 2 gp + 1 give
+// the 64 columns of one packed word (C % 64 == 0). Word id of the wave goes
+// to lane id % 64, slot id / 64; each lane then stores its 4 words.
+// dst in lane `lane` <- val (a uniform value); the other lanes keep dst.
+__device__ __forceinline__ int write_lane(int dst, uint32_t val, int lane) {
+    asm("v_writelane_b32 %0, %1, %2" : "+v"(dst) : "s"(val), "i"(lane));
+    return dst;
+}
+
+__device__ __forceinline__ void pack_from_registers(const ProductArgs &pa, const f32x16_t (&acc)[4][4]) {
+    const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
+    const int m0 = pa.ti * kNsTileM + (wid >> 1) * 128, n0 = pa.tj * kNsTileN + (wid & 1) * 128;
+    int lo[4] = {0, 0, 0, 0}, hi[4] = {0, 0, 0, 0};  // 32-bit halves of each lane's 4 words
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr)
+#pragma unroll
+            for (int gp = 0; gp < 2; ++gp) {
+                const uint64_t b0 = __ballot(pa.gamma * acc[f][2 * gp][rr] >= 0.f);
+                const uint64_t b1 = __ballot(pa.gamma * acc[f][2 * gp + 1][rr] >= 0.f);
+                const int id = ((f * 16 + rr) * 2 + gp) * 2;  // even, 0..254
+                // row R0: lanes 0-31 of both blocks; row R0 + 4: lanes 32-63
+                lo[id >> 6] = write_lane(lo[id >> 6], (uint32_t)b0, id & 63);
+                hi[id >> 6] = write_lane(hi[id >> 6], (uint32_t)b1, id & 63);
+                lo[id >> 6] = write_lane(lo[id >> 6], (uint32_t)(b0 >> 32), (id + 1) & 63);
+                hi[id >> 6] = write_lane(hi[id >> 6], (uint32_t)(b1 >> 32), (id + 1) & 63);
+                // consume each pair of ballots before the next (bounds the
+                // live scalar masks)
+                __builtin_amdgcn_sched_barrier(0);
+            }
+    }
+#pragma unroll
+    for (int sl = 0; sl < 4; ++sl) {
+        const int id = sl * 64 + lane;
+        const int hrow = id & 1, gp = (id >> 1) & 1, rr = (id >> 2) & 15, f = id >> 6;
+        const int gm = m0 + f * 32 + 8 * (rr >> 2) + (rr & 3) + 4 * hrow;
+        const int gn0 = n0 + 64 * gp;
+        const uint64_t word = (uint64_t)(uint32_t)lo[sl] | ((uint64_t)(uint32_t)hi[sl] << 32);
+        if (gm < pa.R && gn0 < pa.C) pa.pk[((int64_t)gm * pa.C + gn0) >> 6] = word;
+    }
+}
+
 template <bool BF16, bool QKC, int EPI>
 __device__ __forceinline__ void product_tile(const Operand &P, const Operand &Q, char *smem,
                                              const ProductArgs &pa) {
     f32x16_t acc[4][4];
-    tile_mainloop<BF16, true, QKC>(P, Q, smem, acc);
+    // wide (Q = X, mn-contiguous): -3 X enters on the P side at the output
+    // rows; tall (Q = A): on the Q side at the output columns.
+    if constexpr (QKC)
+        tile_mainloop<BF16, true, QKC, ID_Q>(P, Q, smem, acc, pa.tj * kNsTileN);
+    else
+        tile_mainloop<BF16, true, QKC, ID_P>(P, Q, smem, acc, pa.ti * kNsTileM);
+    if (EPI == EPI_FINAL && pa.pk && !pa.out) {
+        pack_from_registers(pa, acc);
+        return;
+    }
     const bool fast = P.vec && (pa.ti + 1) * kNsTileM <= pa.R && (pa.tj + 1) * kNsTileN <= pa.C;
     if (fast)
         product_epilogue<BF16, EPI, true>(pa, acc, smem);
@@ -667,13 +826,11 @@ void ns_product_kernel(NsBatch b) {
                      n * (int64_t)sizeof(T) < ((int64_t)1 << 31);
 
     ProductArgs pa;
-    pa.x = x;
     pa.R = R;
     pa.C = C;
     pa.ti = ti;
     pa.tj = tj;
     const float s = b.use_scales ? b.scales[M.unit_begin + w].x : 1.0f;
-    pa.alpha = 1.5f * s;
     pa.gamma = -0.5f * s;
     pa.eta = b.eta;
     if (EPI == EPI_ITER)

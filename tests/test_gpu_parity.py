@@ -398,3 +398,31 @@ def test_gpt2_small_full_size_sampled():
         w_ref = ws_host[j].copy()
         oracle.vote_update(packed, w_ref, wl.eta, want_vote=False)
         np.testing.assert_array_equal(to_host(mat.weight), w_ref, err_msg=f"W {j}")
+
+
+@pytest.mark.parametrize("ns", ["bf16", "f32"])
+@pytest.mark.parametrize("shape", [(768, 3072), (3072, 768), (300, 640), (640, 300), (256, 1024)])
+def test_pack_without_polar_out_matches(ns, shape):
+    """With polar_out NULL the last product packs signs straight from its
+    accumulators; the bits must equal those packed from the stored U (same
+    accumulators) and agree with the oracle's signs."""
+    R, C = shape
+    mw, k = 3, 1
+    g = grads(900 + R, mw, R, C, 1e-3)
+    params = sm.Params(workers=mw, ns_iters=k, mom_dtype=dtype_of(ns)[2], ns_dtype=dtype_of(ns)[2])
+    with_u = make_matrix(g, zeros_m(mw, R, C, ns), np.zeros((R, C), np.float32))
+    without_u = make_matrix(g, zeros_m(mw, R, C, ns), np.zeros((R, C), np.float32), polar=False)
+    run("signmuon_step", [with_u], params)
+    run("signmuon_step", [without_u], params)
+    np.testing.assert_array_equal(to_host(without_u.packed), to_host(with_u.packed))
+    np.testing.assert_array_equal(to_host(without_u.weight), to_host(with_u.weight))
+    m_host = zeros_m(mw, R, C, ns)
+    oracle.momentum(g, m_host, 0.9)
+    u_ref = oracle_u(m_host, k, ns)
+    bits = np.unpackbits(to_host(without_u.packed).view(np.uint8), axis=1, bitorder="little")[:, :R * C]
+    for w in range(mw):
+        ref = (u_ref[w].ravel() >= 0)
+        keep = np.abs(u_ref[w].ravel()) >= 1e-6 * np.abs(u_ref[w]).max()
+        agree = np.mean((bits[w].astype(bool) == ref)[keep])
+        announce(f"  pack without U {ns} {shape} worker {w}: sign agreement {agree:.6f}")
+        assert agree >= 0.999
