@@ -254,10 +254,11 @@ int run_newton_schulz(const signmuon_matrix *mats, int32_t n_mats, const signmuo
                     d.packed = (last && step && q.fused_pack) ? s.packed : nullptr;
                     d.tiles_per_worker = pass == 0 ? sm::ns_gram_tiles(q.R, q.C) : sm::ns_product_tiles(q.R, q.C);
                     d.tile_begin = (int32_t)tiles;
-                    tiles += (int64_t)p->workers * d.tiles_per_worker;
+                    tiles += d.tiles_per_worker;
                 }
-                if (tiles > INT32_MAX) return SIGNMUON_ERANGE;
-                b.total_tiles = (int32_t)tiles;
+                if (tiles * p->workers > INT32_MAX) return SIGNMUON_ERANGE;
+                b.tiles_per_worker_all = (int32_t)tiles;
+                b.total_tiles = (int32_t)(tiles * p->workers);
                 if (pass == 0)
                     sm::launch_ns_gram(b, bf16, st);
                 else
@@ -388,6 +389,8 @@ int run_post_polar(const signmuon_matrix *mats, int32_t n_mats, const signmuon_p
                     d.tile_begin = (int32_t)tiles;
                     tiles += d.tiles_per_worker;
                 }
+                if (tiles > INT32_MAX) return SIGNMUON_ERANGE;
+                b.tiles_per_worker_all = (int32_t)tiles;
                 b.total_tiles = (int32_t)tiles;
                 if (pass == 0)
                     sm::launch_ns_gram(b, bf16, st);

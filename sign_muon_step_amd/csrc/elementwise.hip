@@ -45,59 +45,69 @@ __device__ __forceinline__ int find_mat(const Batch &b, int blk) {
 // the reading taken), plus the sum of squares of the stored M per block for
 // the Frobenius normalisation (summary §4 "nanoGPT": Frobenius scaling).
 // ---------------------------------------------------------------------------
-template <bool GB, bool MB>
-__device__ __forceinline__ double momentum_vec8(const MomBatch &b, const void *gp, void *mp,
-                                                int64_t e) {
-    float g[8], m[8];
-    if (GB) {
-        uint4 v = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(gp) + e);
-        uint32_t wds[4] = {v.x, v.y, v.z, v.w};
+// Raw 16-byte pieces of 8 consecutive entries: fp32 takes two, bf16 one.
+struct Raw8 {
+    uint4 v[2];
+};
+
+template <bool B16>
+__device__ __forceinline__ Raw8 load8(const void *p, int64_t e) {
+    Raw8 r;
+    if (B16) {
+        r.v[0] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(p) + e);
+    } else {
+        const uint4 *q = reinterpret_cast<const uint4 *>(static_cast<const float *>(p) + e);
+        r.v[0] = q[0];
+        r.v[1] = q[1];
+    }
+    return r;
+}
+
+template <bool B16>
+__device__ __forceinline__ void unpack8(const Raw8 &r, float (&x)[8]) {
+    if (B16) {
+        const uint32_t w[4] = {r.v[0].x, r.v[0].y, r.v[0].z, r.v[0].w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            g[2 * i] = bf16_bits_to_f32(wds[i] & 0xffffu);
-            g[2 * i + 1] = bf16_bits_to_f32(wds[i] >> 16);
+            x[2 * i] = bf16_bits_to_f32(w[i] & 0xffffu);
+            x[2 * i + 1] = bf16_bits_to_f32(w[i] >> 16);
         }
     } else {
-        const float4 *p = reinterpret_cast<const float4 *>(static_cast<const float *>(gp) + e);
-        float4 a = p[0], c = p[1];
-        g[0] = a.x; g[1] = a.y; g[2] = a.z; g[3] = a.w;
-        g[4] = c.x; g[5] = c.y; g[6] = c.z; g[7] = c.w;
+        const uint32_t w[8] = {r.v[0].x, r.v[0].y, r.v[0].z, r.v[0].w, r.v[1].x, r.v[1].y, r.v[1].z, r.v[1].w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = __uint_as_float(w[i]);
     }
+}
+
+// y = fmaf(beta, m, g) for 8 entries, stored in the momentum's type; returns
+// the sum of squares of the stored values.
+template <bool MB>
+__device__ __forceinline__ double update8(float beta, const float (&g)[8], const float (&m)[8], void *mp,
+                                          int64_t e) {
     double ss = 0.0;
     if (MB) {
-        uint4 *p = reinterpret_cast<uint4 *>(static_cast<uint16_t *>(mp) + e);
-        uint4 v = *p;
-        uint32_t wds[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            m[2 * i] = bf16_bits_to_f32(wds[i] & 0xffffu);
-            m[2 * i + 1] = bf16_bits_to_f32(wds[i] >> 16);
-        }
         uint32_t out[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            uint32_t lo = f32_to_bf16_bits(__builtin_fmaf(b.beta, m[2 * i], g[2 * i]));
-            uint32_t hi = f32_to_bf16_bits(__builtin_fmaf(b.beta, m[2 * i + 1], g[2 * i + 1]));
+            const uint32_t lo = f32_to_bf16_bits(__builtin_fmaf(beta, m[2 * i], g[2 * i]));
+            const uint32_t hi = f32_to_bf16_bits(__builtin_fmaf(beta, m[2 * i + 1], g[2 * i + 1]));
             out[i] = lo | (hi << 16);
-            double s0 = bf16_bits_to_f32(lo), s1 = bf16_bits_to_f32(hi);
+            const double s0 = bf16_bits_to_f32(lo), s1 = bf16_bits_to_f32(hi);
             ss += s0 * s0;
             ss += s1 * s1;
         }
-        *p = make_uint4(out[0], out[1], out[2], out[3]);
+        *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(mp) + e) = make_uint4(out[0], out[1], out[2], out[3]);
     } else {
-        float4 *p = reinterpret_cast<float4 *>(static_cast<float *>(mp) + e);
-        float4 a = p[0], c = p[1];
-        m[0] = a.x; m[1] = a.y; m[2] = a.z; m[3] = a.w;
-        m[4] = c.x; m[5] = c.y; m[6] = c.z; m[7] = c.w;
         float y[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            y[i] = __builtin_fmaf(b.beta, m[i], g[i]);
-            double d = y[i];
+            y[i] = __builtin_fmaf(beta, m[i], g[i]);
+            const double d = y[i];
             ss += d * d;
         }
-        p[0] = make_float4(y[0], y[1], y[2], y[3]);
-        p[1] = make_float4(y[4], y[5], y[6], y[7]);
+        float4 *q = reinterpret_cast<float4 *>(static_cast<float *>(mp) + e);
+        q[0] = make_float4(y[0], y[1], y[2], y[3]);
+        q[1] = make_float4(y[4], y[5], y[6], y[7]);
     }
     return ss;
 }
@@ -138,10 +148,27 @@ __global__ __launch_bounds__(kMomThreads) void momentum_kernel(MomBatch b) {
     if ((n & 7) == 0) {
         // 8 consecutive entries per thread and round; n % 8 == 0 keeps every
         // worker's slice 16-byte aligned and every 8-group inside the matrix.
+        // All rounds' loads are issued before the first store, so they are
+        // all in flight together.
+        constexpr int kRounds = kMomElemsPerThread / 8;
+        Raw8 graw[kRounds], mraw[kRounds];
 #pragma unroll
-        for (int r = 0; r < kMomElemsPerThread / 8; ++r) {
-            int64_t e = begin + (int64_t)(r * kMomThreads + (int)threadIdx.x) * 8;
-            if (e < n) ss += momentum_vec8<GB, MB>(b, gp, mp, e);
+        for (int r = 0; r < kRounds; ++r) {
+            const int64_t e = begin + (int64_t)(r * kMomThreads + (int)threadIdx.x) * 8;
+            if (e < n) {
+                graw[r] = load8<GB>(gp, e);
+                mraw[r] = load8<MB>(mp, e);
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < kRounds; ++r) {
+            const int64_t e = begin + (int64_t)(r * kMomThreads + (int)threadIdx.x) * 8;
+            if (e < n) {
+                float g[8], m[8];
+                unpack8<GB>(graw[r], g);
+                unpack8<MB>(mraw[r], m);
+                ss += update8<MB>(b.beta, g, m, mp, e);
+            }
         }
     } else {
         for (int r = 0; r < kMomElemsPerThread; ++r) {

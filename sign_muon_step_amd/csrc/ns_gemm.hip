@@ -632,10 +632,10 @@ void ns_gram_kernel(NsBatch b) {
     using T = typename Elem<BF16>::T;
     __shared__ __attribute__((aligned(16))) char smem[kLdsBytes];
     const int lt = xcd_remap(blockIdx.x, gridDim.x);
-    const NsMat &M = b.mat[find_ns_mat(b, lt)];
-    const int local = lt - M.tile_begin;
-    const int w = local / M.tiles_per_worker;
-    int t = local - w * M.tiles_per_worker;
+    const int w = lt / b.tiles_per_worker_all;
+    const int lw = lt - w * b.tiles_per_worker_all;
+    const NsMat &M = b.mat[find_ns_mat(b, lw)];
+    int t = lw - M.tile_begin;
     const bool wide = M.R <= M.C;
     const int r = wide ? M.R : M.C, c = wide ? M.C : M.R;
     const int T_ = (r + kNsTileM - 1) / kNsTileM;
@@ -809,10 +809,10 @@ void ns_product_kernel(NsBatch b) {
     using T = typename Elem<BF16>::T;
     __shared__ __attribute__((aligned(16))) char smem[kLdsBytes];
     const int lt = xcd_remap(blockIdx.x, gridDim.x);
-    const NsMat &M = b.mat[find_ns_mat(b, lt)];
-    const int local = lt - M.tile_begin;
-    const int w = local / M.tiles_per_worker;
-    const int t = local - w * M.tiles_per_worker;
+    const int w = lt / b.tiles_per_worker_all;
+    const int lw = lt - w * b.tiles_per_worker_all;
+    const NsMat &M = b.mat[find_ns_mat(b, lw)];
+    const int t = lw - M.tile_begin;
     const int R = M.R, C = M.C;
     const bool wide = R <= C;
     const int r = wide ? R : C;

@@ -55,17 +55,21 @@ struct NsMat {
                         // nullptr; EPI_WUPD: W fp32 (no worker stride)
     uint64_t *packed;   // EPI_FINAL fused sign+pack target or nullptr
     int32_t R, C;
-    int32_t tile_begin;  // first tile of this matrix in the launch
+    int32_t tile_begin;  // first tile of this matrix within one worker's tiles
     int32_t tiles_per_worker;
     int32_t unit_begin;  // index of (this matrix, worker 0) in scales
     int32_t pad_;
 };
 
+// Tiles are numbered worker-major: worker w's tiles of every matrix of the
+// launch, then worker w + 1's. The XCDs take contiguous ranges of tiles, so
+// each receives the same mix of matrices.
 struct NsBatch {
     NsMat mat[kMaxMatsPerLaunch];
     int32_t nmat;
     int32_t workers;
     int32_t total_tiles;
+    int32_t tiles_per_worker_all;  // tiles of one worker over all matrices
     int32_t use_scales;   // iteration 0: fold s^2 (Gram) and s (product) in
     const float2 *scales;
     float eta;            // EPI_WUPD step size
