@@ -95,25 +95,77 @@ def work_per_kind(wl):
     }
 
 
-def cpu_baseline(wl, j=1):
-    """The oracle, single-threaded, on one matrix of the workload with all
-    workers: one full step (momentum, normalisation, Newton-Schulz, sign/pack,
-    vote, update)."""
+def cpu_baseline(wl, js=(0, 1, 2, 3)):
+    """The oracle, single-threaded, on a bounded sample of the workload: the
+    matrices js (for GPT-2 small, the four matrices of one transformer layer)
+    with all workers, one full step each (momentum, normalisation,
+    Newton-Schulz, sign/pack, vote, update)."""
     import numpy as np
 
     import oracle
     import synthetic
-    R, C = wl.shapes[j]
-    g = synthetic.gradients(wl, j, 0)
-    m = np.zeros((wl.workers, R, C), np.uint16 if wl.mom_dtype == "bf16" else np.float32)
-    w = synthetic.initial_weight(wl, j)
     ns = oracle.BF16 if wl.ns_dtype == "bf16" else oracle.F32
-    t0 = time.perf_counter()
-    oracle.step_matrix(g, m, w, wl.beta, wl.eta, wl.ns_iters, ns, post_k=wl.post_polar_iters)
-    dt = time.perf_counter() - t0
-    return {"value": R * C / dt, "unit": "params/s", "cores": 1, "kind": "oracle",
-            "sample": f"{wl.name} matrix {j} ({R}x{C}), all {wl.workers} workers, one full step; "
-                      f"{dt:.2f} s single-threaded on this host's CPU"}
+    js = [j for j in js if j < len(wl.shapes)]
+    total_s, params = 0.0, 0
+    for j in js:
+        R, C = wl.shapes[j]
+        g = synthetic.gradients(wl, j, 0)
+        m = np.zeros((wl.workers, R, C), np.uint16 if wl.mom_dtype == "bf16" else np.float32)
+        w = synthetic.initial_weight(wl, j)
+        t0 = time.perf_counter()
+        oracle.step_matrix(g, m, w, wl.beta, wl.eta, wl.ns_iters, ns, post_k=wl.post_polar_iters)
+        total_s += time.perf_counter() - t0
+        params += R * C
+    shapes = ", ".join(f"{wl.shapes[j][0]}x{wl.shapes[j][1]}" for j in js)
+    return {"value": params / total_s, "unit": "params/s", "cores": 1, "kind": "oracle",
+            "sample": f"{wl.name} matrices {js[0]}-{js[-1]} ({shapes}; {params} params), all "
+                      f"{wl.workers} workers, one full step each: {total_s:.1f} s single-threaded "
+                      f"on this host's CPU"}
+
+
+KIND_SYMBOL = {"momentum": "momentum_kernel", "scales": "finalize_scales_kernel",
+               "ns_gram": "ns_gram_kernel", "ns_product": "ns_product_kernel",
+               "sign_pack": "sign_pack_kernel", "vote_update": "vote_update_kernel"}
+
+
+def library_source_hash():
+    """sha256 over the library's kernel and host sources (csrc/, sorted)."""
+    import hashlib
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "sign_muon_step_amd", "csrc")
+    for name in sorted(os.listdir(d)):
+        if name.endswith((".hip", ".h")):
+            h.update(name.encode())
+            with open(os.path.join(d, name), "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()
+
+
+def counter_traffic(wl, kind):
+    """HBM bytes per launch of kernel `kind` from the committed rocprofv3
+    counter summary of this workload (FETCH_SIZE and WRITE_SIZE per dispatch,
+    each scaled by the factor a plain copy kernel gives the same counter).
+    None when there is no summary or the library sources changed since the
+    counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{wl.name}.md")
+    if not os.path.exists(path):
+        return None
+    fields, rows = {}, {}
+    with open(path) as f:
+        for line in f:
+            parts = line.split()
+            if len(parts) == 2 and parts[0] in ("source_sha256", "fetch_factor", "write_factor"):
+                fields[parts[0]] = parts[1]
+            elif len(parts) == 4 and parts[0] == "kernel":
+                rows[parts[1]] = (float(parts[2]), float(parts[3]))
+    if fields.get("source_sha256") != library_source_hash():
+        return None
+    sym = KIND_SYMBOL.get(kind)
+    if sym not in rows:
+        return None
+    fetch_kib, write_kib = rows[sym]
+    return int(1024 * (fetch_kib * float(fields["fetch_factor"]) +
+                       write_kib * float(fields["write_factor"])))
 
 
 def main():
@@ -184,6 +236,9 @@ def main():
 
     # per-kernel time per step, from the events around each launch
     per_kind_ms = {}
+    launch_count = {}
+    for kd in traces[0].kinds():
+        launch_count[sm.KERNEL_KINDS[kd]] = launch_count.get(sm.KERNEL_KINDS[kd], 0) + 1
     for tr in traces:
         kinds = tr.kinds()
         if tr.launches + 1 > cap:
@@ -218,7 +273,8 @@ def main():
     d = kernels[dominant]
     roofline = {"bound": d["bound"], "achieved": d["achieved"],
                 "peak": PEAK_HBM_GBS if d["bound"] == "hbm" else mfma_peak, "unit": d["unit"],
-                "frac": d["frac"], "traffic": None, "kernel": dominant}
+                "frac": d["frac"], "traffic": counter_traffic(wl, dominant), "kernel": dominant,
+                "launches_per_step": launch_count.get(dominant, 0)}
     ns_ms = per_kind_ms.get("ns_gram", 0.0) + per_kind_ms.get("ns_product", 0.0)
     ns_flops = work["ns_gram"][1] + work["ns_product"][1]
     ns_util = 100.0 * ns_flops / (ns_ms * 1e-3) / (mfma_peak * 1e12) if ns_ms > 0 else None
