@@ -198,6 +198,7 @@ int run_momentum(const signmuon_matrix *mats, int32_t n_mats, const signmuon_par
             d.m = mats[c0 + j].momentum;
             d.n = q.n;
             d.block_begin = (int32_t)blocks;
+            b.starts.v[j] = d.block_begin;
             d.blocks_per_worker = q.mom_bpw;
             d.partial_begin = q.partial_begin;
             d.unit_begin = q.unit_begin;
@@ -254,6 +255,7 @@ int run_newton_schulz(const signmuon_matrix *mats, int32_t n_mats, const signmuo
                     d.packed = (last && step && q.fused_pack) ? s.packed : nullptr;
                     d.tiles_per_worker = pass == 0 ? sm::ns_gram_tiles(q.R, q.C) : sm::ns_product_tiles(q.R, q.C);
                     d.tile_begin = (int32_t)tiles;
+                    b.starts.v[i] = d.tile_begin;
                     tiles += d.tiles_per_worker;
                 }
                 if (tiles * p->workers > INT32_MAX) return SIGNMUON_ERANGE;
@@ -304,6 +306,7 @@ int run_pack(const signmuon_matrix *mats, int32_t n_mats, const signmuon_params 
             d.unit_begin = q.unit_begin;
             d.blocks_per_worker = (int32_t)((q.nw + sm::kPackWordsPerBlock - 1) / sm::kPackWordsPerBlock);
             d.block_begin = (int32_t)blocks;
+            b.starts.v[i] = d.block_begin;
             blocks += (int64_t)p->workers * d.blocks_per_worker;
         }
         if (blocks > INT32_MAX) return SIGNMUON_ERANGE;
@@ -341,6 +344,7 @@ int run_vote(const signmuon_matrix *mats, int32_t n_mats, const signmuon_params 
             d.nnz = post ? nnz + c0 + i : nullptr;
             d.n = q.n;
             d.block_begin = (int32_t)blocks;
+            b.starts.v[i] = d.block_begin;
             blocks += (q.nw + sm::kVoteWordsPerBlock - 1) / sm::kVoteWordsPerBlock;
         }
         if (blocks > INT32_MAX) return SIGNMUON_ERANGE;
@@ -387,6 +391,7 @@ int run_post_polar(const signmuon_matrix *mats, int32_t n_mats, const signmuon_p
                     d.packed = nullptr;
                     d.tiles_per_worker = pass == 0 ? sm::ns_gram_tiles(q.R, q.C) : sm::ns_product_tiles(q.R, q.C);
                     d.tile_begin = (int32_t)tiles;
+                    b.starts.v[i] = d.tile_begin;
                     tiles += d.tiles_per_worker;
                 }
                 if (tiles > INT32_MAX) return SIGNMUON_ERANGE;
@@ -497,6 +502,7 @@ int signmuon_sign_pack(const void *u, signmuon_dtype u_dtype, int64_t n, int32_t
     b.mat[0].u_out = nullptr;
     b.mat[0].n = n;
     b.mat[0].block_begin = 0;
+    b.starts.v[0] = 0;
     b.mat[0].blocks_per_worker = (int32_t)bpw;
     b.mat[0].unit_begin = 0;
     b.total_blocks = (int32_t)(bpw * workers);
@@ -523,6 +529,7 @@ int signmuon_vote_update(const uint64_t *packed, int32_t workers, int64_t n, flo
     b.mat[0].nnz = nullptr;
     b.mat[0].n = n;
     b.mat[0].block_begin = 0;
+    b.starts.v[0] = 0;
     b.total_blocks = (int32_t)((nw + sm::kVoteWordsPerBlock - 1) / sm::kVoteWordsPerBlock);
     sm::launch_vote_update(b, static_cast<hipStream_t>(stream));
     return last_launch();

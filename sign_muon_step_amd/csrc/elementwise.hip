@@ -34,9 +34,7 @@ __device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
 // Matrix of a flat block index: the descriptors are sorted by block_begin.
 template <typename Batch>
 __device__ __forceinline__ int find_mat(const Batch &b, int blk) {
-    int mi = 0;
-    while (mi + 1 < b.nmat && blk >= b.mat[mi + 1].block_begin) ++mi;
-    return mi;
+    return find_start(b.starts, blk);
 }
 
 // ---------------------------------------------------------------------------

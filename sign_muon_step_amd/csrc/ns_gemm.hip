@@ -31,6 +31,9 @@
 // in memory (X in a wide product, both Gram operands of a tall X) is loaded
 // as 8 x 8 (bf16) or 4 x 4 (fp32) blocks and transposed in registers before
 // the LDS write.
+#include <type_traits>
+#include <utility>
+
 #include "sm_internal.h"
 
 namespace sm {
@@ -211,6 +214,13 @@ struct DmaLoader {
         kstep = KC ? (uint32_t)E::BK * sz : (uint32_t)(E::BK * op.ld) * sz;
     }
 
+    // Load i (0..3) of slice kt only.
+    __device__ __forceinline__ void issue_one(int kt, uint32_t lds, int i) const {
+        const bool ok = ((valid >> i) & 1u) && kt * E::BK + kofs[i] < K;
+        const uint32_t o = ok ? off[i] + (uint32_t)kt * kstep : kOOB;
+        dma16(lds + (uint32_t)(i * 4 + wid) * 1024u, o, rsrc);
+    }
+
     // lds: LDS byte address of this operand's slice buffer.
     __device__ __forceinline__ void issue(int kt, uint32_t lds) const {
         const int k0 = kt * E::BK;
@@ -316,6 +326,23 @@ __device__ __forceinline__ void read_frags(Frags<BF16> &fr, const char *lds_p, c
     }
 }
 
+// Fragment j (0..7) of one half: j < 4 is P block j, j >= 4 is Q block j - 4.
+template <bool BF16, bool PKC, bool QKC>
+__device__ __forceinline__ void read_frag(Frags<BF16> &fr, const char *lds_p, const char *lds_q,
+                                          int wm0, int wn0, int half, int j) {
+    if constexpr (BF16) {
+        if (j < 4)
+            fr.p[j] = frag_bf16<PKC>(lds_p, wm0 + j * 32, half);
+        else
+            fr.q[j - 4] = frag_bf16<QKC>(lds_q, wn0 + (j - 4) * 32, half);
+    } else {
+        if (j < 4)
+            fr.p[j] = frag_f32<PKC>(lds_p, wm0 + j * 32, half);
+        else
+            fr.q[j - 4] = frag_f32<QKC>(lds_q, wn0 + (j - 4) * 32, half);
+    }
+}
+
 // acc[f][g]: 32 x 32 block (f along m, g along n) of the wave's 128 x 128.
 // MFMA 32x32 layout: lane l holds column (l & 31) and, in register r, row
 // 8*(r/4) + 4*(l/32) + (r%4) of the block.
@@ -336,6 +363,19 @@ __device__ __forceinline__ void mma_half(const Frags<BF16> &fr, f32x16_t (&acc)[
 #pragma unroll
                 for (int g = 0; g < 4; ++g)
                     acc[f][g] = __builtin_amdgcn_mfma_f32_32x32x2f32(fr.p[f][st], fr.q[g][st], acc[f][g], 0, 0, 0);
+    }
+}
+
+// Block i (f = i / 4, g = i % 4) of mma_half.
+template <bool BF16>
+__device__ __forceinline__ void mma_step(const Frags<BF16> &fr, f32x16_t (&acc)[4][4], int i) {
+    const int f = i >> 2, g = i & 3;
+    if constexpr (BF16) {
+        acc[f][g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr.p[f], fr.q[g], acc[f][g], 0, 0, 0);
+    } else {
+#pragma unroll
+        for (int st = 0; st < 4; ++st)
+            acc[f][g] = __builtin_amdgcn_mfma_f32_32x32x2f32(fr.p[f][st], fr.q[g][st], acc[f][g], 0, 0, 0);
     }
 }
 
@@ -404,16 +444,50 @@ __device__ __forceinline__ void mma_identity(const Frags<BF16> &fr, f32x16_t (&a
     }
 }
 
-__device__ __forceinline__ void wait_slices(int n) {
-    // vmcnt = 8 loads per slice (4 per operand) times the slices allowed in flight
-    if (n >= 3)
-        wait_vm_lgkm0<24>();
-    else if (n == 2)
-        wait_vm_lgkm0<16>();
-    else if (n == 1)
-        wait_vm_lgkm0<8>();
-    else
-        wait_vm_lgkm0<0>();
+// Identity term of iteration J of a rotated k loop (the tile's own 256 k
+// come first, see tile_mainloop): the slice covers k = J * BK .. + BK - 1 of
+// the tile, i.e. rows (ID_P) or columns (ID_Q) w0 + 32 b + roff .. of the
+// wave's 128 when J * BK lies in [w0, w0 + 128); other waves multiply a zero
+// fragment, so the sequence has no branch.
+template <bool BF16, int SIDE, int J>
+__device__ __forceinline__ void mma_identity_at(const Frags<BF16> &fr, f32x16_t (&acc)[4][4], int w0,
+                                                int half) {
+    constexpr int RS = Elem<BF16>::BK;
+    constexpr int kb = J * RS;
+    constexpr int b = (kb % 128) / 32, roff = kb % 32;
+    const bool active = (kb >= 128) == (w0 >= 128);
+    if constexpr (BF16) {
+        const bf16x8_t one = id_frag_bf16(roff, half);
+        bf16x8_t id;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) id[e] = active ? one[e] : (__bf16)0.0f;
+#pragma unroll
+        for (int o = 0; o < 4; ++o) {
+            if (SIDE == ID_P)
+                acc[b][o] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(id, fr.q[o], acc[b][o], 0, 0, 0);
+            else
+                acc[o][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr.p[o], id, acc[o][b], 0, 0, 0);
+        }
+    } else {
+        const f32x4_t one = id_frag_f32(roff, half);
+        f32x4_t id;
+#pragma unroll
+        for (int st = 0; st < 4; ++st) id[st] = active ? one[st] : 0.0f;
+#pragma unroll
+        for (int st = 0; st < 4; ++st)
+#pragma unroll
+            for (int o = 0; o < 4; ++o) {
+                if (SIDE == ID_P)
+                    acc[b][o] = __builtin_amdgcn_mfma_f32_32x32x2f32(id[st], fr.q[o][st], acc[b][o], 0, 0, 0);
+                else
+                    acc[o][b] = __builtin_amdgcn_mfma_f32_32x32x2f32(fr.p[o][st], id[st], acc[o][b], 0, 0, 0);
+            }
+    }
+}
+
+template <int... Js, class F>
+__device__ __forceinline__ void static_for(std::integer_sequence<int, Js...>, F &&f) {
+    (f(std::integral_constant<int, Js>{}), ...);
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const char *p) {
@@ -432,7 +506,7 @@ template <bool BF16, bool PKC, bool QKC, int SIDE = ID_NONE>
 __device__ __forceinline__ void tile_mainloop(const Operand &P, const Operand &Q, char *smem,
                                               f32x16_t (&acc)[4][4], int id_origin = 0) {
     using E = Elem<BF16>;
-    const int wid = threadIdx.x / kWave;
+    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int wm0 = (wid >> 1) * 128, wn0 = (wid & 1) * 128;
     const int id0 = (id_origin + (SIDE == ID_P ? wm0 : wn0)) / E::BK;  // first identity slice
 #pragma unroll
@@ -448,37 +522,74 @@ __device__ __forceinline__ void tile_mainloop(const Operand &P, const Operand &Q
         lp.init(P);
         lq.init(Q);
         const uint32_t lds0 = lds_addr(smem);
+        // The product visits its k slices starting at the tile's own 256 k
+        // (rotation), so that the identity term falls on the first NID
+        // iterations, which are unrolled. Iteration j reads slice
+        // (j + rot) mod kt_n; iterations j >= kt_n, and every load issued
+        // past the last iteration, read beyond K and land as zeros, so every
+        // iteration issues the same loads and waits for the same count.
+        constexpr int NID = SIDE == ID_NONE ? 0 : kNsTileM / E::BK;
+        const int rot = SIDE == ID_NONE ? 0 : (id_origin / E::BK) % kt_n;
+        const int iters = kt_n > NID ? kt_n : NID;
+        auto slice_of = [&](int j) {
+            const int t = j + rot;
+            return j >= kt_n ? kt_n : (t < kt_n ? t : t - kt_n);
+        };
+        // Slice j + 3's Q loads go out in the first half of iteration j and
+        // slice j + 4's P loads in its second half (one load every other
+        // MFMA), so the prologue issues slices 0-2 and the P part of slice 3.
 #pragma unroll
-        for (int s = 0; s < kStages; ++s)
-            if (s < kt_n) {
-                lp.issue(s, lds0 + s * kStageBytes);
-                lq.issue(s, lds0 + s * kStageBytes + kOpBytes);
-            }
-        const int pre = kt_n - 1 < kStages - 1 ? kt_n - 1 : kStages - 1;
-        wait_slices(pre);
+        for (int st = 0; st < kStages - 1; ++st) {
+            lp.issue(slice_of(st), lds0 + st * kStageBytes);
+            lq.issue(slice_of(st), lds0 + st * kStageBytes + kOpBytes);
+        }
+        lp.issue(slice_of(kStages - 1), lds0 + (kStages - 1) * kStageBytes);
+        wait_vm_lgkm0<20>();  // slice 0 landed; slices 1, 2 and half of 3 in flight
         lds_barrier();
         Frags<BF16> fa, fb;
         read_frags<BF16, PKC, QKC>(fa, smem, smem + kOpBytes, wm0, wn0, 0);
-        for (int kt = 0; kt < kt_n; ++kt) {
-            const char *cur = smem + (kt % kStages) * kStageBytes;
-            read_frags<BF16, PKC, QKC>(fb, cur, cur + kOpBytes, wm0, wn0, 1);
-            mma_half<BF16>(fa, acc);
-            mma_identity<BF16, SIDE>(fa, acc, kt - id0, 0);
-            if (kt + 1 < kt_n) {
-                const int after = kt_n - 2 - kt;  // slices issued after kt + 1
-                wait_slices(after < 2 ? after : 2);
-                lds_barrier();
-                if (kt + kStages < kt_n) {
-                    const uint32_t dst = lds0 + (kt % kStages) * kStageBytes;
-                    lp.issue(kt + kStages, dst);
-                    lq.issue(kt + kStages, dst + kOpBytes);
-                }
-                const char *nxt = smem + ((kt + 1) % kStages) * kStageBytes;
-                read_frags<BF16, PKC, QKC>(fa, nxt, nxt + kOpBytes, wm0, wn0, 0);
+        // Iteration j: the MFMAs of the first half (fa) run while the second
+        // half's fragments (fb) are read and the Q part of slice j + 3 is
+        // loaded into the buffer slice j - 1 left; after the barrier that
+        // hands over slice j + 1, the MFMAs of fb run while the first half of
+        // slice j + 1 is read and the P part of slice j + 4 is loaded into
+        // the buffer slice j leaves. Each read or load sits after one MFMA so
+        // that the matrix pipe does not wait behind a run of them.
+        const int w0 = SIDE == ID_Q ? wn0 : wm0;
+        auto iteration = [&](int j, auto jid) {
+            constexpr int JID = decltype(jid)::value;  // unrolled identity iteration, or -1
+            const char *cur = smem + (j % kStages) * kStageBytes;
+            const int late = slice_of(j + kStages - 1);  // its buffer was freed by barrier j - 1
+            const uint32_t late_dst = lds0 + ((j + kStages - 1) % kStages) * kStageBytes + kOpBytes;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                mma_step<BF16>(fa, acc, i);
+                if (i < 8)
+                    read_frag<BF16, PKC, QKC>(fb, cur, cur + kOpBytes, wm0, wn0, 1, i);
+                else if (i & 1)
+                    lq.issue_one(late, late_dst, (i - 8) >> 1);
+                __builtin_amdgcn_sched_barrier(0);
             }
-            mma_half<BF16>(fb, acc);
-            mma_identity<BF16, SIDE>(fb, acc, kt - id0, 1);
-        }
+            if constexpr (JID >= 0) mma_identity_at<BF16, SIDE, JID>(fa, acc, w0, 0);
+            wait_vm_lgkm0<16>();
+            lds_barrier();
+            const char *nxt = smem + ((j + 1) % kStages) * kStageBytes;
+            const uint32_t dst = lds0 + (j % kStages) * kStageBytes;
+            const int refill = slice_of(j + kStages);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                mma_step<BF16>(fb, acc, i);
+                if (i < 8)
+                    read_frag<BF16, PKC, QKC>(fa, nxt, nxt + kOpBytes, wm0, wn0, 0, i);
+                else if (i & 1)
+                    lp.issue_one(refill, dst, (i - 8) >> 1);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            if constexpr (JID >= 0) mma_identity_at<BF16, SIDE, JID>(fb, acc, w0, 1);
+        };
+        static_for(std::make_integer_sequence<int, NID>{}, [&](auto jid) { iteration(decltype(jid)::value, jid); });
+        for (int j = NID; j < iters; ++j) iteration(j, std::integral_constant<int, -1>{});
+        wait_vm_lgkm0<0>();  // the zero-fill loads past the end write LDS too
     } else {
         SlowLoader<BF16, PKC> lp;
         SlowLoader<BF16, QKC> lq;
@@ -501,18 +612,14 @@ __device__ __forceinline__ void tile_mainloop(const Operand &P, const Operand &Q
     __syncthreads();  // every wave is done with the slices before LDS is reused
 }
 
-__device__ __forceinline__ int find_ns_mat(const NsBatch &b, int t) {
-    int mi = 0;
-    while (mi + 1 < b.nmat && t >= b.mat[mi + 1].tile_begin) ++mi;
-    return mi;
-}
+__device__ __forceinline__ int find_ns_mat(const NsBatch &b, int t) { return find_start(b.starts, t); }
 
 // ---------------------------------------------------------------------------
 // Epilogue helpers. A wave stages 32 rows x 128 columns of fp32 in LDS
 // (row stride kStageStride floats) to turn the MFMA register layout into
 // row-major 4-column pieces.
 // ---------------------------------------------------------------------------
-constexpr int kStageStride = 132;
+constexpr int kStageStride = 136;  // 4 rows apart = 32 banks apart
 static_assert(4 * 32 * kStageStride * 4 <= kLdsBytes, "epilogue stage exceeds LDS");
 
 __device__ __forceinline__ void stage_rows(const f32x16_t (&acc)[4][4], int f, float *stage,
@@ -525,6 +632,13 @@ __device__ __forceinline__ void stage_rows(const f32x16_t (&acc)[4][4], int f, f
             const int row = 8 * (rr >> 2) + 4 * (lane >> 5) + (rr & 3);
             stage[row * kStageStride + 32 * g + (lane & 31)] = acc[f][g][rr] * scale;
         }
+}
+
+// Orders one wave's LDS staging writes before its reads of other lanes'
+// entries (LDS executes a wave's instructions in order; this keeps the
+// compiler from reordering them).
+__device__ __forceinline__ void wave_lds_fence() {
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
 }
 
 // 4 consecutive values at element index idx. FAST: one vector access (the
@@ -573,6 +687,38 @@ __device__ __forceinline__ void store4(void *p, int64_t idx, const float (&v)[4]
 // Each orientation is its own instantiation so that the accumulators stay in
 // registers from the main loop through the epilogue.
 // ---------------------------------------------------------------------------
+// 32 consecutive values at element index idx (one mirrored row segment).
+// FAST: 16-byte stores (the caller guarantees bounds and alignment).
+template <bool BF16, bool FAST>
+__device__ __forceinline__ void store32(void *p, int64_t idx, const float (&v)[32], bool row_ok,
+                                        int cols_left) {
+    if (FAST && BF16) {
+        uint4 *q = reinterpret_cast<uint4 *>(static_cast<uint16_t *>(p) + idx);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            uint32_t w[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                w[e] = f32_to_bf16_bits(v[8 * c + 2 * e]) | (f32_to_bf16_bits(v[8 * c + 2 * e + 1]) << 16);
+            q[c] = make_uint4(w[0], w[1], w[2], w[3]);
+        }
+    } else if (FAST) {
+        float4 *q = reinterpret_cast<float4 *>(static_cast<float *>(p) + idx);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) q[c] = make_float4(v[4 * c], v[4 * c + 1], v[4 * c + 2], v[4 * c + 3]);
+    } else {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            const float w[4] = {v[4 * c], v[4 * c + 1], v[4 * c + 2], v[4 * c + 3]};
+            store4<BF16, false>(p, idx + 4 * c, w, row_ok, cols_left - 4 * c);
+        }
+    }
+}
+
+// Each wave stages its 128 x 128 result 32 rows at a time in its own LDS
+// area, then writes the rows (4 columns per lane) and, above the diagonal,
+// the mirrored tile: lane l reads column l of the staged rows, which is 32
+// consecutive entries of mirrored row n0 + l, and stores them as one run.
 template <bool BF16, bool FAST>
 __device__ __forceinline__ void gram_epilogue(f32x16_t (&acc)[4][4], char *smem, int ti, int tj,
                                               int r, float scale, void *a) {
@@ -583,23 +729,7 @@ __device__ __forceinline__ void gram_epilogue(f32x16_t (&acc)[4][4], char *smem,
 #pragma unroll
     for (int f = 0; f < 4; ++f) {
         stage_rows(acc, f, stage, scale);
-        // Mirror (below the diagonal) straight from the registers: lane holds
-        // 4 consecutive rows of one column, i.e. 4 consecutive entries of the
-        // mirrored row.
-        if (mirror) {
-#pragma unroll
-            for (int g = 0; g < 4; ++g)
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int gi = m0 + f * 32 + 8 * q + 4 * (lane >> 5);
-                    const int gj = n0 + 32 * g + (lane & 31);
-                    float v[4];
-#pragma unroll
-                    for (int t = 0; t < 4; ++t) v[t] = acc[f][g][4 * q + t] * scale;
-                    store4<BF16, FAST>(a, (int64_t)gj * r + gi, v, gj < r, r - gi);
-                }
-        }
-        __syncthreads();
+        wave_lds_fence();
         // Direct tile, row-major: 4 columns per lane, 2 rows per instruction.
 #pragma unroll 4
         for (int it = 0; it < 16; ++it) {
@@ -609,7 +739,18 @@ __device__ __forceinline__ void gram_epilogue(f32x16_t (&acc)[4][4], char *smem,
             float v[4] = {v4.x, v4.y, v4.z, v4.w};
             store4<BF16, FAST>(a, (int64_t)gi * r + gj, v, gi < r, r - gj);
         }
-        __syncthreads();
+        if (mirror) {
+#pragma unroll
+            for (int it = 0; it < 2; ++it) {
+                const int col = it * 64 + lane;
+                float v[32];
+#pragma unroll
+                for (int t = 0; t < 32; ++t) v[t] = stage[t * kStageStride + col];
+                const int gj = n0 + col, gi = m0 + f * 32;
+                store32<BF16, FAST>(a, (int64_t)gj * r + gi, v, gj < r, r - gi);
+            }
+        }
+        wave_lds_fence();
     }
 }
 
@@ -690,7 +831,7 @@ __device__ __forceinline__ void product_epilogue(const ProductArgs &pa, f32x16_t
 #pragma unroll
     for (int f = 0; f < 4; ++f) {
         stage_rows(acc, f, stage, 1.0f);
-        __syncthreads();
+        wave_lds_fence();
 #pragma unroll 4
         for (int it = 0; it < 16; ++it) {
             const int row = it * 2 + (lane >> 5), c4 = (lane & 31) * 4;
@@ -721,7 +862,7 @@ __device__ __forceinline__ void product_epilogue(const ProductArgs &pa, f32x16_t
             if (want_pack) *reinterpret_cast<float4 *>(sp) = make_float4(u[0], u[1], u[2], u[3]);
         }
         if (want_pack) {
-            __syncthreads();
+            wave_lds_fence();
             uint64_t mine = 0;
 #pragma unroll 8
             for (int q = 0; q < 64; ++q) {
@@ -732,7 +873,7 @@ __device__ __forceinline__ void product_epilogue(const ProductArgs &pa, f32x16_t
             const int gm = m0 + f * 32 + (lane >> 1), gn0 = n0 + 64 * (lane & 1);
             if (gm < R && gn0 < C) pa.pk[((int64_t)gm * C + gn0) >> 6] = mine;
         }
-        __syncthreads();
+        wave_lds_fence();
     }
 }
 

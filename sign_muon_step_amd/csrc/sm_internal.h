@@ -4,12 +4,32 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <limits.h>
 
 namespace sm {
 
 // Matrices per kernel launch: the descriptors travel by value in the kernel
 // arguments, which must stay well under the 4 KiB argument limit.
 constexpr int kMaxMatsPerLaunch = 48;
+
+// First block (or tile) of each matrix of a launch, packed contiguously so
+// that a block finds its matrix with a few wide scalar loads and unrolled
+// compares. Entries past the launch's matrices hold INT32_MAX.
+struct Starts {
+    int32_t v[kMaxMatsPerLaunch];
+    __host__ __device__ Starts() {
+        for (int i = 0; i < kMaxMatsPerLaunch; ++i) v[i] = INT32_MAX;
+    }
+};
+
+// Index of the matrix whose range holds block t (starts are non-decreasing
+// and start at 0).
+__device__ __forceinline__ int find_start(const Starts &s, int t) {
+    int mi = 0;
+#pragma unroll
+    for (int j = 1; j < kMaxMatsPerLaunch; ++j) mi += t >= s.v[j] ? 1 : 0;
+    return mi;
+}
 
 // ---------------------------------------------------------------------------
 // Momentum + Frobenius partial sums.
@@ -38,6 +58,7 @@ struct MomBatch {
     int32_t m_bf16;
     double *partials;       // sum of squares of the stored momentum, per block
     float2 *scales;         // per unit: {s = 1/||M||_F, s^2} (0 when ||M|| = 0)
+    Starts starts;         // first block (tile) of each matrix
 };
 
 void launch_momentum(const MomBatch &b, hipStream_t s);
@@ -74,6 +95,7 @@ struct NsBatch {
     const float2 *scales;
     float eta;            // EPI_WUPD step size
     int32_t pad_;
+    Starts starts;         // first block (tile) of each matrix
 };
 
 // Output tile of every Newton-Schulz GEMM.
@@ -116,6 +138,7 @@ struct PackBatch {
     int32_t total_blocks;
     int32_t u_bf16;
     const float2 *scales;  // nullptr: plain sign of u; else sign of s*u
+    Starts starts;         // first block (tile) of each matrix
 };
 
 constexpr int kPackWordsPerWave = 8;
@@ -148,6 +171,7 @@ struct VoteBatch {
     int32_t v_ns_bf16;
     float eta;
     int32_t pad_;
+    Starts starts;         // first block (tile) of each matrix
 };
 
 void launch_vote_update(const VoteBatch &b, hipStream_t s);
@@ -157,4 +181,11 @@ void launch_zero_u32(uint32_t *p, int32_t count, hipStream_t s);
 // scales[unit_begin + i] = {1/sqrt(nnz[i]), 1/nnz[i]} (0 when nnz = 0)
 void launch_nnz_scales(const uint32_t *nnz, int32_t count, float2 *scales, hipStream_t s);
 
+}  // namespace sm
+
+namespace sm {
+// Launch descriptors travel as kernel arguments (4 KiB at most).
+static_assert(sizeof(MomBatch) <= 4000 && sizeof(NsBatch) <= 4000 && sizeof(PackBatch) <= 4000 &&
+                  sizeof(VoteBatch) <= 4000,
+              "launch descriptor exceeds the kernel argument space");
 }  // namespace sm
