@@ -44,19 +44,31 @@ __device__ __forceinline__ int find_mat(const Batch &b, int blk) {
 // the Frobenius normalisation (summary §4 "nanoGPT": Frobenius scaling).
 // ---------------------------------------------------------------------------
 // Raw 16-byte pieces of 8 consecutive entries: fp32 takes two, bf16 one.
+// G and M stream through once, so their loads and stores are nontemporal:
+// they do not displace cache lines that the next kernels reuse.
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
 struct Raw8 {
-    uint4 v[2];
+    u32x4_t v[2];
 };
+
+__device__ __forceinline__ u32x4_t load16_nt(const void *p) {
+    return __builtin_nontemporal_load(static_cast<const u32x4_t *>(p));
+}
+
+__device__ __forceinline__ void store16_nt(void *p, u32x4_t v) {
+    __builtin_nontemporal_store(v, static_cast<u32x4_t *>(p));
+}
 
 template <bool B16>
 __device__ __forceinline__ Raw8 load8(const void *p, int64_t e) {
     Raw8 r;
     if (B16) {
-        r.v[0] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(p) + e);
+        r.v[0] = load16_nt(static_cast<const uint16_t *>(p) + e);
     } else {
-        const uint4 *q = reinterpret_cast<const uint4 *>(static_cast<const float *>(p) + e);
-        r.v[0] = q[0];
-        r.v[1] = q[1];
+        const float *q = static_cast<const float *>(p) + e;
+        r.v[0] = load16_nt(q);
+        r.v[1] = load16_nt(q + 4);
     }
     return r;
 }
@@ -64,16 +76,14 @@ __device__ __forceinline__ Raw8 load8(const void *p, int64_t e) {
 template <bool B16>
 __device__ __forceinline__ void unpack8(const Raw8 &r, float (&x)[8]) {
     if (B16) {
-        const uint32_t w[4] = {r.v[0].x, r.v[0].y, r.v[0].z, r.v[0].w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            x[2 * i] = bf16_bits_to_f32(w[i] & 0xffffu);
-            x[2 * i + 1] = bf16_bits_to_f32(w[i] >> 16);
+            x[2 * i] = bf16_bits_to_f32(r.v[0][i] & 0xffffu);
+            x[2 * i + 1] = bf16_bits_to_f32(r.v[0][i] >> 16);
         }
     } else {
-        const uint32_t w[8] = {r.v[0].x, r.v[0].y, r.v[0].z, r.v[0].w, r.v[1].x, r.v[1].y, r.v[1].z, r.v[1].w};
 #pragma unroll
-        for (int i = 0; i < 8; ++i) x[i] = __uint_as_float(w[i]);
+        for (int i = 0; i < 8; ++i) x[i] = __uint_as_float(r.v[i >> 2][i & 3]);
     }
 }
 
@@ -84,7 +94,7 @@ __device__ __forceinline__ double update8(float beta, const float (&g)[8], const
                                           int64_t e) {
     double ss = 0.0;
     if (MB) {
-        uint32_t out[4];
+        u32x4_t out;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const uint32_t lo = f32_to_bf16_bits(__builtin_fmaf(beta, m[2 * i], g[2 * i]));
@@ -94,18 +104,19 @@ __device__ __forceinline__ double update8(float beta, const float (&g)[8], const
             ss += s0 * s0;
             ss += s1 * s1;
         }
-        *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(mp) + e) = make_uint4(out[0], out[1], out[2], out[3]);
+        store16_nt(static_cast<uint16_t *>(mp) + e, out);
     } else {
-        float y[8];
+        u32x4_t y[2];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            y[i] = __builtin_fmaf(beta, m[i], g[i]);
-            const double d = y[i];
+            const float v = __builtin_fmaf(beta, m[i], g[i]);
+            y[i >> 2][i & 3] = __float_as_uint(v);
+            const double d = v;
             ss += d * d;
         }
-        float4 *q = reinterpret_cast<float4 *>(static_cast<float *>(mp) + e);
-        q[0] = make_float4(y[0], y[1], y[2], y[3]);
-        q[1] = make_float4(y[4], y[5], y[6], y[7]);
+        float *q = static_cast<float *>(mp) + e;
+        store16_nt(q, y[0]);
+        store16_nt(q + 4, y[1]);
     }
     return ss;
 }
@@ -186,23 +197,30 @@ __global__ __launch_bounds__(kMomThreads) void momentum_kernel(MomBatch b) {
     }
 }
 
-// s = 1/||M||_F and s^2 per (matrix, worker), from the block partial sums
-// added in block order (summary §2 "Communication efficiency": the
-// normalisation is local to each worker).
-__global__ void finalize_scales_kernel(MomBatch b) {
-    int u = blockIdx.x * blockDim.x + threadIdx.x;
+// s = 1/||M||_F and s^2 per (matrix, worker) (summary §2 "Communication
+// efficiency": the normalisation is local to each worker). One wave per
+// (matrix, worker): lane l adds the block partial sums l, l + 64, ... in fp64,
+// then a fixed butterfly adds the 64 lane sums, so the result does not depend
+// on timing.
+__global__ __launch_bounds__(256) void finalize_scales_kernel(MomBatch b) {
+    const int u = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + threadIdx.x / kWave);
+    const int lane = threadIdx.x & (kWave - 1);
     if (u >= b.nmat * b.workers) return;
     const MomMat &M = b.mat[u / b.workers];
     const int w = u % b.workers;
     const double *p = b.partials + M.partial_begin + (int64_t)w * M.blocks_per_worker;
     double ss = 0.0;
-    for (int i = 0; i < M.blocks_per_worker; ++i) ss += p[i];
-    float s = 0.f, s2 = 0.f;
-    if (ss > 0.0) {
-        s = (float)(1.0 / sqrt(ss));
-        s2 = (float)(1.0 / ss);
+    for (int i = lane; i < M.blocks_per_worker; i += kWave) ss += p[i];
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
+    if (lane == 0) {
+        float s = 0.f, s2 = 0.f;
+        if (ss > 0.0) {
+            s = (float)(1.0 / sqrt(ss));
+            s2 = (float)(1.0 / ss);
+        }
+        b.scales[M.unit_begin + w] = make_float2(s, s2);
     }
-    b.scales[M.unit_begin + w] = make_float2(s, s2);
 }
 
 // ---------------------------------------------------------------------------
@@ -407,7 +425,7 @@ void launch_momentum(const MomBatch &b, hipStream_t s) {
 
 void launch_finalize_scales(const MomBatch &b, hipStream_t s) {
     int units = b.nmat * b.workers;
-    hipLaunchKernelGGL(finalize_scales_kernel, dim3((units + 255) / 256), dim3(256), 0, s, b);
+    hipLaunchKernelGGL(finalize_scales_kernel, dim3((units + 3) / 4), dim3(256), 0, s, b);
 }
 
 void launch_sign_pack(const PackBatch &b, hipStream_t s) {
