@@ -49,6 +49,8 @@ def _load():
     lib.orc_packed_words.restype = i64
     lib.orc_packed_words.argtypes = [i64]
     lib.orc_vote_update.argtypes = [i64, i32, vp, vp, f32, vp]
+    lib.orc_sign_int8.argtypes = [i64, vp, ctypes.c_int, vp]
+    lib.orc_vote_update_int8.argtypes = [i64, i32, vp, vp, f32, vp]
     lib.orc_post_polar.restype = i64
     lib.orc_post_polar.argtypes = [i64, i64, vp, ctypes.c_int, ctypes.c_int, vp, f32]
     lib.orc_step_matrix.restype = ctypes.c_int
@@ -158,6 +160,26 @@ def vote_update(packed, w, eta, want_vote=True):
     assert packed.shape[1] == packed_words(w.size)
     vote = np.empty(w.shape, np.int8) if want_vote else None
     _load().orc_vote_update(w.size, mw, _ptr(packed), _ptr(w), eta, _ptr(vote))
+    return vote
+
+
+def sign_int8(u):
+    """Int8 payload: +1 where u >= 0, -1 elsewhere (the packed bits' rule)."""
+    u = _c(u)
+    out = np.empty(u.shape, np.int8)
+    _load().orc_sign_int8(u.size, _ptr(u), _dtype_code(u), _ptr(out))
+    return out
+
+
+def vote_update_int8(signs, w, eta, want_vote=True):
+    """Int8 payload vote: signs is [mw][n] int8; the vote is the sign of the
+    integer sum over workers; W (float32) is updated in place."""
+    signs = _c(signs, np.int8)
+    mw = signs.shape[0]
+    assert w.dtype == np.float32 and w.flags.c_contiguous
+    assert signs.reshape(mw, -1).shape[1] == w.size
+    vote = np.empty(w.shape, np.int8) if want_vote else None
+    _load().orc_vote_update_int8(w.size, mw, _ptr(signs), _ptr(w), eta, _ptr(vote))
     return vote
 
 

@@ -285,6 +285,37 @@ void orc_vote_update(int64_t n, int32_t mw, const uint64_t *packed, float *w, fl
 }
 
 /* ------------------------------------------------------------------------ */
+/* Int8 payload -- §2 "Core mechanism" (the vote as an integer SUM           */
+/* all-reduce of the workers' signs followed by a local sign) and §2         */
+/* "Communication efficiency" (eight bits per entry with int8). Each worker  */
+/* sends its signs as int8 +1 / -1 with the same rule as the packed bits     */
+/* (u >= 0 gives +1); the vote is the sign of the plain integer sum of the   */
+/* workers' values, and the update is that of O7.                            */
+/* ------------------------------------------------------------------------ */
+void orc_sign_int8(int64_t n, const void *u, int u_dt, int8_t *s)
+{
+    for (int64_t i = 0; i < n; ++i)
+        s[i] = load_elem(u, u_dt, i) >= 0.0 ? (int8_t)1 : (int8_t)-1;
+}
+
+void orc_vote_update_int8(int64_t n, int32_t mw, const int8_t *signs, float *w, float eta,
+                          int8_t *vote)
+{
+    for (int64_t i = 0; i < n; ++i) {
+        int64_t sum = 0;
+        for (int32_t m = 0; m < mw; ++m)
+            sum += signs[(int64_t)m * n + i];
+        int8_t v = sum > 0 ? 1 : (sum < 0 ? -1 : 0);
+        if (w && v > 0)
+            w[i] = w[i] - eta;
+        else if (w && v < 0)
+            w[i] = w[i] + eta;
+        if (vote)
+            vote[i] = v;
+    }
+}
+
+/* ------------------------------------------------------------------------ */
 /* O8 optional post-vote polar step -- §2 "Algorithmic flow" step 5 (a local */
 /* polar step on the aggregated sign matrix, no extra communication).        */
 /* Readings: the same Frobenius-normalised Newton-Schulz as O2-O3 applied to */

@@ -72,6 +72,13 @@ int64_t orc_packed_words(int64_t n);
 void orc_vote_update(int64_t n, int32_t mw, const uint64_t *packed, float *w, float eta,
                      int8_t *vote);
 
+/* Int8 payload: s[i] = +1 if u >= 0 else -1 (as the packed bits), and the
+ * vote as the sign of the integer sum of the mw workers' int8 values
+ * ([mw][n]), with the update of orc_vote_update. */
+void orc_sign_int8(int64_t n, const void *u, int u_dt, int8_t *s);
+void orc_vote_update_int8(int64_t n, int32_t mw, const int8_t *signs, float *w, float eta,
+                          int8_t *vote);
+
 /* O8 optional post-vote polar step: W <- fmaf(-eta, Y, W) with Y the k-step
  * Newton-Schulz factor of V / ||V||_F. Returns nnz(V); W is unchanged when
  * nnz(V) = 0. Returns -1 when memory runs out. */

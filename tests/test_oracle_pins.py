@@ -405,6 +405,73 @@ def test_vote_random_against_counting(mw):
     np.testing.assert_array_equal(w2, w)
 
 
+# ---------------------------------------------------------------------------
+# int8 payload: the vote as the sign of the integer sum of the workers' signs
+# (summary §2 "Core mechanism" and "Communication efficiency")
+# ---------------------------------------------------------------------------
+def test_int8_signs_follow_the_packed_rule():
+    rng = np.random.default_rng(31)
+    u = rng.standard_normal(1000).astype(np.float32)
+    u[:4] = [0.0, -0.0, np.nan, -np.inf]
+    s = oracle.sign_int8(u)
+    bits = np.unpackbits(oracle.sign_pack(u).view(np.uint8), bitorder="little")[:u.size]
+    np.testing.assert_array_equal(s, 2 * bits.astype(np.int8) - 1)
+    assert set(np.unique(s)) <= {-1, 1}
+
+
+def test_int8_payload_is_eight_bits_per_entry(golden_dir):
+    spec = json.load(open(os.path.join(golden_dir, "payload_ratio.json")))
+    n = 4096
+    s = oracle.sign_int8(np.ones(n, np.float32))
+    assert s.nbytes * 8 == spec["bits_per_param_int8"] * n
+    assert 32 // spec["bits_per_param_int8"] == spec["reduction_vs_fp32_int8"]
+
+
+@pytest.mark.parametrize("mw", [1, 2, 3, 4, 5, 8, 10, 16, 17])
+def test_int8_vote_equals_packed_vote(mw):
+    """Two formulations of the same vote: the integer sum of +-1 values and
+    the count of set bits."""
+    rng = np.random.default_rng(100 + mw)
+    n = 2049
+    u = rng.standard_normal((mw, n)).astype(np.float32)
+    u[:, :7] = 0.0  # ties of +0 values and (even mw) tied votes
+    packed = np.stack([oracle.sign_pack(u[m]) for m in range(mw)])
+    signs = np.stack([oracle.sign_int8(u[m]) for m in range(mw)])
+    w0 = rng.standard_normal(n).astype(np.float32)
+    w_a, w_b = w0.copy(), w0.copy()
+    v_a = oracle.vote_update(packed, w_a, 1e-3)
+    v_b = oracle.vote_update_int8(signs, w_b, 1e-3)
+    np.testing.assert_array_equal(v_a, v_b)
+    np.testing.assert_array_equal(w_a.view(np.uint32), w_b.view(np.uint32))
+
+
+def test_int8_vote_brute_force_general_values():
+    """The sum is the plain integer sum of the int8 values (any value, not
+    only +-1): checked entry by entry in Python."""
+    rng = np.random.default_rng(5)
+    mw, n = 6, 300
+    signs = rng.integers(-128, 128, (mw, n)).astype(np.int8)
+    signs[:, :5] = 0
+    w0 = rng.standard_normal(n).astype(np.float32)
+    w = w0.copy()
+    vote = oracle.vote_update_int8(signs, w, 0.5)
+    for i in range(n):
+        total = sum(int(signs[m, i]) for m in range(mw))
+        expect = (total > 0) - (total < 0)
+        assert vote[i] == expect
+        assert w[i] == np.float32(w0[i] - np.float32(0.5) * expect)
+
+
+def test_int8_vote_worked_example_from_pages(golden_dir):
+    spec = json.load(open(os.path.join(golden_dir, "vote_worked_example.json")))
+    for case in spec["cases"]:
+        mw, plus = case["workers"], case["plus_votes"]
+        signs = -np.ones((mw, 1), np.int8)
+        signs[:plus, 0] = 1
+        w = np.zeros(1, np.float32)
+        assert oracle.vote_update_int8(signs, w, 1.0)[0] == case["expected_vote"]
+
+
 def test_update_moves_exactly_eta_on_dyadic_grid():
     rng = np.random.default_rng(9)
     n = 5000
