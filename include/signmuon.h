@@ -143,6 +143,32 @@ int signmuon_vote_update(const uint64_t *packed, int32_t workers, int64_t n, flo
                          float eta, int8_t *vote_out, signmuon_stream stream);
 
 /*
+ * signmuon_sign_int8 -- the int8 payload of the signs (summary §2
+ * "Communication efficiency": eight bits per entry with int8, 4x below fp32):
+ * signs[i] = +1 where u[i] >= 0, else -1 -- the rule of the packed bits, so
+ * +0 and -0 give +1 and NaN gives -1. u is [workers][n] of u_dtype (F32 or
+ * BF16); signs receives [workers][n] int8.
+ */
+int signmuon_sign_int8(const void *u, signmuon_dtype u_dtype, int64_t n, int32_t workers,
+                       int8_t *signs, signmuon_stream stream);
+
+/*
+ * signmuon_vote_update_int8 -- the vote from int8 payloads (summary §2 "Core
+ * mechanism": an integer SUM all-reduce of the workers' signs followed by a
+ * local sign; "Algorithmic flow" step 4 for the update):
+ *   t_i = sum over workers m of signs[m][i]   (plain integer sum)
+ *   S-bar_i = sign(t_i), and W as in signmuon_vote_update.
+ * On one GPU the sum runs over the workers' buffers in memory, as every rank
+ * would after an integer all-reduce. With +-1 inputs (signmuon_sign_int8) the
+ * vote and W equal those of signmuon_vote_update on the packed bits. signs
+ * is [workers][n] int8 (any int8 values are summed as integers); weight [n]
+ * fp32 in place (NULL: vote only); vote_out [n] int8 or NULL. At least one of
+ * weight and vote_out must be non-NULL; workers <= 255.
+ */
+int signmuon_vote_update_int8(const int8_t *signs, int32_t workers, int64_t n, float *weight,
+                              float eta, int8_t *vote_out, signmuon_stream stream);
+
+/*
  * signmuon_step -- one whole optimizer step for every matrix (summary §2
  * "Algorithmic flow", steps 1-5 with the collective of step 3 replaced by the
  * workers' packed buffers being local): signmuon_momentum_ns, the sign and

@@ -79,6 +79,10 @@ def library() -> ctypes.CDLL:
     lib.signmuon_sign_pack.argtypes = [vp, ctypes.c_int, i64, i32, vp, vp]
     lib.signmuon_vote_update.restype = ctypes.c_int
     lib.signmuon_vote_update.argtypes = [vp, i32, i64, vp, ctypes.c_float, vp, vp]
+    lib.signmuon_sign_int8.restype = ctypes.c_int
+    lib.signmuon_sign_int8.argtypes = [vp, ctypes.c_int, i64, i32, vp, vp]
+    lib.signmuon_vote_update_int8.restype = ctypes.c_int
+    lib.signmuon_vote_update_int8.argtypes = [vp, i32, i64, vp, ctypes.c_float, vp, vp]
     lib.signmuon_packed_words.restype = ctypes.c_size_t
     lib.signmuon_packed_words.argtypes = [i64]
     lib.signmuon_workspace_bytes.restype = ctypes.c_size_t
@@ -234,6 +238,19 @@ def signmuon_vote_update(packed: torch.Tensor, workers: int, n: int, weight: Opt
                          eta: float, vote_out: Optional[torch.Tensor] = None, stream=None) -> None:
     _check(library().signmuon_vote_update(_ptr(packed), workers, n, _ptr(weight), eta,
                                           _ptr(vote_out), _stream(stream)))
+
+
+def signmuon_sign_int8(u: torch.Tensor, n: int, workers: int, signs: torch.Tensor,
+                       stream=None) -> None:
+    _check(library().signmuon_sign_int8(_ptr(u), _dtype_code(u), n, workers, _ptr(signs),
+                                        _stream(stream)))
+
+
+def signmuon_vote_update_int8(signs: torch.Tensor, workers: int, n: int,
+                              weight: Optional[torch.Tensor], eta: float,
+                              vote_out: Optional[torch.Tensor] = None, stream=None) -> None:
+    _check(library().signmuon_vote_update_int8(_ptr(signs), workers, n, _ptr(weight), eta,
+                                               _ptr(vote_out), _stream(stream)))
 
 
 def dtype_code(t: torch.dtype) -> int:

@@ -535,4 +535,27 @@ int signmuon_vote_update(const uint64_t *packed, int32_t workers, int64_t n, flo
     return last_launch();
 }
 
+int signmuon_sign_int8(const void *u, signmuon_dtype u_dtype, int64_t n, int32_t workers, int8_t *signs,
+                       signmuon_stream stream) {
+    if (!u || !signs || n < 1 || workers < 1) return SIGNMUON_EINVAL;
+    if (!dtype_ok(u_dtype)) return SIGNMUON_EDTYPE;
+    if (!aligned16(u) || !aligned16(signs)) return SIGNMUON_EALIGN;
+    if (n > kMaxN || workers > kMaxWorkers) return SIGNMUON_ERANGE;
+    const int64_t total = n * workers;
+    if (sm::sign_int8_blocks(total) > INT32_MAX) return SIGNMUON_ERANGE;
+    sm::launch_sign_int8(u, u_dtype == SIGNMUON_BF16, total, signs, static_cast<hipStream_t>(stream));
+    return last_launch();
+}
+
+int signmuon_vote_update_int8(const int8_t *signs, int32_t workers, int64_t n, float *weight, float eta,
+                              int8_t *vote_out, signmuon_stream stream) {
+    if (!signs || n < 1 || workers < 1 || (!weight && !vote_out)) return SIGNMUON_EINVAL;
+    if (!std::isfinite(eta)) return SIGNMUON_EINVAL;
+    if (workers > kMaxWorkers || n > kMaxN) return SIGNMUON_ERANGE;
+    if (!aligned16(signs) || (weight && !aligned16(weight)) || (vote_out && !aligned16(vote_out)))
+        return SIGNMUON_EALIGN;
+    sm::launch_vote_update_int8(signs, workers, n, weight, eta, vote_out, static_cast<hipStream_t>(stream));
+    return last_launch();
+}
+
 }  // extern "C"

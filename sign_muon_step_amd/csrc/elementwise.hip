@@ -409,6 +409,117 @@ __global__ void nnz_scales_kernel(const uint32_t *nnz, int32_t count, float2 *sc
     scales[i] = c > 0.0 ? make_float2((float)(1.0 / sqrt(c)), (float)(1.0 / c)) : make_float2(0.f, 0.f);
 }
 
+// ---------------------------------------------------------------------------
+// Int8 payload (summary §2 "Core mechanism": the vote as an integer SUM
+// all-reduce of the workers' signs followed by a local sign; §2
+// "Communication efficiency": eight bits per entry with int8). Both kernels
+// stream 16 entries per thread.
+// ---------------------------------------------------------------------------
+constexpr int kI8PerThread = 16;
+constexpr int kI8PerBlock = 256 * kI8PerThread;
+
+// signs[i] = +1 where u[i] >= 0, else -1, over the flat [workers][n] array.
+template <bool UB>
+__global__ __launch_bounds__(256) void sign_int8_kernel(const void *u, int64_t total, int8_t *signs) {
+    const int64_t e0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * kI8PerThread;
+    if (e0 >= total) return;
+    if (e0 + kI8PerThread <= total) {
+        float x[kI8PerThread];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            Raw8 r = load8<UB>(u, e0 + 8 * h);
+            float y[8];
+            unpack8<UB>(r, y);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) x[8 * h + i] = y[i];
+        }
+        u32x4_t out;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            uint32_t wd = 0;
+#pragma unroll
+            for (int b = 0; b < 4; ++b) wd |= (x[4 * q + b] >= 0.f ? 0x01u : 0xffu) << (8 * b);
+            out[q] = wd;
+        }
+        store16_nt(signs + e0, out);
+    } else {
+        for (int64_t e = e0; e < total; ++e) {
+            const float v = UB ? bf16_bits_to_f32(static_cast<const uint16_t *>(u)[e]) : static_cast<const float *>(u)[e];
+            signs[e] = v >= 0.f ? (int8_t)1 : (int8_t)-1;
+        }
+    }
+}
+
+// vote_i = sign(sum over workers of signs[m][i]) and the update of W. VEC:
+// n % 16 == 0, so every worker's row of 16 entries is one 16-byte load.
+template <bool VEC>
+__global__ __launch_bounds__(256) void vote_update_int8_kernel(const int8_t *signs, int32_t mw, int64_t n,
+                                                              float *w, float eta, int8_t *vote) {
+    const int64_t e0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * kI8PerThread;
+    if (e0 >= n) return;
+    if (VEC) {
+        int32_t t[kI8PerThread];
+#pragma unroll
+        for (int i = 0; i < kI8PerThread; ++i) t[i] = 0;
+        const int8_t *p = signs + e0;
+        auto add = [&](const u32x4_t &r) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int b = 0; b < 4; ++b) t[4 * q + b] += (int32_t)(int8_t)(r[q] >> (8 * b));
+        };
+        int m = 0;
+        for (; m + 4 <= mw; m += 4) {  // four workers' loads in flight together
+            u32x4_t r[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) r[k] = load16_nt(p + (int64_t)(m + k) * n);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) add(r[k]);
+        }
+        for (; m < mw; ++m) add(load16_nt(p + (int64_t)m * n));
+        if (w) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                float4 *wp = reinterpret_cast<float4 *>(w + e0 + 4 * q);
+                float4 v = *wp;
+                float *f = &v.x;
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    const int32_t ti = t[4 * q + b];
+                    f[b] = ti > 0 ? f[b] - eta : (ti < 0 ? f[b] + eta : f[b]);
+                }
+                *wp = v;
+            }
+        }
+        if (vote) {
+            u32x4_t out;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                uint32_t wd = 0;
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    const int32_t ti = t[4 * q + b];
+                    wd |= (uint32_t)(uint8_t)(int8_t)(ti > 0 ? 1 : (ti < 0 ? -1 : 0)) << (8 * b);
+                }
+                out[q] = wd;
+            }
+            *reinterpret_cast<u32x4_t *>(vote + e0) = out;
+        }
+    } else {
+        const int64_t e1 = e0 + kI8PerThread < n ? e0 + kI8PerThread : n;
+        for (int64_t e = e0; e < e1; ++e) {
+            int32_t ti = 0;
+            for (int m = 0; m < mw; ++m) ti += signs[(int64_t)m * n + e];
+            const int v = ti > 0 ? 1 : (ti < 0 ? -1 : 0);
+            if (w && v > 0)
+                w[e] = w[e] - eta;
+            else if (w && v < 0)
+                w[e] = w[e] + eta;
+            if (vote) vote[e] = (int8_t)v;
+        }
+    }
+}
+
 }  // namespace
 
 void launch_momentum(const MomBatch &b, hipStream_t s) {
@@ -460,6 +571,29 @@ void launch_nnz_scales(const uint32_t *nnz, int32_t count, float2 *scales, hipSt
     if (count <= 0) return;
     hipLaunchKernelGGL(nnz_scales_kernel, dim3((count + 255) / 256), dim3(256), 0, s, nnz, count,
                        scales);
+}
+
+}  // namespace sm
+
+namespace sm {
+
+int64_t sign_int8_blocks(int64_t total) { return (total + kI8PerBlock - 1) / kI8PerBlock; }
+
+void launch_sign_int8(const void *u, bool u_bf16, int64_t total, int8_t *signs, hipStream_t s) {
+    dim3 grid((unsigned)sign_int8_blocks(total)), block(256);
+    if (u_bf16)
+        hipLaunchKernelGGL(sign_int8_kernel<true>, grid, block, 0, s, u, total, signs);
+    else
+        hipLaunchKernelGGL(sign_int8_kernel<false>, grid, block, 0, s, u, total, signs);
+}
+
+void launch_vote_update_int8(const int8_t *signs, int32_t workers, int64_t n, float *w, float eta,
+                             int8_t *vote, hipStream_t s) {
+    dim3 grid((unsigned)sign_int8_blocks(n)), block(256);
+    if (n % kI8PerThread == 0)
+        hipLaunchKernelGGL(vote_update_int8_kernel<true>, grid, block, 0, s, signs, workers, n, w, eta, vote);
+    else
+        hipLaunchKernelGGL(vote_update_int8_kernel<false>, grid, block, 0, s, signs, workers, n, w, eta, vote);
 }
 
 }  // namespace sm

@@ -176,6 +176,13 @@ struct VoteBatch {
 
 void launch_vote_update(const VoteBatch &b, hipStream_t s);
 
+// Int8 payload: signs of a flat [workers][n] array, and the vote as the sign
+// of the integer sum over workers with the update of W.
+int64_t sign_int8_blocks(int64_t total);
+void launch_sign_int8(const void *u, bool u_bf16, int64_t total, int8_t *signs, hipStream_t s);
+void launch_vote_update_int8(const int8_t *signs, int32_t workers, int64_t n, float *w, float eta,
+                             int8_t *vote, hipStream_t s);
+
 // Post-vote polar step helpers.
 void launch_zero_u32(uint32_t *p, int32_t count, hipStream_t s);
 // scales[unit_begin + i] = {1/sqrt(nnz[i]), 1/nnz[i]} (0 when nnz = 0)

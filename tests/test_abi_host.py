@@ -128,3 +128,21 @@ def test_sign_pack_and_vote_argument_errors(lib):
     assert lib.signmuon_vote_update(a, 3, 10, a, float("nan"), None, None) == -1
     assert lib.signmuon_vote_update(a, 256, 10, a, 1e-3, None, None) == -6
     assert lib.signmuon_vote_update(a, 3, 10, a + 8, 1e-3, None, None) == -3
+
+
+def test_int8_payload_argument_errors(lib):
+    a = 0x7f0000000000
+    assert lib.signmuon_sign_int8(None, 0, 10, 1, a, None) == -1
+    assert lib.signmuon_sign_int8(a, 0, 10, 1, None, None) == -1
+    assert lib.signmuon_sign_int8(a, 0, 0, 1, a, None) == -1
+    assert lib.signmuon_sign_int8(a, 0, 10, 0, a, None) == -1
+    assert lib.signmuon_sign_int8(a, 7, 10, 1, a, None) == -2
+    assert lib.signmuon_sign_int8(a, 0, 10, 1, a + 1, None) == -3
+    assert lib.signmuon_sign_int8(a, 0, 10, 256, a, None) == -6
+    assert lib.signmuon_vote_update_int8(None, 3, 10, a, 1e-3, None, None) == -1
+    assert lib.signmuon_vote_update_int8(a, 3, 10, None, 1e-3, None, None) == -1
+    assert lib.signmuon_vote_update_int8(a, 0, 10, a, 1e-3, None, None) == -1
+    assert lib.signmuon_vote_update_int8(a, 3, 10, a, float("inf"), None, None) == -1
+    assert lib.signmuon_vote_update_int8(a, 256, 10, a, 1e-3, None, None) == -6
+    assert lib.signmuon_vote_update_int8(a + 2, 3, 10, a, 1e-3, None, None) == -3
+    assert lib.signmuon_vote_update_int8(a, 3, 10, a, 1e-3, a + 4, None) == -3
