@@ -75,6 +75,15 @@ class Hip:
     def destroy(self, e):
         self.lib.hipEventDestroy(e)
 
+    def record(self, e, stream):
+        self.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        if self.lib.hipEventRecord(e, stream) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def sync(self, e):
+        self.lib.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.lib.hipEventSynchronize(e)
+
 
 def work_per_kind(wl):
     """Algorithmic work of each kernel kind in one step: flops for the
@@ -93,6 +102,41 @@ def work_per_kind(wl):
         "sign_pack": ("hbm", mw * unfused * (4 + 1 / 8)),
         "vote_update": ("hbm", n * (mw / 8 + 8)),
     }
+
+
+def time_int8_payload(sm, mats, wl, hip, dev, reps=10):
+    """The int8 payload on the workload's matrices: every worker's signs of
+    its (stored) momentum as int8, then the vote from the int8 buffers with
+    the update of W. HIP events on the library's stream bracket each kind's
+    launches (one launch per matrix); times are per step of all matrices."""
+    import torch
+    stream = torch.cuda.current_stream().cuda_stream
+    signs = [torch.empty((wl.workers, R * C), dtype=torch.int8, device=dev) for R, C in wl.shapes]
+    ev = [hip.event() for _ in range(3)]
+    acc = [0.0, 0.0]
+    for rep in range(reps + 1):
+        hip.record(ev[0], stream)
+        for j, (R, C) in enumerate(wl.shapes):
+            sm.signmuon_sign_int8(mats[j].momentum, R * C, wl.workers, signs[j])
+        hip.record(ev[1], stream)
+        for j, (R, C) in enumerate(wl.shapes):
+            sm.signmuon_vote_update_int8(signs[j], wl.workers, R * C, mats[j].weight, wl.eta, None)
+        hip.record(ev[2], stream)
+        hip.sync(ev[2])
+        if rep:  # the first round warms up
+            acc[0] += hip.elapsed_ms(ev[0], ev[1])
+            acc[1] += hip.elapsed_ms(ev[1], ev[2])
+    for e in ev:
+        hip.destroy(e)
+    s_m = 4 if wl.mom_dtype == "f32" else 2
+    out = {}
+    for name, ms, nbytes in [("sign_int8", acc[0] / reps, wl.workers * wl.params * (s_m + 1)),
+                             ("vote_update_int8", acc[1] / reps, wl.params * (wl.workers + 8))]:
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        out[name] = {"ms": round(ms, 5), "bound": "hbm", "achieved": round(gbs, 1), "unit": "GB/s",
+                     "frac": round(gbs / PEAK_HBM_GBS, 4), "algorithmic_bytes": int(nbytes),
+                     "launches": len(wl.shapes)}
+    return out
 
 
 def cpu_baseline(wl, js=(0, 1, 2, 3)):
@@ -280,6 +324,9 @@ def main():
     ns_util = 100.0 * ns_flops / (ns_ms * 1e-3) / (mfma_peak * 1e12) if ns_ms > 0 else None
     vote_gbs = kernels.get("vote_update", {}).get("achieved")
 
+    log("[bench] timing the int8 payload (sign_int8 + vote_update_int8)")
+    int8 = time_int8_payload(sm, mats, wl, hip, dev)
+
     base = None
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample")
@@ -302,12 +349,13 @@ def main():
         "vote_update_hbm_gbs": vote_gbs,
         "kernels_ms_per_step": kernels,
         "launches_per_step": launches,
+        "int8_payload": int8,
         "roofline": roofline,
         "cpu_baseline": base,
     }
     log("[bench] " + ", ".join(f"{k} {v['ms']:.3f} ms" + (f" ({v['frac'] * 100:.1f}% of "
                                                           f"{v['bound']})" if "frac" in v else "")
-                               for k, v in kernels.items()))
+                               for k, v in list(kernels.items()) + list(int8.items())))
     print(json.dumps(out), flush=True)
     del np
 
