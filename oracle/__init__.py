@@ -43,6 +43,16 @@ def _load():
     lib.orc_normalise.argtypes = [i64, vp, ctypes.c_int, vp]
     lib.orc_newton_schulz.restype = ctypes.c_int
     lib.orc_newton_schulz.argtypes = [i64, i64, vp, ctypes.c_int, ctypes.c_int, vp]
+    lib.orc_newton_schulz_a0.restype = ctypes.c_int
+    lib.orc_newton_schulz_a0.argtypes = [i64, i64, vp, vp, ctypes.c_int, ctypes.c_int, vp]
+    lib.orc_power_lambda.restype = f64
+    lib.orc_power_lambda.argtypes = [i64, vp, ctypes.c_int]
+    lib.orc_spectral_x0_a0.restype = f64
+    lib.orc_spectral_x0_a0.argtypes = [i64, i64, vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp]
+    lib.orc_step_matrix_norm.restype = ctypes.c_int
+    lib.orc_step_matrix_norm.argtypes = [i64, i64, i32, f32, f32, ctypes.c_int, ctypes.c_int,
+                                         ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                         ctypes.c_int, vp, vp, vp, vp, vp, vp]
     lib.orc_ns1_entries.restype = ctypes.c_int
     lib.orc_ns1_entries.argtypes = [i64, i64, vp, ctypes.c_int, i64, vp, vp, vp]
     lib.orc_sign_pack.argtypes = [i64, vp, ctypes.c_int, vp]
@@ -123,6 +133,45 @@ def newton_schulz(x0, k, ns_dtype):
     return u
 
 
+NORM_FROB, NORM_SPECTRAL = 0, 1
+
+
+def newton_schulz_a0(x0, a0, k, ns_dtype):
+    """O3 with the first iteration's Gram matrix a0 (r x r, already rounded)."""
+    x0 = _c(x0, np.float64)
+    a0 = _c(a0, np.float64)
+    R, C = x0.shape
+    r = min(R, C)
+    assert a0.shape == (r, r)
+    u = np.empty_like(x0)
+    if _load().orc_newton_schulz_a0(R, C, _ptr(x0), _ptr(a0), k, ns_dtype, _ptr(u)) != 0:
+        raise MemoryError("oracle newton_schulz_a0")
+    return u
+
+
+def power_lambda(a, p):
+    """Spectral normalisation: p power-iteration steps on the symmetric a
+    from the all-ones vector; the last ||A v||."""
+    a = _c(a, np.float64)
+    lam = _load().orc_power_lambda(a.shape[0], _ptr(a), p)
+    if lam < 0:
+        raise MemoryError("oracle power_lambda")
+    return float(lam)
+
+
+def spectral_x0_a0(m, ns_dtype, p):
+    """Spectral normalisation of one stored R x C momentum: (lambda, x0, a0)."""
+    m = _c(m)
+    R, C = m.shape
+    r = min(R, C)
+    x0 = np.empty((R, C), np.float64)
+    a0 = np.empty((r, r), np.float64)
+    lam = _load().orc_spectral_x0_a0(R, C, _ptr(m), _dtype_code(m), ns_dtype, p, _ptr(x0), _ptr(a0))
+    if lam < 0:
+        raise MemoryError("oracle spectral_x0_a0")
+    return float(lam), x0, a0
+
+
 def ns1_entries(x0, ns_dtype, rows, cols):
     """O3 with k = 1, evaluated only at the (rows[t], cols[t]) entries."""
     x0 = _c(x0, np.float64)
@@ -194,7 +243,7 @@ def post_polar(vote, w, eta, k, ns_dtype):
     return int(nnz)
 
 
-def step_matrix(g, m, w, beta, eta, k, ns_dtype, post_k=0, want_u=False):
+def step_matrix(g, m, w, beta, eta, k, ns_dtype, post_k=0, want_u=False, norm=0, power_iters=0):
     """One full step for one R x C matrix and all workers.
 
     g: [mw][R][C] float32 (or bf16 uint16); m: [mw][R][C] float32 or uint16,
@@ -208,9 +257,9 @@ def step_matrix(g, m, w, beta, eta, k, ns_dtype, post_k=0, want_u=False):
     packed = np.empty((mw, packed_words(R * C)), np.uint64)
     vote = np.empty((R, C), np.int8)
     u = np.empty((mw, R, C), np.float64) if want_u else None
-    rc = _load().orc_step_matrix(R, C, mw, beta, eta, k, post_k, _dtype_code(g), _dtype_code(m),
-                                 ns_dtype, _ptr(g), _ptr(m), _ptr(u), _ptr(packed), _ptr(w),
-                                 _ptr(vote))
+    rc = _load().orc_step_matrix_norm(R, C, mw, beta, eta, k, post_k, _dtype_code(g),
+                                      _dtype_code(m), ns_dtype, norm, power_iters, _ptr(g), _ptr(m),
+                                      _ptr(u), _ptr(packed), _ptr(w), _ptr(vote))
     if rc != 0:
         raise MemoryError("oracle step_matrix")
     return packed, vote, u

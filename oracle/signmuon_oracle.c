@@ -173,7 +173,24 @@ static void gram_product(int64_t R, int64_t C, const double *a, const double *x,
     }
 }
 
+static int newton_schulz(int64_t R, int64_t C, const double *x0, const double *a0, int k,
+                         int ns_dt, double *u);
+
 int orc_newton_schulz(int64_t R, int64_t C, const double *x0, int k, int ns_dt, double *u)
+{
+    return newton_schulz(R, C, x0, NULL, k, ns_dt, u);
+}
+
+int orc_newton_schulz_a0(int64_t R, int64_t C, const double *x0, const double *a0, int k,
+                         int ns_dt, double *u)
+{
+    return newton_schulz(R, C, x0, a0, k, ns_dt, u);
+}
+
+/* a0 (nullable): the first iteration's Gram matrix, already rounded; the
+ * later iterations form their own. */
+static int newton_schulz(int64_t R, int64_t C, const double *x0, const double *a0, int k,
+                         int ns_dt, double *u)
 {
     int64_t n = R * C, r = R <= C ? R : C;
     double *x = (double *)malloc(sizeof(double) * (size_t)n);
@@ -185,7 +202,10 @@ int orc_newton_schulz(int64_t R, int64_t C, const double *x0, int k, int ns_dt, 
     }
     memcpy(x, x0, sizeof(double) * (size_t)n);
     for (int j = 0; j < k; ++j) {
-        gram(R, C, x, ns_dt, a);
+        if (j == 0 && a0)
+            memcpy(a, a0, sizeof(double) * (size_t)(r * r));
+        else
+            gram(R, C, x, ns_dt, a);
         gram_product(R, C, a, x, p);
         int last = (j == k - 1);
         for (int64_t t = 0; t < n; ++t) {
@@ -233,6 +253,69 @@ int orc_ns1_entries(int64_t R, int64_t C, const double *x0, int ns_dt, int64_t n
     }
     free(arow);
     return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Spectral normalisation -- §4 "nanoGPT" (the results hold with spectral as */
+/* with Frobenius scaling of the Newton-Schulz input) and §3 "Geometry" (the */
+/* polar direction lives in the spectral-norm geometry). The summary gives   */
+/* no procedure; readings: ||M||_2^2 is the largest eigenvalue of the Gram   */
+/* matrix of the stored M (the Newton-Schulz orientation), estimated by p    */
+/* power-iteration steps from the all-ones vector: w = A v, lambda = ||w||,  */
+/* v = w / lambda. The Gram is stored (rounded) before its scale is known,   */
+/* so A_0 = round(fp32(s^2) * A_raw) with s = 1 / sqrt(lambda), and the      */
+/* first iteration starts from X_0 = s M with that A_0. lambda = 0 gives     */
+/* s = 0 (U = 0).                                                            */
+/* ------------------------------------------------------------------------ */
+double orc_power_lambda(int64_t r, const double *a, int p)
+{
+    double *v = (double *)malloc(sizeof(double) * (size_t)r);
+    double *w = (double *)malloc(sizeof(double) * (size_t)r);
+    if (!v || !w) {
+        free(v); free(w);
+        return -1.0;
+    }
+    for (int64_t i = 0; i < r; ++i)
+        v[i] = 1.0 / sqrt((double)r);
+    double lambda = 0.0;
+    for (int it = 0; it < p; ++it) {
+        double ss = 0.0;
+        for (int64_t i = 0; i < r; ++i) {
+            double acc = 0.0;
+            for (int64_t l = 0; l < r; ++l)
+                acc += a[i * r + l] * v[l];
+            w[i] = acc;
+            ss += acc * acc;
+        }
+        lambda = sqrt(ss);
+        if (lambda == 0.0)
+            break;
+        for (int64_t i = 0; i < r; ++i)
+            v[i] = w[i] / lambda;
+    }
+    free(v); free(w);
+    return lambda;
+}
+
+double orc_spectral_x0_a0(int64_t R, int64_t C, const void *m, int m_dt, int ns_dt, int p,
+                          double *x0, double *a0)
+{
+    int64_t n = R * C, r = R <= C ? R : C;
+    for (int64_t i = 0; i < n; ++i)
+        x0[i] = load_elem(m, m_dt, i);
+    gram(R, C, x0, ns_dt, a0); /* A_raw of the stored M */
+    double lambda = orc_power_lambda(r, a0, p);
+    if (lambda < 0.0)
+        return lambda;
+    double s = lambda > 0.0 ? 1.0 / sqrt(lambda) : 0.0;
+    float s2 = lambda > 0.0 ? (float)(1.0 / lambda) : 0.0f;
+    for (int64_t i = 0; i < n; ++i)
+        x0[i] *= s;
+    /* exact mode: no storage, so no fp32 scale either */
+    double s2d = ns_dt == ORC_F64 ? (lambda > 0.0 ? 1.0 / lambda : 0.0) : (double)s2;
+    for (int64_t t = 0; t < r * r; ++t)
+        a0[t] = round_ns(s2d * a0[t], ns_dt);
+    return lambda;
 }
 
 /* ------------------------------------------------------------------------ */
@@ -363,12 +446,22 @@ int orc_step_matrix(int64_t R, int64_t C, int32_t mw, float beta, float eta, int
                     int g_dt, int m_dt, int ns_dt, const void *g, void *m, double *u_out,
                     uint64_t *packed, float *w, int8_t *vote_out)
 {
-    int64_t n = R * C, nw = orc_packed_words(n);
+    return orc_step_matrix_norm(R, C, mw, beta, eta, k, post_k, g_dt, m_dt, ns_dt, ORC_NORM_FROB,
+                                0, g, m, u_out, packed, w, vote_out);
+}
+
+int orc_step_matrix_norm(int64_t R, int64_t C, int32_t mw, float beta, float eta, int k,
+                         int post_k, int g_dt, int m_dt, int ns_dt, int norm, int power_iters,
+                         const void *g, void *m, double *u_out, uint64_t *packed, float *w,
+                         int8_t *vote_out)
+{
+    int64_t n = R * C, nw = orc_packed_words(n), r = R <= C ? R : C;
     double *x0 = (double *)malloc(sizeof(double) * (size_t)n);
     double *u = (double *)malloc(sizeof(double) * (size_t)n);
     int8_t *vote = (int8_t *)malloc((size_t)n);
-    if (!x0 || !u || !vote) {
-        free(x0); free(u); free(vote);
+    double *a0 = norm == ORC_NORM_SPECTRAL ? (double *)malloc(sizeof(double) * (size_t)(r * r)) : NULL;
+    if (!x0 || !u || !vote || (norm == ORC_NORM_SPECTRAL && !a0)) {
+        free(x0); free(u); free(vote); free(a0);
         return -1;
     }
     int rc = 0;
@@ -376,8 +469,15 @@ int orc_step_matrix(int64_t R, int64_t C, int32_t mw, float beta, float eta, int
         const char *gw = (const char *)g + (size_t)(wk * n) * (size_t)elem_bytes(g_dt);
         char *mwp = (char *)m + (size_t)(wk * n) * (size_t)elem_bytes(m_dt);
         orc_momentum(n, beta, gw, g_dt, mwp, m_dt);
-        orc_normalise(n, mwp, m_dt, x0);
-        rc = orc_newton_schulz(R, C, x0, k, ns_dt, u);
+        if (norm == ORC_NORM_SPECTRAL) {
+            if (orc_spectral_x0_a0(R, C, mwp, m_dt, ns_dt, power_iters, x0, a0) < 0.0)
+                rc = -1;
+            else
+                rc = newton_schulz(R, C, x0, a0, k, ns_dt, u);
+        } else {
+            orc_normalise(n, mwp, m_dt, x0);
+            rc = orc_newton_schulz(R, C, x0, k, ns_dt, u);
+        }
         if (rc == 0) {
             orc_sign_pack(n, u, ORC_F64, packed + wk * nw);
             if (u_out)
@@ -396,6 +496,6 @@ int orc_step_matrix(int64_t R, int64_t C, int32_t mw, float beta, float eta, int
         if (rc == 0 && vote_out)
             memcpy(vote_out, vote, (size_t)n);
     }
-    free(x0); free(u); free(vote);
+    free(x0); free(u); free(vote); free(a0);
     return rc;
 }

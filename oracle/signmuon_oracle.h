@@ -36,6 +36,7 @@ extern "C" {
 #endif
 
 enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_F64 = 2 };
+enum { ORC_NORM_FROB = 0, ORC_NORM_SPECTRAL = 1 };
 
 /* fp32 <-> bf16 bit patterns, round to nearest even. */
 uint16_t orc_bf16_from_f32(float x);
@@ -56,6 +57,19 @@ double orc_normalise(int64_t n, const void *m, int m_dt, double *x0);
  * X_k is returned unrounded. ORC_F64 rounds nowhere. Returns 0, or -1 when
  * memory runs out. */
 int orc_newton_schulz(int64_t R, int64_t C, const double *x0, int k, int ns_dt, double *u);
+
+/* O3 with the first iteration's Gram matrix given (a0: r x r, rounded). */
+int orc_newton_schulz_a0(int64_t R, int64_t C, const double *x0, const double *a0, int k,
+                         int ns_dt, double *u);
+
+/* Spectral normalisation: p power-iteration steps on the symmetric r x r
+ * matrix a from the all-ones vector (w = a v, lambda = ||w||, v = w/lambda);
+ * returns the last lambda (-1 when memory runs out). */
+double orc_power_lambda(int64_t r, const double *a, int p);
+/* X0 = M / sqrt(lambda) and the first Gram A0 = round(fp32(1/lambda) A_raw),
+ * A_raw the stored Gram of M; returns lambda. */
+double orc_spectral_x0_a0(int64_t R, int64_t C, const void *m, int m_dt, int ns_dt, int p,
+                          double *x0, double *a0);
 
 /* O3 for k = 1, one output entry at a time: out[t] = X_1[ri[t]][ci[t]].
  * Same sums in the same order as orc_newton_schulz with k = 1. */
@@ -92,6 +106,13 @@ int64_t orc_post_polar(int64_t R, int64_t C, const int8_t *vote, int k, int ns_d
 int orc_step_matrix(int64_t R, int64_t C, int32_t mw, float beta, float eta, int k, int post_k,
                     int g_dt, int m_dt, int ns_dt, const void *g, void *m, double *u_out,
                     uint64_t *packed, float *w, int8_t *vote_out);
+
+/* orc_step_matrix with the normalisation of the Newton-Schulz input chosen:
+ * ORC_NORM_FROB, or ORC_NORM_SPECTRAL with power_iters steps. */
+int orc_step_matrix_norm(int64_t R, int64_t C, int32_t mw, float beta, float eta, int k,
+                         int post_k, int g_dt, int m_dt, int ns_dt, int norm, int power_iters,
+                         const void *g, void *m, double *u_out, uint64_t *packed, float *w,
+                         int8_t *vote_out);
 
 #ifdef __cplusplus
 }

@@ -406,6 +406,134 @@ def test_vote_random_against_counting(mw):
 
 
 # ---------------------------------------------------------------------------
+# spectral normalisation (summary §4 "nanoGPT": spectral as well as
+# Frobenius scaling): power iteration on the Gram matrix
+# ---------------------------------------------------------------------------
+def _psd(rng, r, c):
+    m = rng.standard_normal((r, c))
+    return m @ m.T
+
+
+@pytest.mark.parametrize("r,c", [(8, 20), (16, 16), (5, 40)])
+def test_power_lambda_below_top_eigenvalue_and_nondecreasing(r, c):
+    a = _psd(np.random.default_rng(r * c), r, c)
+    top = np.linalg.eigvalsh(a)[-1]
+    prev = 0.0
+    for p in (1, 2, 3, 5, 10, 30):
+        lam = oracle.power_lambda(a, p)
+        assert lam <= top * (1 + 1e-12)
+        assert lam >= prev * (1 - 1e-12)
+        prev = lam
+
+
+def test_power_lambda_converges_to_top_eigenvalue():
+    rng = np.random.default_rng(3)
+    q, _ = np.linalg.qr(rng.standard_normal((12, 12)))
+    d = np.linspace(1.0, 3.0, 12)
+    d[-1] = 6.0  # a clear gap
+    a = (q * d) @ q.T
+    assert oracle.power_lambda(a, 400) == pytest.approx(6.0, rel=1e-12)
+
+
+def test_power_lambda_rank_one_is_exact_after_two_steps():
+    rng = np.random.default_rng(4)
+    v = rng.standard_normal(9)
+    a = np.outer(v, v)
+    assert oracle.power_lambda(a, 2) == pytest.approx(float(v @ v), rel=1e-13)
+
+
+def test_power_lambda_diagonal_closed_form():
+    """From the all-ones start, the p-th step's ||A v|| on A = diag(d) is
+    sqrt(sum d^(2p)) / sqrt(sum d^(2p-2))."""
+    d = np.array([0.5, 1.0, 2.0, 3.0, 3.5], np.float64)
+    for p in (1, 2, 4, 7):
+        expect = math.sqrt(float(np.sum(d ** (2 * p)))) / math.sqrt(float(np.sum(d ** (2 * p - 2))))
+        assert oracle.power_lambda(np.diag(d), p) == pytest.approx(expect, rel=1e-13)
+
+
+@pytest.mark.parametrize("shape", [(6, 10), (10, 6), (8, 8)])
+@pytest.mark.parametrize("k", [0, 1, 2, 5])
+def test_spectral_ns_is_the_cubic_on_sigma_over_sigma_max(shape, k):
+    """Exact mode, converged power iteration: X_k = U p^k(S / s_max) V^T (SVD
+    from numpy), so the top singular value is 1 for every k."""
+    R, C = shape
+    rng = np.random.default_rng(R * 100 + C + k)
+    u_, _, vt = np.linalg.svd(rng.standard_normal((R, C)), full_matrices=False)
+    sig = np.linspace(0.3, 1.0, min(R, C)) * 2.5
+    sig[0] = 4.0  # gap so that 300 steps converge
+    m = (u_ * sig) @ vt
+    lam, x0, a0 = oracle.spectral_x0_a0(m, oracle.F64, 300)
+    assert lam == pytest.approx(16.0, rel=1e-12)
+    x = oracle.newton_schulz_a0(x0, a0, k, oracle.F64)
+    expect = (u_ * scalar_map(sig / 4.0, k)) @ vt
+    assert rel_fro(x, expect) < 1e-10
+    assert np.linalg.svd(x, compute_uv=False)[0] == pytest.approx(1.0, abs=1e-10)
+
+
+@pytest.mark.parametrize("mode", [F32, BF16])
+def test_spectral_power_of_two_scale_invariance_exact(mode):
+    rng = np.random.default_rng(21)
+    m = rng.standard_normal((24, 40)).astype(np.float32)
+    if mode == BF16:
+        m = oracle.bf16_from_f32(m)
+        m4 = oracle.bf16_from_f32(oracle.bf16_to_f32(m) * np.float32(4.0))
+    else:
+        m4 = m * np.float32(4.0)
+    l1, x1, a1 = oracle.spectral_x0_a0(m, mode, 6)
+    l4, x4, a4 = oracle.spectral_x0_a0(m4, mode, 6)
+    assert l4 == 16.0 * l1
+    np.testing.assert_array_equal(a1, a4)
+    np.testing.assert_array_equal(x1, x4)
+    np.testing.assert_array_equal(oracle.newton_schulz_a0(x1, a1, 3, mode),
+                                  oracle.newton_schulz_a0(x4, a4, 3, mode))
+
+
+def test_spectral_k0_is_m_over_sigma_hat():
+    rng = np.random.default_rng(22)
+    m = rng.standard_normal((12, 30)).astype(np.float32)
+    lam, x0, _ = oracle.spectral_x0_a0(m, F32, 5)
+    np.testing.assert_allclose(x0, m.astype(np.float64) / math.sqrt(lam), rtol=1e-15)
+
+
+def test_spectral_equals_frobenius_on_rank_one_momentum():
+    """Rank one: ||M||_F = ||M||_2, and power iteration is exact after two
+    steps, so both normalisations give the same iterate (exact mode)."""
+    rng = np.random.default_rng(23)
+    m = np.outer(rng.standard_normal(7), rng.standard_normal(11))
+    _, x0f = oracle.normalise(m)
+    _, x0s, a0 = oracle.spectral_x0_a0(m, oracle.F64, 2)
+    assert rel_fro(x0s, x0f) < 1e-14
+    assert rel_fro(oracle.newton_schulz_a0(x0s, a0, 3, oracle.F64),
+                   oracle.newton_schulz(x0f, 3, oracle.F64)) < 1e-13
+
+
+def test_step_spectral_matches_its_parts():
+    """The step with spectral normalisation is momentum, spectral scaling,
+    Newton-Schulz, sign, vote: assembled here from the separately pinned
+    parts."""
+    rng = np.random.default_rng(24)
+    mw, R, C = 3, 16, 24
+    g = rng.standard_normal((mw, R, C)).astype(np.float32)
+    m = np.zeros((mw, R, C), np.float32)
+    w0 = rng.standard_normal((R, C)).astype(np.float32)
+    w = w0.copy()
+    packed, vote, u = oracle.step_matrix(g, m.copy(), w, 0.9, 1e-3, 2, F32, want_u=True,
+                                         norm=oracle.NORM_SPECTRAL, power_iters=4)
+    m_ref = m.copy()
+    oracle.momentum(g, m_ref, 0.9)
+    pk = []
+    for j in range(mw):
+        _, x0, a0 = oracle.spectral_x0_a0(m_ref[j], F32, 4)
+        uj = oracle.newton_schulz_a0(x0, a0, 2, F32)
+        np.testing.assert_array_equal(u[j], uj)
+        pk.append(oracle.sign_pack(uj))
+    np.testing.assert_array_equal(packed, np.stack(pk))
+    w_ref = w0.copy()
+    np.testing.assert_array_equal(vote, oracle.vote_update(np.stack(pk), w_ref, 1e-3))
+    np.testing.assert_array_equal(w, w_ref)
+
+
+# ---------------------------------------------------------------------------
 # int8 payload: the vote as the sign of the integer sum of the workers' signs
 # (summary §2 "Core mechanism" and "Communication efficiency")
 # ---------------------------------------------------------------------------
