@@ -157,7 +157,9 @@ def cpu_baseline(wl, js=(0, 1, 2, 3)):
         m = np.zeros((wl.workers, R, C), np.uint16 if wl.mom_dtype == "bf16" else np.float32)
         w = synthetic.initial_weight(wl, j)
         t0 = time.perf_counter()
-        oracle.step_matrix(g, m, w, wl.beta, wl.eta, wl.ns_iters, ns, post_k=wl.post_polar_iters)
+        oracle.step_matrix(g, m, w, wl.beta, wl.eta, wl.ns_iters, ns, post_k=wl.post_polar_iters,
+                       norm=oracle.NORM_SPECTRAL if wl.norm == "spectral" else oracle.NORM_FROB,
+                       power_iters=wl.power_iters)
         total_s += time.perf_counter() - t0
         params += R * C
     shapes = ", ".join(f"{wl.shapes[j][0]}x{wl.shapes[j][1]}" for j in js)
@@ -247,7 +249,9 @@ def main():
         grads[j] = None
     params = sm.Params(workers=wl.workers, beta=wl.beta, eta=wl.eta, ns_iters=wl.ns_iters,
                        post_polar_iters=wl.post_polar_iters, grad_dtype=code[wl.grad_dtype],
-                       mom_dtype=code[wl.mom_dtype], ns_dtype=code[wl.ns_dtype])
+                       mom_dtype=code[wl.mom_dtype], ns_dtype=code[wl.ns_dtype],
+                       norm=sm.NORM_SPECTRAL if wl.norm == "spectral" else sm.NORM_FROBENIUS,
+                       power_iters=wl.power_iters)
     ws = sm.workspace_tensor(mats, params, dev)
     torch.cuda.synchronize()
     log(f"[bench] inputs resident in HBM after {time.perf_counter() - t0:.1f} s; workspace "
@@ -342,7 +346,8 @@ def main():
                    "matrices": len(wl.shapes), "params": wl.params, "workers": wl.workers,
                    "ns_iters": wl.ns_iters, "post_polar_iters": wl.post_polar_iters,
                    "grad_dtype": wl.grad_dtype, "momentum_dtype": wl.mom_dtype,
-                   "ns_dtype": wl.ns_dtype, "weight_dtype": "f32"},
+                   "ns_dtype": wl.ns_dtype, "weight_dtype": "f32", "norm": wl.norm,
+                   "power_iters": wl.power_iters},
         "steps_per_s": round(1e3 / ms_per_step, 2),
         "worker_params_per_s": round(params_per_s * wl.workers, 1),
         "ns_mfma_util_pct": None if ns_util is None else round(ns_util, 2),

@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define SIGNMUON_ABI_VERSION 1
+#define SIGNMUON_ABI_VERSION 2
 
 /* Status codes. */
 enum {
@@ -61,6 +61,14 @@ enum {
 };
 
 typedef enum { SIGNMUON_F32 = 0, SIGNMUON_BF16 = 1 } signmuon_dtype;
+
+/* Normalisation of the Newton-Schulz input X_0 = s M (summary §4 "nanoGPT":
+ * Frobenius and spectral scaling both evaluated). */
+typedef enum {
+    SIGNMUON_NORM_FROBENIUS = 0, /* s = 1 / ||M||_F */
+    SIGNMUON_NORM_SPECTRAL = 1   /* s = 1 / sqrt(lambda), lambda the power-iteration estimate of
+                                    ||M||_2^2 on the Gram matrix (see signmuon_params) */
+} signmuon_norm;
 
 /* A hipStream_t, passed as an opaque pointer so that this header needs no
  * HIP header. */
@@ -96,6 +104,16 @@ typedef struct {
     signmuon_dtype grad_dtype; /* G storage: F32 or BF16 */
     signmuon_dtype mom_dtype;  /* M storage: F32 or BF16 */
     signmuon_dtype ns_dtype;   /* Newton-Schulz operand storage: F32 or BF16 */
+    int32_t norm;              /* signmuon_norm of X_0 (0 = Frobenius) */
+    int32_t power_iters;       /* SIGNMUON_NORM_SPECTRAL: power-iteration steps p >= 1 (ignored
+                                  otherwise). The summary gives no procedure; the one taken:
+                                  A_raw = the stored Gram matrix of the stored M (M M^T if
+                                  R <= C, else M^T M); from v = all-ones / sqrt(r), p times
+                                  w = A_raw v, lambda = ||w||, v = w / lambda; s = 1/sqrt(lambda);
+                                  the first iteration uses A_0 = round(fp32(1/lambda) * A_raw)
+                                  and X_0 = s M. lambda = 0 gives U = 0. Needs min(R, C) <= 8192
+                                  (SIGNMUON_ERANGE). The post-vote polar step keeps its exact
+                                  Frobenius scale. */
 } signmuon_params;
 
 /* Largest number of matrices one call accepts. */
@@ -190,7 +208,8 @@ enum {
     SIGNMUON_K_PRODUCT = 4,  /* Newton-Schulz product (+ fused sign/pack on the last) */
     SIGNMUON_K_PACK = 5,     /* standalone sign + pack */
     SIGNMUON_K_VOTE = 6,     /* majority vote + update */
-    SIGNMUON_K_AUX = 7       /* post-vote polar step bookkeeping */
+    SIGNMUON_K_AUX = 7,      /* post-vote polar step bookkeeping */
+    SIGNMUON_K_POWER = 8     /* spectral normalisation: power step, scale, Gram rescale */
 };
 
 /* Instrumentation for stage timing: events[0] (a hipEvent_t created by the

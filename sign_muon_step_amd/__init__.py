@@ -21,7 +21,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libsignmuon.so")
 
 F32, BF16 = 0, 1
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 STATUS = {0: "SIGNMUON_OK", -1: "SIGNMUON_EINVAL", -2: "SIGNMUON_EDTYPE", -3: "SIGNMUON_EALIGN",
           -4: "SIGNMUON_EWORKSPACE", -5: "SIGNMUON_EHIP", -6: "SIGNMUON_ERANGE"}
@@ -44,7 +44,8 @@ class _Params(ctypes.Structure):
     _fields_ = [("workers", ctypes.c_int32), ("beta", ctypes.c_float), ("eta", ctypes.c_float),
                 ("ns_iters", ctypes.c_int32), ("post_polar_iters", ctypes.c_int32),
                 ("grad_dtype", ctypes.c_int), ("mom_dtype", ctypes.c_int),
-                ("ns_dtype", ctypes.c_int)]
+                ("ns_dtype", ctypes.c_int), ("norm", ctypes.c_int32),
+                ("power_iters", ctypes.c_int32)]
 
 
 class _Trace(ctypes.Structure):
@@ -53,7 +54,8 @@ class _Trace(ctypes.Structure):
 
 
 KERNEL_KINDS = {1: "momentum", 2: "scales", 3: "ns_gram", 4: "ns_product", 5: "sign_pack",
-                6: "vote_update", 7: "aux"}
+                6: "vote_update", 7: "aux", 8: "power"}
+NORM_FROBENIUS, NORM_SPECTRAL = 0, 1
 
 _lib = None
 
@@ -154,6 +156,8 @@ class Params:
     grad_dtype: int = F32
     mom_dtype: int = F32
     ns_dtype: int = F32
+    norm: int = NORM_FROBENIUS
+    power_iters: int = 0
 
 
 def _marshal(mats: Sequence[Matrix], params: Params):
@@ -163,7 +167,8 @@ def _marshal(mats: Sequence[Matrix], params: Params):
         arr[i] = _Matrix(R, C, _ptr(m.grad), _ptr(m.momentum), _ptr(m.polar_out), _ptr(m.packed),
                          _ptr(m.weight), _ptr(m.vote_out))
     p = _Params(params.workers, params.beta, params.eta, params.ns_iters,
-                params.post_polar_iters, params.grad_dtype, params.mom_dtype, params.ns_dtype)
+                params.post_polar_iters, params.grad_dtype, params.mom_dtype, params.ns_dtype,
+                params.norm, params.power_iters)
     return arr, p
 
 

@@ -11,7 +11,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libsignmuon.so")
-SOURCES = [os.path.join(HERE, "csrc", f) for f in ("api.hip", "elementwise.hip", "ns_gemm.hip")]
+SOURCES = [os.path.join(HERE, "csrc", f) for f in ("api.hip", "elementwise.hip", "ns_gemm.hip", "spectral.hip")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -22,7 +22,7 @@ def flags():
             "-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc")]
 
 
-def build(verbose: bool = False, jobs: int = 3) -> str:
+def build(verbose: bool = False, jobs: int = 4) -> str:
     """Compile each source to an object in parallel, then link the library."""
     objdir = os.path.join(HERE, "_build")
     os.makedirs(objdir, exist_ok=True)

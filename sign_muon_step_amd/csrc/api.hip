@@ -69,6 +69,9 @@ struct MatPlan {
     size_t post_iter_off;   // post-vote step: [n]
     size_t vns_off;         // vote in NS storage: [n]
     size_t u_off;           // fp32 U scratch [Mw][n] (unfused pack only)
+    size_t pw_off;          // spectral: power vectors [2][Mw][r] (floats from the section)
+    size_t pwp_off;         // spectral: block sums [2][Mw][pw_bpw] (doubles from the section)
+    int32_t pw_bpw;         // spectral: power-step blocks per worker
     bool fused_pack;        // the last product packs the signs itself
     bool u_scratch;         // U goes through workspace scratch
 };
@@ -77,7 +80,8 @@ struct Plan {
     std::vector<MatPlan> m;
     int32_t units = 0, post_unit_base = 0, partials = 0;
     size_t off_partials = 0, off_scales = 0, off_nnz = 0, off_gram = 0, off_iter[2] = {0, 0};
-    size_t off_vns = 0, off_u = 0, total = 0;
+    size_t off_vns = 0, off_u = 0, off_pw = 0, off_pwp = 0, total = 0;
+    bool spectral = false;
 };
 
 // Shapes, counts and dtypes (not pointers). Fills the plan.
@@ -91,9 +95,14 @@ int make_plan(const signmuon_matrix *mats, int32_t n_mats, const signmuon_params
     if (!dtype_ok(p->grad_dtype) || !dtype_ok(p->mom_dtype) || !dtype_ok(p->ns_dtype))
         return SIGNMUON_EDTYPE;
     if (p->mom_dtype != p->ns_dtype) return SIGNMUON_EDTYPE;  // X0 is read in place from M
+    if (p->norm != SIGNMUON_NORM_FROBENIUS && p->norm != SIGNMUON_NORM_SPECTRAL) return SIGNMUON_EINVAL;
+    pl.spectral = p->norm == SIGNMUON_NORM_SPECTRAL;
+    if (pl.spectral && p->power_iters < 1) return SIGNMUON_EINVAL;
+    if (pl.spectral && p->power_iters > kMaxIters) return SIGNMUON_ERANGE;
     const int64_t mw = p->workers;
     const size_t ns = esize(p->ns_dtype);
     const bool post = step && p->post_polar_iters > 0;
+    size_t pw = 0, pwp = 0;
     pl.m.assign(n_mats, MatPlan{});
     size_t gram = 0, iter = 0, post_gram = 0, post_iter = 0, vns = 0, u = 0;
     int64_t partials = 0;
@@ -126,6 +135,14 @@ int make_plan(const signmuon_matrix *mats, int32_t n_mats, const signmuon_params
         q.u_scratch = step && p->ns_iters > 0 && !q.fused_pack && s.polar_out == nullptr;
         q.u_off = u;
         if (q.u_scratch) u += align_up((size_t)(mw * q.n) * 4, kSectionAlign);
+        q.pw_bpw = sm::power_blocks_per_worker(q.r);
+        q.pw_off = pw;
+        q.pwp_off = pwp;
+        if (pl.spectral) {
+            if (q.r > sm::kMaxPowR) return SIGNMUON_ERANGE;
+            pw += (size_t)(2 * mw * q.r + 63) / 64 * 64;
+            pwp += (size_t)(2 * mw * q.pw_bpw + 31) / 32 * 32;
+        }
     }
     if (partials > INT32_MAX / 2) return SIGNMUON_ERANGE;
     pl.partials = (int32_t)partials;
@@ -139,8 +156,12 @@ int make_plan(const signmuon_matrix *mats, int32_t n_mats, const signmuon_params
     off += align_up((size_t)scale_count * sizeof(float2), kSectionAlign);
     pl.off_nnz = off;
     off += align_up((size_t)n_mats * sizeof(uint32_t), kSectionAlign);
+    pl.off_pw = off;
+    off += align_up(pw * sizeof(float), kSectionAlign);
+    pl.off_pwp = off;
+    off += align_up(pwp * sizeof(double), kSectionAlign);
     pl.off_gram = off;
-    const bool need_gram = p->ns_iters > 0 || post;
+    const bool need_gram = p->ns_iters > 0 || post || pl.spectral;
     off += need_gram ? (gram > post_gram ? gram : post_gram) : 0;
     size_t iter_need = 0;
     if (p->ns_iters >= 2) iter_need = iter;
@@ -214,60 +235,125 @@ int run_momentum(const signmuon_matrix *mats, int32_t n_mats, const signmuon_par
     return SIGNMUON_OK;
 }
 
-// Newton-Schulz iterations of every (matrix, worker). final_epi selects the
-// last product's epilogue: EPI_FINAL writes U (polar_out or scratch) and, for
-// step, the fused packed signs.
-int run_newton_schulz(const signmuon_matrix *mats, int32_t n_mats, const signmuon_params *p,
-                      const Plan &pl, void *ws, bool step, hipStream_t st, Tracer &tr) {
+// One Newton-Schulz launch pass over every (matrix, worker): iteration j's
+// Gram matrix (pass 0) or product (pass 1). use_scales folds s^2 (Gram) or s
+// (product) of iteration 0 in. The last product's epilogue writes U
+// (polar_out or scratch) and, for step, the fused packed signs.
+int ns_pass(const signmuon_matrix *mats, int32_t n_mats, const signmuon_params *p, const Plan &pl,
+            void *ws, bool step, int j, int pass, bool use_scales, hipStream_t st, Tracer &tr) {
     const int k = p->ns_iters;
+    const bool last = j == k - 1;
     const bool bf16 = p->ns_dtype == SIGNMUON_BF16;
     const float2 *scales = ws_at<float2>(ws, pl.off_scales);
-    for (int j = 0; j < k; ++j) {
-        const bool last = j == k - 1;
-        for (int pass = 0; pass < 2; ++pass) {  // 0 = Gram, 1 = product
-            for (int32_t c0 = 0; c0 < n_mats; c0 += sm::kMaxMatsPerLaunch) {
-                const int32_t cn =
-                    n_mats - c0 < sm::kMaxMatsPerLaunch ? n_mats - c0 : sm::kMaxMatsPerLaunch;
-                sm::NsBatch b{};
-                b.nmat = cn;
-                b.workers = p->workers;
-                b.use_scales = j == 0;
-                b.scales = scales;
-                int64_t tiles = 0;
-                for (int32_t i = 0; i < cn; ++i) {
-                    const MatPlan &q = pl.m[c0 + i];
-                    const signmuon_matrix &s = mats[c0 + i];
-                    sm::NsMat &d = b.mat[i];
-                    d.R = (int32_t)q.R;
-                    d.C = (int32_t)q.C;
-                    d.unit_begin = q.unit_begin;
-                    d.x = j == 0 ? s.momentum : ws_at<const char>(ws, pl.off_iter[(j - 1) & 1] + q.iter_off);
-                    d.a = ws_at<char>(ws, pl.off_gram + q.gram_off);
-                    if (!last) {
-                        d.out = ws_at<char>(ws, pl.off_iter[j & 1] + q.iter_off);
-                    } else if (s.polar_out) {
-                        d.out = s.polar_out;
-                    } else if (q.u_scratch) {
-                        d.out = ws_at<char>(ws, pl.off_u + q.u_off);
-                    } else {
-                        d.out = nullptr;
-                    }
-                    d.packed = (last && step && q.fused_pack) ? s.packed : nullptr;
-                    d.tiles_per_worker = pass == 0 ? sm::ns_gram_tiles(q.R, q.C) : sm::ns_product_tiles(q.R, q.C);
-                    d.tile_begin = (int32_t)tiles;
-                    b.starts.v[i] = d.tile_begin;
-                    tiles += d.tiles_per_worker;
-                }
-                if (tiles * p->workers > INT32_MAX) return SIGNMUON_ERANGE;
-                b.tiles_per_worker_all = (int32_t)tiles;
-                b.total_tiles = (int32_t)(tiles * p->workers);
-                if (pass == 0)
-                    sm::launch_ns_gram(b, bf16, st);
-                else
-                    sm::launch_ns_product(b, bf16, last ? sm::EPI_FINAL : sm::EPI_ITER, st);
-                if (int rc = tr.after(pass == 0 ? SIGNMUON_K_GRAM : SIGNMUON_K_PRODUCT)) return rc;
+    for (int32_t c0 = 0; c0 < n_mats; c0 += sm::kMaxMatsPerLaunch) {
+        const int32_t cn = n_mats - c0 < sm::kMaxMatsPerLaunch ? n_mats - c0 : sm::kMaxMatsPerLaunch;
+        sm::NsBatch b{};
+        b.nmat = cn;
+        b.workers = p->workers;
+        b.use_scales = use_scales;
+        b.scales = scales;
+        int64_t tiles = 0;
+        for (int32_t i = 0; i < cn; ++i) {
+            const MatPlan &q = pl.m[c0 + i];
+            const signmuon_matrix &s = mats[c0 + i];
+            sm::NsMat &d = b.mat[i];
+            d.R = (int32_t)q.R;
+            d.C = (int32_t)q.C;
+            d.unit_begin = q.unit_begin;
+            d.x = j == 0 ? s.momentum : ws_at<const char>(ws, pl.off_iter[(j - 1) & 1] + q.iter_off);
+            d.a = ws_at<char>(ws, pl.off_gram + q.gram_off);
+            if (!last) {
+                d.out = ws_at<char>(ws, pl.off_iter[j & 1] + q.iter_off);
+            } else if (s.polar_out) {
+                d.out = s.polar_out;
+            } else if (q.u_scratch) {
+                d.out = ws_at<char>(ws, pl.off_u + q.u_off);
+            } else {
+                d.out = nullptr;
             }
+            d.packed = (last && step && q.fused_pack) ? s.packed : nullptr;
+            d.tiles_per_worker = pass == 0 ? sm::ns_gram_tiles(q.R, q.C) : sm::ns_product_tiles(q.R, q.C);
+            d.tile_begin = (int32_t)tiles;
+            b.starts.v[i] = d.tile_begin;
+            tiles += d.tiles_per_worker;
         }
+        if (tiles * p->workers > INT32_MAX) return SIGNMUON_ERANGE;
+        b.tiles_per_worker_all = (int32_t)tiles;
+        b.total_tiles = (int32_t)(tiles * p->workers);
+        if (pass == 0)
+            sm::launch_ns_gram(b, bf16, st);
+        else
+            sm::launch_ns_product(b, bf16, last ? sm::EPI_FINAL : sm::EPI_ITER, st);
+        if (int rc = tr.after(pass == 0 ? SIGNMUON_K_GRAM : SIGNMUON_K_PRODUCT)) return rc;
+    }
+    return SIGNMUON_OK;
+}
+
+// Spectral normalisation (see signmuon_params.power_iters): the unscaled Gram
+// matrix of the stored momentum, power_iters power steps on it, the scales
+// {s, s^2}, and (rescale) A_0 = round(s^2 A_raw) in place for the first
+// product.
+int run_spectral(const signmuon_matrix *mats, int32_t n_mats, const signmuon_params *p,
+                 const Plan &pl, void *ws, bool rescale, hipStream_t st, Tracer &tr) {
+    if (int rc = ns_pass(mats, n_mats, p, pl, ws, false, 0, 0, false, st, tr)) return rc;
+    const bool bf16 = p->ns_dtype == SIGNMUON_BF16;
+    for (int32_t c0 = 0; c0 < n_mats; c0 += sm::kMaxMatsPerLaunch) {
+        const int32_t cn = n_mats - c0 < sm::kMaxMatsPerLaunch ? n_mats - c0 : sm::kMaxMatsPerLaunch;
+        sm::PowBatch b{};
+        b.nmat = cn;
+        b.workers = p->workers;
+        b.scales = ws_at<float2>(ws, pl.off_scales);
+        int64_t blocks = 0;
+        for (int32_t i = 0; i < cn; ++i) {
+            const MatPlan &q = pl.m[c0 + i];
+            sm::PowMat &d = b.mat[i];
+            d.a = ws_at<char>(ws, pl.off_gram + q.gram_off);
+            d.w = ws_at<float>(ws, pl.off_pw) + q.pw_off;
+            d.part = ws_at<double>(ws, pl.off_pwp) + q.pwp_off;
+            d.r = (int32_t)q.r;
+            d.bpw = q.pw_bpw;
+            d.unit_begin = q.unit_begin;
+            b.starts.v[i] = (int32_t)blocks;
+            blocks += (int64_t)p->workers * q.pw_bpw;
+        }
+        if (blocks > INT32_MAX) return SIGNMUON_ERANGE;
+        b.total_blocks = (int32_t)blocks;
+        for (int it = 0; it < p->power_iters; ++it) {
+            b.it = it;
+            sm::launch_power_step(b, bf16, st);
+            if (int rc = tr.after(SIGNMUON_K_POWER)) return rc;
+        }
+        b.it = p->power_iters - 1;
+        sm::launch_power_finalize(b, st);
+        if (int rc = tr.after(SIGNMUON_K_POWER)) return rc;
+        if (rescale) {
+            int64_t rblocks = 0;
+            for (int32_t i = 0; i < cn; ++i) {
+                const MatPlan &q = pl.m[c0 + i];
+                b.mat[i].bpw = sm::rescale_blocks_per_worker(q.r);
+                b.starts.v[i] = (int32_t)rblocks;
+                rblocks += (int64_t)p->workers * b.mat[i].bpw;
+            }
+            if (rblocks > INT32_MAX) return SIGNMUON_ERANGE;
+            b.total_blocks = (int32_t)rblocks;
+            sm::launch_gram_rescale(b, bf16, st);
+            if (int rc = tr.after(SIGNMUON_K_POWER)) return rc;
+        }
+    }
+    return SIGNMUON_OK;
+}
+
+// Newton-Schulz iterations of every (matrix, worker); with spectral
+// normalisation the first Gram matrix comes from run_spectral.
+int run_newton_schulz(const signmuon_matrix *mats, int32_t n_mats, const signmuon_params *p,
+                      const Plan &pl, void *ws, bool step, hipStream_t st, Tracer &tr) {
+    for (int j = 0; j < p->ns_iters; ++j) {
+        if (j == 0 && pl.spectral) {
+            if (int rc = run_spectral(mats, n_mats, p, pl, ws, true, st, tr)) return rc;
+        } else {
+            if (int rc = ns_pass(mats, n_mats, p, pl, ws, step, j, 0, j == 0, st, tr)) return rc;
+        }
+        if (int rc = ns_pass(mats, n_mats, p, pl, ws, step, j, 1, j == 0, st, tr)) return rc;
     }
     return SIGNMUON_OK;
 }
@@ -451,7 +537,11 @@ int signmuon_momentum_ns(const signmuon_matrix *mats, int32_t n_mats, const sign
     hipStream_t st = static_cast<hipStream_t>(stream);
     Tracer tr;
     if (int rc = run_momentum(mats, n_mats, p, pl, workspace, st, tr)) return rc;
-    if (p->ns_iters == 0) return run_pack(mats, n_mats, p, pl, workspace, false, st, tr);
+    if (p->ns_iters == 0) {
+        if (pl.spectral)
+            if (int rc = run_spectral(mats, n_mats, p, pl, workspace, false, st, tr)) return rc;
+        return run_pack(mats, n_mats, p, pl, workspace, false, st, tr);
+    }
     return run_newton_schulz(mats, n_mats, p, pl, workspace, false, st, tr);
 }
 
@@ -469,8 +559,11 @@ int signmuon_step_traced(const signmuon_matrix *mats, int32_t n_mats, const sign
     tr.st = st;
     if (int rc = tr.begin()) return rc;
     if (int rc = run_momentum(mats, n_mats, p, pl, workspace, st, tr)) return rc;
-    if (p->ns_iters > 0)
+    if (p->ns_iters > 0) {
         if (int rc = run_newton_schulz(mats, n_mats, p, pl, workspace, true, st, tr)) return rc;
+    } else if (pl.spectral) {
+        if (int rc = run_spectral(mats, n_mats, p, pl, workspace, false, st, tr)) return rc;
+    }
     if (int rc = run_pack(mats, n_mats, p, pl, workspace, true, st, tr)) return rc;
     if (int rc = run_vote(mats, n_mats, p, pl, workspace, st, tr)) return rc;
     if (p->post_polar_iters > 0)

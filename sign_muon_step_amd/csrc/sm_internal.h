@@ -183,6 +183,39 @@ void launch_sign_int8(const void *u, bool u_bf16, int64_t total, int8_t *signs, 
 void launch_vote_update_int8(const int8_t *signs, int32_t workers, int64_t n, float *w, float eta,
                              int8_t *vote, hipStream_t s);
 
+// ---------------------------------------------------------------------------
+// Spectral normalisation: power iteration on each worker's Gram matrix.
+// ---------------------------------------------------------------------------
+constexpr int kPowRowsPerBlock = 16;  // rows of A per power-step block
+constexpr int kMaxPowR = 8192;         // the power vector of a Gram lives in LDS
+
+struct PowMat {
+    const void *a;   // worker 0's Gram matrix [r][r] (ns type); worker stride r*r
+    float *w;        // [2][Mw][r] power vectors (ping-pong by step parity)
+    double *part;    // [2][Mw][bpw] block sums of squares of w
+    int32_t r;
+    int32_t bpw;     // blocks per worker of the launch
+    int32_t unit_begin;
+    int32_t pad_;
+};
+
+struct PowBatch {
+    PowMat mat[kMaxMatsPerLaunch];
+    int32_t nmat;
+    int32_t workers;
+    int32_t total_blocks;
+    int32_t it;      // power step (power_step), or the last step (finalize)
+    float2 *scales;  // per unit: {s, s^2}
+    Starts starts;   // first block of each matrix
+};
+
+int32_t power_blocks_per_worker(int64_t r);
+int32_t rescale_blocks_per_worker(int64_t r);
+void launch_power_step(const PowBatch &b, bool bf16, hipStream_t s);
+void launch_power_finalize(const PowBatch &b, hipStream_t s);
+// bpw of the batch: rescale_blocks_per_worker
+void launch_gram_rescale(const PowBatch &b, bool bf16, hipStream_t s);
+
 // Post-vote polar step helpers.
 void launch_zero_u32(uint32_t *p, int32_t count, hipStream_t s);
 // scales[unit_begin + i] = {1/sqrt(nnz[i]), 1/nnz[i]} (0 when nnz = 0)
@@ -193,6 +226,6 @@ void launch_nnz_scales(const uint32_t *nnz, int32_t count, float2 *scales, hipSt
 namespace sm {
 // Launch descriptors travel as kernel arguments (4 KiB at most).
 static_assert(sizeof(MomBatch) <= 4000 && sizeof(NsBatch) <= 4000 && sizeof(PackBatch) <= 4000 &&
-                  sizeof(VoteBatch) <= 4000,
+                  sizeof(VoteBatch) <= 4000 && sizeof(PowBatch) <= 4000,
               "launch descriptor exceeds the kernel argument space");
 }  // namespace sm

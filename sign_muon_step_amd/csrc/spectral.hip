@@ -1,0 +1,203 @@
+// spectral.hip -- spectral normalisation of the Newton-Schulz input for
+// gfx950: power iteration on each worker's Gram matrix, the scale it gives,
+// and the rescaling of the stored Gram matrix.
+//
+// Method: "SignMuon: Communication-Efficient Distributed Muon Optimization"
+// (gist.science, paper 2605.16311, technical summary), §4 "nanoGPT" (the
+// results hold with spectral as with Frobenius scaling of the Newton-Schulz
+// input). The summary gives no procedure; the one built here: A_raw is the
+// stored Gram matrix of the stored momentum (the Newton-Schulz orientation),
+// lambda is the last ||A v|| of p power-iteration steps from the all-ones
+// vector (w = A v, lambda = ||w||, v = w / lambda), s = 1 / sqrt(lambda), and
+// the first iteration uses A_0 = round(fp32(1 / lambda) * A_raw) with
+// X_0 = s M. lambda = 0 gives s = 0 (U = 0).
+#include "sm_internal.h"
+
+namespace sm {
+namespace {
+
+constexpr int kWave = 64;
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float x) {
+    uint32_t u = __float_as_uint(x);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+// Fixed butterfly over the wave: the order does not depend on timing.
+__device__ __forceinline__ double wave_sum(double v) {
+    for (int off = kWave / 2; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
+    return v;
+}
+
+__device__ __forceinline__ float wave_sum_f32(float v) {
+    for (int off = kWave / 2; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
+    return v;
+}
+
+// Sum of squares of the previous step's vector of one worker, from its block
+// partial sums in block order (one wave).
+__device__ __forceinline__ double prev_norm2(const double *part, int bpw) {
+    const int lane = threadIdx.x & (kWave - 1);
+    double ss = 0.0;
+    for (int i = lane; i < bpw; i += kWave) ss += part[i];
+    return wave_sum(ss);
+}
+
+// One power-iteration step: w = A v with v the all-ones vector / sqrt(r)
+// (step 0) or the previous step's w / ||w||. Each block takes 16 rows of one
+// worker's Gram matrix: v goes to LDS, each wave reduces 4 rows in a fixed
+// order, and the block writes the sum of squares of its rows.
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void power_step_kernel(PowBatch b) {
+    __shared__ float v[kMaxPowR];
+    __shared__ double red[kThreads / kWave];
+    __shared__ float inv_s;
+    const int blk = blockIdx.x;
+    const int mi = find_start(b.starts, blk);
+    const PowMat &M = b.mat[mi];
+    const int local = blk - b.starts.v[mi];
+    const int w = local / M.bpw, rb = local - w * M.bpw;
+    const int r = M.r;
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    const int cur = b.it & 1, prev = cur ^ 1;
+    float *wcur = M.w + ((int64_t)cur * b.workers + w) * r;
+    const float *wprev = M.w + ((int64_t)prev * b.workers + w) * r;
+    if (b.it == 0) {
+        const float v0 = (float)(1.0 / sqrt((double)r));
+        for (int l = threadIdx.x; l < r; l += kThreads) v[l] = v0;
+    } else {
+        if (wave == 0) {
+            const double n2 = prev_norm2(M.part + ((int64_t)prev * b.workers + w) * M.bpw, M.bpw);
+            if (lane == 0) inv_s = n2 > 0.0 ? (float)(1.0 / sqrt(n2)) : 0.0f;
+        }
+        __syncthreads();
+        const float inv = inv_s;
+        for (int l = threadIdx.x; l < r; l += kThreads) v[l] = wprev[l] * inv;
+    }
+    __syncthreads();
+    const char *a = static_cast<const char *>(M.a) + ((int64_t)w * r * r) * (BF16 ? 2 : 4);
+    const bool vec = BF16 ? (r % 8) == 0 : (r % 4) == 0;
+    double sq = 0.0;
+#pragma unroll
+    for (int q = 0; q < kPowRowsPerBlock / (kThreads / kWave); ++q) {
+        const int i = rb * kPowRowsPerBlock + wave * (kPowRowsPerBlock / (kThreads / kWave)) + q;
+        if (i >= r) break;  // uniform over the wave
+        float acc = 0.f;
+        if (BF16) {
+            const uint16_t *row = reinterpret_cast<const uint16_t *>(a) + (int64_t)i * r;
+            if (vec) {
+                for (int l0 = lane * 8; l0 < r; l0 += kWave * 8) {
+                    const uint4 h = *reinterpret_cast<const uint4 *>(row + l0);
+                    const uint32_t hw[4] = {h.x, h.y, h.z, h.w};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        acc = __builtin_fmaf(bf16_bits_to_f32(hw[e] & 0xffffu), v[l0 + 2 * e], acc);
+                        acc = __builtin_fmaf(bf16_bits_to_f32(hw[e] >> 16), v[l0 + 2 * e + 1], acc);
+                    }
+                }
+            } else {
+                for (int l = lane; l < r; l += kWave) acc = __builtin_fmaf(bf16_bits_to_f32(row[l]), v[l], acc);
+            }
+        } else {
+            const float *row = reinterpret_cast<const float *>(a) + (int64_t)i * r;
+            if (vec) {
+                for (int l0 = lane * 4; l0 < r; l0 += kWave * 4) {
+                    const float4 f = *reinterpret_cast<const float4 *>(row + l0);
+                    acc = __builtin_fmaf(f.x, v[l0], acc);
+                    acc = __builtin_fmaf(f.y, v[l0 + 1], acc);
+                    acc = __builtin_fmaf(f.z, v[l0 + 2], acc);
+                    acc = __builtin_fmaf(f.w, v[l0 + 3], acc);
+                }
+            } else {
+                for (int l = lane; l < r; l += kWave) acc = __builtin_fmaf(row[l], v[l], acc);
+            }
+        }
+        acc = wave_sum_f32(acc);
+        if (lane == 0) wcur[i] = acc;
+        sq += (double)acc * acc;
+    }
+    if (lane == 0) red[wave] = sq;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        double t = 0.0;
+        for (int k = 0; k < kThreads / kWave; ++k) t += red[k];
+        M.part[((int64_t)cur * b.workers + w) * M.bpw + rb] = t;
+    }
+}
+
+// lambda = ||A v|| of the last step; s = 1 / sqrt(lambda), s^2 = 1 / lambda
+// per (matrix, worker) (0 when lambda = 0). One wave per (matrix, worker).
+__global__ __launch_bounds__(kThreads) void power_finalize_kernel(PowBatch b) {
+    const int u = __builtin_amdgcn_readfirstlane(blockIdx.x * (kThreads / kWave) + threadIdx.x / kWave);
+    if (u >= b.nmat * b.workers) return;
+    const PowMat &M = b.mat[u / b.workers];
+    const int w = u % b.workers;
+    const int last = b.it & 1;
+    const double n2 = prev_norm2(M.part + ((int64_t)last * b.workers + w) * M.bpw, M.bpw);
+    if ((threadIdx.x & (kWave - 1)) == 0) {
+        const double lambda = sqrt(n2);
+        float s = 0.f, s2 = 0.f;
+        if (lambda > 0.0) {
+            s = (float)(1.0 / sqrt(lambda));
+            s2 = (float)(1.0 / lambda);
+        }
+        b.scales[M.unit_begin + w] = make_float2(s, s2);
+    }
+}
+
+// A <- round(s^2 * A) in place for every (matrix, worker) Gram matrix; 8
+// entries per thread. Blocks: per matrix, workers x rescale_bpw.
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void gram_rescale_kernel(PowBatch b) {
+    const int blk = blockIdx.x;
+    const int mi = find_start(b.starts, blk);
+    const PowMat &M = b.mat[mi];
+    const int local = blk - b.starts.v[mi];
+    const int w = local / M.bpw, cb = local - w * M.bpw;
+    const int64_t rr = (int64_t)M.r * M.r;
+    const float s2 = b.scales[M.unit_begin + w].y;
+    const int64_t e0 = ((int64_t)cb * kThreads + threadIdx.x) * 8;
+    char *a = static_cast<char *>(const_cast<void *>(M.a)) + (int64_t)w * rr * (BF16 ? 2 : 4);
+    for (int64_t e = e0; e < e0 + 8 && e < rr; ++e) {
+        if (BF16) {
+            uint16_t *p = reinterpret_cast<uint16_t *>(a) + e;
+            *p = (uint16_t)f32_to_bf16_bits(s2 * bf16_bits_to_f32(*p));
+        } else {
+            float *p = reinterpret_cast<float *>(a) + e;
+            *p = s2 * *p;
+        }
+    }
+}
+
+}  // namespace
+
+int32_t power_blocks_per_worker(int64_t r) { return (int32_t)((r + kPowRowsPerBlock - 1) / kPowRowsPerBlock); }
+int32_t rescale_blocks_per_worker(int64_t r) { return (int32_t)((r * r + kThreads * 8 - 1) / (kThreads * 8)); }
+
+void launch_power_step(const PowBatch &b, bool bf16, hipStream_t s) {
+    dim3 grid(b.total_blocks), block(kThreads);
+    if (bf16)
+        hipLaunchKernelGGL(power_step_kernel<true>, grid, block, 0, s, b);
+    else
+        hipLaunchKernelGGL(power_step_kernel<false>, grid, block, 0, s, b);
+}
+
+void launch_power_finalize(const PowBatch &b, hipStream_t s) {
+    const int units = b.nmat * b.workers;
+    hipLaunchKernelGGL(power_finalize_kernel, dim3((units + 3) / 4), dim3(kThreads), 0, s, b);
+}
+
+void launch_gram_rescale(const PowBatch &b, bool bf16, hipStream_t s) {
+    dim3 grid(b.total_blocks), block(kThreads);
+    if (bf16)
+        hipLaunchKernelGGL(gram_rescale_kernel<true>, grid, block, 0, s, b);
+    else
+        hipLaunchKernelGGL(gram_rescale_kernel<false>, grid, block, 0, s, b);
+}
+
+}  // namespace sm

@@ -61,6 +61,8 @@ class Workload:
     eta: float = 1e-3
     w_scale: float = 0.02
     post_polar_iters: int = 0
+    norm: str = "frobenius"            # or "spectral" (power iteration on the Gram matrix)
+    power_iters: int = 0
     description: str = field(default="", compare=False)
 
     @property
@@ -101,6 +103,11 @@ WORKLOADS = {
         mom_dtype="bf16", ns_dtype="bf16",
         description="GPT-2 small 48 matrices (84.9M params), bf16 momentum and NS, fp32 W, "
                     "8 workers, grads N(0,1e-3), 1 NS iter"),
+    "gpt2s_mw8_k1_spectral": Workload(
+        "gpt2s_mw8_k1_spectral", 3, _gpt2_small_shapes(), workers=8, ns_iters=1, grad_scale=1e-3,
+        mom_dtype="bf16", ns_dtype="bf16", norm="spectral", power_iters=8,
+        description="as gpt2s_mw8_k1 with spectral scaling of the Newton-Schulz input "
+                    "(8 power-iteration steps on the Gram matrix)"),
     "gpt2s_mw16_k5_t3": Workload(
         "gpt2s_mw16_k5_t3", 4, _gpt2_small_shapes(), workers=16, ns_iters=5,
         grad_dist="student_t3", grad_scale=1e-3, mom_dtype="bf16", ns_dtype="bf16",

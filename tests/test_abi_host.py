@@ -57,7 +57,8 @@ def _fake(R, C, mw, *, aligned=True, polar=False, vote=False):
 def _call(fn, mats, params, ws=0x7f1000000000, ws_bytes=1 << 40):
     arr = (sm._Matrix * len(mats))(*mats)
     p = sm._Params(params.workers, params.beta, params.eta, params.ns_iters,
-                   params.post_polar_iters, params.grad_dtype, params.mom_dtype, params.ns_dtype)
+                   params.post_polar_iters, params.grad_dtype, params.mom_dtype, params.ns_dtype,
+                   params.norm, params.power_iters)
     return fn(arr, len(mats), ctypes.byref(p), ws, ws_bytes, None)
 
 
@@ -146,3 +147,25 @@ def test_int8_payload_argument_errors(lib):
     assert lib.signmuon_vote_update_int8(a, 256, 10, a, 1e-3, None, None) == -6
     assert lib.signmuon_vote_update_int8(a + 2, 3, 10, a, 1e-3, None, None) == -3
     assert lib.signmuon_vote_update_int8(a, 3, 10, a, 1e-3, a + 4, None) == -3
+
+
+@pytest.mark.parametrize("fn", ["signmuon_step", "signmuon_momentum_ns"])
+def test_spectral_argument_errors(lib, fn):
+    f = getattr(lib, fn)
+    polar = fn == "signmuon_momentum_ns"
+    ok = _fake(64, 64, 4, polar=polar)
+    assert _call(f, [ok], sm.Params(workers=4, norm=2)) == -1
+    assert _call(f, [ok], sm.Params(workers=4, norm=sm.NORM_SPECTRAL, power_iters=0)) == -1
+    assert _call(f, [ok], sm.Params(workers=4, norm=sm.NORM_SPECTRAL, power_iters=1001)) == -6
+    big = _fake(8200, 8200, 1, polar=polar)
+    assert _call(f, [big], sm.Params(workers=1, norm=sm.NORM_SPECTRAL, power_iters=4)) == -6
+
+
+def test_spectral_workspace_adds_power_vectors(lib):
+    arr = (sm._Matrix * 1)(sm._Matrix(300, 700, None, None, None, None, None, None))
+    frob = sm._Params(4, 0.9, 1e-3, 0, 0, sm.F32, sm.F32, sm.F32, sm.NORM_FROBENIUS, 0)
+    spec = sm._Params(4, 0.9, 1e-3, 0, 0, sm.F32, sm.F32, sm.F32, sm.NORM_SPECTRAL, 3)
+    nf = lib.signmuon_workspace_bytes(arr, 1, ctypes.byref(frob))
+    ns = lib.signmuon_workspace_bytes(arr, 1, ctypes.byref(spec))
+    # k = 0 with spectral scaling still needs the Gram matrix and the power vectors
+    assert ns >= nf + 4 * 300 * 300 * 4 + 2 * 4 * 300 * 4
