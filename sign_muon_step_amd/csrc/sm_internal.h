@@ -186,7 +186,7 @@ void launch_vote_update_int8(const int8_t *signs, int32_t workers, int64_t n, fl
 // ---------------------------------------------------------------------------
 // Spectral normalisation: power iteration on each worker's Gram matrix.
 // ---------------------------------------------------------------------------
-constexpr int kPowRowsPerBlock = 16;  // rows of A per power-step block
+constexpr int kPowRowsPerBlock = 32;  // rows of A per power-step block (8 per wave)
 constexpr int kMaxPowR = 8192;         // the power vector of a Gram lives in LDS
 
 struct PowMat {

@@ -49,12 +49,15 @@ __device__ __forceinline__ double prev_norm2(const double *part, int bpw) {
 }
 
 // One power-iteration step: w = A v with v the all-ones vector / sqrt(r)
-// (step 0) or the previous step's w / ||w||. Each block takes 16 rows of one
-// worker's Gram matrix: v goes to LDS, each wave reduces 4 rows in a fixed
-// order, and the block writes the sum of squares of its rows.
+// (step 0) or the previous step's w / ||w||. Each block takes 32 rows of one
+// worker's Gram matrix: v goes to LDS (r floats, sized at launch), each wave
+// computes 8 rows with the loads of all 8 in flight together and reduces
+// each in a fixed order, and the block writes the sum of squares of its rows.
+constexpr int kRowsPerWave = kPowRowsPerBlock / (kThreads / kWave);
+
 template <bool BF16>
 __global__ __launch_bounds__(kThreads) void power_step_kernel(PowBatch b) {
-    __shared__ float v[kMaxPowR];
+    extern __shared__ float v[];
     __shared__ double red[kThreads / kWave];
     __shared__ float inv_s;
     const int blk = blockIdx.x;
@@ -81,45 +84,64 @@ __global__ __launch_bounds__(kThreads) void power_step_kernel(PowBatch b) {
     }
     __syncthreads();
     const char *a = static_cast<const char *>(M.a) + ((int64_t)w * r * r) * (BF16 ? 2 : 4);
-    const bool vec = BF16 ? (r % 8) == 0 : (r % 4) == 0;
-    double sq = 0.0;
+    const int i0 = rb * kPowRowsPerBlock + wave * kRowsPerWave;
+    const int nrows = r - i0 < kRowsPerWave ? (r - i0 > 0 ? r - i0 : 0) : kRowsPerWave;  // uniform
+    float acc[kRowsPerWave];
 #pragma unroll
-    for (int q = 0; q < kPowRowsPerBlock / (kThreads / kWave); ++q) {
-        const int i = rb * kPowRowsPerBlock + wave * (kPowRowsPerBlock / (kThreads / kWave)) + q;
-        if (i >= r) break;  // uniform over the wave
-        float acc = 0.f;
-        if (BF16) {
-            const uint16_t *row = reinterpret_cast<const uint16_t *>(a) + (int64_t)i * r;
-            if (vec) {
-                for (int l0 = lane * 8; l0 < r; l0 += kWave * 8) {
-                    const uint4 h = *reinterpret_cast<const uint4 *>(row + l0);
-                    const uint32_t hw[4] = {h.x, h.y, h.z, h.w};
+    for (int q = 0; q < kRowsPerWave; ++q) acc[q] = 0.f;
+    if (BF16 && (r % 8) == 0) {
+        const uint16_t *rows = reinterpret_cast<const uint16_t *>(a) + (int64_t)i0 * r;
+        for (int l0 = lane * 8; l0 < r; l0 += kWave * 8) {
+            uint4 h[kRowsPerWave];
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        acc = __builtin_fmaf(bf16_bits_to_f32(hw[e] & 0xffffu), v[l0 + 2 * e], acc);
-                        acc = __builtin_fmaf(bf16_bits_to_f32(hw[e] >> 16), v[l0 + 2 * e + 1], acc);
-                    }
+            for (int q = 0; q < kRowsPerWave; ++q)
+                h[q] = q < nrows ? *reinterpret_cast<const uint4 *>(rows + (int64_t)q * r + l0) : make_uint4(0, 0, 0, 0);
+            float vv[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) vv[e] = v[l0 + e];
+#pragma unroll
+            for (int q = 0; q < kRowsPerWave; ++q) {
+                const uint32_t hw[4] = {h[q].x, h[q].y, h[q].z, h[q].w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    acc[q] = __builtin_fmaf(bf16_bits_to_f32(hw[e] & 0xffffu), vv[2 * e], acc[q]);
+                    acc[q] = __builtin_fmaf(bf16_bits_to_f32(hw[e] >> 16), vv[2 * e + 1], acc[q]);
                 }
-            } else {
-                for (int l = lane; l < r; l += kWave) acc = __builtin_fmaf(bf16_bits_to_f32(row[l]), v[l], acc);
-            }
-        } else {
-            const float *row = reinterpret_cast<const float *>(a) + (int64_t)i * r;
-            if (vec) {
-                for (int l0 = lane * 4; l0 < r; l0 += kWave * 4) {
-                    const float4 f = *reinterpret_cast<const float4 *>(row + l0);
-                    acc = __builtin_fmaf(f.x, v[l0], acc);
-                    acc = __builtin_fmaf(f.y, v[l0 + 1], acc);
-                    acc = __builtin_fmaf(f.z, v[l0 + 2], acc);
-                    acc = __builtin_fmaf(f.w, v[l0 + 3], acc);
-                }
-            } else {
-                for (int l = lane; l < r; l += kWave) acc = __builtin_fmaf(row[l], v[l], acc);
             }
         }
-        acc = wave_sum_f32(acc);
-        if (lane == 0) wcur[i] = acc;
-        sq += (double)acc * acc;
+    } else if (!BF16 && (r % 4) == 0) {
+        const float *rows = reinterpret_cast<const float *>(a) + (int64_t)i0 * r;
+        for (int l0 = lane * 4; l0 < r; l0 += kWave * 4) {
+            float4 f[kRowsPerWave];
+#pragma unroll
+            for (int q = 0; q < kRowsPerWave; ++q)
+                f[q] = q < nrows ? *reinterpret_cast<const float4 *>(rows + (int64_t)q * r + l0) : make_float4(0, 0, 0, 0);
+#pragma unroll
+            for (int q = 0; q < kRowsPerWave; ++q) {
+                acc[q] = __builtin_fmaf(f[q].x, v[l0], acc[q]);
+                acc[q] = __builtin_fmaf(f[q].y, v[l0 + 1], acc[q]);
+                acc[q] = __builtin_fmaf(f[q].z, v[l0 + 2], acc[q]);
+                acc[q] = __builtin_fmaf(f[q].w, v[l0 + 3], acc[q]);
+            }
+        }
+    } else {
+        for (int q = 0; q < nrows; ++q) {
+            const int64_t base = (int64_t)(i0 + q) * r;
+            for (int l = lane; l < r; l += kWave) {
+                const float aij = BF16 ? bf16_bits_to_f32(reinterpret_cast<const uint16_t *>(a)[base + l])
+                                       : reinterpret_cast<const float *>(a)[base + l];
+                acc[q] = __builtin_fmaf(aij, v[l], acc[q]);
+            }
+        }
+    }
+    double sq = 0.0;
+#pragma unroll
+    for (int q = 0; q < kRowsPerWave; ++q) {
+        const float t = wave_sum_f32(acc[q]);
+        if (q < nrows) {
+            if (lane == 0) wcur[i0 + q] = t;
+            sq += (double)t * t;
+        }
     }
     if (lane == 0) red[wave] = sq;
     __syncthreads();
@@ -181,10 +203,13 @@ int32_t rescale_blocks_per_worker(int64_t r) { return (int32_t)((r * r + kThread
 
 void launch_power_step(const PowBatch &b, bool bf16, hipStream_t s) {
     dim3 grid(b.total_blocks), block(kThreads);
+    int rmax = 0;
+    for (int i = 0; i < b.nmat; ++i) rmax = b.mat[i].r > rmax ? b.mat[i].r : rmax;
+    const size_t lds = (size_t)rmax * sizeof(float);  // v; rmax <= kMaxPowR
     if (bf16)
-        hipLaunchKernelGGL(power_step_kernel<true>, grid, block, 0, s, b);
+        hipLaunchKernelGGL(power_step_kernel<true>, grid, block, lds, s, b);
     else
-        hipLaunchKernelGGL(power_step_kernel<false>, grid, block, 0, s, b);
+        hipLaunchKernelGGL(power_step_kernel<false>, grid, block, lds, s, b);
 }
 
 void launch_power_finalize(const PowBatch &b, hipStream_t s) {
