@@ -14,12 +14,17 @@ constexpr int kWave = 64;
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
 
 // Round-to-nearest-even fp32 -> bf16 pattern; NaN stays a quiet NaN.
-__device__ __forceinline__ uint32_t f32_to_bf16_bits(float x) {
-    uint32_t u = __float_as_uint(x);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return u >> 16;
+// fp32 -> bf16 bits, round to nearest even, NaN quieted with its sign and
+// top payload bits: one v_cvt_pk_bf16_f32 per pair of values (the hardware
+// conversion gives exactly this rule on every fp32 bit pattern).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    const f32x2_t v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
+
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float x) { return pack_bf16x2(x, x) & 0xffffu; }
 
 __device__ __forceinline__ double wave_sum(double v) {
     for (int off = kWave / 2; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
@@ -97,9 +102,10 @@ __device__ __forceinline__ double update8(float beta, const float (&g)[8], const
         u32x4_t out;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const uint32_t lo = f32_to_bf16_bits(__builtin_fmaf(beta, m[2 * i], g[2 * i]));
-            const uint32_t hi = f32_to_bf16_bits(__builtin_fmaf(beta, m[2 * i + 1], g[2 * i + 1]));
-            out[i] = lo | (hi << 16);
+            const uint32_t both = pack_bf16x2(__builtin_fmaf(beta, m[2 * i], g[2 * i]),
+                                              __builtin_fmaf(beta, m[2 * i + 1], g[2 * i + 1]));
+            const uint32_t lo = both & 0xffffu, hi = both >> 16;
+            out[i] = both;
             const double s0 = bf16_bits_to_f32(lo), s1 = bf16_bits_to_f32(hi);
             ss += s0 * s0;
             ss += s1 * s1;

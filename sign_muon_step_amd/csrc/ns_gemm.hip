@@ -64,12 +64,17 @@ template <> struct Elem<false> {
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
 
-__device__ __forceinline__ uint32_t f32_to_bf16_bits(float x) {
-    uint32_t u = __float_as_uint(x);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return u >> 16;
+// fp32 -> bf16 bits, round to nearest even, NaN quieted with its sign and
+// top payload bits: one v_cvt_pk_bf16_f32 per pair of values (the hardware
+// conversion gives exactly this rule on every fp32 bit pattern).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    const f32x2_t v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
+
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float x) { return pack_bf16x2(x, x) & 0xffffu; }
 
 // LDS layouts of one operand's k-slice (16 KiB):
 //  k-contiguous ("KL"): 256 rows x 64 bytes (BK of k), 16-byte chunk c of row
@@ -669,8 +674,8 @@ __device__ __forceinline__ void store4(void *p, int64_t idx, const float (&v)[4]
                                        int cols_left) {
     if (FAST) {
         if (BF16) {
-            const uint32_t lo = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
-            const uint32_t hi = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
+            const uint32_t lo = pack_bf16x2(v[0], v[1]);
+            const uint32_t hi = pack_bf16x2(v[2], v[3]);
             *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(p) + idx) = make_uint2(lo, hi);
         } else {
             *reinterpret_cast<float4 *>(static_cast<float *>(p) + idx) = make_float4(v[0], v[1], v[2], v[3]);
@@ -699,7 +704,7 @@ __device__ __forceinline__ void store32(void *p, int64_t idx, const float (&v)[3
             uint32_t w[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                w[e] = f32_to_bf16_bits(v[8 * c + 2 * e]) | (f32_to_bf16_bits(v[8 * c + 2 * e + 1]) << 16);
+                w[e] = pack_bf16x2(v[8 * c + 2 * e], v[8 * c + 2 * e + 1]);
             q[c] = make_uint4(w[0], w[1], w[2], w[3]);
         }
     } else if (FAST) {
