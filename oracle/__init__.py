@@ -53,6 +53,10 @@ def _load():
     lib.orc_step_matrix_norm.argtypes = [i64, i64, i32, f32, f32, ctypes.c_int, ctypes.c_int,
                                          ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                          ctypes.c_int, vp, vp, vp, vp, vp, vp]
+    lib.orc_muon_step_matrix.restype = ctypes.c_int
+    lib.orc_muon_step_matrix.argtypes = [i64, i64, f32, f32, ctypes.c_int, ctypes.c_int,
+                                         ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                         vp, vp, vp, vp]
     lib.orc_ns1_entries.restype = ctypes.c_int
     lib.orc_ns1_entries.argtypes = [i64, i64, vp, ctypes.c_int, i64, vp, vp, vp]
     lib.orc_sign_pack.argtypes = [i64, vp, ctypes.c_int, vp]
@@ -263,3 +267,18 @@ def step_matrix(g, m, w, beta, eta, k, ns_dtype, post_k=0, want_u=False, norm=0,
     if rc != 0:
         raise MemoryError("oracle step_matrix")
     return packed, vote, u
+
+
+def muon_step_matrix(g, m, w, beta, eta, k, ns_dtype, norm=0, power_iters=0, want_u=False):
+    """Full-precision Muon step for one worker: g, m are [R][C] (m updated in
+    place), w [R][C] float32 updated in place. Returns U (fp64) or None."""
+    assert m.flags.c_contiguous and w.flags.c_contiguous and w.dtype == np.float32
+    g = _c(g)
+    R, C = m.shape
+    assert g.shape == m.shape == w.shape
+    u = np.empty((R, C), np.float64) if want_u else None
+    rc = _load().orc_muon_step_matrix(R, C, beta, eta, k, _dtype_code(g), _dtype_code(m), ns_dtype,
+                                      norm, power_iters, _ptr(g), _ptr(m), _ptr(u), _ptr(w))
+    if rc != 0:
+        raise MemoryError("oracle muon_step_matrix")
+    return u

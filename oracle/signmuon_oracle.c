@@ -399,6 +399,48 @@ void orc_vote_update_int8(int64_t n, int32_t mw, const int8_t *signs, float *w, 
 }
 
 /* ------------------------------------------------------------------------ */
+/* Full-precision Muon step, the comparison point the summary's §1 "Problem  */
+/* statement" and §4 "Empirical results" name (Muon): one worker's momentum, */
+/* its normalised Newton-Schulz polar factor U, and W <- W - eta U with no   */
+/* sign and no vote. Readings: the same momentum, normalisation (norm,       */
+/* power_iters as in orc_step_matrix_norm) and iteration as the Sign-Muon    */
+/* step; the update is one fp32 fused multiply-add on the fp32 value of U,   */
+/* as in the post-vote polar step.                                           */
+/* ------------------------------------------------------------------------ */
+int orc_muon_step_matrix(int64_t R, int64_t C, float beta, float eta, int k, int g_dt, int m_dt,
+                         int ns_dt, int norm, int power_iters, const void *g, void *m,
+                         double *u_out, float *w)
+{
+    int64_t n = R * C, r = R <= C ? R : C;
+    double *x0 = (double *)malloc(sizeof(double) * (size_t)n);
+    double *u = (double *)malloc(sizeof(double) * (size_t)n);
+    double *a0 = norm == ORC_NORM_SPECTRAL ? (double *)malloc(sizeof(double) * (size_t)(r * r)) : NULL;
+    if (!x0 || !u || (norm == ORC_NORM_SPECTRAL && !a0)) {
+        free(x0); free(u); free(a0);
+        return -1;
+    }
+    int rc = 0;
+    orc_momentum(n, beta, g, g_dt, m, m_dt);
+    if (norm == ORC_NORM_SPECTRAL) {
+        if (orc_spectral_x0_a0(R, C, m, m_dt, ns_dt, power_iters, x0, a0) < 0.0)
+            rc = -1;
+        else
+            rc = newton_schulz(R, C, x0, a0, k, ns_dt, u);
+    } else {
+        orc_normalise(n, m, m_dt, x0);
+        rc = orc_newton_schulz(R, C, x0, k, ns_dt, u);
+    }
+    if (rc == 0) {
+        for (int64_t i = 0; i < n; ++i)
+            w[i] = fmaf(-eta, (float)u[i], w[i]);
+        if (u_out)
+            memcpy(u_out, u, sizeof(double) * (size_t)n);
+    }
+    free(x0); free(u); free(a0);
+    return rc;
+}
+
+/* ------------------------------------------------------------------------ */
 /* O8 optional post-vote polar step -- §2 "Algorithmic flow" step 5 (a local */
 /* polar step on the aggregated sign matrix, no extra communication).        */
 /* Readings: the same Frobenius-normalised Newton-Schulz as O2-O3 applied to */

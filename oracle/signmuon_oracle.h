@@ -114,6 +114,13 @@ int orc_step_matrix_norm(int64_t R, int64_t C, int32_t mw, float beta, float eta
                          const void *g, void *m, double *u_out, uint64_t *packed, float *w,
                          int8_t *vote_out);
 
+/* Full-precision Muon step for one worker (no sign, no vote): momentum,
+ * normalised Newton-Schulz U (k iterations), W <- fmaf(-eta, (float)U, W).
+ * u_out (nullable) receives U in fp64. */
+int orc_muon_step_matrix(int64_t R, int64_t C, float beta, float eta, int k, int g_dt, int m_dt,
+                         int ns_dt, int norm, int power_iters, const void *g, void *m,
+                         double *u_out, float *w);
+
 #ifdef __cplusplus
 }
 #endif

@@ -734,3 +734,63 @@ def test_generators_are_seeded_and_distinct():
     assert not np.array_equal(a, synthetic.gradient(wl, 0, 2, 0))
     assert not np.array_equal(a, synthetic.gradient(wl, 0, 1, 1))
     assert a.dtype == np.float32 and a.shape == (256, 256)
+
+
+# ---------------------------------------------------------------------------
+# full-precision Muon step (the comparison point of the summary, one worker,
+# no sign): U = NS(M / ||M||), W <- fmaf(-eta, U, W)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("shape", [(6, 10), (10, 6), (8, 8)])
+@pytest.mark.parametrize("k", [1, 3])
+def test_muon_step_direction_is_the_svd_closed_form(shape, k):
+    R, C = shape
+    rng = np.random.default_rng(R * 31 + C + k)
+    g = rng.standard_normal((R, C)).astype(np.float32)
+    m = np.zeros((R, C), np.float32)
+    w = np.zeros((R, C), np.float32)
+    u = oracle.muon_step_matrix(g, m, w, 0.9, 1e-3, k, oracle.F64, want_u=True)
+    np.testing.assert_array_equal(m, g)  # first step from M_0 = 0
+    us, sig, vt = np.linalg.svd(g.astype(np.float64), full_matrices=False)
+    expect = (us * scalar_map(sig / np.linalg.norm(sig), k)) @ vt
+    assert rel_fro(u, expect) < 1e-12
+
+
+def test_muon_step_update_is_one_fused_multiply_add():
+    """W_new = fp32(-eta * fp32(U) + W_old), the product and sum exact before
+    the one rounding (checked with exact rationals)."""
+    rng = np.random.default_rng(32)
+    R, C = 7, 9
+    g = rng.standard_normal((R, C)).astype(np.float32)
+    w0 = rng.standard_normal((R, C)).astype(np.float32)
+    w = w0.copy()
+    eta = np.float32(0.3)
+    u = oracle.muon_step_matrix(g, np.zeros((R, C), np.float32), w, 0.9, float(eta), 2, F32,
+                                want_u=True)
+    u32 = u.astype(np.float32)
+    for i in range(R):
+        for j in range(C):
+            q = -Fraction(float(eta)) * Fraction(float(u32[i, j])) + Fraction(float(w0[i, j]))
+            assert w[i, j] == exact_round_f32(q)
+
+
+def test_muon_step_rank_one_momentum_is_a_fixed_point():
+    rng = np.random.default_rng(33)
+    a, b = rng.integers(-3, 4, 7), rng.integers(-3, 4, 11)
+    a[0], b[0] = 1, 2
+    g = np.outer(a, b).astype(np.float32)  # exact in fp32
+    for k in (1, 4):
+        u = oracle.muon_step_matrix(g, np.zeros_like(g), np.zeros_like(g), 0.9, 1e-3, k,
+                                    oracle.F64, want_u=True)
+        assert rel_fro(u, g / np.linalg.norm(g.astype(np.float64))) < 1e-13
+
+
+def test_single_worker_sign_muon_moves_by_eta_times_the_sign_of_the_muon_direction():
+    rng = np.random.default_rng(34)
+    R, C = 12, 20
+    g = rng.standard_normal((R, C)).astype(np.float32)
+    w = np.zeros((R, C), np.float32)
+    u = oracle.muon_step_matrix(g, np.zeros((R, C), np.float32), w.copy(), 0.9, 1e-3, 2, F32,
+                                want_u=True)
+    w_sign = np.zeros((R, C), np.float32)
+    oracle.step_matrix(g[None], np.zeros((1, R, C), np.float32), w_sign, 0.9, 1e-3, 2, F32)
+    np.testing.assert_array_equal(w_sign, np.where(u >= 0, np.float32(-1e-3), np.float32(1e-3)))
