@@ -200,6 +200,20 @@ int signmuon_vote_update_int8(const int8_t *signs, int32_t workers, int64_t n, f
 int signmuon_step(const signmuon_matrix *mats, int32_t n_mats, const signmuon_params *p,
                   void *workspace, size_t workspace_bytes, signmuon_stream stream);
 
+/*
+ * signmuon_muon_step -- the full-precision Muon step that the summary
+ * compares against (§1 "Problem statement", §4 "Empirical results"): for one
+ * worker, the momentum and normalised Newton-Schulz factor U of
+ * signmuon_momentum_ns, then W <- fmaf(-eta, U, W) on the fp32 value of U,
+ * with no sign and no vote. p->workers must be 1 and p->ns_iters >= 1
+ * (p->post_polar_iters must be 0; norm and power_iters apply as in
+ * signmuon_step). mats[i].grad, .momentum and .weight are required;
+ * .polar_out receives U when non-NULL; .packed and .vote_out are ignored.
+ * workspace: signmuon_workspace_bytes(mats, n_mats, p) bytes.
+ */
+int signmuon_muon_step(const signmuon_matrix *mats, int32_t n_mats, const signmuon_params *p,
+                       void *workspace, size_t workspace_bytes, signmuon_stream stream);
+
 /* Kernel kinds reported by signmuon_step_traced, one per launch. */
 enum {
     SIGNMUON_K_MOMENTUM = 1, /* momentum update + Frobenius partial sums */

@@ -75,6 +75,8 @@ def library() -> ctypes.CDLL:
     lib.signmuon_momentum_ns.argtypes = [mp, i32, pp, vp, ctypes.c_size_t, vp]
     lib.signmuon_step.restype = ctypes.c_int
     lib.signmuon_step.argtypes = [mp, i32, pp, vp, ctypes.c_size_t, vp]
+    lib.signmuon_muon_step.restype = ctypes.c_int
+    lib.signmuon_muon_step.argtypes = [mp, i32, pp, vp, ctypes.c_size_t, vp]
     lib.signmuon_step_traced.restype = ctypes.c_int
     lib.signmuon_step_traced.argtypes = [mp, i32, pp, vp, ctypes.c_size_t, vp, ctypes.POINTER(_Trace)]
     lib.signmuon_sign_pack.restype = ctypes.c_int
@@ -203,6 +205,14 @@ def signmuon_step(mats: Sequence[Matrix], params: Params, workspace: Optional[to
     nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(library().signmuon_step(arr, len(mats), ctypes.byref(p), _ptr(workspace), nbytes,
                                    _stream(stream)))
+
+
+def signmuon_muon_step(mats: Sequence[Matrix], params: Params, workspace: Optional[torch.Tensor],
+                       stream=None) -> None:
+    arr, p = _marshal(mats, params)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(library().signmuon_muon_step(arr, len(mats), ctypes.byref(p), _ptr(workspace), nbytes,
+                                        _stream(stream)))
 
 
 class Trace:

@@ -240,7 +240,8 @@ int run_momentum(const signmuon_matrix *mats, int32_t n_mats, const signmuon_par
 // (product) of iteration 0 in. The last product's epilogue writes U
 // (polar_out or scratch) and, for step, the fused packed signs.
 int ns_pass(const signmuon_matrix *mats, int32_t n_mats, const signmuon_params *p, const Plan &pl,
-            void *ws, bool step, int j, int pass, bool use_scales, hipStream_t st, Tracer &tr) {
+            void *ws, bool step, int j, int pass, bool use_scales, hipStream_t st, Tracer &tr,
+            bool muon = false) {
     const int k = p->ns_iters;
     const bool last = j == k - 1;
     const bool bf16 = p->ns_dtype == SIGNMUON_BF16;
@@ -252,6 +253,7 @@ int ns_pass(const signmuon_matrix *mats, int32_t n_mats, const signmuon_params *
         b.workers = p->workers;
         b.use_scales = use_scales;
         b.scales = scales;
+        b.eta = p->eta;  // the W-update epilogue
         int64_t tiles = 0;
         for (int32_t i = 0; i < cn; ++i) {
             const MatPlan &q = pl.m[c0 + i];
@@ -264,6 +266,9 @@ int ns_pass(const signmuon_matrix *mats, int32_t n_mats, const signmuon_params *
             d.a = ws_at<char>(ws, pl.off_gram + q.gram_off);
             if (!last) {
                 d.out = ws_at<char>(ws, pl.off_iter[j & 1] + q.iter_off);
+            } else if (muon) {
+                d.out = s.weight;
+                d.u_out = s.polar_out;
             } else if (s.polar_out) {
                 d.out = s.polar_out;
             } else if (q.u_scratch) {
@@ -283,7 +288,7 @@ int ns_pass(const signmuon_matrix *mats, int32_t n_mats, const signmuon_params *
         if (pass == 0)
             sm::launch_ns_gram(b, bf16, st);
         else
-            sm::launch_ns_product(b, bf16, last ? sm::EPI_FINAL : sm::EPI_ITER, st);
+            sm::launch_ns_product(b, bf16, !last ? sm::EPI_ITER : (muon ? sm::EPI_WUPD : sm::EPI_FINAL), st);
         if (int rc = tr.after(pass == 0 ? SIGNMUON_K_GRAM : SIGNMUON_K_PRODUCT)) return rc;
     }
     return SIGNMUON_OK;
@@ -346,14 +351,15 @@ int run_spectral(const signmuon_matrix *mats, int32_t n_mats, const signmuon_par
 // Newton-Schulz iterations of every (matrix, worker); with spectral
 // normalisation the first Gram matrix comes from run_spectral.
 int run_newton_schulz(const signmuon_matrix *mats, int32_t n_mats, const signmuon_params *p,
-                      const Plan &pl, void *ws, bool step, hipStream_t st, Tracer &tr) {
+                      const Plan &pl, void *ws, bool step, hipStream_t st, Tracer &tr,
+                      bool muon = false) {
     for (int j = 0; j < p->ns_iters; ++j) {
         if (j == 0 && pl.spectral) {
             if (int rc = run_spectral(mats, n_mats, p, pl, ws, true, st, tr)) return rc;
         } else {
             if (int rc = ns_pass(mats, n_mats, p, pl, ws, step, j, 0, j == 0, st, tr)) return rc;
         }
-        if (int rc = ns_pass(mats, n_mats, p, pl, ws, step, j, 1, j == 0, st, tr)) return rc;
+        if (int rc = ns_pass(mats, n_mats, p, pl, ws, step, j, 1, j == 0, st, tr, muon)) return rc;
     }
     return SIGNMUON_OK;
 }
@@ -569,6 +575,25 @@ int signmuon_step_traced(const signmuon_matrix *mats, int32_t n_mats, const sign
     if (p->post_polar_iters > 0)
         if (int rc = run_post_polar(mats, n_mats, p, pl, workspace, st, tr)) return rc;
     return SIGNMUON_OK;
+}
+
+int signmuon_muon_step(const signmuon_matrix *mats, int32_t n_mats, const signmuon_params *p,
+                       void *workspace, size_t workspace_bytes, signmuon_stream stream) {
+    Plan pl;
+    if (int rc = make_plan(mats, n_mats, p, false, pl)) return rc;
+    if (p->workers != 1 || p->ns_iters < 1 || p->post_polar_iters != 0) return SIGNMUON_EINVAL;
+    for (int32_t i = 0; i < n_mats; ++i) {
+        const signmuon_matrix &s = mats[i];
+        if (!s.grad || !s.momentum || !s.weight) return SIGNMUON_EINVAL;
+        const void *ptrs[4] = {s.grad, s.momentum, s.weight, s.polar_out};
+        for (const void *q : ptrs)
+            if (q && !aligned16(q)) return SIGNMUON_EALIGN;
+    }
+    if (int rc = check_workspace(pl, workspace, workspace_bytes)) return rc;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    Tracer tr;
+    if (int rc = run_momentum(mats, n_mats, p, pl, workspace, st, tr)) return rc;
+    return run_newton_schulz(mats, n_mats, p, pl, workspace, false, st, tr, true);
 }
 
 int signmuon_step(const signmuon_matrix *mats, int32_t n_mats, const signmuon_params *p,

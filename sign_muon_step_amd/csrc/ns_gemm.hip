@@ -816,6 +816,7 @@ void ns_gram_kernel(NsBatch b) {
 struct ProductArgs {
     void *out;       // this worker's output (U / next iterate) or W
     uint64_t *pk;    // this worker's packed words or nullptr
+    float *u_out;    // EPI_WUPD: U (fp32) as well, or nullptr
     int R, C, ti, tj;
     float gamma, eta;
 };
@@ -862,6 +863,7 @@ __device__ __forceinline__ void product_epilogue(const ProductArgs &pa, f32x16_t
 #pragma unroll
                     for (int t = 0; t < 4; ++t) w[t] = __builtin_fmaf(-pa.eta, u[t], w[t]);
                     store4<false, FAST>(pa.out, idx, w, gm < R, C - gn);
+                    if (pa.u_out) store4<false, FAST>(pa.u_out, idx, u, gm < R, C - gn);
                 }
             }
             if (want_pack) *reinterpret_cast<float4 *>(sp) = make_float4(u[0], u[1], u[2], u[3]);
@@ -985,6 +987,7 @@ void ns_product_kernel(NsBatch b) {
         pa.out = M.out ? static_cast<void *>(static_cast<float *>(M.out) + (int64_t)w * n) : nullptr;
     else
         pa.out = M.out;
+    pa.u_out = EPI == EPI_WUPD ? M.u_out : nullptr;
     pa.pk = M.packed ? M.packed + (int64_t)w * ((n + 63) >> 6) : nullptr;
 
     if (wide) {

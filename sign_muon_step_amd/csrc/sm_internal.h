@@ -73,8 +73,10 @@ struct NsMat {
     const void *x;      // current iterate, worker 0; worker stride n (ns dtype)
     void *a;            // Gram buffer, worker 0; worker stride r*r (ns dtype)
     void *out;          // EPI_ITER: next iterate (ns dtype); EPI_FINAL: U fp32 or
-                        // nullptr; EPI_WUPD: W fp32 (no worker stride)
+                        // nullptr; EPI_WUPD: W fp32, W <- fmaf(-eta, U, W) (no worker
+                        // stride: one worker)
     uint64_t *packed;   // EPI_FINAL fused sign+pack target or nullptr
+    float *u_out;       // EPI_WUPD: U (fp32) as well, or nullptr (one worker)
     int32_t R, C;
     int32_t tile_begin;  // first tile of this matrix within one worker's tiles
     int32_t tiles_per_worker;

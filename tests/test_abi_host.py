@@ -169,3 +169,16 @@ def test_spectral_workspace_adds_power_vectors(lib):
     ns = lib.signmuon_workspace_bytes(arr, 1, ctypes.byref(spec))
     # k = 0 with spectral scaling still needs the Gram matrix and the power vectors
     assert ns >= nf + 4 * 300 * 300 * 4 + 2 * 4 * 300 * 4
+
+
+def test_muon_step_argument_errors(lib):
+    one = _fake(64, 64, 1)
+    assert _call(lib.signmuon_muon_step, [one], sm.Params(workers=2, ns_iters=1)) == -1
+    assert _call(lib.signmuon_muon_step, [one], sm.Params(workers=1, ns_iters=0)) == -1
+    assert _call(lib.signmuon_muon_step, [one], sm.Params(workers=1, ns_iters=1,
+                                                          post_polar_iters=1)) == -1
+    no_w = _fake(64, 64, 1)
+    no_w.weight = None
+    assert _call(lib.signmuon_muon_step, [no_w], sm.Params(workers=1, ns_iters=1)) == -1
+    assert _call(lib.signmuon_muon_step, [_fake(64, 64, 1, aligned=False)],
+                 sm.Params(workers=1, ns_iters=1)) == -3

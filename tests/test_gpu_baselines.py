@@ -1,0 +1,116 @@
+"""GPU parity of the comparison steps: the full-precision Muon step
+(signmuon_muon_step, one worker, no sign) and majority-vote signum with
+momentum (signmuon_step with ns_iters = 0), against the CPU oracle.
+
+Bar: Muon's U within 1e-5 (fp32) / 2e-2 (bf16) relative Frobenius error and
+W = fmaf(-eta, U, W) exactly on the GPU's own U; signum bit-exact (momentum,
+packed signs, vote, W)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sign_muon_step_amd as sm
+import synthetic
+from gpu_util import DEV, announce, dtype_of, make_matrix, rel_fro, run, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+NS_TOL = {"f32": 1e-5, "bf16": 2e-2}
+ORC_DT = {"f32": oracle.F32, "bf16": oracle.BF16}
+
+
+@pytest.fixture(autouse=True)
+def _name_the_case(request):
+    announce(f"[gpu-test] {request.node.nodeid}")
+    yield
+    torch.cuda.synchronize()
+
+
+def fmaf32(a: np.float32, b: np.ndarray, c: np.ndarray) -> np.ndarray:
+    """Correctly rounded fp32 a*b + c. The fp64 product of two fp32 values is
+    exact; the fp64 sum s and its rounding error e (two-sum) hold a*b + c
+    exactly, so rounding s to fp32 is right except when s sits exactly on a
+    midpoint between two fp32 values, where the sign of e decides."""
+    p = np.float64(a) * b.astype(np.float64)
+    c64 = c.astype(np.float64)
+    s = p + c64
+    bb = s - p
+    e = (p - (s - bb)) + (c64 - bb)
+    out = s.astype(np.float32)
+    above = out.astype(np.float64) > s
+    lo = np.where(above, np.nextafter(out, np.float32(-np.inf)), out)
+    hi = np.where(above, out, np.nextafter(out, np.float32(np.inf)))
+    mid = (lo.astype(np.float64) + hi.astype(np.float64)) / 2
+    on_mid = s == mid
+    return np.where(on_mid & (e > 0), hi, np.where(on_mid & (e < 0), lo, out)).astype(np.float32)
+
+
+MUON_CASES = [("f32", s, k, n) for s in [(256, 256), (300, 700), (700, 300)] for k in (1, 3)
+              for n in ("frobenius", "spectral")] + \
+             [("bf16", s, k, n) for s in [(384, 1024), (1024, 384), (768, 768)] for k in (1, 3)
+              for n in ("frobenius", "spectral")]
+
+
+@pytest.mark.parametrize("ns,shape,k,norm", MUON_CASES)
+def test_muon_step_parity(ns, shape, k, norm):
+    R, C = shape
+    g = synthetic.random_matrix(61, (1, R, C), 1e-3, "normal")
+    m0 = np.zeros((1, R, C), np.float32 if ns == "f32" else np.uint16)
+    w0 = synthetic.random_matrix(62, (R, C), 0.02, "normal")
+    eta = np.float32(1e-2)
+    spectral = norm == "spectral"
+    code = dtype_of(ns)[2]
+    p = sm.Params(workers=1, beta=0.9, eta=float(eta), ns_iters=k, mom_dtype=code, ns_dtype=code,
+                  norm=sm.NORM_SPECTRAL if spectral else sm.NORM_FROBENIUS,
+                  power_iters=6 if spectral else 0)
+    mat = make_matrix(g, m0, w0, polar=True, vote=False, packed=False)
+    run("signmuon_muon_step", [mat], p)
+    u = to_host(mat.polar_out)[0]
+    w = to_host(mat.weight)
+    np.testing.assert_array_equal(w, fmaf32(-eta, u, w0))
+    m_ref = m0[0].copy()
+    w_ref = w0.copy()
+    u_ref = oracle.muon_step_matrix(g[0], m_ref, w_ref, 0.9, float(eta), k, ORC_DT[ns],
+                                    norm=oracle.NORM_SPECTRAL if spectral else oracle.NORM_FROB,
+                                    power_iters=6 if spectral else 0, want_u=True)
+    np.testing.assert_array_equal(to_host(mat.momentum)[0], m_ref)
+    err = rel_fro(u, u_ref)
+    announce(f"    rel err {err:.2e}")
+    assert err < NS_TOL[ns]
+    # the update moves W by eta U: the deviation from the oracle's W is eta times U's
+    assert np.abs(w - w_ref).max() <= float(eta) * np.abs(u - u_ref).max() * 1.001 + 1e-7
+
+
+def test_muon_step_without_polar_out_moves_w_the_same():
+    R, C = 300, 520
+    g = synthetic.random_matrix(63, (1, R, C), 1.0, "normal")
+    w0 = synthetic.random_matrix(64, (R, C), 0.02, "normal")
+    p = sm.Params(workers=1, beta=0.9, eta=1e-3, ns_iters=2)
+    a = make_matrix(g, np.zeros((1, R, C), np.float32), w0, polar=True, vote=False, packed=False)
+    b = make_matrix(g, np.zeros((1, R, C), np.float32), w0, polar=False, vote=False, packed=False)
+    run("signmuon_muon_step", [a], p)
+    run("signmuon_muon_step", [b], p)
+    np.testing.assert_array_equal(to_host(a.weight), to_host(b.weight))
+
+
+@pytest.mark.parametrize("mom", ["f32", "bf16"])
+@pytest.mark.parametrize("mw", [1, 4, 7])
+def test_majority_vote_signum_is_the_k0_step(mom, mw):
+    """k = 0: each worker's sign of its momentum, the majority vote, the
+    update -- bit-exact against the oracle (no Newton-Schulz rounding)."""
+    R, C = 192, 320
+    g = np.stack([synthetic.random_matrix(70 + i, (R, C), 1e-3, "normal") for i in range(mw)])
+    m0 = np.zeros((mw, R, C), np.float32 if mom == "f32" else np.uint16)
+    w0 = synthetic.random_matrix(80, (R, C), 0.02, "normal")
+    code = dtype_of(mom)[2]
+    mat = make_matrix(g, m0, w0)
+    run("signmuon_step", [mat], sm.Params(workers=mw, beta=0.9, eta=1e-3, ns_iters=0,
+                                          mom_dtype=code, ns_dtype=code))
+    w_ref = w0.copy()
+    m_ref = m0.copy()
+    packed, vote, _ = oracle.step_matrix(g, m_ref, w_ref, 0.9, 1e-3, 0, ORC_DT[mom])
+    np.testing.assert_array_equal(to_host(mat.momentum), m_ref)
+    np.testing.assert_array_equal(to_host(mat.packed), packed)
+    np.testing.assert_array_equal(to_host(mat.vote_out), vote)
+    np.testing.assert_array_equal(to_host(mat.weight), w_ref)
