@@ -24,7 +24,8 @@
 // 2-3), or (post-vote polar step) applies W <- fmaf(-eta, Y, W).
 //
 // Every GEMM is C[m][n] = sum_k P[m][k] Q[n][k] on a 256 x 256 output tile
-// with 4 waves of 128 x 128. Operands are staged through LDS in a [row][k]
+// with 8 waves of 128 x 64 (two waves per SIMD, so that one wave's LDS reads
+// and waits overlap the other's matrix instructions). Operands are staged through LDS in a [row][k]
 // layout, 128 bytes of k per row (64 bf16 or 32 fp32), 16-byte chunks
 // XOR-swizzled by row so that both the MFMA fragment reads and the staging
 // writes spread over all banks. An operand whose k index is the strided one
@@ -43,8 +44,18 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;
 constexpr int kWave = 64;
+constexpr int kWaves = kThreads / kWave;
+// Wave tile kWaveM x kWaveN of the 256 x 256 output, in 32 x 32 MFMA blocks.
+constexpr int kWaveM = 128, kWaveN = 64;
+constexpr int kFM = kWaveM / 32, kFN = kWaveN / 32;
+constexpr int kWavesN = 256 / kWaveN;     // waves along n
+constexpr int kLoadsPerOp = 16 / kWaves;  // 1 KiB loads per wave per operand slice
+static_assert(kWaves * kLoadsPerOp == 16 && (256 / kWaveM) * kWavesN == kWaves, "wave grid");
+
+__device__ __forceinline__ int wave_m0(int wid) { return (wid / kWavesN) * kWaveM; }
+__device__ __forceinline__ int wave_n0(int wid) { return (wid % kWavesN) * kWaveN; }
 constexpr int kStages = 4;                        // LDS pipeline depth
 constexpr int kOpBytes = 16 * 1024;               // one operand's k-slice
 constexpr int kStageBytes = 2 * kOpBytes;
@@ -169,14 +180,15 @@ __device__ __forceinline__ void dma16(uint32_t lds, uint32_t voffset, v4u32 rsrc
 // registers and several slices can be in flight. The LDS destination of lane
 // L is fixed (base + 16 L); the lane therefore fetches whichever global chunk
 // the layout puts there. Chunks outside the operand read the out-of-bounds
-// buffer offset and land as zeros. Each thread issues 4 loads per slice.
+// buffer offset and land as zeros. Each thread issues kLoadsPerOp loads per
+// slice.
 template <bool BF16, bool KC>
 struct DmaLoader {
     using E = Elem<BF16>;
     using T = typename E::T;
     v4u32 rsrc;
-    uint32_t off[4];   // byte offset of each of the thread's chunks in slice 0
-    int kofs[4];       // k of the chunk relative to the slice start
+    uint32_t off[kLoadsPerOp];  // byte offset of each of the thread's chunks in slice 0
+    int kofs[kLoadsPerOp];      // k of the chunk relative to the slice start
     uint32_t valid;    // bit i: chunk i's rows lie inside the operand
     uint32_t kstep;    // bytes per slice
     int K;
@@ -196,8 +208,8 @@ struct DmaLoader {
         valid = 0;
         const uint32_t sz = sizeof(T);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int b = i * 4 + wid;          // 1 KiB block of the slice
+        for (int i = 0; i < kLoadsPerOp; ++i) {
+            const int b = i * kWaves + wid;     // 1 KiB block of the slice
             int mn, k;
             if (KC) {                           // 16 rows of 64 bytes
                 const int row = b * 16 + (lane >> 2);
@@ -219,11 +231,11 @@ struct DmaLoader {
         kstep = KC ? (uint32_t)E::BK * sz : (uint32_t)(E::BK * op.ld) * sz;
     }
 
-    // Load i (0..3) of slice kt only.
+    // Load i (0 .. kLoadsPerOp - 1) of slice kt only.
     __device__ __forceinline__ void issue_one(int kt, uint32_t lds, int i) const {
         const bool ok = ((valid >> i) & 1u) && kt * E::BK + kofs[i] < K;
         const uint32_t o = ok ? off[i] + (uint32_t)kt * kstep : kOOB;
-        dma16(lds + (uint32_t)(i * 4 + wid) * 1024u, o, rsrc);
+        dma16(lds + (uint32_t)(i * kWaves + wid) * 1024u, o, rsrc);
     }
 
     // lds: LDS byte address of this operand's slice buffer.
@@ -231,10 +243,10 @@ struct DmaLoader {
         const int k0 = kt * E::BK;
         const uint32_t kb = (uint32_t)kt * kstep;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < kLoadsPerOp; ++i) {
             const bool ok = ((valid >> i) & 1u) && k0 + kofs[i] < K;
             const uint32_t o = ok ? off[i] + kb : kOOB;
-            dma16(lds + (uint32_t)(i * 4 + wid) * 1024u, o, rsrc);
+            dma16(lds + (uint32_t)(i * kWaves + wid) * 1024u, o, rsrc);
         }
     }
 };
@@ -311,70 +323,63 @@ __device__ __forceinline__ f32x4_t frag_f32(const char *lds, int row0, int cp) {
 }
 
 // Fragments of one half of a k-slice (bf16: one k16 step; fp32: one pair of
-// 16-byte chunks) for the wave's 4 m-blocks and 4 n-blocks.
+// 16-byte chunks) for the wave's kFM m-blocks and kFN n-blocks.
 template <bool BF16> struct Frags;
-template <> struct Frags<true> { bf16x8_t p[4], q[4]; };
-template <> struct Frags<false> { f32x4_t p[4], q[4]; };
+template <> struct Frags<true> { bf16x8_t p[kFM], q[kFN]; };
+template <> struct Frags<false> { f32x4_t p[kFM], q[kFN]; };
+
+// Fragment j (0 .. kFM + kFN - 1) of one half: j < kFM is P block j, the
+// rest Q block j - kFM.
+template <bool BF16, bool PKC, bool QKC>
+__device__ __forceinline__ void read_frag(Frags<BF16> &fr, const char *lds_p, const char *lds_q,
+                                          int wm0, int wn0, int half, int j) {
+    if constexpr (BF16) {
+        if (j < kFM)
+            fr.p[j] = frag_bf16<PKC>(lds_p, wm0 + j * 32, half);
+        else
+            fr.q[j - kFM] = frag_bf16<QKC>(lds_q, wn0 + (j - kFM) * 32, half);
+    } else {
+        if (j < kFM)
+            fr.p[j] = frag_f32<PKC>(lds_p, wm0 + j * 32, half);
+        else
+            fr.q[j - kFM] = frag_f32<QKC>(lds_q, wn0 + (j - kFM) * 32, half);
+    }
+}
 
 template <bool BF16, bool PKC, bool QKC>
 __device__ __forceinline__ void read_frags(Frags<BF16> &fr, const char *lds_p, const char *lds_q,
                                            int wm0, int wn0, int half) {
 #pragma unroll
-    for (int f = 0; f < 4; ++f) {
-        if constexpr (BF16) {
-            fr.p[f] = frag_bf16<PKC>(lds_p, wm0 + f * 32, half);
-            fr.q[f] = frag_bf16<QKC>(lds_q, wn0 + f * 32, half);
-        } else {
-            fr.p[f] = frag_f32<PKC>(lds_p, wm0 + f * 32, half);
-            fr.q[f] = frag_f32<QKC>(lds_q, wn0 + f * 32, half);
-        }
-    }
+    for (int j = 0; j < kFM + kFN; ++j) read_frag<BF16, PKC, QKC>(fr, lds_p, lds_q, wm0, wn0, half, j);
 }
 
-// Fragment j (0..7) of one half: j < 4 is P block j, j >= 4 is Q block j - 4.
-template <bool BF16, bool PKC, bool QKC>
-__device__ __forceinline__ void read_frag(Frags<BF16> &fr, const char *lds_p, const char *lds_q,
-                                          int wm0, int wn0, int half, int j) {
-    if constexpr (BF16) {
-        if (j < 4)
-            fr.p[j] = frag_bf16<PKC>(lds_p, wm0 + j * 32, half);
-        else
-            fr.q[j - 4] = frag_bf16<QKC>(lds_q, wn0 + (j - 4) * 32, half);
-    } else {
-        if (j < 4)
-            fr.p[j] = frag_f32<PKC>(lds_p, wm0 + j * 32, half);
-        else
-            fr.q[j - 4] = frag_f32<QKC>(lds_q, wn0 + (j - 4) * 32, half);
-    }
-}
-
-// acc[f][g]: 32 x 32 block (f along m, g along n) of the wave's 128 x 128.
+// acc[f][g]: 32 x 32 block (f along m, g along n) of the wave's tile.
 // MFMA 32x32 layout: lane l holds column (l & 31) and, in register r, row
 // 8*(r/4) + 4*(l/32) + (r%4) of the block.
 template <bool BF16>
-__device__ __forceinline__ void mma_half(const Frags<BF16> &fr, f32x16_t (&acc)[4][4]) {
+__device__ __forceinline__ void mma_half(const Frags<BF16> &fr, f32x16_t (&acc)[kFM][kFN]) {
     if constexpr (BF16) {
 #pragma unroll
-        for (int f = 0; f < 4; ++f)
+        for (int f = 0; f < kFM; ++f)
 #pragma unroll
-            for (int g = 0; g < 4; ++g)
+            for (int g = 0; g < kFN; ++g)
                 acc[f][g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr.p[f], fr.q[g], acc[f][g], 0, 0, 0);
     } else {
         // fp32: MFMA step s contracts element s of each lane's 4 k values.
 #pragma unroll
         for (int st = 0; st < 4; ++st)
 #pragma unroll
-            for (int f = 0; f < 4; ++f)
+            for (int f = 0; f < kFM; ++f)
 #pragma unroll
-                for (int g = 0; g < 4; ++g)
+                for (int g = 0; g < kFN; ++g)
                     acc[f][g] = __builtin_amdgcn_mfma_f32_32x32x2f32(fr.p[f][st], fr.q[g][st], acc[f][g], 0, 0, 0);
     }
 }
 
-// Block i (f = i / 4, g = i % 4) of mma_half.
+// Block i (f = i / kFN, g = i % kFN) of mma_half.
 template <bool BF16>
-__device__ __forceinline__ void mma_step(const Frags<BF16> &fr, f32x16_t (&acc)[4][4], int i) {
-    const int f = i >> 2, g = i & 3;
+__device__ __forceinline__ void mma_step(const Frags<BF16> &fr, f32x16_t (&acc)[kFM][kFN], int i) {
+    const int f = i / kFN, g = i % kFN;
     if constexpr (BF16) {
         acc[f][g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr.p[f], fr.q[g], acc[f][g], 0, 0, 0);
     } else {
@@ -415,18 +420,20 @@ __device__ __forceinline__ f32x4_t id_frag_f32(int roff, int cp) {
 
 // d = slice index minus the wave's first identity slice.
 template <bool BF16, int SIDE>
-__device__ __forceinline__ void mma_identity(const Frags<BF16> &fr, f32x16_t (&acc)[4][4], int d,
+__device__ __forceinline__ void mma_identity(const Frags<BF16> &fr, f32x16_t (&acc)[kFM][kFN], int d,
                                              int half) {
     constexpr int RS = Elem<BF16>::BK;  // k rows per slice
-    if (SIDE == ID_NONE || d < 0 || d >= 128 / RS) return;
+    constexpr int WS = SIDE == ID_Q ? kWaveN : kWaveM;  // wave extent on the identity side
+    constexpr int NB = WS / 32, NO = SIDE == ID_Q ? kFM : kFN;
+    if (SIDE == ID_NONE || d < 0 || d >= WS / RS) return;
     const int blk = d * RS / 32, roff = (d * RS) % 32;
     if constexpr (BF16) {
         const bf16x8_t id = id_frag_bf16(roff, half);
 #pragma unroll
-        for (int b = 0; b < 4; ++b)
+        for (int b = 0; b < NB; ++b)
             if (b == blk)
 #pragma unroll
-                for (int o = 0; o < 4; ++o) {
+                for (int o = 0; o < NO; ++o) {
                     if (SIDE == ID_P)
                         acc[b][o] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(id, fr.q[o], acc[b][o], 0, 0, 0);
                     else
@@ -435,12 +442,12 @@ __device__ __forceinline__ void mma_identity(const Frags<BF16> &fr, f32x16_t (&a
     } else {
         const f32x4_t id = id_frag_f32(roff, half);
 #pragma unroll
-        for (int b = 0; b < 4; ++b)
+        for (int b = 0; b < NB; ++b)
             if (b == blk)
 #pragma unroll
                 for (int st = 0; st < 4; ++st)
 #pragma unroll
-                    for (int o = 0; o < 4; ++o) {
+                    for (int o = 0; o < NO; ++o) {
                         if (SIDE == ID_P)
                             acc[b][o] = __builtin_amdgcn_mfma_f32_32x32x2f32(id[st], fr.q[o][st], acc[b][o], 0, 0, 0);
                         else
@@ -452,22 +459,24 @@ __device__ __forceinline__ void mma_identity(const Frags<BF16> &fr, f32x16_t (&a
 // Identity term of iteration J of a rotated k loop (the tile's own 256 k
 // come first, see tile_mainloop): the slice covers k = J * BK .. + BK - 1 of
 // the tile, i.e. rows (ID_P) or columns (ID_Q) w0 + 32 b + roff .. of the
-// wave's 128 when J * BK lies in [w0, w0 + 128); other waves multiply a zero
-// fragment, so the sequence has no branch.
+// wave's extent WS on that side when J * BK lies in [w0, w0 + WS); other
+// waves multiply a zero fragment, so the sequence has no branch.
 template <bool BF16, int SIDE, int J>
-__device__ __forceinline__ void mma_identity_at(const Frags<BF16> &fr, f32x16_t (&acc)[4][4], int w0,
+__device__ __forceinline__ void mma_identity_at(const Frags<BF16> &fr, f32x16_t (&acc)[kFM][kFN], int w0,
                                                 int half) {
     constexpr int RS = Elem<BF16>::BK;
+    constexpr int WS = SIDE == ID_Q ? kWaveN : kWaveM;
+    constexpr int NO = SIDE == ID_Q ? kFM : kFN;
     constexpr int kb = J * RS;
-    constexpr int b = (kb % 128) / 32, roff = kb % 32;
-    const bool active = (kb >= 128) == (w0 >= 128);
+    constexpr int b = (kb % WS) / 32, roff = kb % 32;
+    const bool active = kb / WS == w0 / WS;
     if constexpr (BF16) {
         const bf16x8_t one = id_frag_bf16(roff, half);
         bf16x8_t id;
 #pragma unroll
         for (int e = 0; e < 8; ++e) id[e] = active ? one[e] : (__bf16)0.0f;
 #pragma unroll
-        for (int o = 0; o < 4; ++o) {
+        for (int o = 0; o < NO; ++o) {
             if (SIDE == ID_P)
                 acc[b][o] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(id, fr.q[o], acc[b][o], 0, 0, 0);
             else
@@ -481,7 +490,7 @@ __device__ __forceinline__ void mma_identity_at(const Frags<BF16> &fr, f32x16_t 
 #pragma unroll
         for (int st = 0; st < 4; ++st)
 #pragma unroll
-            for (int o = 0; o < 4; ++o) {
+            for (int o = 0; o < NO; ++o) {
                 if (SIDE == ID_P)
                     acc[b][o] = __builtin_amdgcn_mfma_f32_32x32x2f32(id[st], fr.q[o][st], acc[b][o], 0, 0, 0);
                 else
@@ -509,15 +518,15 @@ __device__ __forceinline__ uint32_t lds_addr(const char *p) {
 // term; unused for ID_NONE.
 template <bool BF16, bool PKC, bool QKC, int SIDE = ID_NONE>
 __device__ __forceinline__ void tile_mainloop(const Operand &P, const Operand &Q, char *smem,
-                                              f32x16_t (&acc)[4][4], int id_origin = 0) {
+                                              f32x16_t (&acc)[kFM][kFN], int id_origin = 0) {
     using E = Elem<BF16>;
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int wm0 = (wid >> 1) * 128, wn0 = (wid & 1) * 128;
+    const int wm0 = wave_m0(wid), wn0 = wave_n0(wid);
     const int id0 = (id_origin + (SIDE == ID_P ? wm0 : wn0)) / E::BK;  // first identity slice
 #pragma unroll
-    for (int f = 0; f < 4; ++f)
+    for (int f = 0; f < kFM; ++f)
 #pragma unroll
-        for (int g = 0; g < 4; ++g)
+        for (int g = 0; g < kFN; ++g)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[f][g][r] = 0.f;
     const int kt_n = (P.K + E::BK - 1) / E::BK;
@@ -549,7 +558,7 @@ __device__ __forceinline__ void tile_mainloop(const Operand &P, const Operand &Q
             lq.issue(slice_of(st), lds0 + st * kStageBytes + kOpBytes);
         }
         lp.issue(slice_of(kStages - 1), lds0 + (kStages - 1) * kStageBytes);
-        wait_vm_lgkm0<20>();  // slice 0 landed; slices 1, 2 and half of 3 in flight
+        wait_vm_lgkm0<5 * kLoadsPerOp>();  // slice 0 landed; slices 1, 2 and half of 3 in flight
         lds_barrier();
         Frags<BF16> fa, fb;
         read_frags<BF16, PKC, QKC>(fa, smem, smem + kOpBytes, wm0, wn0, 0);
@@ -560,6 +569,9 @@ __device__ __forceinline__ void tile_mainloop(const Operand &P, const Operand &Q
         // slice j + 1 is read and the P part of slice j + 4 is loaded into
         // the buffer slice j leaves. Each read or load sits after one MFMA so
         // that the matrix pipe does not wait behind a run of them.
+        constexpr int kSteps = kFM * kFN, kFrag = kFM + kFN;
+        constexpr int kEvery = (kSteps - kFrag) / kLoadsPerOp;  // MFMAs per load
+        static_assert(kEvery >= 1 && kFrag + kEvery * kLoadsPerOp == kSteps, "interleave");
         const int w0 = SIDE == ID_Q ? wn0 : wm0;
         auto iteration = [&](int j, auto jid) {
             constexpr int JID = decltype(jid)::value;  // unrolled identity iteration, or -1
@@ -567,27 +579,27 @@ __device__ __forceinline__ void tile_mainloop(const Operand &P, const Operand &Q
             const int late = slice_of(j + kStages - 1);  // its buffer was freed by barrier j - 1
             const uint32_t late_dst = lds0 + ((j + kStages - 1) % kStages) * kStageBytes + kOpBytes;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
+            for (int i = 0; i < kSteps; ++i) {
                 mma_step<BF16>(fa, acc, i);
-                if (i < 8)
+                if (i < kFrag)
                     read_frag<BF16, PKC, QKC>(fb, cur, cur + kOpBytes, wm0, wn0, 1, i);
-                else if (i & 1)
-                    lq.issue_one(late, late_dst, (i - 8) >> 1);
+                else if ((i - kFrag) % kEvery == kEvery - 1)
+                    lq.issue_one(late, late_dst, (i - kFrag) / kEvery);
                 __builtin_amdgcn_sched_barrier(0);
             }
             if constexpr (JID >= 0) mma_identity_at<BF16, SIDE, JID>(fa, acc, w0, 0);
-            wait_vm_lgkm0<16>();
+            wait_vm_lgkm0<4 * kLoadsPerOp>();
             lds_barrier();
             const char *nxt = smem + ((j + 1) % kStages) * kStageBytes;
             const uint32_t dst = lds0 + (j % kStages) * kStageBytes;
             const int refill = slice_of(j + kStages);
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
+            for (int i = 0; i < kSteps; ++i) {
                 mma_step<BF16>(fb, acc, i);
-                if (i < 8)
+                if (i < kFrag)
                     read_frag<BF16, PKC, QKC>(fa, nxt, nxt + kOpBytes, wm0, wn0, 0, i);
-                else if (i & 1)
-                    lp.issue_one(refill, dst, (i - 8) >> 1);
+                else if ((i - kFrag) % kEvery == kEvery - 1)
+                    lp.issue_one(refill, dst, (i - kFrag) / kEvery);
                 __builtin_amdgcn_sched_barrier(0);
             }
             if constexpr (JID >= 0) mma_identity_at<BF16, SIDE, JID>(fb, acc, w0, 1);
@@ -620,18 +632,22 @@ __device__ __forceinline__ void tile_mainloop(const Operand &P, const Operand &Q
 __device__ __forceinline__ int find_ns_mat(const NsBatch &b, int t) { return find_start(b.starts, t); }
 
 // ---------------------------------------------------------------------------
-// Epilogue helpers. A wave stages 32 rows x 128 columns of fp32 in LDS
+// Epilogue helpers. A wave stages 32 rows x kWaveN columns of fp32 in LDS
 // (row stride kStageStride floats) to turn the MFMA register layout into
-// row-major 4-column pieces.
+// row-major 4-column pieces: kLanesPerRow lanes cover one staged row, so one
+// instruction covers kRowsPerInstr rows.
 // ---------------------------------------------------------------------------
-constexpr int kStageStride = 136;  // 4 rows apart = 32 banks apart
-static_assert(4 * 32 * kStageStride * 4 <= kLdsBytes, "epilogue stage exceeds LDS");
+constexpr int kStageStride = kWaveN + 8;  // 4 rows apart = 32 banks apart
+constexpr int kLanesPerRow = kWaveN / 4, kRowsPerInstr = kWave / kLanesPerRow;
+constexpr int kWordsPerRow = kWaveN / 64;  // packed sign words per wave row
+static_assert(kWaves * 32 * kStageStride * 4 <= kLdsBytes, "epilogue stage exceeds LDS");
+static_assert(kWaveN % 64 == 0, "a packed word spans 64 columns of one wave");
 
-__device__ __forceinline__ void stage_rows(const f32x16_t (&acc)[4][4], int f, float *stage,
+__device__ __forceinline__ void stage_rows(const f32x16_t (&acc)[kFM][kFN], int f, float *stage,
                                            float scale) {
     const int lane = threadIdx.x & (kWave - 1);
 #pragma unroll
-    for (int g = 0; g < 4; ++g)
+    for (int g = 0; g < kFN; ++g)
 #pragma unroll
         for (int rr = 0; rr < 16; ++rr) {
             const int row = 8 * (rr >> 2) + 4 * (lane >> 5) + (rr & 3);
@@ -720,25 +736,26 @@ __device__ __forceinline__ void store32(void *p, int64_t idx, const float (&v)[3
     }
 }
 
-// Each wave stages its 128 x 128 result 32 rows at a time in its own LDS
-// area, then writes the rows (4 columns per lane) and, above the diagonal,
-// the mirrored tile: lane l reads column l of the staged rows, which is 32
-// consecutive entries of mirrored row n0 + l, and stores them as one run.
+// Each wave stages its kWaveM x kWaveN result 32 rows at a time in its own
+// LDS area, then writes the rows (4 columns per lane) and, above the
+// diagonal, the mirrored tile: a lane reads one column of the staged rows,
+// which is 32 consecutive entries of a mirrored row, and stores them as one
+// run.
 template <bool BF16, bool FAST>
-__device__ __forceinline__ void gram_epilogue(f32x16_t (&acc)[4][4], char *smem, int ti, int tj,
+__device__ __forceinline__ void gram_epilogue(f32x16_t (&acc)[kFM][kFN], char *smem, int ti, int tj,
                                               int r, float scale, void *a) {
     const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
-    const int m0 = ti * kNsTileM + (wid >> 1) * 128, n0 = tj * kNsTileN + (wid & 1) * 128;
+    const int m0 = ti * kNsTileM + wave_m0(wid), n0 = tj * kNsTileN + wave_n0(wid);
     float *stage = reinterpret_cast<float *>(smem) + wid * 32 * kStageStride;
     const bool mirror = ti < tj;
 #pragma unroll
-    for (int f = 0; f < 4; ++f) {
+    for (int f = 0; f < kFM; ++f) {
         stage_rows(acc, f, stage, scale);
         wave_lds_fence();
-        // Direct tile, row-major: 4 columns per lane, 2 rows per instruction.
+        // Direct tile, row-major: 4 columns per lane.
 #pragma unroll 4
-        for (int it = 0; it < 16; ++it) {
-            const int row = it * 2 + (lane >> 5), c4 = (lane & 31) * 4;
+        for (int it = 0; it < 32 / kRowsPerInstr; ++it) {
+            const int row = it * kRowsPerInstr + lane / kLanesPerRow, c4 = (lane % kLanesPerRow) * 4;
             const int gi = m0 + f * 32 + row, gj = n0 + c4;
             const float4 v4 = *reinterpret_cast<const float4 *>(stage + row * kStageStride + c4);
             float v[4] = {v4.x, v4.y, v4.z, v4.w};
@@ -746,8 +763,8 @@ __device__ __forceinline__ void gram_epilogue(f32x16_t (&acc)[4][4], char *smem,
         }
         if (mirror) {
 #pragma unroll
-            for (int it = 0; it < 2; ++it) {
-                const int col = it * 64 + lane;
+            for (int it = 0; it < kWaveN / kWave; ++it) {
+                const int col = it * kWave + lane;
                 float v[32];
 #pragma unroll
                 for (int t = 0; t < 32; ++t) v[t] = stage[t * kStageStride + col];
@@ -762,7 +779,7 @@ __device__ __forceinline__ void gram_epilogue(f32x16_t (&acc)[4][4], char *smem,
 template <bool BF16, bool KC>
 __device__ __forceinline__ void gram_tile(const Operand &P, const Operand &Q, char *smem, int ti,
                                           int tj, int r, float scale, void *a) {
-    f32x16_t acc[4][4];
+    f32x16_t acc[kFM][kFN];
     tile_mainloop<BF16, KC, KC>(P, Q, smem, acc);
     const bool fast = P.vec && (r % Elem<BF16>::EPC) == 0 && (ti + 1) * kNsTileM <= r &&
                       (tj + 1) * kNsTileN <= r;
@@ -773,7 +790,7 @@ __device__ __forceinline__ void gram_tile(const Operand &P, const Operand &Q, ch
 }
 
 template <bool BF16>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves / 4, kWaves / 4)))
 void ns_gram_kernel(NsBatch b) {
     using T = typename Elem<BF16>::T;
     __shared__ __attribute__((aligned(16))) char smem[kLdsBytes];
@@ -821,26 +838,26 @@ struct ProductArgs {
     float gamma, eta;
 };
 
-// Epilogue of the product, 32 rows of the wave's 128 x 128 at a time through
+// Epilogue of the product, 32 rows of the wave's tile at a time through
 // LDS: u = gamma * acc row-major (4 columns per lane), stored as
 // EPI asks; for the fused sign + pack, u goes back to LDS and each packed word
 // is the ballot of 64 consecutive columns of one row (needs C % 64 == 0).
 template <bool BF16, int EPI, bool FAST>
-__device__ __forceinline__ void product_epilogue(const ProductArgs &pa, f32x16_t (&acc)[4][4],
+__device__ __forceinline__ void product_epilogue(const ProductArgs &pa, f32x16_t (&acc)[kFM][kFN],
                                                  char *smem) {
     const int R = pa.R, C = pa.C;
     const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
-    const int m0 = pa.ti * kNsTileM + (wid >> 1) * 128, n0 = pa.tj * kNsTileN + (wid & 1) * 128;
+    const int m0 = pa.ti * kNsTileM + wave_m0(wid), n0 = pa.tj * kNsTileN + wave_n0(wid);
     float *stage = reinterpret_cast<float *>(smem) + wid * 32 * kStageStride;
     const bool want_out = EPI == EPI_ITER || EPI == EPI_WUPD || (EPI == EPI_FINAL && pa.out);
     const bool want_pack = EPI == EPI_FINAL && pa.pk;
 #pragma unroll
-    for (int f = 0; f < 4; ++f) {
+    for (int f = 0; f < kFM; ++f) {
         stage_rows(acc, f, stage, 1.0f);
         wave_lds_fence();
 #pragma unroll 4
-        for (int it = 0; it < 16; ++it) {
-            const int row = it * 2 + (lane >> 5), c4 = (lane & 31) * 4;
+        for (int it = 0; it < 32 / kRowsPerInstr; ++it) {
+            const int row = it * kRowsPerInstr + lane / kLanesPerRow, c4 = (lane % kLanesPerRow) * 4;
             const int gm = m0 + f * 32 + row, gn = n0 + c4;
             const int64_t idx = (int64_t)gm * C + gn;
             float *sp = stage + row * kStageStride + c4;
@@ -870,15 +887,16 @@ __device__ __forceinline__ void product_epilogue(const ProductArgs &pa, f32x16_t
         }
         if (want_pack) {
             wave_lds_fence();
+            // word q: row q / kWordsPerRow, columns 64 (q % kWordsPerRow) ..
             uint64_t mine = 0;
 #pragma unroll 8
-            for (int q = 0; q < 64; ++q) {
-                const float v = stage[(q >> 1) * kStageStride + 64 * (q & 1) + lane];
+            for (int q = 0; q < 32 * kWordsPerRow; ++q) {
+                const float v = stage[(q / kWordsPerRow) * kStageStride + 64 * (q % kWordsPerRow) + lane];
                 const uint64_t bal = __ballot(v >= 0.f);
                 if (lane == q) mine = bal;
             }
-            const int gm = m0 + f * 32 + (lane >> 1), gn0 = n0 + 64 * (lane & 1);
-            if (gm < R && gn0 < C) pa.pk[((int64_t)gm * C + gn0) >> 6] = mine;
+            const int gm = m0 + f * 32 + lane / kWordsPerRow, gn0 = n0 + 64 * (lane % kWordsPerRow);
+            if (lane < 32 * kWordsPerRow && gm < R && gn0 < C) pa.pk[((int64_t)gm * C + gn0) >> 6] = mine;
         }
         wave_lds_fence();
     }
@@ -889,26 +907,29 @@ __device__ __forceinline__ void product_epilogue(const ProductArgs &pa, f32x16_t
 // register rr of block (f, g) holds row R0 (lanes 0-31) and row R0 + 4
 // (lanes 32-63) over the block's 32 columns; blocks 2 gp and 2 gp + 1 give
 // the 64 columns of one packed word (C % 64 == 0). Word id of the wave goes
-// to lane id % 64, slot id / 64; each lane then stores its 4 words.
+// to lane id % 64, slot id / 64; each lane then stores its kSlots words.
 // dst in lane `lane` <- val (a uniform value); the other lanes keep dst.
 __device__ __forceinline__ int write_lane(int dst, uint32_t val, int lane) {
     asm("v_writelane_b32 %0, %1, %2" : "+v"(dst) : "s"(val), "i"(lane));
     return dst;
 }
 
-__device__ __forceinline__ void pack_from_registers(const ProductArgs &pa, const f32x16_t (&acc)[4][4]) {
+__device__ __forceinline__ void pack_from_registers(const ProductArgs &pa, const f32x16_t (&acc)[kFM][kFN]) {
     const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
-    const int m0 = pa.ti * kNsTileM + (wid >> 1) * 128, n0 = pa.tj * kNsTileN + (wid & 1) * 128;
-    int lo[4] = {0, 0, 0, 0}, hi[4] = {0, 0, 0, 0};  // 32-bit halves of each lane's 4 words
+    const int m0 = pa.ti * kNsTileM + wave_m0(wid), n0 = pa.tj * kNsTileN + wave_n0(wid);
+    constexpr int kSlots = kWaveM * kWordsPerRow / kWave;
+    int lo[kSlots], hi[kSlots];  // 32-bit halves of each lane's words
 #pragma unroll
-    for (int f = 0; f < 4; ++f) {
+    for (int sl = 0; sl < kSlots; ++sl) lo[sl] = hi[sl] = 0;
+#pragma unroll
+    for (int f = 0; f < kFM; ++f) {
 #pragma unroll
         for (int rr = 0; rr < 16; ++rr)
 #pragma unroll
-            for (int gp = 0; gp < 2; ++gp) {
+            for (int gp = 0; gp < kWordsPerRow; ++gp) {
                 const uint64_t b0 = __ballot(pa.gamma * acc[f][2 * gp][rr] >= 0.f);
                 const uint64_t b1 = __ballot(pa.gamma * acc[f][2 * gp + 1][rr] >= 0.f);
-                const int id = ((f * 16 + rr) * 2 + gp) * 2;  // even, 0..254
+                const int id = ((f * 16 + rr) * kWordsPerRow + gp) * 2;  // even
                 // row R0: lanes 0-31 of both blocks; row R0 + 4: lanes 32-63
                 lo[id >> 6] = write_lane(lo[id >> 6], (uint32_t)b0, id & 63);
                 hi[id >> 6] = write_lane(hi[id >> 6], (uint32_t)b1, id & 63);
@@ -920,9 +941,10 @@ __device__ __forceinline__ void pack_from_registers(const ProductArgs &pa, const
             }
     }
 #pragma unroll
-    for (int sl = 0; sl < 4; ++sl) {
+    for (int sl = 0; sl < kSlots; ++sl) {
         const int id = sl * 64 + lane;
-        const int hrow = id & 1, gp = (id >> 1) & 1, rr = (id >> 2) & 15, f = id >> 6;
+        const int hrow = id & 1, gp = (id >> 1) % kWordsPerRow, fr = (id >> 1) / kWordsPerRow;
+        const int rr = fr & 15, f = fr >> 4;
         const int gm = m0 + f * 32 + 8 * (rr >> 2) + (rr & 3) + 4 * hrow;
         const int gn0 = n0 + 64 * gp;
         const uint64_t word = (uint64_t)(uint32_t)lo[sl] | ((uint64_t)(uint32_t)hi[sl] << 32);
@@ -933,7 +955,7 @@ __device__ __forceinline__ void pack_from_registers(const ProductArgs &pa, const
 template <bool BF16, bool QKC, int EPI>
 __device__ __forceinline__ void product_tile(const Operand &P, const Operand &Q, char *smem,
                                              const ProductArgs &pa) {
-    f32x16_t acc[4][4];
+    f32x16_t acc[kFM][kFN];
     // wide (Q = X, mn-contiguous): -3 X enters on the P side at the output
     // rows; tall (Q = A): on the Q side at the output columns.
     if constexpr (QKC)
@@ -952,7 +974,7 @@ __device__ __forceinline__ void product_tile(const Operand &P, const Operand &Q,
 }
 
 template <bool BF16, int EPI>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves / 4, kWaves / 4)))
 void ns_product_kernel(NsBatch b) {
     using T = typename Elem<BF16>::T;
     __shared__ __attribute__((aligned(16))) char smem[kLdsBytes];
