@@ -23,9 +23,13 @@
 // ballot of the accumulator registers (summary §2 "Algorithmic flow", steps
 // 2-3), or (post-vote polar step) applies W <- fmaf(-eta, Y, W).
 //
-// Every GEMM is C[m][n] = sum_k P[m][k] Q[n][k] on a 256 x 256 output tile
-// with 8 waves of 128 x 64 (two waves per SIMD, so that one wave's LDS reads
-// and waits overlap the other's matrix instructions). Operands are staged through LDS in a [row][k]
+// Every GEMM is C[m][n] = sum_k P[m][k] Q[n][k] on a 256 x TN output tile
+// computed by waves of 128 x 64, two waves per SIMD (one wave's LDS reads and
+// waits overlap the other's matrix instructions). Both kernels use TN = 256:
+// 8 waves and 128 KiB of LDS, one workgroup per CU (the Gram's tiles must be
+// square for the mirror; for the product, 256 x 128 tiles with two
+// workgroups per CU were faster on single-shape batches but slower on a
+// transformer's mixed batch, where the 256 x 256 tile reuses more in L2). Operands are staged through LDS in a [row][k]
 // layout, 128 bytes of k per row (64 bf16 or 32 fp32), 16-byte chunks
 // XOR-swizzled by row so that both the MFMA fragment reads and the staging
 // writes spread over all banks. An operand whose k index is the strided one
@@ -44,22 +48,33 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kThreads = 512;
 constexpr int kWave = 64;
-constexpr int kWaves = kThreads / kWave;
-// Wave tile kWaveM x kWaveN of the 256 x 256 output, in 32 x 32 MFMA blocks.
+// Wave tile kWaveM x kWaveN, in 32 x 32 MFMA blocks.
 constexpr int kWaveM = 128, kWaveN = 64;
 constexpr int kFM = kWaveM / 32, kFN = kWaveN / 32;
-constexpr int kWavesN = 256 / kWaveN;     // waves along n
-constexpr int kLoadsPerOp = 16 / kWaves;  // 1 KiB loads per wave per operand slice
-static_assert(kWaves * kLoadsPerOp == 16 && (256 / kWaveM) * kWavesN == kWaves, "wave grid");
+constexpr int kRowBytes = 64;  // LDS bytes of one operand row per k-slice
 
-__device__ __forceinline__ int wave_m0(int wid) { return (wid / kWavesN) * kWaveM; }
-__device__ __forceinline__ int wave_n0(int wid) { return (wid % kWavesN) * kWaveN; }
-constexpr int kStages = 4;                        // LDS pipeline depth
-constexpr int kOpBytes = 16 * 1024;               // one operand's k-slice
-constexpr int kStageBytes = 2 * kOpBytes;
-constexpr int kLdsBytes = kStages * kStageBytes;  // 128 KiB
+// Workgroup layout of a 256 x TN output tile: two rows of TN / kWaveN waves;
+// each LDS stage holds one k-slice of P (256 rows) then of Q (TN rows).
+template <int TN>
+struct Lay {
+    static constexpr int kTileM = 256, kTileN = TN;
+    static constexpr int kWavesN = TN / kWaveN;
+    static constexpr int kWaves = (kTileM / kWaveM) * kWavesN;
+    static constexpr int kThreads = kWaves * kWave;
+    static constexpr int kPBytes = kTileM * kRowBytes, kQBytes = TN * kRowBytes;
+    static constexpr int kStageBytes = kPBytes + kQBytes;
+    static constexpr int kStages = TN == 256 ? 4 : 3;  // pipeline depth
+    static constexpr int kLdsBytes = kStages * kStageBytes;
+    static constexpr int kPLoads = kPBytes / 1024 / kWaves;  // 1 KiB loads per wave per slice
+    static constexpr int kQLoads = kQBytes / 1024 / kWaves;
+    static_assert(kPLoads * kWaves * 1024 == kPBytes && kQLoads * kWaves * 1024 == kQBytes, "loads");
+    __device__ static int m0(int wid) { return (wid / kWavesN) * kWaveM; }
+    __device__ static int n0(int wid) { return (wid % kWavesN) * kWaveN; }
+};
+using GramLay = Lay<256>;
+using ProdLay = Lay<kNsProdTileN>;
+static_assert(GramLay::kLdsBytes <= 160 * 1024 && ProdLay::kLdsBytes <= 160 * 1024, "LDS");
 
 template <bool BF16> struct Elem;
 template <> struct Elem<true> {
@@ -87,21 +102,23 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float x) { return pack_bf16x2(x, x) & 0xffffu; }
 
-// LDS layouts of one operand's k-slice (16 KiB):
-//  k-contiguous ("KL"): 256 rows x 64 bytes (BK of k), 16-byte chunk c of row
-//    r stored at chunk c ^ ((r >> 2) & 3): the MFMA reads of 16 consecutive
-//    rows then hit 16 distinct 16-byte bank groups.
+// LDS layouts of one operand's k-slice (ROWS rows of the tile, 64 bytes each):
+//  k-contiguous ("KL"): ROWS rows x 64 bytes (BK of k), 16-byte chunk c of
+//    row r stored at chunk c ^ ((r >> 2) & 3): the MFMA reads of 16
+//    consecutive rows then hit 16 distinct 16-byte bank groups.
 //  mn-contiguous bf16 ("ML"): 4 (k) x 16 (mn) blocks of 128 bytes, block
-//    (k/4, mn/16) at ((k/4) * 16 + mn/16) * 128: one LDS transpose read of a
-//    16-lane group covers exactly one block.
-//  mn-contiguous fp32: plain rows of 256 mn (1 KiB) per k.
+//    (k/4, mn/16) at ((k/4) * ROWS/16 + mn/16) * 128: one LDS transpose read
+//    of a 16-lane group covers exactly one block.
+//  mn-contiguous fp32: plain rows of ROWS mn per k.
 __device__ __forceinline__ uint32_t kl_off(int row, int chunk) {
     return (uint32_t)(row * 64 + ((chunk ^ ((row >> 2) & 3)) << 4));
 }
+template <int ROWS>
 __device__ __forceinline__ uint32_t ml_off_bf16(int k, int mn) {
-    return (uint32_t)((((k >> 2) * 16 + (mn >> 4)) << 7) + ((k & 3) << 5) + ((mn & 15) << 1));
+    return (uint32_t)((((k >> 2) * (ROWS / 16) + (mn >> 4)) << 7) + ((k & 3) << 5) + ((mn & 15) << 1));
 }
-__device__ __forceinline__ uint32_t ml_off_f32(int k, int mn) { return (uint32_t)(k * 1024 + mn * 4); }
+template <int ROWS>
+__device__ __forceinline__ uint32_t ml_off_f32(int k, int mn) { return (uint32_t)((k * ROWS + mn) * 4); }
 
 // s_waitcnt with vmcnt = N, lgkmcnt = 0 (expcnt untouched).
 template <int N>
@@ -175,20 +192,22 @@ __device__ __forceinline__ void dma16(uint32_t lds, uint32_t voffset, v4u32 rsrc
                  : "memory");
 }
 
-// Direct-to-LDS loader of one operand: each wave instruction moves 1 KiB (16
-// bytes per lane) from global memory straight into LDS, so a k-slice costs no
-// registers and several slices can be in flight. The LDS destination of lane
-// L is fixed (base + 16 L); the lane therefore fetches whichever global chunk
-// the layout puts there. Chunks outside the operand read the out-of-bounds
-// buffer offset and land as zeros. Each thread issues kLoadsPerOp loads per
-// slice.
-template <bool BF16, bool KC>
+// Direct-to-LDS loader of one operand (ROWS rows of the tile, WAVES waves):
+// each wave instruction moves 1 KiB (16 bytes per lane) from global memory
+// straight into LDS, so a k-slice costs no registers and several slices can
+// be in flight. The LDS destination of lane L is fixed (base + 16 L); the
+// lane therefore fetches whichever global chunk the layout puts there.
+// Chunks outside the operand read the out-of-bounds buffer offset and land as
+// zeros. Each thread issues NL = ROWS / 16 / WAVES loads per slice.
+template <bool BF16, bool KC, int ROWS, int WAVES>
 struct DmaLoader {
     using E = Elem<BF16>;
     using T = typename E::T;
+    static constexpr int NL = ROWS / 16 / WAVES;
+    static_assert(NL * 16 * WAVES == ROWS, "loads per wave");
     v4u32 rsrc;
-    uint32_t off[kLoadsPerOp];  // byte offset of each of the thread's chunks in slice 0
-    int kofs[kLoadsPerOp];      // k of the chunk relative to the slice start
+    uint32_t off[NL];  // byte offset of each of the thread's chunks in slice 0
+    int kofs[NL];      // k of the chunk relative to the slice start
     uint32_t valid;    // bit i: chunk i's rows lie inside the operand
     uint32_t kstep;    // bytes per slice
     int K;
@@ -208,8 +227,8 @@ struct DmaLoader {
         valid = 0;
         const uint32_t sz = sizeof(T);
 #pragma unroll
-        for (int i = 0; i < kLoadsPerOp; ++i) {
-            const int b = i * kWaves + wid;     // 1 KiB block of the slice
+        for (int i = 0; i < NL; ++i) {
+            const int b = i * WAVES + wid;      // 1 KiB block of the slice
             int mn, k;
             if (KC) {                           // 16 rows of 64 bytes
                 const int row = b * 16 + (lane >> 2);
@@ -218,11 +237,11 @@ struct DmaLoader {
                 k = c * E::EPC;
             } else if (BF16) {                  // 8 blocks of 4 (k) x 16 (mn)
                 const int blk = b * 8 + (lane >> 3), w = lane & 7;
-                k = (blk >> 4) * 4 + (w >> 1);
-                mn = (blk & 15) * 16 + (w & 1) * 8;
-            } else {                            // one k row of 256 fp32
-                k = b;
-                mn = lane * 4;
+                k = (blk / (ROWS / 16)) * 4 + (w >> 1);
+                mn = (blk % (ROWS / 16)) * 16 + (w & 1) * 8;
+            } else {                            // 256 / ROWS k rows of ROWS fp32
+                k = b * (256 / ROWS) + lane / (ROWS / 4);
+                mn = (lane % (ROWS / 4)) * 4;
             }
             off[i] = KC ? (uint32_t)(mn * op.ld + k) * sz : (uint32_t)(k * op.ld + mn) * sz;
             kofs[i] = k;
@@ -231,11 +250,11 @@ struct DmaLoader {
         kstep = KC ? (uint32_t)E::BK * sz : (uint32_t)(E::BK * op.ld) * sz;
     }
 
-    // Load i (0 .. kLoadsPerOp - 1) of slice kt only.
+    // Load i (0 .. NL - 1) of slice kt only.
     __device__ __forceinline__ void issue_one(int kt, uint32_t lds, int i) const {
         const bool ok = ((valid >> i) & 1u) && kt * E::BK + kofs[i] < K;
         const uint32_t o = ok ? off[i] + (uint32_t)kt * kstep : kOOB;
-        dma16(lds + (uint32_t)(i * kWaves + wid) * 1024u, o, rsrc);
+        dma16(lds + (uint32_t)(i * WAVES + wid) * 1024u, o, rsrc);
     }
 
     // lds: LDS byte address of this operand's slice buffer.
@@ -243,17 +262,17 @@ struct DmaLoader {
         const int k0 = kt * E::BK;
         const uint32_t kb = (uint32_t)kt * kstep;
 #pragma unroll
-        for (int i = 0; i < kLoadsPerOp; ++i) {
+        for (int i = 0; i < NL; ++i) {
             const bool ok = ((valid >> i) & 1u) && k0 + kofs[i] < K;
             const uint32_t o = ok ? off[i] + kb : kOOB;
-            dma16(lds + (uint32_t)(i * kWaves + wid) * 1024u, o, rsrc);
+            dma16(lds + (uint32_t)(i * WAVES + wid) * 1024u, o, rsrc);
         }
     }
 };
 
 // Element-by-element loader for shapes whose rows break 16-byte alignment:
 // writes the same LDS layouts with plain loads and stores (synchronous).
-template <bool BF16, bool KC>
+template <bool BF16, bool KC, int ROWS, int THREADS>
 struct SlowLoader {
     using E = Elem<BF16>;
     using T = typename E::T;
@@ -270,7 +289,7 @@ struct SlowLoader {
 
     __device__ __forceinline__ void load_store(int kt, char *lds) const {
         const int k0 = kt * E::BK;
-        for (int e = threadIdx.x; e < kNsTileM * E::BK; e += kThreads) {
+        for (int e = threadIdx.x; e < ROWS * E::BK; e += THREADS) {
             const int mn = e / E::BK, k = e % E::BK;
             T v = (T)0;
             if (mn < rows && k0 + k < K) v = KC ? p[(int64_t)mn * ld + k0 + k] : p[(int64_t)(k0 + k) * ld + mn];
@@ -278,7 +297,7 @@ struct SlowLoader {
             if (KC)
                 o = kl_off(mn, k / E::EPC) + (k % E::EPC) * sizeof(T);
             else
-                o = BF16 ? ml_off_bf16(k, mn) : ml_off_f32(k, mn);
+                o = BF16 ? ml_off_bf16<ROWS>(k, mn) : ml_off_f32<ROWS>(k, mn);
             *reinterpret_cast<T *>(lds + o) = v;
         }
     }
@@ -286,7 +305,7 @@ struct SlowLoader {
 
 // MFMA fragments of one 32-row (m or n) block for k16 step kk (bf16): lane l
 // holds row (l & 31) and k = 16 kk + 8 (l / 32) .. + 7.
-template <bool KC>
+template <bool KC, int ROWS>
 __device__ __forceinline__ bf16x8_t frag_bf16(const char *lds, int row0, int kk) {
     const int lane = threadIdx.x & (kWave - 1);
     if (KC) {
@@ -301,8 +320,8 @@ __device__ __forceinline__ bf16x8_t frag_bf16(const char *lds, int row0, int kk)
         const int g = lane >> 4, i = lane & 15;
         const int mn = row0 + 16 * (g & 1) + 4 * (i & 3);
         const int k = 16 * kk + 8 * (g >> 1) + (i >> 2);
-        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(lds + ml_off_bf16(k, mn)));
-        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(lds + ml_off_bf16(k + 4, mn)));
+        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(lds + ml_off_bf16<ROWS>(k, mn)));
+        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(lds + ml_off_bf16<ROWS>(k + 4, mn)));
         typedef short v8i16 __attribute__((ext_vector_type(8)));
         const v8i16 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         return __builtin_bit_cast(bf16x8_t, both);
@@ -311,14 +330,14 @@ __device__ __forceinline__ bf16x8_t frag_bf16(const char *lds, int row0, int kk)
 
 // fp32 fragments for chunk pair cp: lane l holds 4 consecutive k
 // (k = 8 cp + 4 (l / 32) .. + 3) of row (l & 31); MFMA step s uses element s.
-template <bool KC>
+template <bool KC, int ROWS>
 __device__ __forceinline__ f32x4_t frag_f32(const char *lds, int row0, int cp) {
     const int lane = threadIdx.x & (kWave - 1);
     if (KC) return *reinterpret_cast<const f32x4_t *>(lds + kl_off(row0 + (lane & 31), 2 * cp + (lane >> 5)));
     const int mn = row0 + (lane & 31), k = 8 * cp + 4 * (lane >> 5);
     f32x4_t v;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) v[s] = *reinterpret_cast<const float *>(lds + ml_off_f32(k + s, mn));
+    for (int s = 0; s < 4; ++s) v[s] = *reinterpret_cast<const float *>(lds + ml_off_f32<ROWS>(k + s, mn));
     return v;
 }
 
@@ -330,27 +349,27 @@ template <> struct Frags<false> { f32x4_t p[kFM], q[kFN]; };
 
 // Fragment j (0 .. kFM + kFN - 1) of one half: j < kFM is P block j, the
 // rest Q block j - kFM.
-template <bool BF16, bool PKC, bool QKC>
+template <bool BF16, bool PKC, bool QKC, int TN>
 __device__ __forceinline__ void read_frag(Frags<BF16> &fr, const char *lds_p, const char *lds_q,
                                           int wm0, int wn0, int half, int j) {
     if constexpr (BF16) {
         if (j < kFM)
-            fr.p[j] = frag_bf16<PKC>(lds_p, wm0 + j * 32, half);
+            fr.p[j] = frag_bf16<PKC, 256>(lds_p, wm0 + j * 32, half);
         else
-            fr.q[j - kFM] = frag_bf16<QKC>(lds_q, wn0 + (j - kFM) * 32, half);
+            fr.q[j - kFM] = frag_bf16<QKC, TN>(lds_q, wn0 + (j - kFM) * 32, half);
     } else {
         if (j < kFM)
-            fr.p[j] = frag_f32<PKC>(lds_p, wm0 + j * 32, half);
+            fr.p[j] = frag_f32<PKC, 256>(lds_p, wm0 + j * 32, half);
         else
-            fr.q[j - kFM] = frag_f32<QKC>(lds_q, wn0 + (j - kFM) * 32, half);
+            fr.q[j - kFM] = frag_f32<QKC, TN>(lds_q, wn0 + (j - kFM) * 32, half);
     }
 }
 
-template <bool BF16, bool PKC, bool QKC>
+template <bool BF16, bool PKC, bool QKC, int TN>
 __device__ __forceinline__ void read_frags(Frags<BF16> &fr, const char *lds_p, const char *lds_q,
                                            int wm0, int wn0, int half) {
 #pragma unroll
-    for (int j = 0; j < kFM + kFN; ++j) read_frag<BF16, PKC, QKC>(fr, lds_p, lds_q, wm0, wn0, half, j);
+    for (int j = 0; j < kFM + kFN; ++j) read_frag<BF16, PKC, QKC, TN>(fr, lds_p, lds_q, wm0, wn0, half, j);
 }
 
 // acc[f][g]: 32 x 32 block (f along m, g along n) of the wave's tile.
@@ -508,20 +527,21 @@ __device__ __forceinline__ uint32_t lds_addr(const char *p) {
     return (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) char *)p);
 }
 
-// Full K loop of one tile. kStages LDS buffers hold k-slices kt .. kt + 3;
-// the direct-to-LDS loads run up to four slices ahead of the MFMAs. Each
-// slice is consumed in two halves; the barrier that hands over slice kt + 1
-// (and frees slice kt's buffer for slice kt + 4) sits between them, and the
-// first fragments of slice kt + 1 are read while the second half of slice kt
-// is still in the MFMA pipe.
+// Full K loop of one tile. S = L::kStages LDS buffers hold k-slices
+// kt .. kt + S - 1; the direct-to-LDS loads run up to S slices ahead of the
+// MFMAs. Each slice is consumed in two halves; the barrier that hands over
+// slice kt + 1 (and frees slice kt's buffer for slice kt + S) sits between
+// them, and the first fragments of slice kt + 1 are read while the second
+// half of slice kt is still in the MFMA pipe.
 // id_origin: tile origin (rows for ID_P, columns for ID_Q) of the identity
 // term; unused for ID_NONE.
-template <bool BF16, bool PKC, bool QKC, int SIDE = ID_NONE>
+template <class L, bool BF16, bool PKC, bool QKC, int SIDE = ID_NONE>
 __device__ __forceinline__ void tile_mainloop(const Operand &P, const Operand &Q, char *smem,
                                               f32x16_t (&acc)[kFM][kFN], int id_origin = 0) {
     using E = Elem<BF16>;
+    constexpr int TN = L::kTileN, S = L::kStages;
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int wm0 = wave_m0(wid), wn0 = wave_n0(wid);
+    const int wm0 = L::m0(wid), wn0 = L::n0(wid);
     const int id0 = (id_origin + (SIDE == ID_P ? wm0 : wn0)) / E::BK;  // first identity slice
 #pragma unroll
     for (int f = 0; f < kFM; ++f)
@@ -531,75 +551,73 @@ __device__ __forceinline__ void tile_mainloop(const Operand &P, const Operand &Q
             for (int r = 0; r < 16; ++r) acc[f][g][r] = 0.f;
     const int kt_n = (P.K + E::BK - 1) / E::BK;
     if (P.vec && Q.vec) {
-        DmaLoader<BF16, PKC> lp;
-        DmaLoader<BF16, QKC> lq;
+        DmaLoader<BF16, PKC, L::kTileM, L::kWaves> lp;
+        DmaLoader<BF16, QKC, TN, L::kWaves> lq;
         lp.init(P);
         lq.init(Q);
+        constexpr int PL = L::kPLoads, QL = L::kQLoads, NLD = PL + QL;
         const uint32_t lds0 = lds_addr(smem);
-        // The product visits its k slices starting at the tile's own 256 k
-        // (rotation), so that the identity term falls on the first NID
-        // iterations, which are unrolled. Iteration j reads slice
-        // (j + rot) mod kt_n; iterations j >= kt_n, and every load issued
-        // past the last iteration, read beyond K and land as zeros, so every
-        // iteration issues the same loads and waits for the same count.
-        constexpr int NID = SIDE == ID_NONE ? 0 : kNsTileM / E::BK;
+        // The product visits its k slices starting at the tile's own k range
+        // on the identity side (rotation), so that the identity term falls on
+        // the first NID iterations, which are unrolled. Iteration j reads
+        // slice (j + rot) mod kt_n; iterations j >= kt_n, and every load
+        // issued past the last iteration, read beyond K and land as zeros, so
+        // every iteration issues the same loads and waits for the same count.
+        constexpr int NID = SIDE == ID_NONE ? 0 : (SIDE == ID_Q ? TN : L::kTileM) / E::BK;
         const int rot = SIDE == ID_NONE ? 0 : (id_origin / E::BK) % kt_n;
         const int iters = kt_n > NID ? kt_n : NID;
         auto slice_of = [&](int j) {
             const int t = j + rot;
             return j >= kt_n ? kt_n : (t < kt_n ? t : t - kt_n);
         };
-        // Slice j + 3's Q loads go out in the first half of iteration j and
-        // slice j + 4's P loads in its second half (one load every other
-        // MFMA), so the prologue issues slices 0-2 and the P part of slice 3.
+        // Slice j + S - 1's Q loads go out in the first half of iteration j
+        // and slice j + S's P loads in its second half, so the prologue issues
+        // slices 0 .. S - 2 and the P part of slice S - 1.
 #pragma unroll
-        for (int st = 0; st < kStages - 1; ++st) {
-            lp.issue(slice_of(st), lds0 + st * kStageBytes);
-            lq.issue(slice_of(st), lds0 + st * kStageBytes + kOpBytes);
+        for (int st = 0; st < S - 1; ++st) {
+            lp.issue(slice_of(st), lds0 + st * L::kStageBytes);
+            lq.issue(slice_of(st), lds0 + st * L::kStageBytes + L::kPBytes);
         }
-        lp.issue(slice_of(kStages - 1), lds0 + (kStages - 1) * kStageBytes);
-        wait_vm_lgkm0<5 * kLoadsPerOp>();  // slice 0 landed; slices 1, 2 and half of 3 in flight
+        lp.issue(slice_of(S - 1), lds0 + (S - 1) * L::kStageBytes);
+        wait_vm_lgkm0<(S - 2) * NLD + PL>();  // slice 0 landed
         lds_barrier();
         Frags<BF16> fa, fb;
-        read_frags<BF16, PKC, QKC>(fa, smem, smem + kOpBytes, wm0, wn0, 0);
+        read_frags<BF16, PKC, QKC, TN>(fa, smem, smem + L::kPBytes, wm0, wn0, 0);
         // Iteration j: the MFMAs of the first half (fa) run while the second
-        // half's fragments (fb) are read and the Q part of slice j + 3 is
+        // half's fragments (fb) are read and the Q part of slice j + S - 1 is
         // loaded into the buffer slice j - 1 left; after the barrier that
         // hands over slice j + 1, the MFMAs of fb run while the first half of
-        // slice j + 1 is read and the P part of slice j + 4 is loaded into
-        // the buffer slice j leaves. Each read or load sits after one MFMA so
-        // that the matrix pipe does not wait behind a run of them.
+        // slice j + 1 is read and the P part of slice j + S is loaded into the
+        // buffer slice j leaves. Each MFMA step carries at most one fragment
+        // read and one load, so the matrix pipe does not wait behind a run of
+        // them.
         constexpr int kSteps = kFM * kFN, kFrag = kFM + kFN;
-        constexpr int kEvery = (kSteps - kFrag) / kLoadsPerOp;  // MFMAs per load
-        static_assert(kEvery >= 1 && kFrag + kEvery * kLoadsPerOp == kSteps, "interleave");
+        constexpr int eQ = kSteps / QL, eP = kSteps / PL;  // MFMA steps per load
+        static_assert(kFrag <= kSteps && eQ * QL == kSteps && eP * PL == kSteps, "interleave");
         const int w0 = SIDE == ID_Q ? wn0 : wm0;
         auto iteration = [&](int j, auto jid) {
             constexpr int JID = decltype(jid)::value;  // unrolled identity iteration, or -1
-            const char *cur = smem + (j % kStages) * kStageBytes;
-            const int late = slice_of(j + kStages - 1);  // its buffer was freed by barrier j - 1
-            const uint32_t late_dst = lds0 + ((j + kStages - 1) % kStages) * kStageBytes + kOpBytes;
+            const char *cur = smem + (j % S) * L::kStageBytes;
+            const int late = slice_of(j + S - 1);  // its buffer was freed by barrier j - 1
+            const uint32_t late_dst = lds0 + ((j + S - 1) % S) * L::kStageBytes + L::kPBytes;
 #pragma unroll
             for (int i = 0; i < kSteps; ++i) {
                 mma_step<BF16>(fa, acc, i);
-                if (i < kFrag)
-                    read_frag<BF16, PKC, QKC>(fb, cur, cur + kOpBytes, wm0, wn0, 1, i);
-                else if ((i - kFrag) % kEvery == kEvery - 1)
-                    lq.issue_one(late, late_dst, (i - kFrag) / kEvery);
+                if (i < kFrag) read_frag<BF16, PKC, QKC, TN>(fb, cur, cur + L::kPBytes, wm0, wn0, 1, i);
+                if (i % eQ == eQ - 1) lq.issue_one(late, late_dst, i / eQ);
                 __builtin_amdgcn_sched_barrier(0);
             }
             if constexpr (JID >= 0) mma_identity_at<BF16, SIDE, JID>(fa, acc, w0, 0);
-            wait_vm_lgkm0<4 * kLoadsPerOp>();
+            wait_vm_lgkm0<(S - 2) * NLD>();
             lds_barrier();
-            const char *nxt = smem + ((j + 1) % kStages) * kStageBytes;
-            const uint32_t dst = lds0 + (j % kStages) * kStageBytes;
-            const int refill = slice_of(j + kStages);
+            const char *nxt = smem + ((j + 1) % S) * L::kStageBytes;
+            const uint32_t dst = lds0 + (j % S) * L::kStageBytes;
+            const int refill = slice_of(j + S);
 #pragma unroll
             for (int i = 0; i < kSteps; ++i) {
                 mma_step<BF16>(fb, acc, i);
-                if (i < kFrag)
-                    read_frag<BF16, PKC, QKC>(fa, nxt, nxt + kOpBytes, wm0, wn0, 0, i);
-                else if ((i - kFrag) % kEvery == kEvery - 1)
-                    lp.issue_one(refill, dst, (i - kFrag) / kEvery);
+                if (i < kFrag) read_frag<BF16, PKC, QKC, TN>(fa, nxt, nxt + L::kPBytes, wm0, wn0, 0, i);
+                if (i % eP == eP - 1) lp.issue_one(refill, dst, i / eP);
                 __builtin_amdgcn_sched_barrier(0);
             }
             if constexpr (JID >= 0) mma_identity_at<BF16, SIDE, JID>(fb, acc, w0, 1);
@@ -608,19 +626,19 @@ __device__ __forceinline__ void tile_mainloop(const Operand &P, const Operand &Q
         for (int j = NID; j < iters; ++j) iteration(j, std::integral_constant<int, -1>{});
         wait_vm_lgkm0<0>();  // the zero-fill loads past the end write LDS too
     } else {
-        SlowLoader<BF16, PKC> lp;
-        SlowLoader<BF16, QKC> lq;
+        SlowLoader<BF16, PKC, L::kTileM, L::kThreads> lp;
+        SlowLoader<BF16, QKC, TN, L::kThreads> lq;
         lp.init(P);
         lq.init(Q);
         for (int kt = 0; kt < kt_n; ++kt) {
             lp.load_store(kt, smem);
-            lq.load_store(kt, smem + kOpBytes);
+            lq.load_store(kt, smem + L::kPBytes);
             __syncthreads();
             Frags<BF16> fa;
-            read_frags<BF16, PKC, QKC>(fa, smem, smem + kOpBytes, wm0, wn0, 0);
+            read_frags<BF16, PKC, QKC, TN>(fa, smem, smem + L::kPBytes, wm0, wn0, 0);
             mma_half<BF16>(fa, acc);
             mma_identity<BF16, SIDE>(fa, acc, kt - id0, 0);
-            read_frags<BF16, PKC, QKC>(fa, smem, smem + kOpBytes, wm0, wn0, 1);
+            read_frags<BF16, PKC, QKC, TN>(fa, smem, smem + L::kPBytes, wm0, wn0, 1);
             mma_half<BF16>(fa, acc);
             mma_identity<BF16, SIDE>(fa, acc, kt - id0, 1);
             __syncthreads();
@@ -640,7 +658,9 @@ __device__ __forceinline__ int find_ns_mat(const NsBatch &b, int t) { return fin
 constexpr int kStageStride = kWaveN + 8;  // 4 rows apart = 32 banks apart
 constexpr int kLanesPerRow = kWaveN / 4, kRowsPerInstr = kWave / kLanesPerRow;
 constexpr int kWordsPerRow = kWaveN / 64;  // packed sign words per wave row
-static_assert(kWaves * 32 * kStageStride * 4 <= kLdsBytes, "epilogue stage exceeds LDS");
+static_assert(GramLay::kWaves * 32 * kStageStride * 4 <= GramLay::kLdsBytes &&
+                  ProdLay::kWaves * 32 * kStageStride * 4 <= ProdLay::kLdsBytes,
+              "epilogue stage exceeds LDS");
 static_assert(kWaveN % 64 == 0, "a packed word spans 64 columns of one wave");
 
 __device__ __forceinline__ void stage_rows(const f32x16_t (&acc)[kFM][kFN], int f, float *stage,
@@ -745,7 +765,7 @@ template <bool BF16, bool FAST>
 __device__ __forceinline__ void gram_epilogue(f32x16_t (&acc)[kFM][kFN], char *smem, int ti, int tj,
                                               int r, float scale, void *a) {
     const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
-    const int m0 = ti * kNsTileM + wave_m0(wid), n0 = tj * kNsTileN + wave_n0(wid);
+    const int m0 = ti * kNsTileM + GramLay::m0(wid), n0 = tj * kNsTileM + GramLay::n0(wid);
     float *stage = reinterpret_cast<float *>(smem) + wid * 32 * kStageStride;
     const bool mirror = ti < tj;
 #pragma unroll
@@ -780,9 +800,9 @@ template <bool BF16, bool KC>
 __device__ __forceinline__ void gram_tile(const Operand &P, const Operand &Q, char *smem, int ti,
                                           int tj, int r, float scale, void *a) {
     f32x16_t acc[kFM][kFN];
-    tile_mainloop<BF16, KC, KC>(P, Q, smem, acc);
+    tile_mainloop<GramLay, BF16, KC, KC>(P, Q, smem, acc);
     const bool fast = P.vec && (r % Elem<BF16>::EPC) == 0 && (ti + 1) * kNsTileM <= r &&
-                      (tj + 1) * kNsTileN <= r;
+                      (tj + 1) * kNsTileM <= r;
     if (fast)
         gram_epilogue<BF16, true>(acc, smem, ti, tj, r, scale, a);
     else
@@ -790,10 +810,10 @@ __device__ __forceinline__ void gram_tile(const Operand &P, const Operand &Q, ch
 }
 
 template <bool BF16>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves / 4, kWaves / 4)))
+__global__ __launch_bounds__(GramLay::kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void ns_gram_kernel(NsBatch b) {
     using T = typename Elem<BF16>::T;
-    __shared__ __attribute__((aligned(16))) char smem[kLdsBytes];
+    __shared__ __attribute__((aligned(16))) char smem[GramLay::kLdsBytes];
     const int lt = xcd_remap(blockIdx.x, gridDim.x);
     const int w = lt / b.tiles_per_worker_all;
     const int lw = lt - w * b.tiles_per_worker_all;
@@ -847,7 +867,7 @@ __device__ __forceinline__ void product_epilogue(const ProductArgs &pa, f32x16_t
                                                  char *smem) {
     const int R = pa.R, C = pa.C;
     const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
-    const int m0 = pa.ti * kNsTileM + wave_m0(wid), n0 = pa.tj * kNsTileN + wave_n0(wid);
+    const int m0 = pa.ti * kNsTileM + ProdLay::m0(wid), n0 = pa.tj * kNsProdTileN + ProdLay::n0(wid);
     float *stage = reinterpret_cast<float *>(smem) + wid * 32 * kStageStride;
     const bool want_out = EPI == EPI_ITER || EPI == EPI_WUPD || (EPI == EPI_FINAL && pa.out);
     const bool want_pack = EPI == EPI_FINAL && pa.pk;
@@ -916,7 +936,7 @@ __device__ __forceinline__ int write_lane(int dst, uint32_t val, int lane) {
 
 __device__ __forceinline__ void pack_from_registers(const ProductArgs &pa, const f32x16_t (&acc)[kFM][kFN]) {
     const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
-    const int m0 = pa.ti * kNsTileM + wave_m0(wid), n0 = pa.tj * kNsTileN + wave_n0(wid);
+    const int m0 = pa.ti * kNsTileM + ProdLay::m0(wid), n0 = pa.tj * kNsProdTileN + ProdLay::n0(wid);
     constexpr int kSlots = kWaveM * kWordsPerRow / kWave;
     int lo[kSlots], hi[kSlots];  // 32-bit halves of each lane's words
 #pragma unroll
@@ -959,14 +979,14 @@ __device__ __forceinline__ void product_tile(const Operand &P, const Operand &Q,
     // wide (Q = X, mn-contiguous): -3 X enters on the P side at the output
     // rows; tall (Q = A): on the Q side at the output columns.
     if constexpr (QKC)
-        tile_mainloop<BF16, true, QKC, ID_Q>(P, Q, smem, acc, pa.tj * kNsTileN);
+        tile_mainloop<ProdLay, BF16, true, QKC, ID_Q>(P, Q, smem, acc, pa.tj * kNsProdTileN);
     else
-        tile_mainloop<BF16, true, QKC, ID_P>(P, Q, smem, acc, pa.ti * kNsTileM);
+        tile_mainloop<ProdLay, BF16, true, QKC, ID_P>(P, Q, smem, acc, pa.ti * kNsTileM);
     if (EPI == EPI_FINAL && pa.pk && !pa.out) {
         pack_from_registers(pa, acc);
         return;
     }
-    const bool fast = P.vec && (pa.ti + 1) * kNsTileM <= pa.R && (pa.tj + 1) * kNsTileN <= pa.C;
+    const bool fast = P.vec && (pa.ti + 1) * kNsTileM <= pa.R && (pa.tj + 1) * kNsProdTileN <= pa.C;
     if (fast)
         product_epilogue<BF16, EPI, true>(pa, acc, smem);
     else
@@ -974,10 +994,10 @@ __device__ __forceinline__ void product_tile(const Operand &P, const Operand &Q,
 }
 
 template <bool BF16, int EPI>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves / 4, kWaves / 4)))
+__global__ __launch_bounds__(ProdLay::kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void ns_product_kernel(NsBatch b) {
     using T = typename Elem<BF16>::T;
-    __shared__ __attribute__((aligned(16))) char smem[kLdsBytes];
+    __shared__ __attribute__((aligned(16))) char smem[ProdLay::kLdsBytes];
     const int lt = xcd_remap(blockIdx.x, gridDim.x);
     const int w = lt / b.tiles_per_worker_all;
     const int lw = lt - w * b.tiles_per_worker_all;
@@ -986,7 +1006,7 @@ void ns_product_kernel(NsBatch b) {
     const int R = M.R, C = M.C;
     const bool wide = R <= C;
     const int r = wide ? R : C;
-    const int tiles_n = (C + kNsTileN - 1) / kNsTileN;
+    const int tiles_n = (C + kNsProdTileN - 1) / kNsProdTileN;
     const int ti = t / tiles_n, tj = t - ti * tiles_n;
     const int64_t n = (int64_t)R * C;
     const char *x = static_cast<const char *>(M.x) + (int64_t)w * n * (int64_t)sizeof(T);
@@ -1015,12 +1035,12 @@ void ns_product_kernel(NsBatch b) {
     if (wide) {
         // out[m][n] = sum_k A[m][k] X[k][n]: P = A (k-contiguous), Q(n, k) = X[k][n]
         Operand P{a + (int64_t)ti * kNsTileM * r * (int64_t)sizeof(T), r, R - ti * kNsTileM, r, vec};
-        Operand Q{x + (int64_t)tj * kNsTileN * (int64_t)sizeof(T), C, C - tj * kNsTileN, r, vec};
+        Operand Q{x + (int64_t)tj * kNsProdTileN * (int64_t)sizeof(T), C, C - tj * kNsProdTileN, r, vec};
         product_tile<BF16, false, EPI>(P, Q, smem, pa);
     } else {
         // out[m][n] = sum_k X[m][k] A[k][n] = sum_k X[m][k] A[n][k] (A symmetric)
         Operand P{x + (int64_t)ti * kNsTileM * C * (int64_t)sizeof(T), C, R - ti * kNsTileM, r, vec};
-        Operand Q{a + (int64_t)tj * kNsTileN * r * (int64_t)sizeof(T), r, C - tj * kNsTileN, r, vec};
+        Operand Q{a + (int64_t)tj * kNsProdTileN * r * (int64_t)sizeof(T), r, C - tj * kNsProdTileN, r, vec};
         product_tile<BF16, true, EPI>(P, Q, smem, pa);
     }
 }
@@ -1028,7 +1048,7 @@ void ns_product_kernel(NsBatch b) {
 }  // namespace
 
 void launch_ns_gram(const NsBatch &b, bool ns_bf16, hipStream_t s) {
-    dim3 grid(b.total_tiles), block(kThreads);
+    dim3 grid(b.total_tiles), block(GramLay::kThreads);
     if (ns_bf16)
         hipLaunchKernelGGL(ns_gram_kernel<true>, grid, block, 0, s, b);
     else
@@ -1036,7 +1056,7 @@ void launch_ns_gram(const NsBatch &b, bool ns_bf16, hipStream_t s) {
 }
 
 void launch_ns_product(const NsBatch &b, bool ns_bf16, NsEpilogue epi, hipStream_t s) {
-    dim3 grid(b.total_tiles), block(kThreads);
+    dim3 grid(b.total_tiles), block(ProdLay::kThreads);
 #define SM_PROD(BF, E) hipLaunchKernelGGL((ns_product_kernel<BF, E>), grid, block, 0, s, b)
     if (ns_bf16) {
         if (epi == EPI_ITER) SM_PROD(true, EPI_ITER);

@@ -100,9 +100,10 @@ struct NsBatch {
     Starts starts;         // first block (tile) of each matrix
 };
 
-// Output tile of every Newton-Schulz GEMM.
+// Output tiles of the Newton-Schulz GEMMs: the Gram's are kNsTileM square,
+// the product's kNsTileM rows by kNsProdTileN columns.
 constexpr int kNsTileM = 256;
-constexpr int kNsTileN = 256;
+constexpr int kNsProdTileN = 256;
 
 // Tiles one worker of an R x C matrix needs.
 inline int32_t ns_gram_tiles(int64_t R, int64_t C) {
@@ -112,7 +113,7 @@ inline int32_t ns_gram_tiles(int64_t R, int64_t C) {
 }
 inline int32_t ns_product_tiles(int64_t R, int64_t C) {
     // output rows = R, cols = C in both orientations
-    return (int32_t)(((R + kNsTileM - 1) / kNsTileM) * ((C + kNsTileN - 1) / kNsTileN));
+    return (int32_t)(((R + kNsTileM - 1) / kNsTileM) * ((C + kNsProdTileN - 1) / kNsProdTileN));
 }
 
 // ns_bf16 selects the operand storage type; epi the epilogue.
