@@ -139,6 +139,92 @@ def time_int8_payload(sm, mats, wl, hip, dev, reps=10):
     return out
 
 
+def traced_kernel_ms(sm, hip, traces):
+    """Per kernel kind, the summed time per step from the events recorded
+    around each launch of signmuon_step_traced, and the launch counts."""
+    per_kind_ms, launch_count = {}, {}
+    for kd in traces[0].kinds():
+        launch_count[sm.KERNEL_KINDS[kd]] = launch_count.get(sm.KERNEL_KINDS[kd], 0) + 1
+    for tr in traces:
+        kinds = tr.kinds()
+        if tr.launches + 1 > len(tr._events):
+            raise RuntimeError("trace capacity too small")
+        evs = list(tr._events)
+        for i, kd in enumerate(kinds):
+            name = sm.KERNEL_KINDS[kd]
+            per_kind_ms[name] = per_kind_ms.get(name, 0.0) + hip.elapsed_ms(evs[i], evs[i + 1])
+    return {k: v / len(traces) for k, v in per_kind_ms.items()}, launch_count
+
+
+def time_comparison_steps(sm, mats, wl, code, hip, dev, reps=10):
+    """The comparison steps on the workload's matrices, each timed as whole
+    calls between HIP events on the library's stream:
+      muon:   the full-precision Muon step of one worker (worker 0's
+              gradients, its own momentum, the workload's Newton-Schulz
+              settings, W <- fmaf(-eta, U, W) on a copy of W);
+      signum: majority-vote signum with momentum, i.e. the whole step with
+              k = 0, over all the workload's workers."""
+    import torch
+    stream = torch.cuda.current_stream().cuda_stream
+    mom_t = torch.bfloat16 if wl.mom_dtype == "bf16" else torch.float32
+    norm = sm.NORM_SPECTRAL if wl.norm == "spectral" else sm.NORM_FROBENIUS
+    s_g = 4 if wl.grad_dtype == "f32" else 2
+    s_m = 4 if wl.mom_dtype == "f32" else 2
+    mfma_peak = PEAK_BF16_TFLOPS if wl.ns_dtype == "bf16" else PEAK_FP32_TFLOPS
+
+    def timed(call):
+        ev = [hip.event() for _ in range(2)]
+        call()
+        total = 0.0
+        for _ in range(reps):
+            hip.record(ev[0], stream)
+            call()
+            hip.record(ev[1], stream)
+            hip.sync(ev[1])
+            total += hip.elapsed_ms(ev[0], ev[1])
+        for e in ev:
+            hip.destroy(e)
+        return total / reps
+
+    out = {}
+    if wl.ns_iters >= 1:
+        one = [sm.Matrix(grad=m.grad[0:1], momentum=torch.zeros((1,) + m.shape, dtype=mom_t, device=dev),
+                         weight=m.weight.clone()) for m in mats]
+        p1 = sm.Params(workers=1, beta=wl.beta, eta=wl.eta, ns_iters=wl.ns_iters,
+                       grad_dtype=code[wl.grad_dtype], mom_dtype=code[wl.mom_dtype],
+                       ns_dtype=code[wl.ns_dtype], norm=norm, power_iters=wl.power_iters)
+        ws1 = sm.workspace_tensor(one, p1, dev)
+        ms = timed(lambda: sm.signmuon_muon_step(one, p1, ws1))
+        flops = sum(3 * min(R, C) ** 2 * max(R, C) for R, C in wl.shapes) * wl.ns_iters
+        out["muon"] = {"workers": 1, "ms_per_step": round(ms, 5),
+                       "params_per_s": round(wl.params / (ms * 1e-3), 1),
+                       "ns_flops": int(flops),
+                       "step_mfma_frac": round(flops / (ms * 1e-3) / (mfma_peak * 1e12), 4)}
+        del one, ws1
+    p0 = sm.Params(workers=wl.workers, beta=wl.beta, eta=wl.eta, ns_iters=0,
+                   grad_dtype=code[wl.grad_dtype], mom_dtype=code[wl.mom_dtype],
+                   ns_dtype=code[wl.ns_dtype])
+    ws0 = sm.workspace_tensor(mats, p0, dev)
+    ms = timed(lambda: sm.signmuon_step(mats, p0, ws0))
+    traces = [sm.Trace([hip.event() for _ in range(16)]) for _ in range(reps)]
+    for tr in traces:
+        sm.signmuon_step_traced(mats, p0, ws0, tr)
+    torch.cuda.synchronize()
+    kinds_ms, _ = traced_kernel_ms(sm, hip, traces)
+    for tr in traces:
+        for e in list(tr._events):
+            hip.destroy(e)
+    mw, n = wl.workers, wl.params
+    nbytes = mw * n * (s_g + 2 * s_m) + mw * n * (s_m + 1 / 8) + n * (mw / 8 + 8)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    out["signum"] = {"workers": mw, "ms_per_step": round(ms, 5),
+                     "params_per_s": round(n / (ms * 1e-3), 1),
+                     "algorithmic_bytes": int(nbytes), "achieved": round(gbs, 1), "unit": "GB/s",
+                     "frac": round(gbs / PEAK_HBM_GBS, 4),
+                     "kernels_ms": {k: round(v, 5) for k, v in kinds_ms.items()}}
+    return out
+
+
 def cpu_baseline(wl, js=(0, 1, 2, 3)):
     """The oracle, single-threaded, on a bounded sample of the workload: the
     matrices js (for GPT-2 small, the four matrices of one transformer layer)
@@ -283,19 +369,7 @@ def main():
     ms_per_step = 1e3 * wall / args.steps
 
     # per-kernel time per step, from the events around each launch
-    per_kind_ms = {}
-    launch_count = {}
-    for kd in traces[0].kinds():
-        launch_count[sm.KERNEL_KINDS[kd]] = launch_count.get(sm.KERNEL_KINDS[kd], 0) + 1
-    for tr in traces:
-        kinds = tr.kinds()
-        if tr.launches + 1 > cap:
-            raise RuntimeError("trace capacity too small")
-        evs = list(tr._events)
-        for i, kd in enumerate(kinds):
-            name = sm.KERNEL_KINDS[kd]
-            per_kind_ms[name] = per_kind_ms.get(name, 0.0) + hip.elapsed_ms(evs[i], evs[i + 1])
-    per_kind_ms = {k: v / args.steps for k, v in per_kind_ms.items()}
+    per_kind_ms, launch_count = traced_kernel_ms(sm, hip, traces)
     launches = traces[0].launches
     for tr in traces:
         for e in list(tr._events):
@@ -330,6 +404,8 @@ def main():
 
     log("[bench] timing the int8 payload (sign_int8 + vote_update_int8)")
     int8 = time_int8_payload(sm, mats, wl, hip, dev)
+    log("[bench] timing the comparison steps (Muon, one worker; majority-vote signum)")
+    comparison = time_comparison_steps(sm, mats, wl, code, hip, dev)
 
     base = None
     if not args.no_cpu_baseline:
@@ -355,12 +431,15 @@ def main():
         "kernels_ms_per_step": kernels,
         "launches_per_step": launches,
         "int8_payload": int8,
+        "comparison_steps": comparison,
         "roofline": roofline,
         "cpu_baseline": base,
     }
     log("[bench] " + ", ".join(f"{k} {v['ms']:.3f} ms" + (f" ({v['frac'] * 100:.1f}% of "
                                                           f"{v['bound']})" if "frac" in v else "")
                                for k, v in list(kernels.items()) + list(int8.items())))
+    log("[bench] comparison steps: " + ", ".join(f"{k} {v['ms_per_step']:.3f} ms per step"
+                                                 for k, v in comparison.items()))
     print(json.dumps(out), flush=True)
     del np
 

@@ -232,7 +232,12 @@ __global__ __launch_bounds__(256) void finalize_scales_kernel(MomBatch b) {
 // ---------------------------------------------------------------------------
 // Sign + 1-bit pack (summary §2 "Core mechanism"; "Algorithmic flow" steps
 // 2-3): word w of a worker holds entries 64w..64w+63, bit j = (u >= 0) for
-// entry 64w + j, exactly the wave64 ballot of lane j. Each wave packs 8 words.
+// entry 64w + j. In little-endian byte order, byte c of a worker's words is
+// then the 8 signs of entries 8c..8c+7 (bit t = entry 8c + t), so each lane
+// packs whole 8-entry chunks: one 16-byte load (bf16) or two (fp32), one byte
+// stored. A block's chunks are interleaved by thread, so every wave load
+// covers 1 KiB (bf16) of consecutive entries and every store 64 consecutive
+// bytes. Entries past n, up to the end of the last word, pack as 0.
 // ---------------------------------------------------------------------------
 template <bool UB>
 __global__ __launch_bounds__(256) void sign_pack_kernel(PackBatch b) {
@@ -241,35 +246,69 @@ __global__ __launch_bounds__(256) void sign_pack_kernel(PackBatch b) {
     const int local = blk - M.block_begin;
     const int w = local / M.blocks_per_worker;
     const int wb = local - w * M.blocks_per_worker;
-    const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x / kWave;
     const int64_t n = M.n;
-    const int64_t nw = (n + 63) >> 6;
-    const int64_t word0 = (int64_t)wb * kPackWordsPerBlock + wave * kPackWordsPerWave;
+    const int64_t nbytes = ((n + 63) >> 6) * 8;  // packed bytes of one worker
     const float s = b.scales ? b.scales[M.unit_begin + w].x : 1.0f;
     const size_t usz = UB ? 2 : 4;
     const char *u = static_cast<const char *>(M.u) + (size_t)w * (size_t)n * usz;
-    float vals[kPackWordsPerWave];
+    uint8_t *pk = M.packed ? reinterpret_cast<uint8_t *>(M.packed) + (size_t)w * (size_t)nbytes : nullptr;
+    float *uo = M.u_out ? M.u_out + (size_t)w * (size_t)n : nullptr;
+    // n % 8 == 0: every chunk is whole and 16-byte aligned (bf16) or
+    // 32-byte aligned (fp32) given a 16-byte aligned base.
+    const bool vec = (n & 7) == 0;
+    const int64_t c0 = (int64_t)wb * kPackChunksPerBlock + threadIdx.x;
+    float v[kPackChunksPerThread][8];
 #pragma unroll
-    for (int j = 0; j < kPackWordsPerWave; ++j) {
-        int64_t e = (word0 + j) * 64 + lane;
-        float v = -1.0f;  // entries past n pack as 0
-        if (e < n) {
-            v = UB ? bf16_bits_to_f32(reinterpret_cast<const uint16_t *>(u)[e])
-                   : reinterpret_cast<const float *>(u)[e];
-            if (b.scales) v = s * v;
-            if (M.u_out) M.u_out[(size_t)w * (size_t)n + e] = v;
+    for (int i = 0; i < kPackChunksPerThread; ++i) {
+        const int64_t e0 = (c0 + i * 256) * 8;
+        if (vec && e0 < n) {
+            if (UB) {
+                const uint4 q = *reinterpret_cast<const uint4 *>(u + e0 * 2);
+                const uint32_t h[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    v[i][2 * t] = bf16_bits_to_f32(h[t] & 0xffffu);
+                    v[i][2 * t + 1] = bf16_bits_to_f32(h[t] >> 16);
+                }
+            } else {
+                const float4 a = *reinterpret_cast<const float4 *>(u + e0 * 4);
+                const float4 c = *reinterpret_cast<const float4 *>(u + e0 * 4 + 16);
+                v[i][0] = a.x; v[i][1] = a.y; v[i][2] = a.z; v[i][3] = a.w;
+                v[i][4] = c.x; v[i][5] = c.y; v[i][6] = c.z; v[i][7] = c.w;
+            }
+        } else {
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                const int64_t e = e0 + t;
+                v[i][t] = e < n ? (UB ? bf16_bits_to_f32(reinterpret_cast<const uint16_t *>(u)[e])
+                                      : reinterpret_cast<const float *>(u)[e])
+                                : 0.0f;
+            }
         }
-        vals[j] = v;
     }
-    uint64_t mine = 0;
 #pragma unroll
-    for (int j = 0; j < kPackWordsPerWave; ++j) {
-        uint64_t bal = __ballot(vals[j] >= 0.0f);
-        if (lane == j) mine = bal;
+    for (int i = 0; i < kPackChunksPerThread; ++i) {
+        const int64_t c = c0 + i * 256, e0 = c * 8;
+        if (c >= nbytes) continue;
+        uint32_t byte = 0;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const float x = b.scales ? s * v[i][t] : v[i][t];
+            v[i][t] = x;
+            byte |= (uint32_t)(e0 + t < n && x >= 0.0f) << t;
+        }
+        if (pk) pk[c] = (uint8_t)byte;
+        if (uo) {
+            if (vec && e0 < n) {
+                *reinterpret_cast<float4 *>(uo + e0) = make_float4(v[i][0], v[i][1], v[i][2], v[i][3]);
+                *reinterpret_cast<float4 *>(uo + e0 + 4) = make_float4(v[i][4], v[i][5], v[i][6], v[i][7]);
+            } else {
+#pragma unroll
+                for (int t = 0; t < 8; ++t)
+                    if (e0 + t < n) uo[e0 + t] = v[i][t];
+            }
+        }
     }
-    if (M.packed && lane < kPackWordsPerWave && word0 + lane < nw)
-        M.packed[(size_t)w * nw + word0 + lane] = mine;
 }
 
 // ---------------------------------------------------------------------------

@@ -144,8 +144,11 @@ struct PackBatch {
     Starts starts;         // first block (tile) of each matrix
 };
 
-constexpr int kPackWordsPerWave = 8;
-constexpr int kPackWordsPerBlock = 4 * kPackWordsPerWave;  // 256 threads
+// 256 threads, each packing kPackChunksPerThread chunks of 8 entries (one
+// byte of packed words each).
+constexpr int kPackChunksPerThread = 4;
+constexpr int kPackChunksPerBlock = 256 * kPackChunksPerThread;
+constexpr int kPackWordsPerBlock = kPackChunksPerBlock / 8;
 
 void launch_sign_pack(const PackBatch &b, hipStream_t s);
 
