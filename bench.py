@@ -104,38 +104,44 @@ def work_per_kind(wl):
     }
 
 
-def time_int8_payload(sm, mats, wl, hip, dev, reps=10):
-    """The int8 payload on the workload's matrices: every worker's signs of
-    its (stored) momentum as int8, then the vote from the int8 buffers with
-    the update of W. HIP events on the library's stream bracket each kind's
-    launches (one launch per matrix); times are per step of all matrices."""
+def time_int8_payload(sm, mats, wl, code, hip, dev, reps=10):
+    """The whole step with the int8 payload on the workload's matrices: the
+    last Newton-Schulz product writes each worker's signs as int8, and one
+    batched launch takes the vote as the sign of their integer sum and
+    updates W. Timed as whole traced steps (HIP events on the library's
+    stream); the vote kernel's rate is its algorithmic bytes over its time."""
     import torch
-    stream = torch.cuda.current_stream().cuda_stream
-    signs = [torch.empty((wl.workers, R * C), dtype=torch.int8, device=dev) for R, C in wl.shapes]
-    ev = [hip.event() for _ in range(3)]
-    acc = [0.0, 0.0]
-    for rep in range(reps + 1):
-        hip.record(ev[0], stream)
-        for j, (R, C) in enumerate(wl.shapes):
-            sm.signmuon_sign_int8(mats[j].momentum, R * C, wl.workers, signs[j])
-        hip.record(ev[1], stream)
-        for j, (R, C) in enumerate(wl.shapes):
-            sm.signmuon_vote_update_int8(signs[j], wl.workers, R * C, mats[j].weight, wl.eta, None)
-        hip.record(ev[2], stream)
-        hip.sync(ev[2])
-        if rep:  # the first round warms up
-            acc[0] += hip.elapsed_ms(ev[0], ev[1])
-            acc[1] += hip.elapsed_ms(ev[1], ev[2])
-    for e in ev:
-        hip.destroy(e)
-    s_m = 4 if wl.mom_dtype == "f32" else 2
-    out = {}
-    for name, ms, nbytes in [("sign_int8", acc[0] / reps, wl.workers * wl.params * (s_m + 1)),
-                             ("vote_update_int8", acc[1] / reps, wl.params * (wl.workers + 8))]:
-        gbs = nbytes / (ms * 1e-3) / 1e9
-        out[name] = {"ms": round(ms, 5), "bound": "hbm", "achieved": round(gbs, 1), "unit": "GB/s",
-                     "frac": round(gbs / PEAK_HBM_GBS, 4), "algorithmic_bytes": int(nbytes),
-                     "launches": len(wl.shapes)}
+    norm = sm.NORM_SPECTRAL if wl.norm == "spectral" else sm.NORM_FROBENIUS
+    i8 = [sm.Matrix(grad=m.grad, momentum=m.momentum, weight=m.weight,
+                    signs_i8=torch.empty((wl.workers,) + m.shape, dtype=torch.int8, device=dev))
+          for m in mats]
+    p8 = sm.Params(workers=wl.workers, beta=wl.beta, eta=wl.eta, ns_iters=wl.ns_iters,
+                   grad_dtype=code[wl.grad_dtype], mom_dtype=code[wl.mom_dtype],
+                   ns_dtype=code[wl.ns_dtype], norm=norm, power_iters=wl.power_iters,
+                   payload=sm.PAYLOAD_INT8)
+    ws8 = sm.workspace_tensor(i8, p8, dev)
+    sm.signmuon_step(i8, p8, ws8)
+    traces = [sm.Trace([hip.event() for _ in range(64)]) for _ in range(reps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for tr in traces:
+        sm.signmuon_step_traced(i8, p8, ws8, tr)
+    torch.cuda.synchronize()
+    ms_step = 1e3 * (time.perf_counter() - t0) / reps
+    kinds_ms, launches = traced_kernel_ms(sm, hip, traces)
+    for tr in traces:
+        for e in list(tr._events):
+            hip.destroy(e)
+    out = {"ms_per_step": round(ms_step, 5), "params_per_s": round(wl.params / (ms_step * 1e-3), 1),
+           "kernels_ms": {k: round(v, 5) for k, v in kinds_ms.items()}}
+    vms = kinds_ms.get("vote_update_int8")
+    if vms:
+        nbytes = wl.params * (wl.workers + 8)
+        gbs = nbytes / (vms * 1e-3) / 1e9
+        out["vote_update_int8"] = {"ms": round(vms, 5), "bound": "hbm", "achieved": round(gbs, 1),
+                                   "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                                   "algorithmic_bytes": int(nbytes),
+                                   "launches": launches.get("vote_update_int8", 0)}
     return out
 
 
@@ -402,8 +408,8 @@ def main():
     ns_util = 100.0 * ns_flops / (ns_ms * 1e-3) / (mfma_peak * 1e12) if ns_ms > 0 else None
     vote_gbs = kernels.get("vote_update", {}).get("achieved")
 
-    log("[bench] timing the int8 payload (sign_int8 + vote_update_int8)")
-    int8 = time_int8_payload(sm, mats, wl, hip, dev)
+    log("[bench] timing the step with the int8 payload")
+    int8 = time_int8_payload(sm, mats, wl, code, hip, dev)
     log("[bench] timing the comparison steps (Muon, one worker; majority-vote signum)")
     comparison = time_comparison_steps(sm, mats, wl, code, hip, dev)
 
@@ -437,7 +443,10 @@ def main():
     }
     log("[bench] " + ", ".join(f"{k} {v['ms']:.3f} ms" + (f" ({v['frac'] * 100:.1f}% of "
                                                           f"{v['bound']})" if "frac" in v else "")
-                               for k, v in list(kernels.items()) + list(int8.items())))
+                               for k, v in kernels.items()))
+    log(f"[bench] int8 payload: step {int8['ms_per_step']:.3f} ms" +
+        (f", vote_update_int8 {int8['vote_update_int8']['ms']:.3f} ms "
+         f"({int8['vote_update_int8']['frac'] * 100:.1f}% of hbm)" if "vote_update_int8" in int8 else ""))
     log("[bench] comparison steps: " + ", ".join(f"{k} {v['ms_per_step']:.3f} ms per step"
                                                  for k, v in comparison.items()))
     print(json.dumps(out), flush=True)

@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define SIGNMUON_ABI_VERSION 2
+#define SIGNMUON_ABI_VERSION 3
 
 /* Status codes. */
 enum {
@@ -70,6 +70,16 @@ typedef enum {
                                     ||M||_2^2 on the Gram matrix (see signmuon_params) */
 } signmuon_norm;
 
+/* Sign payload of signmuon_step (summary §2 "Communication efficiency": one
+ * bit per entry, or eight "for implementation simplicity"). */
+typedef enum {
+    SIGNMUON_PAYLOAD_BITS = 0, /* packed 1-bit signs in signmuon_matrix.packed; the vote counts
+                                  the +1 bits */
+    SIGNMUON_PAYLOAD_INT8 = 1  /* int8 +-1 signs in signmuon_matrix.signs_i8; the vote is the
+                                  sign of their integer sum (what an integer SUM all-reduce
+                                  of the workers' buffers would give) */
+} signmuon_payload;
+
 /* A hipStream_t, passed as an opaque pointer so that this header needs no
  * HIP header. */
 typedef void *signmuon_stream;
@@ -90,6 +100,10 @@ typedef struct {
     float *weight;       /* [R][C] fp32, in place: the weights W (required by
                             signmuon_step) */
     int8_t *vote_out;    /* [R][C] or NULL: the vote S-bar in {-1, 0, +1} */
+    int8_t *signs_i8;    /* [Mw][R][C] int8: each worker's signs as +1 / -1 (same rule as
+                            the packed bits). Required by signmuon_step with
+                            params.payload == SIGNMUON_PAYLOAD_INT8 (then `packed` is not
+                            used); ignored otherwise */
 } signmuon_matrix;
 
 /* Hyper-parameters of one step (summary §2 "Algorithmic flow"). */
@@ -114,6 +128,8 @@ typedef struct {
                                   and X_0 = s M. lambda = 0 gives U = 0. Needs min(R, C) <= 8192
                                   (SIGNMUON_ERANGE). The post-vote polar step keeps its exact
                                   Frobenius scale. */
+    int32_t payload;           /* signmuon_payload of signmuon_step (0 = packed bits). INT8
+                                  does not combine with post_polar_iters > 0 (SIGNMUON_EINVAL). */
 } signmuon_params;
 
 /* Largest number of matrices one call accepts. */
@@ -195,7 +211,12 @@ int signmuon_vote_update_int8(const int8_t *signs, int32_t workers, int64_t n, f
  * directly: W <- fmaf(-eta, Y, W) with Y the post_polar_iters-step
  * Newton-Schulz factor of S-bar / ||S-bar||_F (W unchanged if S-bar = 0).
  * mats[i].grad, .momentum, .packed and .weight are required; .polar_out and
- * .vote_out are written when non-NULL.
+ * .vote_out are written when non-NULL. With params.payload ==
+ * SIGNMUON_PAYLOAD_INT8 (summary §2 "Core mechanism" 3 and "Communication
+ * efficiency": the integer all-reduce variant), the last product writes each
+ * worker's signs as int8 to .signs_i8 (required; .packed is not used) and the
+ * vote is the sign of the integer sum over workers; W and the vote then equal
+ * the packed path's bit for bit.
  */
 int signmuon_step(const signmuon_matrix *mats, int32_t n_mats, const signmuon_params *p,
                   void *workspace, size_t workspace_bytes, signmuon_stream stream);
@@ -223,7 +244,8 @@ enum {
     SIGNMUON_K_PACK = 5,     /* standalone sign + pack */
     SIGNMUON_K_VOTE = 6,     /* majority vote + update */
     SIGNMUON_K_AUX = 7,      /* post-vote polar step bookkeeping */
-    SIGNMUON_K_POWER = 8     /* spectral normalisation: power step, scale, Gram rescale */
+    SIGNMUON_K_POWER = 8,    /* spectral normalisation: power step, scale, Gram rescale */
+    SIGNMUON_K_VOTE_I8 = 9   /* vote from the int8 payload + update */
 };
 
 /* Instrumentation for stage timing: events[0] (a hipEvent_t created by the

@@ -21,7 +21,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libsignmuon.so")
 
 F32, BF16 = 0, 1
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 STATUS = {0: "SIGNMUON_OK", -1: "SIGNMUON_EINVAL", -2: "SIGNMUON_EDTYPE", -3: "SIGNMUON_EALIGN",
           -4: "SIGNMUON_EWORKSPACE", -5: "SIGNMUON_EHIP", -6: "SIGNMUON_ERANGE"}
@@ -37,7 +37,7 @@ class _Matrix(ctypes.Structure):
     _fields_ = [("rows", ctypes.c_int64), ("cols", ctypes.c_int64), ("grad", ctypes.c_void_p),
                 ("momentum", ctypes.c_void_p), ("polar_out", ctypes.c_void_p),
                 ("packed", ctypes.c_void_p), ("weight", ctypes.c_void_p),
-                ("vote_out", ctypes.c_void_p)]
+                ("vote_out", ctypes.c_void_p), ("signs_i8", ctypes.c_void_p)]
 
 
 class _Params(ctypes.Structure):
@@ -45,7 +45,7 @@ class _Params(ctypes.Structure):
                 ("ns_iters", ctypes.c_int32), ("post_polar_iters", ctypes.c_int32),
                 ("grad_dtype", ctypes.c_int), ("mom_dtype", ctypes.c_int),
                 ("ns_dtype", ctypes.c_int), ("norm", ctypes.c_int32),
-                ("power_iters", ctypes.c_int32)]
+                ("power_iters", ctypes.c_int32), ("payload", ctypes.c_int32)]
 
 
 class _Trace(ctypes.Structure):
@@ -54,8 +54,9 @@ class _Trace(ctypes.Structure):
 
 
 KERNEL_KINDS = {1: "momentum", 2: "scales", 3: "ns_gram", 4: "ns_product", 5: "sign_pack",
-                6: "vote_update", 7: "aux", 8: "power"}
+                6: "vote_update", 7: "aux", 8: "power", 9: "vote_update_int8"}
 NORM_FROBENIUS, NORM_SPECTRAL = 0, 1
+PAYLOAD_BITS, PAYLOAD_INT8 = 0, 1
 
 _lib = None
 
@@ -134,7 +135,8 @@ class Matrix:
 
     grad, momentum, polar_out: [Mw][R][C]; packed: [Mw][packed_words] int64
     (bit pattern of the uint64 words); weight: [R][C] fp32; vote_out: [R][C]
-    int8. Optional fields may be None.
+    int8; signs_i8: [Mw][R][C] int8 (int8 payload). Optional fields may be
+    None.
     """
     grad: torch.Tensor
     momentum: torch.Tensor
@@ -142,6 +144,7 @@ class Matrix:
     weight: Optional[torch.Tensor] = None
     polar_out: Optional[torch.Tensor] = None
     vote_out: Optional[torch.Tensor] = None
+    signs_i8: Optional[torch.Tensor] = None
 
     @property
     def shape(self):
@@ -160,6 +163,7 @@ class Params:
     ns_dtype: int = F32
     norm: int = NORM_FROBENIUS
     power_iters: int = 0
+    payload: int = PAYLOAD_BITS
 
 
 def _marshal(mats: Sequence[Matrix], params: Params):
@@ -167,10 +171,10 @@ def _marshal(mats: Sequence[Matrix], params: Params):
     for i, m in enumerate(mats):
         R, C = m.shape
         arr[i] = _Matrix(R, C, _ptr(m.grad), _ptr(m.momentum), _ptr(m.polar_out), _ptr(m.packed),
-                         _ptr(m.weight), _ptr(m.vote_out))
+                         _ptr(m.weight), _ptr(m.vote_out), _ptr(m.signs_i8))
     p = _Params(params.workers, params.beta, params.eta, params.ns_iters,
                 params.post_polar_iters, params.grad_dtype, params.mom_dtype, params.ns_dtype,
-                params.norm, params.power_iters)
+                params.norm, params.power_iters, params.payload)
     return arr, p
 
 

@@ -72,7 +72,8 @@ struct MatPlan {
     size_t pw_off;          // spectral: power vectors [2][Mw][r] (floats from the section)
     size_t pwp_off;         // spectral: block sums [2][Mw][pw_bpw] (doubles from the section)
     int32_t pw_bpw;         // spectral: power-step blocks per worker
-    bool fused_pack;        // the last product packs the signs itself
+    bool fused_pack;        // the last product packs the signs itself (bits payload)
+    bool fused_i8;          // the last product writes the int8 signs itself (int8 payload)
     bool u_scratch;         // U goes through workspace scratch
 };
 
@@ -82,6 +83,7 @@ struct Plan {
     size_t off_partials = 0, off_scales = 0, off_nnz = 0, off_gram = 0, off_iter[2] = {0, 0};
     size_t off_vns = 0, off_u = 0, off_pw = 0, off_pwp = 0, total = 0;
     bool spectral = false;
+    bool i8 = false;  // int8 payload
 };
 
 // Shapes, counts and dtypes (not pointers). Fills the plan.
@@ -97,6 +99,9 @@ int make_plan(const signmuon_matrix *mats, int32_t n_mats, const signmuon_params
     if (p->mom_dtype != p->ns_dtype) return SIGNMUON_EDTYPE;  // X0 is read in place from M
     if (p->norm != SIGNMUON_NORM_FROBENIUS && p->norm != SIGNMUON_NORM_SPECTRAL) return SIGNMUON_EINVAL;
     pl.spectral = p->norm == SIGNMUON_NORM_SPECTRAL;
+    if (p->payload != SIGNMUON_PAYLOAD_BITS && p->payload != SIGNMUON_PAYLOAD_INT8) return SIGNMUON_EINVAL;
+    pl.i8 = step && p->payload == SIGNMUON_PAYLOAD_INT8;
+    if (pl.i8 && p->post_polar_iters > 0) return SIGNMUON_EINVAL;
     if (pl.spectral && p->power_iters < 1) return SIGNMUON_EINVAL;
     if (pl.spectral && p->power_iters > kMaxIters) return SIGNMUON_ERANGE;
     const int64_t mw = p->workers;
@@ -131,8 +136,9 @@ int make_plan(const signmuon_matrix *mats, int32_t n_mats, const signmuon_params
         post_iter += align_up((size_t)q.n * ns, kSectionAlign);
         q.vns_off = vns;
         if (post) vns += align_up((size_t)q.n * ns, kSectionAlign);
-        q.fused_pack = step && p->ns_iters > 0 && (q.C % 64) == 0;
-        q.u_scratch = step && p->ns_iters > 0 && !q.fused_pack && s.polar_out == nullptr;
+        q.fused_pack = step && !pl.i8 && p->ns_iters > 0 && (q.C % 64) == 0;
+        q.fused_i8 = pl.i8 && p->ns_iters > 0;
+        q.u_scratch = step && p->ns_iters > 0 && !q.fused_pack && !q.fused_i8 && s.polar_out == nullptr;
         q.u_off = u;
         if (q.u_scratch) u += align_up((size_t)(mw * q.n) * 4, kSectionAlign);
         q.pw_bpw = sm::power_blocks_per_worker(q.r);
@@ -178,13 +184,15 @@ int make_plan(const signmuon_matrix *mats, int32_t n_mats, const signmuon_params
     return SIGNMUON_OK;
 }
 
-int check_step_pointers(const signmuon_matrix *mats, int32_t n_mats, bool step) {
+int check_step_pointers(const signmuon_matrix *mats, int32_t n_mats, bool step, bool i8) {
     for (int32_t i = 0; i < n_mats; ++i) {
         const signmuon_matrix &s = mats[i];
         if (!s.grad || !s.momentum) return SIGNMUON_EINVAL;
-        if (step && (!s.packed || !s.weight)) return SIGNMUON_EINVAL;
+        if (step && (!(i8 ? (const void *)s.signs_i8 : (const void *)s.packed) || !s.weight))
+            return SIGNMUON_EINVAL;
         if (!step && !s.polar_out) return SIGNMUON_EINVAL;
-        const void *ptrs[6] = {s.grad, s.momentum, s.polar_out, s.packed, s.weight, s.vote_out};
+        const void *ptrs[7] = {s.grad, s.momentum, s.polar_out, s.packed, s.weight, s.vote_out,
+                               i8 ? s.signs_i8 : nullptr};
         for (const void *q : ptrs)
             if (q && !aligned16(q)) return SIGNMUON_EALIGN;
     }
@@ -277,6 +285,7 @@ int ns_pass(const signmuon_matrix *mats, int32_t n_mats, const signmuon_params *
                 d.out = nullptr;
             }
             d.packed = (last && step && q.fused_pack) ? s.packed : nullptr;
+            d.i8 = (last && step && q.fused_i8) ? s.signs_i8 : nullptr;
             d.tiles_per_worker = pass == 0 ? sm::ns_gram_tiles(q.R, q.C) : sm::ns_product_tiles(q.R, q.C);
             d.tile_begin = (int32_t)tiles;
             b.starts.v[i] = d.tile_begin;
@@ -371,7 +380,7 @@ int run_pack(const signmuon_matrix *mats, int32_t n_mats, const signmuon_params 
     const bool k0 = p->ns_iters == 0;
     std::vector<int32_t> sel;
     for (int32_t i = 0; i < n_mats; ++i)
-        if (k0 || (step && !pl.m[i].fused_pack)) sel.push_back(i);
+        if (k0 || (step && !pl.m[i].fused_pack && !pl.m[i].fused_i8)) sel.push_back(i);
     for (size_t c0 = 0; c0 < sel.size(); c0 += sm::kMaxMatsPerLaunch) {
         const size_t cn = sel.size() - c0 < (size_t)sm::kMaxMatsPerLaunch ? sel.size() - c0
                                                                           : (size_t)sm::kMaxMatsPerLaunch;
@@ -393,7 +402,8 @@ int run_pack(const signmuon_matrix *mats, int32_t n_mats, const signmuon_params 
                 d.u = s.polar_out ? (const void *)s.polar_out : ws_at<const char>(ws, pl.off_u + q.u_off);
                 d.u_out = nullptr;
             }
-            d.packed = step ? s.packed : nullptr;
+            d.packed = step && !pl.i8 ? s.packed : nullptr;
+            d.i8 = step && pl.i8 ? s.signs_i8 : nullptr;
             d.n = q.n;
             d.unit_begin = q.unit_begin;
             d.blocks_per_worker = (int32_t)((q.nw + sm::kPackWordsPerBlock - 1) / sm::kPackWordsPerBlock);
@@ -409,8 +419,53 @@ int run_pack(const signmuon_matrix *mats, int32_t n_mats, const signmuon_params 
     return SIGNMUON_OK;
 }
 
+// The vote from the int8 payload: one batched launch per kMaxMatsPerLaunch
+// matrices (the standalone entry point is a batch of one).
+int run_vote_int8(const int8_t *const *signs, float *const *weights, int8_t *const *votes,
+                  const int64_t *ns, int32_t n_mats, int32_t workers, float eta, hipStream_t st,
+                  Tracer &tr) {
+    for (int32_t c0 = 0; c0 < n_mats; c0 += sm::kMaxMatsPerLaunch) {
+        const int32_t cn = n_mats - c0 < sm::kMaxMatsPerLaunch ? n_mats - c0 : sm::kMaxMatsPerLaunch;
+        sm::VoteI8Batch b{};
+        b.nmat = cn;
+        b.workers = workers;
+        b.eta = eta;
+        int64_t blocks = 0;
+        for (int32_t i = 0; i < cn; ++i) {
+            sm::VoteI8Mat &d = b.mat[i];
+            d.signs = signs[c0 + i];
+            d.w = weights[c0 + i];
+            d.vote = votes[c0 + i];
+            d.n = ns[c0 + i];
+            d.vec = (d.n % 16) == 0;
+            d.block_begin = (int32_t)blocks;
+            b.starts.v[i] = d.block_begin;
+            blocks += sm::vote_int8_blocks(d.n);
+        }
+        if (blocks > INT32_MAX) return SIGNMUON_ERANGE;
+        b.total_blocks = (int32_t)blocks;
+        sm::launch_vote_update_int8(b, st);
+        if (int rc = tr.after(SIGNMUON_K_VOTE_I8)) return rc;
+    }
+    return SIGNMUON_OK;
+}
+
 int run_vote(const signmuon_matrix *mats, int32_t n_mats, const signmuon_params *p, const Plan &pl,
              void *ws, hipStream_t st, Tracer &tr) {
+    if (pl.i8) {
+        std::vector<const int8_t *> sg(n_mats);
+        std::vector<float *> wt(n_mats);
+        std::vector<int8_t *> vt(n_mats);
+        std::vector<int64_t> ns(n_mats);
+        for (int32_t i = 0; i < n_mats; ++i) {
+            sg[i] = mats[i].signs_i8;
+            wt[i] = mats[i].weight;
+            vt[i] = mats[i].vote_out;
+            ns[i] = pl.m[i].n;
+        }
+        return run_vote_int8(sg.data(), wt.data(), vt.data(), ns.data(), n_mats, p->workers, p->eta,
+                             st, tr);
+    }
     const bool post = p->post_polar_iters > 0;
     uint32_t *nnz = ws_at<uint32_t>(ws, pl.off_nnz);
     if (post) {
@@ -538,7 +593,7 @@ int signmuon_momentum_ns(const signmuon_matrix *mats, int32_t n_mats, const sign
                          void *workspace, size_t workspace_bytes, signmuon_stream stream) {
     Plan pl;
     if (int rc = make_plan(mats, n_mats, p, false, pl)) return rc;
-    if (int rc = check_step_pointers(mats, n_mats, false)) return rc;
+    if (int rc = check_step_pointers(mats, n_mats, false, false)) return rc;
     if (int rc = check_workspace(pl, workspace, workspace_bytes)) return rc;
     hipStream_t st = static_cast<hipStream_t>(stream);
     Tracer tr;
@@ -556,7 +611,7 @@ int signmuon_step_traced(const signmuon_matrix *mats, int32_t n_mats, const sign
                          signmuon_trace *trace) {
     Plan pl;
     if (int rc = make_plan(mats, n_mats, p, true, pl)) return rc;
-    if (int rc = check_step_pointers(mats, n_mats, true)) return rc;
+    if (int rc = check_step_pointers(mats, n_mats, true, pl.i8)) return rc;
     if (int rc = check_workspace(pl, workspace, workspace_bytes)) return rc;
     if (trace && trace->capacity > 0 && !trace->events) return SIGNMUON_EINVAL;
     hipStream_t st = static_cast<hipStream_t>(stream);
@@ -672,7 +727,10 @@ int signmuon_vote_update_int8(const int8_t *signs, int32_t workers, int64_t n, f
     if (workers > kMaxWorkers || n > kMaxN) return SIGNMUON_ERANGE;
     if (!aligned16(signs) || (weight && !aligned16(weight)) || (vote_out && !aligned16(vote_out)))
         return SIGNMUON_EALIGN;
-    sm::launch_vote_update_int8(signs, workers, n, weight, eta, vote_out, static_cast<hipStream_t>(stream));
+    Tracer tr;
+    if (int rc = run_vote_int8(&signs, &weight, &vote_out, &n, 1, workers, eta,
+                               static_cast<hipStream_t>(stream), tr))
+        return rc;
     return last_launch();
 }
 

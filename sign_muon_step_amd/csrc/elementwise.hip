@@ -237,7 +237,9 @@ __global__ __launch_bounds__(256) void finalize_scales_kernel(MomBatch b) {
 // packs whole 8-entry chunks: one 16-byte load (bf16) or two (fp32), one byte
 // stored. A block's chunks are interleaved by thread, so every wave load
 // covers 1 KiB (bf16) of consecutive entries and every store 64 consecutive
-// bytes. Entries past n, up to the end of the last word, pack as 0.
+// bytes. Entries past n, up to the end of the last word, pack as 0. With an
+// int8 target the chunk's 8 signs are stored as +1 / -1 bytes instead (one
+// 8-byte store per chunk).
 // ---------------------------------------------------------------------------
 template <bool UB>
 __global__ __launch_bounds__(256) void sign_pack_kernel(PackBatch b) {
@@ -253,6 +255,7 @@ __global__ __launch_bounds__(256) void sign_pack_kernel(PackBatch b) {
     const char *u = static_cast<const char *>(M.u) + (size_t)w * (size_t)n * usz;
     uint8_t *pk = M.packed ? reinterpret_cast<uint8_t *>(M.packed) + (size_t)w * (size_t)nbytes : nullptr;
     float *uo = M.u_out ? M.u_out + (size_t)w * (size_t)n : nullptr;
+    int8_t *i8 = M.i8 ? M.i8 + (size_t)w * (size_t)n : nullptr;
     // n % 8 == 0: every chunk is whole and 16-byte aligned (bf16) or
     // 32-byte aligned (fp32) given a 16-byte aligned base.
     const bool vec = (n & 7) == 0;
@@ -298,6 +301,22 @@ __global__ __launch_bounds__(256) void sign_pack_kernel(PackBatch b) {
             byte |= (uint32_t)(e0 + t < n && x >= 0.0f) << t;
         }
         if (pk) pk[c] = (uint8_t)byte;
+        if (i8 && e0 < n) {
+            // bit t set: +1 (0x01), clear: -1 (0xff)
+            uint32_t lo = 0, hi = 0;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                lo |= (((byte >> t) & 1u) ? 0x01u : 0xffu) << (8 * t);
+                hi |= (((byte >> (t + 4)) & 1u) ? 0x01u : 0xffu) << (8 * t);
+            }
+            if (vec) {
+                *reinterpret_cast<uint2 *>(i8 + e0) = make_uint2(lo, hi);
+            } else {
+#pragma unroll
+                for (int t = 0; t < 8; ++t)
+                    if (e0 + t < n) i8[e0 + t] = (int8_t)((t < 4 ? lo >> (8 * t) : hi >> (8 * (t - 4))) & 0xffu);
+            }
+        }
         if (uo) {
             if (vec && e0 < n) {
                 *reinterpret_cast<float4 *>(uo + e0) = make_float4(v[i][0], v[i][1], v[i][2], v[i][3]);
@@ -495,23 +514,29 @@ __global__ __launch_bounds__(256) void sign_int8_kernel(const void *u, int64_t t
     }
 }
 
-// vote_i = sign(sum over workers of signs[m][i]) and the update of W. VEC:
-// n % 16 == 0, so every worker's row of 16 entries is one 16-byte load.
-template <bool VEC>
-__global__ __launch_bounds__(256) void vote_update_int8_kernel(const int8_t *signs, int32_t mw, int64_t n,
-                                                              float *w, float eta, int8_t *vote) {
-    const int64_t e0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * kI8PerThread;
+// vote_i = sign(sum over workers of signs[m][i]) and the update of W, for
+// every matrix of the batch. Each thread takes 16 entries; with n % 16 == 0
+// (vec) every worker's 16 entries are one 16-byte load.
+__global__ __launch_bounds__(256) void vote_update_int8_kernel(VoteI8Batch b) {
+    const int blk = blockIdx.x;
+    const VoteI8Mat &M = b.mat[find_start(b.starts, blk)];
+    const int64_t n = M.n;
+    const int mw = b.workers;
+    const float eta = b.eta;
+    float *w = M.w;
+    int8_t *vote = M.vote;
+    const int64_t e0 = ((int64_t)(blk - M.block_begin) * 256 + threadIdx.x) * kI8PerThread;
     if (e0 >= n) return;
-    if (VEC) {
+    if (M.vec) {
         int32_t t[kI8PerThread];
 #pragma unroll
         for (int i = 0; i < kI8PerThread; ++i) t[i] = 0;
-        const int8_t *p = signs + e0;
+        const int8_t *p = M.signs + e0;
         auto add = [&](const u32x4_t &r) {
 #pragma unroll
             for (int q = 0; q < 4; ++q)
 #pragma unroll
-                for (int b = 0; b < 4; ++b) t[4 * q + b] += (int32_t)(int8_t)(r[q] >> (8 * b));
+                for (int c = 0; c < 4; ++c) t[4 * q + c] += (int32_t)(int8_t)(r[q] >> (8 * c));
         };
         int m = 0;
         for (; m + 4 <= mw; m += 4) {  // four workers' loads in flight together
@@ -529,9 +554,9 @@ __global__ __launch_bounds__(256) void vote_update_int8_kernel(const int8_t *sig
                 float4 v = *wp;
                 float *f = &v.x;
 #pragma unroll
-                for (int b = 0; b < 4; ++b) {
-                    const int32_t ti = t[4 * q + b];
-                    f[b] = ti > 0 ? f[b] - eta : (ti < 0 ? f[b] + eta : f[b]);
+                for (int c = 0; c < 4; ++c) {
+                    const int32_t ti = t[4 * q + c];
+                    f[c] = ti > 0 ? f[c] - eta : (ti < 0 ? f[c] + eta : f[c]);
                 }
                 *wp = v;
             }
@@ -542,9 +567,9 @@ __global__ __launch_bounds__(256) void vote_update_int8_kernel(const int8_t *sig
             for (int q = 0; q < 4; ++q) {
                 uint32_t wd = 0;
 #pragma unroll
-                for (int b = 0; b < 4; ++b) {
-                    const int32_t ti = t[4 * q + b];
-                    wd |= (uint32_t)(uint8_t)(int8_t)(ti > 0 ? 1 : (ti < 0 ? -1 : 0)) << (8 * b);
+                for (int c = 0; c < 4; ++c) {
+                    const int32_t ti = t[4 * q + c];
+                    wd |= (uint32_t)(uint8_t)(int8_t)(ti > 0 ? 1 : (ti < 0 ? -1 : 0)) << (8 * c);
                 }
                 out[q] = wd;
             }
@@ -554,7 +579,7 @@ __global__ __launch_bounds__(256) void vote_update_int8_kernel(const int8_t *sig
         const int64_t e1 = e0 + kI8PerThread < n ? e0 + kI8PerThread : n;
         for (int64_t e = e0; e < e1; ++e) {
             int32_t ti = 0;
-            for (int m = 0; m < mw; ++m) ti += signs[(int64_t)m * n + e];
+            for (int m = 0; m < mw; ++m) ti += M.signs[(int64_t)m * n + e];
             const int v = ti > 0 ? 1 : (ti < 0 ? -1 : 0);
             if (w && v > 0)
                 w[e] = w[e] - eta;
@@ -632,13 +657,10 @@ void launch_sign_int8(const void *u, bool u_bf16, int64_t total, int8_t *signs, 
         hipLaunchKernelGGL(sign_int8_kernel<false>, grid, block, 0, s, u, total, signs);
 }
 
-void launch_vote_update_int8(const int8_t *signs, int32_t workers, int64_t n, float *w, float eta,
-                             int8_t *vote, hipStream_t s) {
-    dim3 grid((unsigned)sign_int8_blocks(n)), block(256);
-    if (n % kI8PerThread == 0)
-        hipLaunchKernelGGL(vote_update_int8_kernel<true>, grid, block, 0, s, signs, workers, n, w, eta, vote);
-    else
-        hipLaunchKernelGGL(vote_update_int8_kernel<false>, grid, block, 0, s, signs, workers, n, w, eta, vote);
+int64_t vote_int8_blocks(int64_t n) { return (n + kI8PerBlock - 1) / kI8PerBlock; }
+
+void launch_vote_update_int8(const VoteI8Batch &b, hipStream_t s) {
+    hipLaunchKernelGGL(vote_update_int8_kernel, dim3(b.total_blocks), dim3(256), 0, s, b);
 }
 
 }  // namespace sm

@@ -854,14 +854,16 @@ struct ProductArgs {
     void *out;       // this worker's output (U / next iterate) or W
     uint64_t *pk;    // this worker's packed words or nullptr
     float *u_out;    // EPI_WUPD: U (fp32) as well, or nullptr
+    int8_t *i8;      // EPI_FINAL: this worker's int8 signs or nullptr
     int R, C, ti, tj;
     float gamma, eta;
 };
 
 // Epilogue of the product, 32 rows of the wave's tile at a time through
 // LDS: u = gamma * acc row-major (4 columns per lane), stored as
-// EPI asks; for the fused sign + pack, u goes back to LDS and each packed word
-// is the ballot of 64 consecutive columns of one row (needs C % 64 == 0).
+// EPI asks; int8 signs (u >= 0 -> +1, else -1) go out 4 per lane; for the
+// fused sign + pack, u goes back to LDS and each packed word is the ballot of
+// 64 consecutive columns of one row (needs C % 64 == 0).
 template <bool BF16, int EPI, bool FAST>
 __device__ __forceinline__ void product_epilogue(const ProductArgs &pa, f32x16_t (&acc)[kFM][kFN],
                                                  char *smem) {
@@ -871,6 +873,7 @@ __device__ __forceinline__ void product_epilogue(const ProductArgs &pa, f32x16_t
     float *stage = reinterpret_cast<float *>(smem) + wid * 32 * kStageStride;
     const bool want_out = EPI == EPI_ITER || EPI == EPI_WUPD || (EPI == EPI_FINAL && pa.out);
     const bool want_pack = EPI == EPI_FINAL && pa.pk;
+    const bool want_i8 = EPI == EPI_FINAL && pa.i8;
 #pragma unroll
     for (int f = 0; f < kFM; ++f) {
         stage_rows(acc, f, stage, 1.0f);
@@ -901,6 +904,18 @@ __device__ __forceinline__ void product_epilogue(const ProductArgs &pa, f32x16_t
                     for (int t = 0; t < 4; ++t) w[t] = __builtin_fmaf(-pa.eta, u[t], w[t]);
                     store4<false, FAST>(pa.out, idx, w, gm < R, C - gn);
                     if (pa.u_out) store4<false, FAST>(pa.u_out, idx, u, gm < R, C - gn);
+                }
+            }
+            if (want_i8) {
+                uint32_t q = 0;
+#pragma unroll
+                for (int t = 0; t < 4; ++t) q |= (u[t] >= 0.f ? 0x01u : 0xffu) << (8 * t);
+                if (FAST) {
+                    *reinterpret_cast<uint32_t *>(pa.i8 + idx) = q;
+                } else {
+#pragma unroll
+                    for (int t = 0; t < 4; ++t)
+                        if (gm < R && gn + t < C) pa.i8[idx + t] = (int8_t)(q >> (8 * t));
                 }
             }
             if (want_pack) *reinterpret_cast<float4 *>(sp) = make_float4(u[0], u[1], u[2], u[3]);
@@ -1031,6 +1046,7 @@ void ns_product_kernel(NsBatch b) {
         pa.out = M.out;
     pa.u_out = EPI == EPI_WUPD ? M.u_out : nullptr;
     pa.pk = M.packed ? M.packed + (int64_t)w * ((n + 63) >> 6) : nullptr;
+    pa.i8 = EPI == EPI_FINAL && M.i8 ? M.i8 + (int64_t)w * n : nullptr;
 
     if (wide) {
         // out[m][n] = sum_k A[m][k] X[k][n]: P = A (k-contiguous), Q(n, k) = X[k][n]

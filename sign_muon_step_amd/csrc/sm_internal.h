@@ -77,6 +77,7 @@ struct NsMat {
                         // stride: one worker)
     uint64_t *packed;   // EPI_FINAL fused sign+pack target or nullptr
     float *u_out;       // EPI_WUPD: U (fp32) as well, or nullptr (one worker)
+    int8_t *i8;         // EPI_FINAL: int8 signs [Mw][n] or nullptr
     int32_t R, C;
     int32_t tile_begin;  // first tile of this matrix within one worker's tiles
     int32_t tiles_per_worker;
@@ -127,6 +128,7 @@ struct PackMat {
     const void *u;       // [Mw][n]
     uint64_t *packed;    // [Mw][words]
     float *u_out;        // optional fp32 copy of the scaled value (k = 0 path)
+    int8_t *i8;          // int8 signs [Mw][n] instead of packed bits, or nullptr
     int64_t n;
     int32_t block_begin;
     int32_t blocks_per_worker;
@@ -186,8 +188,26 @@ void launch_vote_update(const VoteBatch &b, hipStream_t s);
 // of the integer sum over workers with the update of W.
 int64_t sign_int8_blocks(int64_t total);
 void launch_sign_int8(const void *u, bool u_bf16, int64_t total, int8_t *signs, hipStream_t s);
-void launch_vote_update_int8(const int8_t *signs, int32_t workers, int64_t n, float *w, float eta,
-                             int8_t *vote, hipStream_t s);
+struct VoteI8Mat {
+    const int8_t *signs;  // [Mw][n]
+    float *w;             // [n] or nullptr
+    int8_t *vote;         // [n] or nullptr
+    int64_t n;
+    int32_t block_begin;
+    int32_t vec;          // n % 16 == 0: 16-byte loads and stores
+};
+
+struct VoteI8Batch {
+    VoteI8Mat mat[kMaxMatsPerLaunch];
+    int32_t nmat;
+    int32_t workers;
+    int32_t total_blocks;
+    float eta;
+    Starts starts;  // first block of each matrix
+};
+
+int64_t vote_int8_blocks(int64_t n);
+void launch_vote_update_int8(const VoteI8Batch &b, hipStream_t s);
 
 // ---------------------------------------------------------------------------
 // Spectral normalisation: power iteration on each worker's Gram matrix.
@@ -232,6 +252,6 @@ void launch_nnz_scales(const uint32_t *nnz, int32_t count, float2 *scales, hipSt
 namespace sm {
 // Launch descriptors travel as kernel arguments (4 KiB at most).
 static_assert(sizeof(MomBatch) <= 4000 && sizeof(NsBatch) <= 4000 && sizeof(PackBatch) <= 4000 &&
-                  sizeof(VoteBatch) <= 4000 && sizeof(PowBatch) <= 4000,
+                  sizeof(VoteBatch) <= 4000 && sizeof(PowBatch) <= 4000 && sizeof(VoteI8Batch) <= 4000,
               "launch descriptor exceeds the kernel argument space");
 }  // namespace sm

@@ -58,7 +58,7 @@ def _call(fn, mats, params, ws=0x7f1000000000, ws_bytes=1 << 40):
     arr = (sm._Matrix * len(mats))(*mats)
     p = sm._Params(params.workers, params.beta, params.eta, params.ns_iters,
                    params.post_polar_iters, params.grad_dtype, params.mom_dtype, params.ns_dtype,
-                   params.norm, params.power_iters)
+                   params.norm, params.power_iters, params.payload)
     return fn(arr, len(mats), ctypes.byref(p), ws, ws_bytes, None)
 
 
@@ -147,6 +147,42 @@ def test_int8_payload_argument_errors(lib):
     assert lib.signmuon_vote_update_int8(a, 256, 10, a, 1e-3, None, None) == -6
     assert lib.signmuon_vote_update_int8(a + 2, 3, 10, a, 1e-3, None, None) == -3
     assert lib.signmuon_vote_update_int8(a, 3, 10, a, 1e-3, a + 4, None) == -3
+
+
+def test_step_int8_payload_argument_errors(lib):
+    """payload must be BITS or INT8; INT8 needs signs_i8 (16-byte aligned),
+    not packed, and does not combine with the post-vote polar step."""
+    i8 = sm.Params(workers=4, payload=sm.PAYLOAD_INT8)
+    assert _call(lib.signmuon_step, [_fake(64, 64, 4)], sm.Params(workers=4, payload=2)) == -1
+    assert _call(lib.signmuon_step, [_fake(64, 64, 4)], sm.Params(workers=4, payload=-1)) == -1
+    m = _fake(64, 64, 4)  # no signs_i8
+    assert _call(lib.signmuon_step, [m], i8) == -1
+    m = _fake(64, 64, 4)
+    m.signs_i8 = 0x7f0000600000 + 8
+    assert _call(lib.signmuon_step, [m], i8) == -3
+    m = _fake(64, 64, 4)
+    m.signs_i8 = 0x7f0000600000
+    m.packed = None
+    assert _call(lib.signmuon_step, [m], sm.Params(workers=4, payload=sm.PAYLOAD_INT8,
+                                                   post_polar_iters=1)) == -1
+    m.weight = None
+    assert _call(lib.signmuon_step, [m], i8) == -1
+    # the packed payload still needs packed
+    m = _fake(64, 64, 4)
+    m.packed = None
+    m.signs_i8 = 0x7f0000600000
+    assert _call(lib.signmuon_step, [m], sm.Params(workers=4)) == -1
+
+
+def test_int8_payload_needs_no_more_workspace(lib):
+    arr = (sm._Matrix * 2)(sm._Matrix(300, 700, None, None, None, None, None, None),
+                           sm._Matrix(130, 70, None, None, None, None, None, None))
+    bits = sm._Params(4, 0.9, 1e-3, 1, 0, sm.F32, sm.BF16, sm.BF16, 0, 0, sm.PAYLOAD_BITS)
+    i8 = sm._Params(4, 0.9, 1e-3, 1, 0, sm.F32, sm.BF16, sm.BF16, 0, 0, sm.PAYLOAD_INT8)
+    # the int8 payload is written by the last product itself: no fp32 U scratch
+    # for the shape whose columns are not a multiple of 64
+    assert 0 < lib.signmuon_workspace_bytes(arr, 2, ctypes.byref(i8)) < \
+        lib.signmuon_workspace_bytes(arr, 2, ctypes.byref(bits))
 
 
 @pytest.mark.parametrize("fn", ["signmuon_step", "signmuon_momentum_ns"])
