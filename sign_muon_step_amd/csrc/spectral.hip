@@ -190,6 +190,26 @@ __global__ __launch_bounds__(kThreads) void gram_rescale_kernel(PowBatch b) {
     const float s2 = b.scales[M.unit_begin + w].y;
     const int64_t e0 = ((int64_t)cb * kThreads + threadIdx.x) * 8;
     char *a = static_cast<char *>(const_cast<void *>(M.a)) + (int64_t)w * rr * (BF16 ? 2 : 4);
+    if ((rr & 7) == 0 && e0 + 8 <= rr) {  // 16-byte aligned: one (bf16) or two (fp32) vector accesses
+        if (BF16) {
+            uint4 *p = reinterpret_cast<uint4 *>(a + e0 * 2);
+            const uint4 q = *p;
+            uint32_t h[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                h[t] = pack_bf16x2(s2 * bf16_bits_to_f32(h[t] & 0xffffu), s2 * bf16_bits_to_f32(h[t] >> 16));
+            *p = make_uint4(h[0], h[1], h[2], h[3]);
+        } else {
+            float4 *p = reinterpret_cast<float4 *>(a + e0 * 4);
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                float4 v = p[t];
+                v.x *= s2; v.y *= s2; v.z *= s2; v.w *= s2;
+                p[t] = v;
+            }
+        }
+        return;
+    }
     for (int64_t e = e0; e < e0 + 8 && e < rr; ++e) {
         if (BF16) {
             uint16_t *p = reinterpret_cast<uint16_t *>(a) + e;
