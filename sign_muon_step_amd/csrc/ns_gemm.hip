@@ -647,7 +647,54 @@ __device__ __forceinline__ void tile_mainloop(const Operand &P, const Operand &Q
     __syncthreads();  // every wave is done with the slices before LDS is reused
 }
 
-__device__ __forceinline__ int find_ns_mat(const NsBatch &b, int t) { return find_start(b.starts, t); }
+// Tile -> matrix lookup in two steps, so that the table load goes out at
+// kernel entry together with the other kernel-argument loads: lane j reads
+// start j of the batch's table (non-decreasing, entry 0 is 0, unused entries
+// INT32_MAX) with one vector load straight from the kernel-argument segment
+// (the batch is the kernel's only argument); the index of the matrix holding
+// tile t is then the count of starts <= t, less one. A scalar scan of the
+// table waits for its loads in several dependent batches.
+__device__ __forceinline__ int ns_start_of_lane() {
+    static_assert(kMaxMatsPerLaunch <= kWave, "one start per lane");
+    using CChar = const __attribute__((address_space(4))) char;
+    using CInt = const __attribute__((address_space(4))) int;
+    CChar *k = (CChar *)__builtin_amdgcn_kernarg_segment_ptr();
+    CInt *starts = reinterpret_cast<CInt *>(k + offsetof(NsBatch, starts));
+    const int lane = threadIdx.x & (kWave - 1);
+    return lane < kMaxMatsPerLaunch ? starts[lane] : INT32_MAX;
+}
+__device__ __forceinline__ int find_ns_mat(int start_of_lane, int t) {
+    return __popcll(__ballot(start_of_lane <= t)) - 1;
+}
+
+// Descriptor mi of the batch in one vector load (lane d reads its dword d),
+// broadcast back field by field: its fields arrive together, where the
+// compiler's scalar loads would come in several batches with a wait each.
+__device__ __forceinline__ NsMat load_ns_mat(int mi) {
+    constexpr int ND = (int)(sizeof(NsMat) / 4);
+    static_assert(sizeof(NsMat) % 4 == 0 && ND <= kWave, "descriptor dwords");
+    using CChar = const __attribute__((address_space(4))) char;
+    using CInt = const __attribute__((address_space(4))) int;
+    CChar *k = (CChar *)__builtin_amdgcn_kernarg_segment_ptr();
+    CInt *p = reinterpret_cast<CInt *>(k + offsetof(NsBatch, mat) + (size_t)mi * sizeof(NsMat));
+    const int lane = threadIdx.x & (kWave - 1);
+    const int v = lane < ND ? p[lane] : 0;
+    int d[ND];
+#pragma unroll
+    for (int i = 0; i < ND; ++i) d[i] = __builtin_amdgcn_readlane(v, i);
+    NsMat m;
+    __builtin_memcpy(&m, d, sizeof(NsMat));
+    return m;
+}
+
+// The first iteration's scale, loaded at the start of a tile but selected
+// and used only in its epilogue, so that the load does not hold up the
+// tile's start (the array covers every unit, so the read is always valid).
+struct LateScale {
+    float raw;
+    int use;
+    __device__ float get() const { return use ? raw : 1.0f; }
+};
 
 // ---------------------------------------------------------------------------
 // Epilogue helpers. A wave stages 32 rows x kWaveN columns of fp32 in LDS
@@ -763,7 +810,8 @@ __device__ __forceinline__ void store32(void *p, int64_t idx, const float (&v)[3
 // run.
 template <bool BF16, bool FAST>
 __device__ __forceinline__ void gram_epilogue(f32x16_t (&acc)[kFM][kFN], char *smem, int ti, int tj,
-                                              int r, float scale, void *a) {
+                                              int r, LateScale sc, void *a) {
+    const float scale = sc.get();
     const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
     const int m0 = ti * kNsTileM + GramLay::m0(wid), n0 = tj * kNsTileM + GramLay::n0(wid);
     float *stage = reinterpret_cast<float *>(smem) + wid * 32 * kStageStride;
@@ -798,15 +846,15 @@ __device__ __forceinline__ void gram_epilogue(f32x16_t (&acc)[kFM][kFN], char *s
 
 template <bool BF16, bool KC>
 __device__ __forceinline__ void gram_tile(const Operand &P, const Operand &Q, char *smem, int ti,
-                                          int tj, int r, float scale, void *a) {
+                                          int tj, int r, LateScale sc, void *a) {
     f32x16_t acc[kFM][kFN];
     tile_mainloop<GramLay, BF16, KC, KC>(P, Q, smem, acc);
     const bool fast = P.vec && (r % Elem<BF16>::EPC) == 0 && (ti + 1) * kNsTileM <= r &&
                       (tj + 1) * kNsTileM <= r;
     if (fast)
-        gram_epilogue<BF16, true>(acc, smem, ti, tj, r, scale, a);
+        gram_epilogue<BF16, true>(acc, smem, ti, tj, r, sc, a);
     else
-        gram_epilogue<BF16, false>(acc, smem, ti, tj, r, scale, a);
+        gram_epilogue<BF16, false>(acc, smem, ti, tj, r, sc, a);
 }
 
 template <bool BF16>
@@ -814,10 +862,11 @@ __global__ __launch_bounds__(GramLay::kThreads) __attribute__((amdgpu_waves_per_
 void ns_gram_kernel(NsBatch b) {
     using T = typename Elem<BF16>::T;
     __shared__ __attribute__((aligned(16))) char smem[GramLay::kLdsBytes];
-    const int lt = xcd_remap(blockIdx.x, gridDim.x);
+    const int sv = ns_start_of_lane();
+    const int lt = xcd_remap(blockIdx.x, b.total_tiles);  // the grid is one block per tile
     const int w = lt / b.tiles_per_worker_all;
     const int lw = lt - w * b.tiles_per_worker_all;
-    const NsMat &M = b.mat[find_ns_mat(b, lw)];
+    const NsMat M = load_ns_mat(find_ns_mat(sv, lw));
     int t = lw - M.tile_begin;
     const bool wide = M.R <= M.C;
     const int r = wide ? M.R : M.C, c = wide ? M.C : M.R;
@@ -832,18 +881,18 @@ void ns_gram_kernel(NsBatch b) {
     const char *y = static_cast<const char *>(M.x) + (int64_t)w * n * (int64_t)sizeof(T);
     // Buffer offsets are 32-bit: the 16-byte path needs the matrix under 2 GiB.
     const bool vec = (M.C % Elem<BF16>::EPC) == 0 && n * (int64_t)sizeof(T) < ((int64_t)1 << 31);
-    const float scale = b.use_scales ? b.scales[M.unit_begin + w].y : 1.0f;
+    const LateScale sc{b.scales[M.unit_begin + w].y, b.use_scales};
     void *a = static_cast<char *>(M.a) + (int64_t)w * r * r * (int64_t)sizeof(T);
     if (wide) {
         // Y = X (r x c, k-contiguous rows)
         Operand P{y + (int64_t)ti * kNsTileM * M.C * (int64_t)sizeof(T), M.C, r - ti * kNsTileM, c, vec};
         Operand Q{y + (int64_t)tj * kNsTileM * M.C * (int64_t)sizeof(T), M.C, r - tj * kNsTileM, c, vec};
-        gram_tile<BF16, true>(P, Q, smem, ti, tj, r, scale, a);
+        gram_tile<BF16, true>(P, Q, smem, ti, tj, r, sc, a);
     } else {
         // Y = X^T: element (i, k) of Y is X[k][i]: mn-contiguous, ld = C
         Operand P{y + (int64_t)ti * kNsTileM * (int64_t)sizeof(T), M.C, r - ti * kNsTileM, c, vec};
         Operand Q{y + (int64_t)tj * kNsTileM * (int64_t)sizeof(T), M.C, r - tj * kNsTileM, c, vec};
-        gram_tile<BF16, false>(P, Q, smem, ti, tj, r, scale, a);
+        gram_tile<BF16, false>(P, Q, smem, ti, tj, r, sc, a);
     }
 }
 
@@ -856,7 +905,8 @@ struct ProductArgs {
     float *u_out;    // EPI_WUPD: U (fp32) as well, or nullptr
     int8_t *i8;      // EPI_FINAL: this worker's int8 signs or nullptr
     int R, C, ti, tj;
-    float gamma, eta;
+    LateScale s;     // -0.5 s is the epilogue's factor gamma
+    float eta;
 };
 
 // Epilogue of the product, 32 rows of the wave's tile at a time through
@@ -868,6 +918,7 @@ template <bool BF16, int EPI, bool FAST>
 __device__ __forceinline__ void product_epilogue(const ProductArgs &pa, f32x16_t (&acc)[kFM][kFN],
                                                  char *smem) {
     const int R = pa.R, C = pa.C;
+    const float gamma = -0.5f * pa.s.get();
     const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
     const int m0 = pa.ti * kNsTileM + ProdLay::m0(wid), n0 = pa.tj * kNsProdTileN + ProdLay::n0(wid);
     float *stage = reinterpret_cast<float *>(smem) + wid * 32 * kStageStride;
@@ -890,7 +941,7 @@ __device__ __forceinline__ void product_epilogue(const ProductArgs &pa, f32x16_t
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
                 const bool ok = FAST || (gm < R && gn + t < C);
-                u[t] = ok ? pa.gamma * v[t] : 0.f;
+                u[t] = ok ? gamma * v[t] : 0.f;
             }
             if (want_out) {
                 if (EPI == EPI_ITER) {
@@ -950,6 +1001,7 @@ __device__ __forceinline__ int write_lane(int dst, uint32_t val, int lane) {
 }
 
 __device__ __forceinline__ void pack_from_registers(const ProductArgs &pa, const f32x16_t (&acc)[kFM][kFN]) {
+    const float gamma = -0.5f * pa.s.get();
     const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
     const int m0 = pa.ti * kNsTileM + ProdLay::m0(wid), n0 = pa.tj * kNsProdTileN + ProdLay::n0(wid);
     constexpr int kSlots = kWaveM * kWordsPerRow / kWave;
@@ -962,8 +1014,8 @@ __device__ __forceinline__ void pack_from_registers(const ProductArgs &pa, const
         for (int rr = 0; rr < 16; ++rr)
 #pragma unroll
             for (int gp = 0; gp < kWordsPerRow; ++gp) {
-                const uint64_t b0 = __ballot(pa.gamma * acc[f][2 * gp][rr] >= 0.f);
-                const uint64_t b1 = __ballot(pa.gamma * acc[f][2 * gp + 1][rr] >= 0.f);
+                const uint64_t b0 = __ballot(gamma * acc[f][2 * gp][rr] >= 0.f);
+                const uint64_t b1 = __ballot(gamma * acc[f][2 * gp + 1][rr] >= 0.f);
                 const int id = ((f * 16 + rr) * kWordsPerRow + gp) * 2;  // even
                 // row R0: lanes 0-31 of both blocks; row R0 + 4: lanes 32-63
                 lo[id >> 6] = write_lane(lo[id >> 6], (uint32_t)b0, id & 63);
@@ -1013,10 +1065,11 @@ __global__ __launch_bounds__(ProdLay::kThreads) __attribute__((amdgpu_waves_per_
 void ns_product_kernel(NsBatch b) {
     using T = typename Elem<BF16>::T;
     __shared__ __attribute__((aligned(16))) char smem[ProdLay::kLdsBytes];
-    const int lt = xcd_remap(blockIdx.x, gridDim.x);
+    const int sv = ns_start_of_lane();
+    const int lt = xcd_remap(blockIdx.x, b.total_tiles);  // the grid is one block per tile
     const int w = lt / b.tiles_per_worker_all;
     const int lw = lt - w * b.tiles_per_worker_all;
-    const NsMat &M = b.mat[find_ns_mat(b, lw)];
+    const NsMat M = load_ns_mat(find_ns_mat(sv, lw));
     const int t = lw - M.tile_begin;
     const int R = M.R, C = M.C;
     const bool wide = R <= C;
@@ -1035,8 +1088,7 @@ void ns_product_kernel(NsBatch b) {
     pa.C = C;
     pa.ti = ti;
     pa.tj = tj;
-    const float s = b.use_scales ? b.scales[M.unit_begin + w].x : 1.0f;
-    pa.gamma = -0.5f * s;
+    pa.s = LateScale{b.scales[M.unit_begin + w].x, b.use_scales};
     pa.eta = b.eta;
     if (EPI == EPI_ITER)
         pa.out = static_cast<char *>(M.out) + (int64_t)w * n * (int64_t)sizeof(T);

@@ -95,7 +95,8 @@ struct NsBatch {
     int32_t total_tiles;
     int32_t tiles_per_worker_all;  // tiles of one worker over all matrices
     int32_t use_scales;   // iteration 0: fold s^2 (Gram) and s (product) in
-    const float2 *scales;
+    const float2 *scales; // per unit {s, s^2}; must cover every unit of the batch even
+                          // when use_scales = 0 (the kernels read it unconditionally)
     float eta;            // EPI_WUPD step size
     int32_t pad_;
     Starts starts;         // first block (tile) of each matrix
