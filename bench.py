@@ -45,6 +45,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="gpt2s_mw8_k1")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the int8-payload and comparison-step timings (profiler runs, so "
+                         "that per-kernel statistics cover the benchmarked step only)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="run one plain copy kernel of this size first (counter calibration)")
     return ap.parse_args()
@@ -408,10 +411,12 @@ def main():
     ns_util = 100.0 * ns_flops / (ns_ms * 1e-3) / (mfma_peak * 1e12) if ns_ms > 0 else None
     vote_gbs = kernels.get("vote_update", {}).get("achieved")
 
-    log("[bench] timing the step with the int8 payload")
-    int8 = time_int8_payload(sm, mats, wl, code, hip, dev)
-    log("[bench] timing the comparison steps (Muon, one worker; majority-vote signum)")
-    comparison = time_comparison_steps(sm, mats, wl, code, hip, dev)
+    int8 = comparison = None
+    if not args.no_extras:
+        log("[bench] timing the step with the int8 payload")
+        int8 = time_int8_payload(sm, mats, wl, code, hip, dev)
+        log("[bench] timing the comparison steps (Muon, one worker; majority-vote signum)")
+        comparison = time_comparison_steps(sm, mats, wl, code, hip, dev)
 
     base = None
     if not args.no_cpu_baseline:
@@ -444,11 +449,13 @@ def main():
     log("[bench] " + ", ".join(f"{k} {v['ms']:.3f} ms" + (f" ({v['frac'] * 100:.1f}% of "
                                                           f"{v['bound']})" if "frac" in v else "")
                                for k, v in kernels.items()))
-    log(f"[bench] int8 payload: step {int8['ms_per_step']:.3f} ms" +
-        (f", vote_update_int8 {int8['vote_update_int8']['ms']:.3f} ms "
-         f"({int8['vote_update_int8']['frac'] * 100:.1f}% of hbm)" if "vote_update_int8" in int8 else ""))
-    log("[bench] comparison steps: " + ", ".join(f"{k} {v['ms_per_step']:.3f} ms per step"
-                                                 for k, v in comparison.items()))
+    if int8:
+        log(f"[bench] int8 payload: step {int8['ms_per_step']:.3f} ms" +
+            (f", vote_update_int8 {int8['vote_update_int8']['ms']:.3f} ms "
+             f"({int8['vote_update_int8']['frac'] * 100:.1f}% of hbm)" if "vote_update_int8" in int8 else ""))
+    if comparison:
+        log("[bench] comparison steps: " + ", ".join(f"{k} {v['ms_per_step']:.3f} ms per step"
+                                                     for k, v in comparison.items()))
     print(json.dumps(out), flush=True)
     del np
 

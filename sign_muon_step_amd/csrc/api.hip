@@ -297,7 +297,11 @@ int ns_pass(const signmuon_matrix *mats, int32_t n_mats, const signmuon_params *
         if (pass == 0)
             sm::launch_ns_gram(b, bf16, st);
         else
-            sm::launch_ns_product(b, bf16, !last ? sm::EPI_ITER : (muon ? sm::EPI_WUPD : sm::EPI_FINAL), st);
+            sm::launch_ns_product(b, bf16,
+                                  !last ? sm::EPI_ITER
+                                        : (muon ? sm::EPI_WUPD
+                                                : (step && pl.i8 ? sm::EPI_FINAL_I8 : sm::EPI_FINAL)),
+                                  st);
         if (int rc = tr.after(pass == 0 ? SIGNMUON_K_GRAM : SIGNMUON_K_PRODUCT)) return rc;
     }
     return SIGNMUON_OK;

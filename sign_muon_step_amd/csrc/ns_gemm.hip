@@ -903,7 +903,7 @@ struct ProductArgs {
     void *out;       // this worker's output (U / next iterate) or W
     uint64_t *pk;    // this worker's packed words or nullptr
     float *u_out;    // EPI_WUPD: U (fp32) as well, or nullptr
-    int8_t *i8;      // EPI_FINAL: this worker's int8 signs or nullptr
+    int8_t *i8;      // EPI_FINAL_I8: this worker's int8 signs
     int R, C, ti, tj;
     LateScale s;     // -0.5 s is the epilogue's factor gamma
     float eta;
@@ -922,9 +922,10 @@ __device__ __forceinline__ void product_epilogue(const ProductArgs &pa, f32x16_t
     const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
     const int m0 = pa.ti * kNsTileM + ProdLay::m0(wid), n0 = pa.tj * kNsProdTileN + ProdLay::n0(wid);
     float *stage = reinterpret_cast<float *>(smem) + wid * 32 * kStageStride;
-    const bool want_out = EPI == EPI_ITER || EPI == EPI_WUPD || (EPI == EPI_FINAL && pa.out);
+    constexpr bool kFinal = EPI == EPI_FINAL || EPI == EPI_FINAL_I8;
+    const bool want_out = EPI == EPI_ITER || EPI == EPI_WUPD || (kFinal && pa.out);
     const bool want_pack = EPI == EPI_FINAL && pa.pk;
-    const bool want_i8 = EPI == EPI_FINAL && pa.i8;
+    constexpr bool want_i8 = EPI == EPI_FINAL_I8;
 #pragma unroll
     for (int f = 0; f < kFM; ++f) {
         stage_rows(acc, f, stage, 1.0f);
@@ -946,7 +947,7 @@ __device__ __forceinline__ void product_epilogue(const ProductArgs &pa, f32x16_t
             if (want_out) {
                 if (EPI == EPI_ITER) {
                     store4<BF16, FAST>(pa.out, idx, u, gm < R, C - gn);
-                } else if (EPI == EPI_FINAL) {
+                } else if (kFinal) {
                     store4<false, FAST>(pa.out, idx, u, gm < R, C - gn);
                 } else {
                     float w[4];
@@ -1092,13 +1093,13 @@ void ns_product_kernel(NsBatch b) {
     pa.eta = b.eta;
     if (EPI == EPI_ITER)
         pa.out = static_cast<char *>(M.out) + (int64_t)w * n * (int64_t)sizeof(T);
-    else if (EPI == EPI_FINAL)
+    else if (EPI == EPI_FINAL || EPI == EPI_FINAL_I8)
         pa.out = M.out ? static_cast<void *>(static_cast<float *>(M.out) + (int64_t)w * n) : nullptr;
     else
         pa.out = M.out;
     pa.u_out = EPI == EPI_WUPD ? M.u_out : nullptr;
     pa.pk = M.packed ? M.packed + (int64_t)w * ((n + 63) >> 6) : nullptr;
-    pa.i8 = EPI == EPI_FINAL && M.i8 ? M.i8 + (int64_t)w * n : nullptr;
+    pa.i8 = EPI == EPI_FINAL_I8 ? M.i8 + (int64_t)w * n : nullptr;
 
     if (wide) {
         // out[m][n] = sum_k A[m][k] X[k][n]: P = A (k-contiguous), Q(n, k) = X[k][n]
@@ -1129,10 +1130,12 @@ void launch_ns_product(const NsBatch &b, bool ns_bf16, NsEpilogue epi, hipStream
     if (ns_bf16) {
         if (epi == EPI_ITER) SM_PROD(true, EPI_ITER);
         else if (epi == EPI_FINAL) SM_PROD(true, EPI_FINAL);
+        else if (epi == EPI_FINAL_I8) SM_PROD(true, EPI_FINAL_I8);
         else SM_PROD(true, EPI_WUPD);
     } else {
         if (epi == EPI_ITER) SM_PROD(false, EPI_ITER);
         else if (epi == EPI_FINAL) SM_PROD(false, EPI_FINAL);
+        else if (epi == EPI_FINAL_I8) SM_PROD(false, EPI_FINAL_I8);
         else SM_PROD(false, EPI_WUPD);
     }
 #undef SM_PROD

@@ -67,7 +67,9 @@ void launch_finalize_scales(const MomBatch &b, hipStream_t s);
 // ---------------------------------------------------------------------------
 // Newton-Schulz GEMMs (matrix cores).
 // ---------------------------------------------------------------------------
-enum NsEpilogue { EPI_GRAM = 0, EPI_ITER = 1, EPI_FINAL = 2, EPI_WUPD = 3 };
+// EPI_FINAL: U (fp32) and/or packed signs; EPI_FINAL_I8: U (fp32) and/or
+// int8 signs (the int8 payload); EPI_WUPD: W <- fmaf(-eta, U, W).
+enum NsEpilogue { EPI_GRAM = 0, EPI_ITER = 1, EPI_FINAL = 2, EPI_WUPD = 3, EPI_FINAL_I8 = 4 };
 
 struct NsMat {
     const void *x;      // current iterate, worker 0; worker stride n (ns dtype)
@@ -77,7 +79,7 @@ struct NsMat {
                         // stride: one worker)
     uint64_t *packed;   // EPI_FINAL fused sign+pack target or nullptr
     float *u_out;       // EPI_WUPD: U (fp32) as well, or nullptr (one worker)
-    int8_t *i8;         // EPI_FINAL: int8 signs [Mw][n] or nullptr
+    int8_t *i8;         // EPI_FINAL_I8: int8 signs [Mw][n]
     int32_t R, C;
     int32_t tile_begin;  // first tile of this matrix within one worker's tiles
     int32_t tiles_per_worker;
