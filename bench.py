@@ -234,6 +234,17 @@ def time_comparison_steps(sm, mats, wl, code, hip, dev, reps=10):
     return out
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(wl, js=(0, 1, 2, 3)):
     """The oracle, single-threaded, on a bounded sample of the workload: the
     matrices js (for GPT-2 small, the four matrices of one transformer layer)
@@ -246,6 +257,11 @@ def cpu_baseline(wl, js=(0, 1, 2, 3)):
     ns = oracle.BF16 if wl.ns_dtype == "bf16" else oracle.F32
     js = [j for j in js if j < len(wl.shapes)]
     total_s, params = 0.0, 0
+    # one core: the oracle is single-threaded; pin the process to the core it
+    # runs on for the timed calls, and restore the affinity afterwards
+    saved = os.sched_getaffinity(0)
+    core = min(saved)
+    os.sched_setaffinity(0, {core})
     for j in js:
         R, C = wl.shapes[j]
         g = synthetic.gradients(wl, j, 0)
@@ -257,8 +273,10 @@ def cpu_baseline(wl, js=(0, 1, 2, 3)):
                        power_iters=wl.power_iters)
         total_s += time.perf_counter() - t0
         params += R * C
+    os.sched_setaffinity(0, saved)
     shapes = ", ".join(f"{wl.shapes[j][0]}x{wl.shapes[j][1]}" for j in js)
     return {"value": params / total_s, "unit": "params/s", "cores": 1, "kind": "oracle",
+            "cpu_model": cpu_model(), "host_threads": len(saved), "pinned_core": core,
             "sample": f"{wl.name} matrices {js[0]}-{js[-1]} ({shapes}; {params} params), all "
                       f"{wl.workers} workers, one full step each: {total_s:.1f} s single-threaded "
                       f"on this host's CPU"}
@@ -380,6 +398,9 @@ def main():
     # per-kernel time per step, from the events around each launch
     per_kind_ms, launch_count = traced_kernel_ms(sm, hip, traces)
     launches = traces[0].launches
+    # each step's own duration: its first event to its last
+    step_ms = sorted(hip.elapsed_ms(tr._events[0], tr._events[tr.launches]) for tr in traces)
+    ms_median = step_ms[len(step_ms) // 2]
     for tr in traces:
         for e in list(tr._events):
             hip.destroy(e)
@@ -435,6 +456,7 @@ def main():
                    "grad_dtype": wl.grad_dtype, "momentum_dtype": wl.mom_dtype,
                    "ns_dtype": wl.ns_dtype, "weight_dtype": "f32", "norm": wl.norm,
                    "power_iters": wl.power_iters},
+        "ms_per_step_median": round(ms_median, 4),
         "steps_per_s": round(1e3 / ms_per_step, 2),
         "worker_params_per_s": round(params_per_s * wl.workers, 1),
         "ns_mfma_util_pct": None if ns_util is None else round(ns_util, 2),
