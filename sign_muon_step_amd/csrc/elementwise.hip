@@ -265,19 +265,22 @@ __global__ __launch_bounds__(256) void sign_pack_kernel(PackBatch b) {
     for (int i = 0; i < kPackChunksPerThread; ++i) {
         const int64_t e0 = (c0 + i * 256) * 8;
         if (vec && e0 < n) {
-            if (UB) {
-                const uint4 q = *reinterpret_cast<const uint4 *>(u + e0 * 2);
-                const uint32_t h[4] = {q.x, q.y, q.z, q.w};
+            if (UB) {  // read once: nontemporal
+                const u32x4_t q = load16_nt(u + e0 * 2);
+                const uint32_t h[4] = {q[0], q[1], q[2], q[3]};
 #pragma unroll
                 for (int t = 0; t < 4; ++t) {
                     v[i][2 * t] = bf16_bits_to_f32(h[t] & 0xffffu);
                     v[i][2 * t + 1] = bf16_bits_to_f32(h[t] >> 16);
                 }
             } else {
-                const float4 a = *reinterpret_cast<const float4 *>(u + e0 * 4);
-                const float4 c = *reinterpret_cast<const float4 *>(u + e0 * 4 + 16);
-                v[i][0] = a.x; v[i][1] = a.y; v[i][2] = a.z; v[i][3] = a.w;
-                v[i][4] = c.x; v[i][5] = c.y; v[i][6] = c.z; v[i][7] = c.w;
+                const u32x4_t a = load16_nt(u + e0 * 4);
+                const u32x4_t c = load16_nt(u + e0 * 4 + 16);
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    v[i][t] = __uint_as_float(a[t]);
+                    v[i][4 + t] = __uint_as_float(c[t]);
+                }
             }
         } else {
 #pragma unroll
