@@ -21,6 +21,9 @@
  *    every call may be made from any host thread.
  *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
  *    the call returns without waiting for it. The library never synchronises.
+ *    The compute entry points enqueue only kernel launches (no allocation, no
+ *    memset, no copy), so a call may be captured into a HIP graph and
+ *    replayed; the graph keeps the pointers and scalars of the captured call.
  *  - Pointers to device arrays must be 16-byte aligned (SIGNMUON_EALIGN).
  *  - Every argument is checked before anything is enqueued: a call that
  *    returns an error has enqueued no work. A launch failure returns

@@ -1,0 +1,71 @@
+"""signmuon_step captured in a HIP graph: the library enqueues only kernel
+launches on the caller's stream (no allocation, no memset, no host
+synchronisation), so a captured step can be replayed. Two copies of the same
+state advance side by side, one by graph replays and one by eager calls, with
+eager work and synchronisations between the replays; after every replay the
+momentum, the packed signs, the vote and W of both copies must be equal bit
+for bit."""
+import numpy as np
+import pytest
+import torch
+
+import sign_muon_step_amd as sm
+import synthetic
+from gpu_util import DEV, announce, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _name_the_case(request):
+    announce(f"[gpu-test] {request.node.nodeid}")
+    yield
+    torch.cuda.synchronize()
+
+
+def state(shapes, mw, seed, int8):
+    mats = []
+    for j, (R, C) in enumerate(shapes):
+        g = np.stack([synthetic.random_matrix(seed + 10 * j + m, (R, C), 1e-3) for m in range(mw)])
+        mats.append(sm.Matrix(
+            grad=to_dev(g), momentum=torch.zeros((mw, R, C), dtype=torch.bfloat16, device=DEV),
+            packed=None if int8 else torch.zeros((mw, sm.signmuon_packed_words(R * C)),
+                                                 dtype=torch.int64, device=DEV),
+            weight=to_dev(synthetic.random_matrix(seed + 10 * j + 9, (R, C), 0.02)),
+            vote_out=torch.zeros((R, C), dtype=torch.int8, device=DEV),
+            signs_i8=torch.zeros((mw, R, C), dtype=torch.int8, device=DEV) if int8 else None))
+    return mats
+
+
+@pytest.mark.parametrize("payload", ["bits", "int8"])
+@pytest.mark.parametrize("k", [0, 1, 3])
+def test_captured_step_replays_like_eager_steps(payload, k):
+    shapes, mw = [(256, 640), (640, 256), (100, 130)], 4
+    int8 = payload == "int8"
+    p = sm.Params(workers=mw, beta=0.9, eta=1e-3, ns_iters=k, mom_dtype=sm.BF16, ns_dtype=sm.BF16,
+                  payload=sm.PAYLOAD_INT8 if int8 else sm.PAYLOAD_BITS)
+    graphed, eager = state(shapes, mw, 50, int8), state(shapes, mw, 50, int8)
+    ws_g, ws_e = sm.workspace_tensor(graphed, p, DEV), sm.workspace_tensor(eager, p, DEV)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            sm.signmuon_step(graphed, p, ws_g)  # recorded, not run
+    torch.cuda.synchronize()
+    for t in range(3):
+        g.replay()
+        sm.signmuon_step(eager, p, ws_e)
+        torch.cuda.synchronize()
+        for j, (a, b) in enumerate(zip(graphed, eager)):
+            np.testing.assert_array_equal(to_host(a.momentum), to_host(b.momentum), err_msg=f"M {j} t {t}")
+            if int8:
+                np.testing.assert_array_equal(to_host(a.signs_i8), to_host(b.signs_i8))
+            else:
+                np.testing.assert_array_equal(to_host(a.packed), to_host(b.packed))
+            np.testing.assert_array_equal(to_host(a.vote_out), to_host(b.vote_out))
+            np.testing.assert_array_equal(to_host(a.weight), to_host(b.weight), err_msg=f"W {j} t {t}")
+        # eager work of the program between replays
+        for a in graphed:
+            a.grad.mul_(1.0)
+        torch.cuda.synchronize()
