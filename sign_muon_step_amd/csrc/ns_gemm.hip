@@ -18,24 +18,27 @@
 //            i.e. s (1.5 X - 0.5 A X); the -3 X term is accumulated on the
 //            matrix cores with a -3 I fragment, and s folds the Frobenius
 //            scaling of the first iteration in (s = 1 afterwards).
-// The last product's epilogue either stores fp32 U and/or takes the sign of
-// each entry and packs 64 signs per uint64 word straight from the wave64
-// ballot of the accumulator registers (summary §2 "Algorithmic flow", steps
-// 2-3), or (post-vote polar step) applies W <- fmaf(-eta, Y, W).
+// The last product's epilogue stores fp32 U and/or takes the sign of each
+// entry: packed 64 signs per uint64 word straight from the wave64 ballot of
+// the accumulator registers, or int8 +1 / -1 (summary §2 "Algorithmic flow",
+// steps 2-3, and "Communication efficiency"); or (Muon step, post-vote polar
+// step) it applies W <- fmaf(-eta, Y, W).
 //
 // Every GEMM is C[m][n] = sum_k P[m][k] Q[n][k] on a 256 x TN output tile
 // computed by waves of 128 x 64, two waves per SIMD (one wave's LDS reads and
 // waits overlap the other's matrix instructions). Both kernels use TN = 256:
-// 8 waves and 128 KiB of LDS, one workgroup per CU (the Gram's tiles must be
+// 8 waves and 128 KiB of LDS, one workgroup per CU. (The Gram's tiles must be
 // square for the mirror; for the product, 256 x 128 tiles with two
 // workgroups per CU were faster on single-shape batches but slower on a
-// transformer's mixed batch, where the 256 x 256 tile reuses more in L2). Operands are staged through LDS in a [row][k]
-// layout, 128 bytes of k per row (64 bf16 or 32 fp32), 16-byte chunks
-// XOR-swizzled by row so that both the MFMA fragment reads and the staging
-// writes spread over all banks. An operand whose k index is the strided one
-// in memory (X in a wide product, both Gram operands of a tall X) is loaded
-// as 8 x 8 (bf16) or 4 x 4 (fp32) blocks and transposed in registers before
-// the LDS write.
+// transformer's mixed batch, where the 256 x 256 tile reuses more in L2.)
+// Operands stream from global memory straight into LDS, one k-slice of 64
+// bytes per row (32 bf16 or 16 fp32) at a time. A k-contiguous operand is
+// stored by rows with its 16-byte chunks XOR-swizzled, so that the fragment
+// reads spread over all banks. An operand whose k index is the strided one
+// in memory (X in a wide product, both Gram operands of a tall X) lands in
+// LDS mn-contiguous, in 4 (k) x 16 (mn) blocks for bf16, and its bf16
+// fragments come out with the LDS transpose read (ds_read_b64_tr_b16); fp32
+// ones are read element by element.
 #include <type_traits>
 #include <utility>
 
