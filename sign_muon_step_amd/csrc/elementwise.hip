@@ -1,6 +1,7 @@
 // elementwise.hip -- HBM-bound kernels of the Sign-Muon step for gfx950:
-// momentum update with Frobenius partial sums, sign + 1-bit pack, majority
-// vote + weight update, and the small helpers of the post-vote polar step.
+// momentum update with Frobenius partial sums, sign + 1-bit pack (or int8
+// signs), majority vote + weight update from packed bits or from int8
+// signs, and the small helpers of the post-vote polar step.
 //
 // Method: "SignMuon: Communication-Efficient Distributed Muon Optimization"
 // (gist.science, paper 2605.16311, technical summary), cited by section.
@@ -13,7 +14,6 @@ constexpr int kWave = 64;
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
 
-// Round-to-nearest-even fp32 -> bf16 pattern; NaN stays a quiet NaN.
 // fp32 -> bf16 bits, round to nearest even, NaN quieted with its sign and
 // top payload bits: one v_cvt_pk_bf16_f32 per pair of values (the hardware
 // conversion gives exactly this rule on every fp32 bit pattern).
