@@ -295,6 +295,12 @@ def test_step_resnet50_k5_small_shapes():
                label="resnet50 k5")
 
 
+def test_step_resnet50_k5_large_shapes():
+    """The two larger conv shapes (512 x 4608, 2048 x 512) at k = 5 in fp32."""
+    check_step(synthetic.WORKLOADS["resnet50_4shapes_mw4_k5"], steps=1, matrices=[2, 3],
+               label="resnet50 k5 large")
+
+
 def test_step_resnet50_all_convs_subset():
     """Ragged shapes (64 x 147: no fused pack) next to regular ones."""
     check_step(synthetic.WORKLOADS["resnet50_all_convs_mw4_k1"], steps=1,
