@@ -307,6 +307,12 @@ def test_step_resnet50_all_convs_subset():
                matrices=[0, 1, 2, 3, 5, 8], label="resnet50 all")
 
 
+def test_step_resnet50_every_conv():
+    """All 53 ResNet-50 conv weights (23.5M parameters, 4 workers, k = 1, fp32),
+    the ragged ones (C % 64 != 0: no fused pack) included."""
+    check_step(synthetic.WORKLOADS["resnet50_all_convs_mw4_k1"], steps=1, label="resnet50 all 53")
+
+
 def test_step_gpt2_shapes_mw16_k5_one_layer():
     """Student-t gradients, 16 workers (ties), 5 iterations, bf16: one layer."""
     check_step(synthetic.WORKLOADS["gpt2s_mw16_k5_t3"].with_(workers=4), steps=1,
