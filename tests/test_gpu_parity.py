@@ -368,48 +368,53 @@ def test_post_polar_step(ns, shape):
 # the GPT-2 small workload at full size (84.9M parameters, 8 workers)
 # ---------------------------------------------------------------------------
 def test_gpt2_small_full_size_sampled():
+    """Two consecutive steps of the benchmarked workload at full size: the
+    momentum carries over, and every check is repeated at each step."""
     wl = synthetic.WORKLOADS["gpt2s_mw8_k1"]
     mw = wl.workers
     idx = list(range(len(wl.shapes)))
-    gs = list(POOL.map(lambda j: synthetic.gradients(wl, j, 0), idx))
     ws_host = [synthetic.initial_weight(wl, j) for j in idx]
+    m_host = [np.zeros((mw,) + wl.shapes[j], np.uint16) for j in idx]
     mats = []
     for j, (R, C) in enumerate(wl.shapes):
         mats.append(sm.Matrix(
-            grad=to_dev(gs[j]), momentum=torch.zeros((mw, R, C), dtype=torch.bfloat16, device=DEV),
+            grad=torch.empty((mw, R, C), dtype=torch.float32, device=DEV),
+            momentum=torch.zeros((mw, R, C), dtype=torch.bfloat16, device=DEV),
             weight=to_dev(ws_host[j]),
             packed=torch.zeros((mw, sm.signmuon_packed_words(R * C)), dtype=torch.int64, device=DEV),
             polar_out=torch.zeros((mw, R, C), dtype=torch.float32, device=DEV) if j < 4 else None,
             vote_out=None))
-    announce("  full-size step: launching")
-    run("signmuon_step", mats, sm.Params(workers=mw, beta=wl.beta, eta=wl.eta, ns_iters=1,
-                                         mom_dtype=sm.BF16, ns_dtype=sm.BF16))
     rng = np.random.default_rng(0)
-    for j, mat in enumerate(mats):
-        R, C = wl.shapes[j]
-        m_ref = np.zeros((mw, R, C), np.uint16)
-        oracle.momentum(gs[j], m_ref, wl.beta)
-        m_gpu = to_host(mat.momentum)
-        np.testing.assert_array_equal(m_gpu, m_ref, err_msg=f"momentum {j}")
-        packed = to_host(mat.packed)
-        if j < 4:  # the first layer's four shapes: sampled U entries and the fused pack
-            u = to_host(mat.polar_out)
-            for w in (0, mw - 1):
-                np.testing.assert_array_equal(packed[w], oracle.sign_pack(u[w]))
-                _, x0 = oracle.normalise(m_ref[w])
-                ri = rng.integers(0, R, 96)
-                ci = rng.integers(0, C, 96)
-                ref = oracle.ns1_entries(x0, oracle.BF16, ri, ci)
-                got = u[w][ri, ci].astype(np.float64)
-                scale = np.sqrt(np.mean(u[w].astype(np.float64) ** 2))
-                dev_rel = np.abs(got - ref).max() / scale
-                agree = np.mean((got >= 0) == (ref >= 0))
-                announce(f"  gpt2 full matrix {j} {wl.shapes[j]} worker {w}: max|dU|/rms(U) = "
-                         f"{dev_rel:.3e}, sampled sign agreement {agree:.4f}")
-                assert dev_rel <= 2e-2
-        w_ref = ws_host[j].copy()
-        oracle.vote_update(packed, w_ref, wl.eta, want_vote=False)
-        np.testing.assert_array_equal(to_host(mat.weight), w_ref, err_msg=f"W {j}")
+    for t in range(2):
+        gs = list(POOL.map(lambda j: synthetic.gradients(wl, j, t), idx))
+        for j in idx:
+            mats[j].grad.copy_(torch.from_numpy(gs[j]))
+        announce(f"  full-size step {t}: launching")
+        run("signmuon_step", mats, sm.Params(workers=mw, beta=wl.beta, eta=wl.eta, ns_iters=1,
+                                             mom_dtype=sm.BF16, ns_dtype=sm.BF16))
+        for j, mat in enumerate(mats):
+            R, C = wl.shapes[j]
+            oracle.momentum(gs[j], m_host[j], wl.beta)
+            np.testing.assert_array_equal(to_host(mat.momentum), m_host[j],
+                                          err_msg=f"momentum {j} step {t}")
+            packed = to_host(mat.packed)
+            if j < 4:  # the first layer's four shapes: sampled U entries and the fused pack
+                u = to_host(mat.polar_out)
+                for w in (0, mw - 1):
+                    np.testing.assert_array_equal(packed[w], oracle.sign_pack(u[w]))
+                    _, x0 = oracle.normalise(m_host[j][w])
+                    ri = rng.integers(0, R, 96)
+                    ci = rng.integers(0, C, 96)
+                    ref = oracle.ns1_entries(x0, oracle.BF16, ri, ci)
+                    got = u[w][ri, ci].astype(np.float64)
+                    scale = np.sqrt(np.mean(u[w].astype(np.float64) ** 2))
+                    dev_rel = np.abs(got - ref).max() / scale
+                    agree = np.mean((got >= 0) == (ref >= 0))
+                    announce(f"  gpt2 full step {t} matrix {j} {wl.shapes[j]} worker {w}: "
+                             f"max|dU|/rms(U) = {dev_rel:.3e}, sampled sign agreement {agree:.4f}")
+                    assert dev_rel <= 2e-2
+            oracle.vote_update(packed, ws_host[j], wl.eta, want_vote=False)
+            np.testing.assert_array_equal(to_host(mat.weight), ws_host[j], err_msg=f"W {j} step {t}")
 
 
 @pytest.mark.parametrize("ns", ["bf16", "f32"])
