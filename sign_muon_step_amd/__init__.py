@@ -120,6 +120,8 @@ def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
         return None
     if not t.is_contiguous():
         raise ValueError("tensors passed to the library must be contiguous")
+    if t.device.type != "cuda":
+        raise ValueError(f"tensors passed to the library must be in GPU memory (device {t.device})")
     return t.data_ptr()
 
 
@@ -166,7 +168,52 @@ class Params:
     payload: int = PAYLOAD_BITS
 
 
+_TORCH_DTYPE = {F32: torch.float32, BF16: torch.bfloat16}
+
+
+def _expect(t: Optional[torch.Tensor], name: str, dtypes, numel: int) -> None:
+    """Element type, element count and contiguity of one buffer the library
+    reads or writes through a raw pointer (a short buffer would be accessed
+    out of bounds by the kernels)."""
+    if t is None:
+        return
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name}: dtype {t.dtype}, expected {' or '.join(map(str, dtypes))}")
+    if t.numel() != numel:
+        raise ValueError(f"{name}: {t.numel()} elements, expected {numel}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+
+
+def _buffers(m: Matrix):
+    return [("grad", m.grad), ("momentum", m.momentum), ("polar_out", m.polar_out),
+            ("packed", m.packed), ("weight", m.weight), ("vote_out", m.vote_out),
+            ("signs_i8", m.signs_i8)]
+
+
+def _validate(mats: Sequence[Matrix], params: Params) -> None:
+    """Every buffer of every matrix has the type and size the step assumes,
+    then every buffer is in GPU memory (a host pointer would fault)."""
+    mw = params.workers
+    for i, m in enumerate(mats):
+        R, C = m.shape
+        n = R * C
+        tag = f"matrix {i} ({R}x{C})"
+        _expect(m.grad, f"{tag} grad", (_TORCH_DTYPE.get(params.grad_dtype),), mw * n)
+        _expect(m.momentum, f"{tag} momentum", (_TORCH_DTYPE.get(params.mom_dtype),), mw * n)
+        _expect(m.polar_out, f"{tag} polar_out", (torch.float32,), mw * n)
+        _expect(m.packed, f"{tag} packed", (torch.int64,), mw * ((n + 63) // 64))
+        _expect(m.weight, f"{tag} weight", (torch.float32,), n)
+        _expect(m.vote_out, f"{tag} vote_out", (torch.int8,), n)
+        _expect(m.signs_i8, f"{tag} signs_i8", (torch.int8,), mw * n)
+    for i, m in enumerate(mats):
+        for name, t in _buffers(m):
+            if t is not None and t.device.type != "cuda":
+                raise ValueError(f"matrix {i} {name}: must be in GPU memory (device {t.device})")
+
+
 def _marshal(mats: Sequence[Matrix], params: Params):
+    _validate(mats, params)
     arr = (_Matrix * len(mats))()
     for i, m in enumerate(mats):
         R, C = m.shape
@@ -245,6 +292,36 @@ def signmuon_step_traced(mats: Sequence[Matrix], params: Params, workspace: Opti
     _check(library().signmuon_step_traced(arr, len(mats), ctypes.byref(p), _ptr(workspace), nbytes,
                                           _stream(stream),
                                           ctypes.byref(trace.struct) if trace else None))
+
+
+class Prepared:
+    """The matrices, parameters and workspace of repeated calls, checked and
+    marshalled once: each call then only crosses the C ABI. The tensors are
+    kept alive by this object and must stay the same buffers (their
+    contents may change between calls, e.g. new gradients)."""
+
+    def __init__(self, mats: Sequence[Matrix], params: Params, workspace: Optional[torch.Tensor]):
+        self.arr, self.p = _marshal(mats, params)
+        self.n = len(mats)
+        self.ws = _ptr(workspace)
+        self.nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        self._keep = (list(mats), workspace)
+
+    def _args(self, stream):
+        return self.arr, self.n, ctypes.byref(self.p), self.ws, self.nbytes, _stream(stream)
+
+    def step(self, stream=None) -> None:
+        _check(library().signmuon_step(*self._args(stream)))
+
+    def step_traced(self, trace: Optional[Trace], stream=None) -> None:
+        _check(library().signmuon_step_traced(*self._args(stream),
+                                              ctypes.byref(trace.struct) if trace else None))
+
+    def momentum_ns(self, stream=None) -> None:
+        _check(library().signmuon_momentum_ns(*self._args(stream)))
+
+    def muon_step(self, stream=None) -> None:
+        _check(library().signmuon_muon_step(*self._args(stream)))
 
 
 def signmuon_sign_pack(u: torch.Tensor, n: int, workers: int, packed: torch.Tensor,

@@ -69,3 +69,30 @@ def test_captured_step_replays_like_eager_steps(payload, k):
         for a in graphed:
             a.grad.mul_(1.0)
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("payload", ["bits", "int8"])
+def test_prepared_calls_equal_plain_calls(payload):
+    """sm.Prepared (buffers checked and marshalled once) gives the plain
+    calls' results bit for bit over two steps, with new gradients copied into
+    the same buffers between them."""
+    shapes, mw = [(256, 640), (640, 256), (100, 130)], 3
+    int8 = payload == "int8"
+    p = sm.Params(workers=mw, beta=0.9, eta=1e-3, ns_iters=2, mom_dtype=sm.BF16, ns_dtype=sm.BF16,
+                  payload=sm.PAYLOAD_INT8 if int8 else sm.PAYLOAD_BITS)
+    a, b = state(shapes, mw, 70, int8), state(shapes, mw, 70, int8)
+    ws_a, ws_b = sm.workspace_tensor(a, p, DEV), sm.workspace_tensor(b, p, DEV)
+    prep = sm.Prepared(a, p, ws_a)
+    for t in range(2):
+        prep.step()
+        sm.signmuon_step(b, p, ws_b)
+        torch.cuda.synchronize()
+        for x, y in zip(a, b):
+            np.testing.assert_array_equal(to_host(x.momentum), to_host(y.momentum))
+            np.testing.assert_array_equal(to_host(x.weight), to_host(y.weight))
+            np.testing.assert_array_equal(to_host(x.vote_out), to_host(y.vote_out))
+        for j, (x, y) in enumerate(zip(a, b)):
+            g = torch.from_numpy(np.stack([synthetic.random_matrix(900 + 10 * j + m + t, x.shape, 1e-3)
+                                           for m in range(mw)])).to(DEV)
+            x.grad.copy_(g)
+            y.grad.copy_(g)
