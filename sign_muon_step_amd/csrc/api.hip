@@ -3,6 +3,8 @@
 //
 // Method: "SignMuon: Communication-Efficient Distributed Muon Optimization"
 // (gist.science, paper 2605.16311, technical summary), §2 "Algorithmic flow".
+#include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
@@ -243,6 +245,37 @@ int run_momentum(const signmuon_matrix *mats, int32_t n_mats, const signmuon_par
     return SIGNMUON_OK;
 }
 
+// Compute units of the current device (the persistent product's grid), read
+// once per device.
+int device_cus() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n <= 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        cache[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
+// Launch groups of the final product. The persistent kernel takes bf16
+// matrices whose signs are packed from the accumulators and whose k loop
+// suits its tile walk (16-byte operands, k slices a multiple of the 4
+// pipeline stages and at least the 256 identity k plus one stage round);
+// wide and tall matrices go in separate launches. Everything else, and every other
+// product, uses the one-tile-per-block kernel.
+enum ProdGroup { PG_PLAIN = 0, PG_WALK_WIDE = 1, PG_WALK_TALL = 2 };
+
+int product_group(const MatPlan &q, const sm::NsMat &d, bool bf16) {
+    if (!bf16 || !d.packed || d.out || d.i8) return PG_PLAIN;
+    const int64_t kt_n = (q.r + 31) / 32;  // 32-wide bf16 k slices
+    if (q.C % 64 || q.r % 8 || q.n * 2 >= ((int64_t)1 << 31)) return PG_PLAIN;
+    if (kt_n % 4 || kt_n < 256 / 32 + 4) return PG_PLAIN;
+    return q.R > q.C ? PG_WALK_TALL : PG_WALK_WIDE;
+}
+
 // One Newton-Schulz launch pass over every (matrix, worker): iteration j's
 // Gram matrix (pass 0) or product (pass 1). use_scales folds s^2 (Gram) or s
 // (product) of iteration 0 in. The last product's epilogue writes U
@@ -254,55 +287,74 @@ int ns_pass(const signmuon_matrix *mats, int32_t n_mats, const signmuon_params *
     const bool last = j == k - 1;
     const bool bf16 = p->ns_dtype == SIGNMUON_BF16;
     const float2 *scales = ws_at<float2>(ws, pl.off_scales);
-    for (int32_t c0 = 0; c0 < n_mats; c0 += sm::kMaxMatsPerLaunch) {
-        const int32_t cn = n_mats - c0 < sm::kMaxMatsPerLaunch ? n_mats - c0 : sm::kMaxMatsPerLaunch;
-        sm::NsBatch b{};
-        b.nmat = cn;
-        b.workers = p->workers;
-        b.use_scales = use_scales;
-        b.scales = scales;
-        b.eta = p->eta;  // the W-update epilogue
-        int64_t tiles = 0;
-        for (int32_t i = 0; i < cn; ++i) {
-            const MatPlan &q = pl.m[c0 + i];
-            const signmuon_matrix &s = mats[c0 + i];
-            sm::NsMat &d = b.mat[i];
-            d.R = (int32_t)q.R;
-            d.C = (int32_t)q.C;
-            d.unit_begin = q.unit_begin;
-            d.x = j == 0 ? s.momentum : ws_at<const char>(ws, pl.off_iter[(j - 1) & 1] + q.iter_off);
-            d.a = ws_at<char>(ws, pl.off_gram + q.gram_off);
-            if (!last) {
-                d.out = ws_at<char>(ws, pl.off_iter[j & 1] + q.iter_off);
-            } else if (muon) {
-                d.out = s.weight;
-                d.u_out = s.polar_out;
-            } else if (s.polar_out) {
-                d.out = s.polar_out;
-            } else if (q.u_scratch) {
-                d.out = ws_at<char>(ws, pl.off_u + q.u_off);
-            } else {
-                d.out = nullptr;
-            }
-            d.packed = (last && step && q.fused_pack) ? s.packed : nullptr;
-            d.i8 = (last && step && q.fused_i8) ? s.signs_i8 : nullptr;
-            d.tiles_per_worker = pass == 0 ? sm::ns_gram_tiles(q.R, q.C) : sm::ns_product_tiles(q.R, q.C);
-            d.tile_begin = (int32_t)tiles;
-            b.starts.v[i] = d.tile_begin;
-            tiles += d.tiles_per_worker;
+    // Descriptor of matrix i for this pass.
+    auto describe = [&](int32_t i, sm::NsMat &d) {
+        const MatPlan &q = pl.m[i];
+        const signmuon_matrix &s = mats[i];
+        d = sm::NsMat{};
+        d.R = (int32_t)q.R;
+        d.C = (int32_t)q.C;
+        d.unit_begin = q.unit_begin;
+        d.x = j == 0 ? s.momentum : ws_at<const char>(ws, pl.off_iter[(j - 1) & 1] + q.iter_off);
+        d.a = ws_at<char>(ws, pl.off_gram + q.gram_off);
+        if (!last) {
+            d.out = ws_at<char>(ws, pl.off_iter[j & 1] + q.iter_off);
+        } else if (muon) {
+            d.out = s.weight;
+            d.u_out = s.polar_out;
+        } else if (s.polar_out) {
+            d.out = s.polar_out;
+        } else if (q.u_scratch) {
+            d.out = ws_at<char>(ws, pl.off_u + q.u_off);
+        } else {
+            d.out = nullptr;
         }
-        if (tiles * p->workers > INT32_MAX) return SIGNMUON_ERANGE;
-        b.tiles_per_worker_all = (int32_t)tiles;
-        b.total_tiles = (int32_t)(tiles * p->workers);
-        if (pass == 0)
-            sm::launch_ns_gram(b, bf16, st);
-        else
-            sm::launch_ns_product(b, bf16,
-                                  !last ? sm::EPI_ITER
-                                        : (muon ? sm::EPI_WUPD
-                                                : (step && pl.i8 ? sm::EPI_FINAL_I8 : sm::EPI_FINAL)),
-                                  st);
-        if (int rc = tr.after(pass == 0 ? SIGNMUON_K_GRAM : SIGNMUON_K_PRODUCT)) return rc;
+        d.packed = (last && step && q.fused_pack) ? s.packed : nullptr;
+        d.i8 = (last && step && q.fused_i8) ? s.signs_i8 : nullptr;
+        d.tiles_per_worker = pass == 0 ? sm::ns_gram_tiles(q.R, q.C) : sm::ns_product_tiles(q.R, q.C);
+    };
+    const sm::NsEpilogue epi = !last ? sm::EPI_ITER
+                                     : (muon ? sm::EPI_WUPD : (step && pl.i8 ? sm::EPI_FINAL_I8 : sm::EPI_FINAL));
+    // The matrices of each launch group, in order.
+    std::vector<int32_t> groups[3];
+    for (int32_t i = 0; i < n_mats; ++i) {
+        int g = PG_PLAIN;
+        if (pass == 1 && epi == sm::EPI_FINAL) {
+            sm::NsMat d;
+            describe(i, d);
+            g = product_group(pl.m[i], d, bf16);
+        }
+        groups[g].push_back(i);
+    }
+    for (int g = 0; g < 3; ++g) {
+        const std::vector<int32_t> &idx = groups[g];
+        for (size_t c0 = 0; c0 < idx.size(); c0 += sm::kMaxMatsPerLaunch) {
+            const int32_t cn = (int32_t)std::min(idx.size() - c0, (size_t)sm::kMaxMatsPerLaunch);
+            sm::NsBatch b{};
+            b.nmat = cn;
+            b.workers = p->workers;
+            b.use_scales = use_scales;
+            b.scales = scales;
+            b.eta = p->eta;  // the W-update epilogue
+            int64_t tiles = 0;
+            for (int32_t i = 0; i < cn; ++i) {
+                sm::NsMat &d = b.mat[i];
+                describe(idx[c0 + i], d);
+                d.tile_begin = (int32_t)tiles;
+                b.starts.v[i] = d.tile_begin;
+                tiles += d.tiles_per_worker;
+            }
+            if (tiles * p->workers > INT32_MAX) return SIGNMUON_ERANGE;
+            b.tiles_per_worker_all = (int32_t)tiles;
+            b.total_tiles = (int32_t)(tiles * p->workers);
+            if (pass == 0)
+                sm::launch_ns_gram(b, bf16, st);
+            else if (g == PG_PLAIN)
+                sm::launch_ns_product(b, bf16, epi, st);
+            else
+                sm::launch_ns_product_pack(b, g == PG_WALK_TALL, std::min(b.total_tiles, device_cus()), st);
+            if (int rc = tr.after(pass == 0 ? SIGNMUON_K_GRAM : SIGNMUON_K_PRODUCT)) return rc;
+        }
     }
     return SIGNMUON_OK;
 }

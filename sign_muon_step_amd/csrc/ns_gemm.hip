@@ -195,15 +195,16 @@ __device__ __forceinline__ void dma16(uint32_t lds, uint32_t voffset, v4u32 rsrc
                  : "memory");
 }
 
-// Direct-to-LDS loader of one operand (ROWS rows of the tile, WAVES waves):
+// Direct-to-LDS loads of one operand (ROWS rows of the tile, WAVES waves):
 // each wave instruction moves 1 KiB (16 bytes per lane) from global memory
 // straight into LDS, so a k-slice costs no registers and several slices can
 // be in flight. The LDS destination of lane L is fixed (base + 16 L); the
-// lane therefore fetches whichever global chunk the layout puts there.
-// Chunks outside the operand read the out-of-bounds buffer offset and land as
-// zeros. Each thread issues NL = ROWS / 16 / WAVES loads per slice.
-template <bool BF16, bool KC, int ROWS, int WAVES>
-struct DmaLoader {
+// lane therefore fetches whichever global chunk the layout (k- or
+// mn-contiguous, chosen at init) puts there. Chunks outside the operand read
+// the out-of-bounds buffer offset and land as zeros. Each thread issues
+// NL = ROWS / 16 / WAVES loads per slice.
+template <bool BF16, int ROWS, int WAVES>
+struct DmaSlices {
     using E = Elem<BF16>;
     using T = typename E::T;
     static constexpr int NL = ROWS / 16 / WAVES;
@@ -216,9 +217,12 @@ struct DmaLoader {
     int K;
     int wid;
 
-    __device__ __forceinline__ void init(const Operand &op) {
-        const int lane = threadIdx.x & (kWave - 1);
-        wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    // tid: the thread's index in the workgroup (passed in by a caller that
+    // keeps the compiler from hoisting lane arithmetic out of its loops).
+    template <bool KC>
+    __device__ __forceinline__ void setup(const Operand &op, int tid = (int)threadIdx.x) {
+        const int lane = tid & (kWave - 1);
+        wid = __builtin_amdgcn_readfirstlane(tid / kWave);
         // Buffer descriptor: 48-bit base, stride 0, num_records = extent in
         // bytes, raw 32-bit dword format (0x00020000 on this family).
         const uint64_t base = reinterpret_cast<uint64_t>(op.base);
@@ -253,24 +257,48 @@ struct DmaLoader {
         kstep = KC ? (uint32_t)E::BK * sz : (uint32_t)(E::BK * op.ld) * sz;
     }
 
-    // Load i (0 .. NL - 1) of slice kt only.
-    __device__ __forceinline__ void issue_one(int kt, uint32_t lds, int i) const {
+    // A queue with nothing to load: every chunk reads the out-of-bounds offset
+    // of an empty buffer and lands as zeros.
+    __device__ __forceinline__ void init_empty() {
+        wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+        rsrc = v4u32{0u, 0u, 0u, 0x00020000u};
+#pragma unroll
+        for (int i = 0; i < NL; ++i) off[i] = kofs[i] = 0;
+        valid = 0;
+        kstep = 0;
+        K = 0;
+    }
+
+    // Buffer offset of load i of slice kt.
+    __device__ __forceinline__ uint32_t offset(int kt, int i) const {
         const bool ok = ((valid >> i) & 1u) && kt * E::BK + kofs[i] < K;
-        const uint32_t o = ok ? off[i] + (uint32_t)kt * kstep : kOOB;
-        dma16(lds + (uint32_t)(i * WAVES + wid) * 1024u, o, rsrc);
+        return ok ? off[i] + (uint32_t)kt * kstep : kOOB;
     }
 
     // lds: LDS byte address of this operand's slice buffer.
+    __device__ __forceinline__ void issue_at(uint32_t lds, int i, uint32_t o, v4u32 rs) const {
+        dma16(lds + (uint32_t)(i * WAVES + wid) * 1024u, o, rs);
+    }
+
+    // Load i (0 .. NL - 1) of slice kt only.
+    __device__ __forceinline__ void issue_one(int kt, uint32_t lds, int i) const {
+        issue_at(lds, i, offset(kt, i), rsrc);
+    }
+
     __device__ __forceinline__ void issue(int kt, uint32_t lds) const {
         const int k0 = kt * E::BK;
         const uint32_t kb = (uint32_t)kt * kstep;
 #pragma unroll
         for (int i = 0; i < NL; ++i) {
             const bool ok = ((valid >> i) & 1u) && k0 + kofs[i] < K;
-            const uint32_t o = ok ? off[i] + kb : kOOB;
-            dma16(lds + (uint32_t)(i * WAVES + wid) * 1024u, o, rsrc);
+            issue_at(lds, i, ok ? off[i] + kb : kOOB, rsrc);
         }
     }
+};
+
+template <bool BF16, bool KC, int ROWS, int WAVES>
+struct DmaLoader : DmaSlices<BF16, ROWS, WAVES> {
+    __device__ __forceinline__ void init(const Operand &op) { this->template setup<KC>(op); }
 };
 
 // Element-by-element loader for shapes whose rows break 16-byte alignment:
@@ -309,8 +337,8 @@ struct SlowLoader {
 // MFMA fragments of one 32-row (m or n) block for k16 step kk (bf16): lane l
 // holds row (l & 31) and k = 16 kk + 8 (l / 32) .. + 7.
 template <bool KC, int ROWS>
-__device__ __forceinline__ bf16x8_t frag_bf16(const char *lds, int row0, int kk) {
-    const int lane = threadIdx.x & (kWave - 1);
+__device__ __forceinline__ bf16x8_t frag_bf16(const char *lds, int row0, int kk, int tid = (int)threadIdx.x) {
+    const int lane = tid & (kWave - 1);
     if (KC) {
         const uint4 v = *reinterpret_cast<const uint4 *>(lds + kl_off(row0 + (lane & 31), 2 * kk + (lane >> 5)));
         return __builtin_bit_cast(bf16x8_t, v);
@@ -334,8 +362,8 @@ __device__ __forceinline__ bf16x8_t frag_bf16(const char *lds, int row0, int kk)
 // fp32 fragments for chunk pair cp: lane l holds 4 consecutive k
 // (k = 8 cp + 4 (l / 32) .. + 3) of row (l & 31); MFMA step s uses element s.
 template <bool KC, int ROWS>
-__device__ __forceinline__ f32x4_t frag_f32(const char *lds, int row0, int cp) {
-    const int lane = threadIdx.x & (kWave - 1);
+__device__ __forceinline__ f32x4_t frag_f32(const char *lds, int row0, int cp, int tid = (int)threadIdx.x) {
+    const int lane = tid & (kWave - 1);
     if (KC) return *reinterpret_cast<const f32x4_t *>(lds + kl_off(row0 + (lane & 31), 2 * cp + (lane >> 5)));
     const int mn = row0 + (lane & 31), k = 8 * cp + 4 * (lane >> 5);
     f32x4_t v;
@@ -354,25 +382,25 @@ template <> struct Frags<false> { f32x4_t p[kFM], q[kFN]; };
 // rest Q block j - kFM.
 template <bool BF16, bool PKC, bool QKC, int TN>
 __device__ __forceinline__ void read_frag(Frags<BF16> &fr, const char *lds_p, const char *lds_q,
-                                          int wm0, int wn0, int half, int j) {
+                                          int wm0, int wn0, int half, int j, int tid = (int)threadIdx.x) {
     if constexpr (BF16) {
         if (j < kFM)
-            fr.p[j] = frag_bf16<PKC, 256>(lds_p, wm0 + j * 32, half);
+            fr.p[j] = frag_bf16<PKC, 256>(lds_p, wm0 + j * 32, half, tid);
         else
-            fr.q[j - kFM] = frag_bf16<QKC, TN>(lds_q, wn0 + (j - kFM) * 32, half);
+            fr.q[j - kFM] = frag_bf16<QKC, TN>(lds_q, wn0 + (j - kFM) * 32, half, tid);
     } else {
         if (j < kFM)
-            fr.p[j] = frag_f32<PKC, 256>(lds_p, wm0 + j * 32, half);
+            fr.p[j] = frag_f32<PKC, 256>(lds_p, wm0 + j * 32, half, tid);
         else
-            fr.q[j - kFM] = frag_f32<QKC, TN>(lds_q, wn0 + (j - kFM) * 32, half);
+            fr.q[j - kFM] = frag_f32<QKC, TN>(lds_q, wn0 + (j - kFM) * 32, half, tid);
     }
 }
 
 template <bool BF16, bool PKC, bool QKC, int TN>
 __device__ __forceinline__ void read_frags(Frags<BF16> &fr, const char *lds_p, const char *lds_q,
-                                           int wm0, int wn0, int half) {
+                                           int wm0, int wn0, int half, int tid = (int)threadIdx.x) {
 #pragma unroll
-    for (int j = 0; j < kFM + kFN; ++j) read_frag<BF16, PKC, QKC, TN>(fr, lds_p, lds_q, wm0, wn0, half, j);
+    for (int j = 0; j < kFM + kFN; ++j) read_frag<BF16, PKC, QKC, TN>(fr, lds_p, lds_q, wm0, wn0, half, j, tid);
 }
 
 // acc[f][g]: 32 x 32 block (f along m, g along n) of the wave's tile.
@@ -421,8 +449,8 @@ enum IdSide { ID_NONE = 0, ID_P = 1, ID_Q = 2 };
 
 // One-hot -3 fragment: lane l, k index kl (within the 32-row block) holds -3
 // where kl equals the lane's row (l & 31).
-__device__ __forceinline__ bf16x8_t id_frag_bf16(int roff, int kk) {
-    const int lane = threadIdx.x & (kWave - 1);
+__device__ __forceinline__ bf16x8_t id_frag_bf16(int roff, int kk, int tid = (int)threadIdx.x) {
+    const int lane = tid & (kWave - 1);
     const int j = (lane & 31) - roff - 16 * kk - 8 * (lane >> 5);  // element holding -3
     uint32_t w[4];
 #pragma unroll
@@ -431,8 +459,8 @@ __device__ __forceinline__ bf16x8_t id_frag_bf16(int roff, int kk) {
     return __builtin_bit_cast(bf16x8_t, make_uint4(w[0], w[1], w[2], w[3]));
 }
 
-__device__ __forceinline__ f32x4_t id_frag_f32(int roff, int cp) {
-    const int lane = threadIdx.x & (kWave - 1);
+__device__ __forceinline__ f32x4_t id_frag_f32(int roff, int cp, int tid = (int)threadIdx.x) {
+    const int lane = tid & (kWave - 1);
     const int j = (lane & 31) - roff - 8 * cp - 4 * (lane >> 5);
     f32x4_t v;
 #pragma unroll
@@ -485,7 +513,7 @@ __device__ __forceinline__ void mma_identity(const Frags<BF16> &fr, f32x16_t (&a
 // waves multiply a zero fragment, so the sequence has no branch.
 template <bool BF16, int SIDE, int J>
 __device__ __forceinline__ void mma_identity_at(const Frags<BF16> &fr, f32x16_t (&acc)[kFM][kFN], int w0,
-                                                int half) {
+                                                int half, int tid = (int)threadIdx.x) {
     constexpr int RS = Elem<BF16>::BK;
     constexpr int WS = SIDE == ID_Q ? kWaveN : kWaveM;
     constexpr int NO = SIDE == ID_Q ? kFM : kFN;
@@ -493,7 +521,7 @@ __device__ __forceinline__ void mma_identity_at(const Frags<BF16> &fr, f32x16_t 
     constexpr int b = (kb % WS) / 32, roff = kb % 32;
     const bool active = kb / WS == w0 / WS;
     if constexpr (BF16) {
-        const bf16x8_t one = id_frag_bf16(roff, half);
+        const bf16x8_t one = id_frag_bf16(roff, half, tid);
         bf16x8_t id;
 #pragma unroll
         for (int e = 0; e < 8; ++e) id[e] = active ? one[e] : (__bf16)0.0f;
@@ -505,7 +533,7 @@ __device__ __forceinline__ void mma_identity_at(const Frags<BF16> &fr, f32x16_t 
                 acc[o][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr.p[o], id, acc[o][b], 0, 0, 0);
         }
     } else {
-        const f32x4_t one = id_frag_f32(roff, half);
+        const f32x4_t one = id_frag_f32(roff, half, tid);
         f32x4_t id;
 #pragma unroll
         for (int st = 0; st < 4; ++st) id[st] = active ? one[st] : 0.0f;
@@ -688,6 +716,29 @@ __device__ __forceinline__ NsMat load_ns_mat(int mi) {
     NsMat m;
     __builtin_memcpy(&m, d, sizeof(NsMat));
     return m;
+}
+
+// Descriptor mi of the batch (mi uniform) and a unit's {s, s^2}, by scalar
+// loads: for a kernel that decodes its next tile while its own direct-to-LDS
+// loads are in flight, since the waits for scalar loads count only scalar
+// and LDS operations, not the vector memory operations those loads are.
+__device__ __forceinline__ NsMat load_ns_mat_scalar(int mi) {
+    constexpr int ND = (int)(sizeof(NsMat) / 4);
+    using CChar = const __attribute__((address_space(4))) char;
+    using CInt = const __attribute__((address_space(4))) int;
+    CChar *k = (CChar *)__builtin_amdgcn_kernarg_segment_ptr();
+    CInt *p = reinterpret_cast<CInt *>(k + offsetof(NsBatch, mat) + (size_t)mi * sizeof(NsMat));
+    int d[ND];
+#pragma unroll
+    for (int i = 0; i < ND; ++i) d[i] = p[i];
+    NsMat m;
+    __builtin_memcpy(&m, d, sizeof(NsMat));
+    return m;
+}
+__device__ __forceinline__ float load_scale_scalar(const float2 *scales, int unit, int which) {
+    using CFloat = const __attribute__((address_space(4))) float;
+    CFloat *p = (CFloat *)(uintptr_t)scales;
+    return p[2 * unit + which];
 }
 
 // The first iteration's scale, loaded at the start of a tile but selected
@@ -1004,9 +1055,10 @@ __device__ __forceinline__ int write_lane(int dst, uint32_t val, int lane) {
     return dst;
 }
 
-__device__ __forceinline__ void pack_from_registers(const ProductArgs &pa, const f32x16_t (&acc)[kFM][kFN]) {
+__device__ __forceinline__ void pack_from_registers(const ProductArgs &pa, const f32x16_t (&acc)[kFM][kFN],
+                                                    int tid = (int)threadIdx.x) {
     const float gamma = -0.5f * pa.s.get();
-    const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
+    const int lane = tid & (kWave - 1), wid = tid / kWave;
     const int m0 = pa.ti * kNsTileM + ProdLay::m0(wid), n0 = pa.tj * kNsProdTileN + ProdLay::n0(wid);
     constexpr int kSlots = kWaveM * kWordsPerRow / kWave;
     int lo[kSlots], hi[kSlots];  // 32-bit halves of each lane's words
@@ -1117,6 +1169,266 @@ void ns_product_kernel(NsBatch b) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// Persistent final product with sign + pack from the accumulators, for a
+// launch in which every matrix packs that way (no U output, C % 64 == 0,
+// 16-byte operands). One workgroup per CU walks the tiles vb = blockIdx.x,
+// vb + gridDim.x, ... in the same XCD-contiguous order as the one-tile-per-
+// block kernel. The direct-to-LDS pipeline runs on across tile boundaries:
+// the loads that a tile's last iterations would issue past its own k range
+// fetch the first slices of the workgroup's next tile instead, and the
+// epilogue, which touches no LDS, runs while they are in flight. A tile
+// therefore starts with its pipeline full and its first fragments in
+// registers, and its descriptor is decoded while the previous tile computes.
+// ---------------------------------------------------------------------------
+template <bool BF16>
+struct PackTile {
+    Operand P, Q;   // Q = A (k-contiguous) when tall, else Q = X (mn-contiguous)
+    ProductArgs pa;
+    int tall;
+    int kt_n, rot, iters;
+
+    // Slice read by iteration j (the k loop starts at the tile's own 256 k on
+    // the identity side; iterations past kt_n read zeros).
+    __device__ __forceinline__ int slice(int j) const {
+        const int t = j + rot;
+        return j >= kt_n ? kt_n : (t < kt_n ? t : t - kt_n);
+    }
+
+    __device__ __forceinline__ void decode(const NsBatch &b, int sv, int lt) {
+        using T = typename Elem<BF16>::T;
+        constexpr int BK = Elem<BF16>::BK;
+        const int w = lt / b.tiles_per_worker_all;
+        const int lw = lt - w * b.tiles_per_worker_all;
+        const NsMat M = load_ns_mat_scalar(find_ns_mat(sv, lw));
+        const int t = lw - M.tile_begin;
+        const int R = M.R, C = M.C;
+        tall = R > C;
+        const int r = tall ? C : R;
+        const int tiles_n = (C + kNsProdTileN - 1) / kNsProdTileN;
+        const int ti = t / tiles_n, tj = t - ti * tiles_n;
+        const int64_t n = (int64_t)R * C;
+        const char *x = static_cast<const char *>(M.x) + (int64_t)w * n * (int64_t)sizeof(T);
+        const char *a = static_cast<const char *>(M.a) + (int64_t)w * r * r * (int64_t)sizeof(T);
+        pa.out = nullptr;
+        pa.u_out = nullptr;
+        pa.i8 = nullptr;
+        pa.pk = M.packed + (int64_t)w * ((n + 63) >> 6);
+        pa.R = R;
+        pa.C = C;
+        pa.ti = ti;
+        pa.tj = tj;
+        pa.s = LateScale{load_scale_scalar(b.scales, M.unit_begin + w, 0), b.use_scales};
+        pa.eta = 0.f;
+        if (!tall) {
+            // out[m][n] = sum_k A[m][k] X[k][n]; -3 X on the P side at the output rows
+            P = Operand{a + (int64_t)ti * kNsTileM * r * (int64_t)sizeof(T), r, R - ti * kNsTileM, r, true};
+            Q = Operand{x + (int64_t)tj * kNsProdTileN * (int64_t)sizeof(T), C, C - tj * kNsProdTileN, r, true};
+        } else {
+            // out[m][n] = sum_k X[m][k] A[n][k]; -3 X on the Q side at the output columns
+            P = Operand{x + (int64_t)ti * kNsTileM * C * (int64_t)sizeof(T), C, R - ti * kNsTileM, r, true};
+            Q = Operand{a + (int64_t)tj * kNsProdTileN * r * (int64_t)sizeof(T), r, C - tj * kNsProdTileN, r, true};
+        }
+        constexpr int NID = kNsTileM / BK;  // = kNsProdTileN / BK
+        kt_n = (r + BK - 1) / BK;
+        rot = ((tall ? tj * kNsProdTileN : ti * kNsTileM) / BK) % kt_n;
+        iters = kt_n > NID ? kt_n : NID;
+    }
+
+    // No further tile: an empty buffer, so its loads read zeros.
+    __device__ __forceinline__ void none() {
+        P = Q = Operand{nullptr, 0, 0, 0, true};
+        tall = 0;
+        kt_n = 1;
+        rot = 0;
+        iters = 1;
+    }
+};
+
+// Load i of slice kt of a 256-row operand, its buffer offset computed from
+// the operand's scalar description alone (the same chunk that
+// DmaSlices::setup assigns to the lane), for the next tile's first slices:
+// no per-lane state of that tile is held through the current tile's loop.
+template <bool BF16>
+__device__ __forceinline__ uint32_t walk_offset(const Operand &op, bool kc, int kt, int i, int tid) {
+    using E = Elem<BF16>;
+    constexpr uint32_t sz = sizeof(typename E::T);
+    const int lane = tid & (kWave - 1);
+    const int b = i * ProdLay::kWaves + __builtin_amdgcn_readfirstlane(tid / kWave);
+    int mn, k;
+    if (kc) {
+        mn = b * 16 + (lane >> 2);
+        k = ((lane & 3) ^ ((lane >> 4) & 3)) * E::EPC;
+    } else if (BF16) {
+        k = (b >> 1) * 4 + ((lane & 7) >> 1);
+        mn = ((b & 1) * 8 + (lane >> 3)) * 16 + (lane & 1) * 8;
+    } else {
+        k = b;
+        mn = lane * 4;
+    }
+    const int kk = kt * E::BK + k;
+    const bool ok = mn < op.rows && kk < op.K;
+    const uint32_t ld = (uint32_t)op.ld;
+    const uint32_t o = kc ? ((uint32_t)mn * ld + (uint32_t)kk) * sz : ((uint32_t)kk * ld + (uint32_t)mn) * sz;
+    return ok ? o : kOOB;
+}
+
+template <bool BF16>
+__device__ __forceinline__ v4u32 walk_rsrc(const Operand &op, bool kc) {
+    const uint64_t base = reinterpret_cast<uint64_t>(op.base);
+    const int64_t ext = kc ? operand_extent<BF16, true>(op) : operand_extent<BF16, false>(op);
+    return v4u32{(uint32_t)base, (uint32_t)(base >> 32) & 0xffffu, (uint32_t)ext, 0x00020000u};
+}
+
+// One tile of the walk: the k loop of cur (its loads from lp / lq, set up
+// for cur), whose loads past its last iteration fetch nxt's first slices.
+// Every tile's iteration count is a multiple of the stage count S and at
+// least NID + S (the launcher checks), so iteration j of any tile uses LDS
+// stage j % S, nxt's slice s lands in stage s, and the last S iterations
+// (the tail, unrolled) are the only ones that load for nxt. The first
+// fragments are read at the tile's start (slice 0 has landed and the
+// barrier that handed it over has passed).
+template <bool BF16, bool QKC>
+__device__ __forceinline__ void pack_tile_kloop(const PackTile<BF16> &cur, const PackTile<BF16> &nxt,
+                                                const DmaSlices<BF16, 256, ProdLay::kWaves> &lp,
+                                                const DmaSlices<BF16, 256, ProdLay::kWaves> &lq, char *smem,
+                                                f32x16_t (&acc)[kFM][kFN], int tid) {
+    using L = ProdLay;
+    using E = Elem<BF16>;
+    constexpr int TN = L::kTileN, S = L::kStages;
+    constexpr int SIDE = QKC ? ID_Q : ID_P;
+    const int wid = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int wm0 = L::m0(wid), wn0 = L::n0(wid);
+    const int w0 = SIDE == ID_Q ? wn0 : wm0;
+#pragma unroll
+    for (int f = 0; f < kFM; ++f)
+#pragma unroll
+        for (int gg = 0; gg < kFN; ++gg)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[f][gg][r] = 0.f;
+    constexpr int PL = L::kPLoads, QL = L::kQLoads, NLD = PL + QL;
+    const uint32_t lds0 = lds_addr(smem);
+    Frags<BF16> fa, fb;
+    read_frags<BF16, true, QKC, TN>(fa, smem, smem + L::kPBytes, wm0, wn0, 0, tid);
+    constexpr int NID = (SIDE == ID_Q ? TN : L::kTileM) / E::BK;
+    const int iters = cur.iters;
+    constexpr int kSteps = kFM * kFN, kFrag = kFM + kFN;
+    constexpr int eQ = kSteps / QL, eP = kSteps / PL;
+    static_assert(kFrag <= kSteps && eQ * QL == kSteps && eP * PL == kSteps, "interleave");
+    static_assert(NID % S == 0, "identity iterations fill whole stage rounds");
+    // Iteration j: as in tile_mainloop, the first half's MFMAs (fa) run with
+    // the reads of the second half (fb) and the Q loads of walk iteration
+    // j + S - 1; after the barrier that hands over the next slice, the second
+    // half's MFMAs (fb) run with the reads of the next slice's first half and
+    // the P loads of walk iteration j + S. Tail iteration TL (j = iters - S +
+    // TL) loads nxt's slice TL - 1 (Q part, TL >= 1) and slice TL (P part).
+    auto iteration = [&](int j, auto jid, auto tl) {
+        constexpr int JID = decltype(jid)::value, TL = decltype(tl)::value;
+        const int js = TL >= 0 ? TL : j % S;  // j % S
+        const char *cb = smem + js * L::kStageBytes;
+        const uint32_t late_dst = lds0 + ((js + S - 1) % S) * L::kStageBytes + L::kPBytes;
+        const int late = TL >= 1 ? nxt.slice(TL - 1) : cur.slice(j + S - 1);
+#pragma unroll
+        for (int i = 0; i < kSteps; ++i) {
+            mma_step<BF16>(fa, acc, i);
+            if (i < kFrag) read_frag<BF16, true, QKC, TN>(fb, cb, cb + L::kPBytes, wm0, wn0, 1, i, tid);
+            if (i % eQ == eQ - 1) {
+                if constexpr (TL >= 1)
+                    lq.issue_at(late_dst, i / eQ, walk_offset<BF16>(nxt.Q, QKC, late, i / eQ, tid),
+                                walk_rsrc<BF16>(nxt.Q, QKC));
+                else
+                    lq.issue_one(late, late_dst, i / eQ);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if constexpr (JID >= 0) mma_identity_at<BF16, SIDE, JID>(fa, acc, w0, 0, tid);
+        wait_vm_lgkm0<(S - 2) * NLD>();
+        lds_barrier();
+        const char *nb = smem + ((js + 1) % S) * L::kStageBytes;
+        const uint32_t dst = lds0 + js * L::kStageBytes;
+        const int refill = TL >= 0 ? nxt.slice(TL) : cur.slice(j + S);
+#pragma unroll
+        for (int i = 0; i < kSteps; ++i) {
+            mma_step<BF16>(fb, acc, i);
+            if (i < kFrag) read_frag<BF16, true, QKC, TN>(fa, nb, nb + L::kPBytes, wm0, wn0, 0, i, tid);
+            if (i % eP == eP - 1) {
+                if constexpr (TL >= 0)
+                    lp.issue_at(dst, i / eP, walk_offset<BF16>(nxt.P, true, refill, i / eP, tid),
+                                walk_rsrc<BF16>(nxt.P, true));
+                else
+                    lp.issue_one(refill, dst, i / eP);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if constexpr (JID >= 0) mma_identity_at<BF16, SIDE, JID>(fb, acc, w0, 1, tid);
+    };
+    using NoTail = std::integral_constant<int, -1>;
+    static_for(std::make_integer_sequence<int, NID>{},
+               [&](auto jid) { iteration(decltype(jid)::value, jid, NoTail{}); });
+    for (int j = NID; j < iters - S; ++j) iteration(j, std::integral_constant<int, -1>{}, NoTail{});
+    static_for(std::make_integer_sequence<int, S>{},
+               [&](auto tl) { iteration(iters - S + decltype(tl)::value, NoTail{}, tl); });
+}
+
+// QKC: every matrix of the launch is tall (true) or wide (false).
+template <bool BF16, bool QKC>
+__global__ __launch_bounds__(ProdLay::kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void ns_product_pack_kernel(NsBatch b) {
+    using L = ProdLay;
+    constexpr int S = L::kStages, PL = L::kPLoads, QL = L::kQLoads, NLD = PL + QL;
+    __shared__ __attribute__((aligned(16))) char smem[L::kLdsBytes];
+    // The matrix start table, one entry per lane, kept in LDS for the whole
+    // walk (read back per tile: a register copy would be spilled, and its
+    // reload would wait for every load in flight).
+    __shared__ int starts[kWave];
+    const int sv = ns_start_of_lane();
+    if (threadIdx.x < kWave) starts[threadIdx.x] = sv;
+    const int wid0 = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
+    const int total = b.total_tiles, G = gridDim.x;
+    int vb = blockIdx.x;
+    PackTile<BF16> cur, nxt;
+    DmaSlices<BF16, 256, L::kWaves> lp, lq;
+    cur.decode(b, sv, xcd_remap(vb, total));
+    lp.template setup<true>(cur.P);
+    lq.template setup<QKC>(cur.Q);
+    // The first tile fills the pipeline itself: slices 0 .. S - 2 and the P
+    // part of slice S - 1.
+    const uint32_t lds0 = lds_addr(smem);
+#pragma unroll
+    for (int st = 0; st < S - 1; ++st) {
+        lp.issue(cur.slice(st), lds0 + st * L::kStageBytes);
+        lq.issue(cur.slice(st), lds0 + st * L::kStageBytes + L::kPBytes);
+    }
+    lp.issue(cur.slice(S - 1), lds0 + (S - 1) * L::kStageBytes);
+    wait_vm_lgkm0<(S - 2) * NLD + PL>();  // slice 0 landed
+    lds_barrier();
+    f32x16_t acc[kFM][kFN];
+    for (;;) {
+        // The thread index, produced afresh for each tile where the compiler
+        // cannot hoist it (the lane from v_mbcnt in an asm statement, the
+        // wave from a scalar register), so that lane arithmetic (identity
+        // fragments, LDS addresses) is redone per tile instead of held in
+        // registers across the whole walk.
+        int lane;
+        asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane));
+        const int tid = wid0 * kWave + lane;
+        const int vn = vb + G;
+        const bool more = vn < total;
+        if (more)
+            nxt.decode(b, starts[lane], xcd_remap(vn, total));
+        else
+            nxt.none();
+        pack_tile_kloop<BF16, QKC>(cur, nxt, lp, lq, smem, acc, tid);
+        pack_from_registers(cur.pa, acc, tid);
+        if (!more) break;
+        vb = vn;
+        cur = nxt;
+        lp.template setup<true>(cur.P, tid);
+        lq.template setup<QKC>(cur.Q, tid);
+    }
+    wait_vm_lgkm0<0>();  // the zero-fill loads past the last tile write LDS too
+}
+
 }  // namespace
 
 void launch_ns_gram(const NsBatch &b, bool ns_bf16, hipStream_t s) {
@@ -1142,6 +1454,14 @@ void launch_ns_product(const NsBatch &b, bool ns_bf16, NsEpilogue epi, hipStream
         else SM_PROD(false, EPI_WUPD);
     }
 #undef SM_PROD
+}
+
+void launch_ns_product_pack(const NsBatch &b, bool tall, int grid_blocks, hipStream_t s) {
+    dim3 grid(grid_blocks), block(ProdLay::kThreads);
+    if (tall)
+        hipLaunchKernelGGL((ns_product_pack_kernel<true, true>), grid, block, 0, s, b);
+    else
+        hipLaunchKernelGGL((ns_product_pack_kernel<true, false>), grid, block, 0, s, b);
 }
 
 }  // namespace sm

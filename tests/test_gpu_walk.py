@@ -1,0 +1,133 @@
+"""The final product's persistent tile walk (bf16, signs packed from the
+accumulators, no U output): one workgroup per CU walks several tiles, and the
+loads of each tile's last iterations fetch the next tile's first slices.
+
+Its packed bits must equal, bit for bit, those of the one-tile-per-block
+kernel that also stores U (same operands, same k order, same accumulators),
+for batches with several tiles per workgroup: wide and tall matrices (two
+launches), ragged tiles (R or C not a multiple of 256), the shortest k loop
+the walk accepts (min(R, C) = 384: 12 slices of 32), and matrices the walk
+does not take in the same call. The vote and W follow from the bits and must
+match too; U itself is checked against the oracle's k = 1 formula on sampled
+entries, and the walk's bits against the oracle's signs there."""
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sign_muon_step_amd as sm
+import synthetic
+from gpu_util import DEV, announce, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+POOL = ThreadPoolExecutor(max_workers=8)
+
+# walk-eligible (C % 64 == 0, min(R, C) % 8 == 0, ceil(min(R, C) / 32) a
+# multiple of 4 and >= 12), wide and tall, ragged and regular
+WALK = [(640, 1216), (1216, 640), (384, 1024), (1024, 384), (768, 3072), (3072, 768), (768, 768)]
+# not walk-eligible: k loop too short (r = 256), r % 32 leaves a slice count
+# that is not a multiple of 4 (r = 520), C % 64 != 0 (no fused pack at all)
+PLAIN = [(256, 1024), (520, 1088), (300, 640)]
+
+
+@pytest.fixture(autouse=True)
+def _name_the_case(request):
+    announce(f"[gpu-test] {request.node.nodeid}")
+    yield
+    torch.cuda.synchronize()
+
+
+def build(shapes, mw, seed, polar):
+    def grad(jm):
+        j, m = jm
+        return synthetic.random_matrix(seed + 100 * j + m, shapes[j], 1e-3)
+
+    mats, host = [], []
+    for j, (R, C) in enumerate(shapes):
+        g = np.stack(list(POOL.map(grad, [(j, m) for m in range(mw)])))
+        w0 = synthetic.random_matrix(seed + 100 * j + 99, (R, C), 0.02)
+        host.append((g, w0))
+        mats.append(sm.Matrix(
+            grad=to_dev(g), momentum=torch.zeros((mw, R, C), dtype=torch.bfloat16, device=DEV),
+            packed=torch.zeros((mw, sm.signmuon_packed_words(R * C)), dtype=torch.int64, device=DEV),
+            weight=to_dev(w0),
+            polar_out=torch.zeros((mw, R, C), dtype=torch.float32, device=DEV) if polar else None,
+            vote_out=torch.zeros((R, C), dtype=torch.int8, device=DEV)))
+    return mats, host
+
+
+@pytest.mark.parametrize("mw", [16, 5])
+def test_walk_bits_equal_stored_u_bits(mw):
+    shapes = WALK + PLAIN
+    p = sm.Params(workers=mw, beta=0.9, eta=1e-3, ns_iters=1, mom_dtype=sm.BF16, ns_dtype=sm.BF16)
+    walk, host = build(shapes, mw, 7000, polar=False)
+    ref, _ = build(shapes, mw, 7000, polar=True)
+    announce(f"  {mw} workers, {len(shapes)} matrices: walk run")
+    sm.signmuon_step(walk, p, sm.workspace_tensor(walk, p, DEV))
+    announce("  reference run (U stored: one tile per block)")
+    sm.signmuon_step(ref, p, sm.workspace_tensor(ref, p, DEV))
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(mw)
+    for j, (a, b) in enumerate(zip(walk, ref)):
+        R, C = shapes[j]
+        np.testing.assert_array_equal(to_host(a.momentum), to_host(b.momentum), err_msg=f"M {shapes[j]}")
+        pw, pr = to_host(a.packed), to_host(b.packed)
+        np.testing.assert_array_equal(pw, pr, err_msg=f"packed {shapes[j]}")
+        np.testing.assert_array_equal(to_host(a.vote_out), to_host(b.vote_out), err_msg=f"vote {shapes[j]}")
+        np.testing.assert_array_equal(to_host(a.weight), to_host(b.weight), err_msg=f"W {shapes[j]}")
+        # the stored U (reference run) against the oracle at sampled entries,
+        # and the walk's bits against the oracle's signs there
+        u = to_host(b.polar_out)
+        for w in (0, mw - 1):
+            m_ref = np.zeros((R, C), np.uint16)
+            oracle.momentum(host[j][0][w], m_ref, 0.9)
+            _, x0 = oracle.normalise(m_ref)
+            ri, ci = rng.integers(0, R, 48), rng.integers(0, C, 48)
+            want = oracle.ns1_entries(x0, oracle.BF16, ri, ci)
+            got = u[w][ri, ci].astype(np.float64)
+            rms = np.sqrt(np.mean(u[w].astype(np.float64) ** 2))
+            dev_rel = np.abs(got - want).max() / rms
+            flat = ri.astype(np.int64) * C + ci
+            bits = (pw[w].view(np.uint64)[flat >> 6] >> (flat & 63).astype(np.uint64)) & 1
+            clear = np.abs(want) >= 5e-2 * rms  # far from zero: the sign is not in doubt
+            agree = np.mean((bits.astype(bool) == (want >= 0))[clear])
+            announce(f"  {shapes[j]} worker {w}: max|dU|/rms(U) = {dev_rel:.2e}, "
+                     f"walk sign agreement {agree:.4f} on {int(clear.sum())} samples")
+            assert dev_rel <= 2e-2
+            assert agree == 1.0
+
+
+def test_walk_on_gpt2_small_matches_plain_kernel_over_two_steps():
+    """The benchmarked batch itself (48 GPT-2 small matrices, 8 workers): two
+    steps, every packed word, the vote and W equal to the stored-U run's."""
+    wl = synthetic.WORKLOADS["gpt2s_mw8_k1"]
+    mw = wl.workers
+    p = sm.Params(workers=mw, beta=wl.beta, eta=wl.eta, ns_iters=1, mom_dtype=sm.BF16, ns_dtype=sm.BF16)
+
+    def state(polar):
+        return [sm.Matrix(
+            grad=torch.empty((mw, R, C), dtype=torch.float32, device=DEV),
+            momentum=torch.zeros((mw, R, C), dtype=torch.bfloat16, device=DEV),
+            packed=torch.zeros((mw, sm.signmuon_packed_words(R * C)), dtype=torch.int64, device=DEV),
+            weight=to_dev(synthetic.initial_weight(wl, j)),
+            polar_out=torch.zeros((mw, R, C), dtype=torch.float32, device=DEV) if polar else None,
+            vote_out=torch.zeros((R, C), dtype=torch.int8, device=DEV)) for j, (R, C) in enumerate(wl.shapes)]
+
+    walk, ref = state(False), state(True)
+    ws_w, ws_r = sm.workspace_tensor(walk, p, DEV), sm.workspace_tensor(ref, p, DEV)
+    for t in range(2):
+        for j in range(len(wl.shapes)):
+            g = torch.from_numpy(synthetic.gradients(wl, j, t)).to(DEV)
+            walk[j].grad.copy_(g)
+            ref[j].grad.copy_(g)
+        announce(f"  step {t}")
+        sm.signmuon_step(walk, p, ws_w)
+        sm.signmuon_step(ref, p, ws_r)
+        torch.cuda.synchronize()
+        for j, (a, b) in enumerate(zip(walk, ref)):
+            np.testing.assert_array_equal(to_host(a.packed), to_host(b.packed), err_msg=f"packed {j} t {t}")
+            np.testing.assert_array_equal(to_host(a.vote_out), to_host(b.vote_out), err_msg=f"vote {j} t {t}")
+            np.testing.assert_array_equal(to_host(a.weight), to_host(b.weight), err_msg=f"W {j} t {t}")
