@@ -285,11 +285,6 @@ def cpu_baseline(wl, js=(0, 1, 2, 3)):
                       f"on this host's CPU"}
 
 
-KIND_SYMBOL = {"momentum": "momentum_kernel", "scales": "finalize_scales_kernel",
-               "ns_gram": "ns_gram_kernel", "ns_product": "ns_product_kernel",
-               "sign_pack": "sign_pack_kernel", "vote_update": "vote_update_kernel"}
-
-
 def library_source_hash():
     """sha256 over the library's kernel and host sources (csrc/, sorted)."""
     import hashlib
@@ -304,11 +299,11 @@ def library_source_hash():
 
 
 def counter_traffic(wl, kind):
-    """HBM bytes per launch of kernel `kind` from the committed rocprofv3
-    counter summary of this workload (FETCH_SIZE and WRITE_SIZE per dispatch,
-    each scaled by the factor a plain copy kernel gives the same counter).
-    None when there is no summary or the library sources changed since the
-    counters were taken."""
+    """HBM bytes per step of kernel kind `kind` (all its launches in a step)
+    from the committed rocprofv3 counter summary of this workload (FETCH_SIZE
+    and WRITE_SIZE, each scaled by the factor a plain copy kernel gives the
+    same counter). None when there is no summary or the library sources
+    changed since the counters were taken."""
     path = os.path.join(ROOT, "profiles", f"hbm_traffic_{wl.name}.md")
     if not os.path.exists(path):
         return None
@@ -318,14 +313,13 @@ def counter_traffic(wl, kind):
             parts = line.split()
             if len(parts) == 2 and parts[0] in ("source_sha256", "fetch_factor", "write_factor"):
                 fields[parts[0]] = parts[1]
-            elif len(parts) == 4 and parts[0] == "kernel":
+            elif len(parts) == 4 and parts[0] == "kind":
                 rows[parts[1]] = (float(parts[2]), float(parts[3]))
     if fields.get("source_sha256") != library_source_hash():
         return None
-    sym = KIND_SYMBOL.get(kind)
-    if sym not in rows:
+    if kind not in rows:
         return None
-    fetch_kib, write_kib = rows[sym]
+    fetch_kib, write_kib = rows[kind]
     return int(1024 * (fetch_kib * float(fields["fetch_factor"]) +
                        write_kib * float(fields["write_factor"])))
 
@@ -431,7 +425,7 @@ def main():
     roofline = {"bound": d["bound"], "achieved": d["achieved"],
                 "peak": PEAK_HBM_GBS if d["bound"] == "hbm" else mfma_peak, "unit": d["unit"],
                 "frac": d["frac"], "traffic": counter_traffic(wl, dominant), "kernel": dominant,
-                "launches_per_step": launch_count.get(dominant, 0)}
+                "launches_per_step": launch_count.get(dominant, 0), "per": "step"}
     ns_ms = per_kind_ms.get("ns_gram", 0.0) + per_kind_ms.get("ns_product", 0.0)
     ns_flops = work["ns_gram"][1] + work["ns_product"][1]
     ns_util = 100.0 * ns_flops / (ns_ms * 1e-3) / (mfma_peak * 1e12) if ns_ms > 0 else None
