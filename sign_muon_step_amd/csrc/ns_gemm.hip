@@ -57,6 +57,18 @@ constexpr int kWaveM = 128, kWaveN = 64;
 constexpr int kFM = kWaveM / 32, kFN = kWaveN / 32;
 constexpr int kRowBytes = 64;  // LDS bytes of one operand row per k-slice
 
+// Where a helper gets the thread's index: HwTid reads threadIdx.x where it is
+// used; GivenTid carries a value the caller produced (the persistent product
+// makes it afresh per tile, so that the compiler does not keep lane
+// arithmetic in registers across its whole walk).
+struct HwTid {
+    __device__ unsigned operator()() const { return threadIdx.x; }
+};
+struct GivenTid {
+    unsigned v;
+    __device__ unsigned operator()() const { return v; }
+};
+
 // Workgroup layout of a 256 x TN output tile: two rows of TN / kWaveN waves;
 // each LDS stage holds one k-slice of P (256 rows) then of Q (TN rows).
 template <int TN>
@@ -217,12 +229,10 @@ struct DmaSlices {
     int K;
     int wid;
 
-    // tid: the thread's index in the workgroup (passed in by a caller that
-    // keeps the compiler from hoisting lane arithmetic out of its loops).
-    template <bool KC>
-    __device__ __forceinline__ void setup(const Operand &op, int tid = (int)threadIdx.x) {
-        const int lane = tid & (kWave - 1);
-        wid = __builtin_amdgcn_readfirstlane(tid / kWave);
+    template <bool KC, class Tid = HwTid>
+    __device__ __forceinline__ void setup(const Operand &op, Tid tid = Tid{}) {
+        const int lane = tid() & (kWave - 1);
+        wid = __builtin_amdgcn_readfirstlane(tid() / kWave);
         // Buffer descriptor: 48-bit base, stride 0, num_records = extent in
         // bytes, raw 32-bit dword format (0x00020000 on this family).
         const uint64_t base = reinterpret_cast<uint64_t>(op.base);
@@ -336,9 +346,9 @@ struct SlowLoader {
 
 // MFMA fragments of one 32-row (m or n) block for k16 step kk (bf16): lane l
 // holds row (l & 31) and k = 16 kk + 8 (l / 32) .. + 7.
-template <bool KC, int ROWS>
-__device__ __forceinline__ bf16x8_t frag_bf16(const char *lds, int row0, int kk, int tid = (int)threadIdx.x) {
-    const int lane = tid & (kWave - 1);
+template <bool KC, int ROWS, class Tid = HwTid>
+__device__ __forceinline__ bf16x8_t frag_bf16(const char *lds, int row0, int kk, Tid tid = Tid{}) {
+    const int lane = tid() & (kWave - 1);
     if (KC) {
         const uint4 v = *reinterpret_cast<const uint4 *>(lds + kl_off(row0 + (lane & 31), 2 * kk + (lane >> 5)));
         return __builtin_bit_cast(bf16x8_t, v);
@@ -361,9 +371,9 @@ __device__ __forceinline__ bf16x8_t frag_bf16(const char *lds, int row0, int kk,
 
 // fp32 fragments for chunk pair cp: lane l holds 4 consecutive k
 // (k = 8 cp + 4 (l / 32) .. + 3) of row (l & 31); MFMA step s uses element s.
-template <bool KC, int ROWS>
-__device__ __forceinline__ f32x4_t frag_f32(const char *lds, int row0, int cp, int tid = (int)threadIdx.x) {
-    const int lane = tid & (kWave - 1);
+template <bool KC, int ROWS, class Tid = HwTid>
+__device__ __forceinline__ f32x4_t frag_f32(const char *lds, int row0, int cp, Tid tid = Tid{}) {
+    const int lane = tid() & (kWave - 1);
     if (KC) return *reinterpret_cast<const f32x4_t *>(lds + kl_off(row0 + (lane & 31), 2 * cp + (lane >> 5)));
     const int mn = row0 + (lane & 31), k = 8 * cp + 4 * (lane >> 5);
     f32x4_t v;
@@ -380,27 +390,27 @@ template <> struct Frags<false> { f32x4_t p[kFM], q[kFN]; };
 
 // Fragment j (0 .. kFM + kFN - 1) of one half: j < kFM is P block j, the
 // rest Q block j - kFM.
-template <bool BF16, bool PKC, bool QKC, int TN>
+template <bool BF16, bool PKC, bool QKC, int TN, class Tid = HwTid>
 __device__ __forceinline__ void read_frag(Frags<BF16> &fr, const char *lds_p, const char *lds_q,
-                                          int wm0, int wn0, int half, int j, int tid = (int)threadIdx.x) {
+                                          int wm0, int wn0, int half, int j, Tid tid = Tid{}) {
     if constexpr (BF16) {
         if (j < kFM)
-            fr.p[j] = frag_bf16<PKC, 256>(lds_p, wm0 + j * 32, half, tid);
+            fr.p[j] = frag_bf16<PKC, 256, Tid>(lds_p, wm0 + j * 32, half, tid);
         else
-            fr.q[j - kFM] = frag_bf16<QKC, TN>(lds_q, wn0 + (j - kFM) * 32, half, tid);
+            fr.q[j - kFM] = frag_bf16<QKC, TN, Tid>(lds_q, wn0 + (j - kFM) * 32, half, tid);
     } else {
         if (j < kFM)
-            fr.p[j] = frag_f32<PKC, 256>(lds_p, wm0 + j * 32, half, tid);
+            fr.p[j] = frag_f32<PKC, 256, Tid>(lds_p, wm0 + j * 32, half, tid);
         else
-            fr.q[j - kFM] = frag_f32<QKC, TN>(lds_q, wn0 + (j - kFM) * 32, half, tid);
+            fr.q[j - kFM] = frag_f32<QKC, TN, Tid>(lds_q, wn0 + (j - kFM) * 32, half, tid);
     }
 }
 
-template <bool BF16, bool PKC, bool QKC, int TN>
+template <bool BF16, bool PKC, bool QKC, int TN, class Tid = HwTid>
 __device__ __forceinline__ void read_frags(Frags<BF16> &fr, const char *lds_p, const char *lds_q,
-                                           int wm0, int wn0, int half, int tid = (int)threadIdx.x) {
+                                           int wm0, int wn0, int half, Tid tid = Tid{}) {
 #pragma unroll
-    for (int j = 0; j < kFM + kFN; ++j) read_frag<BF16, PKC, QKC, TN>(fr, lds_p, lds_q, wm0, wn0, half, j, tid);
+    for (int j = 0; j < kFM + kFN; ++j) read_frag<BF16, PKC, QKC, TN, Tid>(fr, lds_p, lds_q, wm0, wn0, half, j, tid);
 }
 
 // acc[f][g]: 32 x 32 block (f along m, g along n) of the wave's tile.
@@ -449,8 +459,9 @@ enum IdSide { ID_NONE = 0, ID_P = 1, ID_Q = 2 };
 
 // One-hot -3 fragment: lane l, k index kl (within the 32-row block) holds -3
 // where kl equals the lane's row (l & 31).
-__device__ __forceinline__ bf16x8_t id_frag_bf16(int roff, int kk, int tid = (int)threadIdx.x) {
-    const int lane = tid & (kWave - 1);
+template <class Tid = HwTid>
+__device__ __forceinline__ bf16x8_t id_frag_bf16(int roff, int kk, Tid tid = Tid{}) {
+    const int lane = tid() & (kWave - 1);
     const int j = (lane & 31) - roff - 16 * kk - 8 * (lane >> 5);  // element holding -3
     uint32_t w[4];
 #pragma unroll
@@ -459,8 +470,9 @@ __device__ __forceinline__ bf16x8_t id_frag_bf16(int roff, int kk, int tid = (in
     return __builtin_bit_cast(bf16x8_t, make_uint4(w[0], w[1], w[2], w[3]));
 }
 
-__device__ __forceinline__ f32x4_t id_frag_f32(int roff, int cp, int tid = (int)threadIdx.x) {
-    const int lane = tid & (kWave - 1);
+template <class Tid = HwTid>
+__device__ __forceinline__ f32x4_t id_frag_f32(int roff, int cp, Tid tid = Tid{}) {
+    const int lane = tid() & (kWave - 1);
     const int j = (lane & 31) - roff - 8 * cp - 4 * (lane >> 5);
     f32x4_t v;
 #pragma unroll
@@ -511,9 +523,9 @@ __device__ __forceinline__ void mma_identity(const Frags<BF16> &fr, f32x16_t (&a
 // the tile, i.e. rows (ID_P) or columns (ID_Q) w0 + 32 b + roff .. of the
 // wave's extent WS on that side when J * BK lies in [w0, w0 + WS); other
 // waves multiply a zero fragment, so the sequence has no branch.
-template <bool BF16, int SIDE, int J>
+template <bool BF16, int SIDE, int J, class Tid = HwTid>
 __device__ __forceinline__ void mma_identity_at(const Frags<BF16> &fr, f32x16_t (&acc)[kFM][kFN], int w0,
-                                                int half, int tid = (int)threadIdx.x) {
+                                                int half, Tid tid = Tid{}) {
     constexpr int RS = Elem<BF16>::BK;
     constexpr int WS = SIDE == ID_Q ? kWaveN : kWaveM;
     constexpr int NO = SIDE == ID_Q ? kFM : kFN;
@@ -521,7 +533,7 @@ __device__ __forceinline__ void mma_identity_at(const Frags<BF16> &fr, f32x16_t 
     constexpr int b = (kb % WS) / 32, roff = kb % 32;
     const bool active = kb / WS == w0 / WS;
     if constexpr (BF16) {
-        const bf16x8_t one = id_frag_bf16(roff, half, tid);
+        const bf16x8_t one = id_frag_bf16<Tid>(roff, half, tid);
         bf16x8_t id;
 #pragma unroll
         for (int e = 0; e < 8; ++e) id[e] = active ? one[e] : (__bf16)0.0f;
@@ -533,7 +545,7 @@ __device__ __forceinline__ void mma_identity_at(const Frags<BF16> &fr, f32x16_t 
                 acc[o][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr.p[o], id, acc[o][b], 0, 0, 0);
         }
     } else {
-        const f32x4_t one = id_frag_f32(roff, half, tid);
+        const f32x4_t one = id_frag_f32<Tid>(roff, half, tid);
         f32x4_t id;
 #pragma unroll
         for (int st = 0; st < 4; ++st) id[st] = active ? one[st] : 0.0f;
@@ -861,7 +873,9 @@ __device__ __forceinline__ void store32(void *p, int64_t idx, const float (&v)[3
 // LDS area, then writes the rows (4 columns per lane) and, above the
 // diagonal, the mirrored tile: a lane reads one column of the staged rows,
 // which is 32 consecutive entries of a mirrored row, and stores them as one
-// run.
+// run. (Storing the mirror straight from the accumulators, 4 entries of a
+// mirrored row per lane, was slower: each store instruction then touches 32
+// rows.)
 template <bool BF16, bool FAST>
 __device__ __forceinline__ void gram_epilogue(f32x16_t (&acc)[kFM][kFN], char *smem, int ti, int tj,
                                               int r, LateScale sc, void *a) {
@@ -1055,10 +1069,11 @@ __device__ __forceinline__ int write_lane(int dst, uint32_t val, int lane) {
     return dst;
 }
 
+template <class Tid = HwTid>
 __device__ __forceinline__ void pack_from_registers(const ProductArgs &pa, const f32x16_t (&acc)[kFM][kFN],
-                                                    int tid = (int)threadIdx.x) {
+                                                    Tid tid = Tid{}) {
     const float gamma = -0.5f * pa.s.get();
-    const int lane = tid & (kWave - 1), wid = tid / kWave;
+    const int lane = tid() & (kWave - 1), wid = tid() / kWave;
     const int m0 = pa.ti * kNsTileM + ProdLay::m0(wid), n0 = pa.tj * kNsProdTileN + ProdLay::n0(wid);
     constexpr int kSlots = kWaveM * kWordsPerRow / kWave;
     int lo[kSlots], hi[kSlots];  // 32-bit halves of each lane's words
@@ -1250,11 +1265,11 @@ struct PackTile {
 // DmaSlices::setup assigns to the lane), for the next tile's first slices:
 // no per-lane state of that tile is held through the current tile's loop.
 template <bool BF16>
-__device__ __forceinline__ uint32_t walk_offset(const Operand &op, bool kc, int kt, int i, int tid) {
+__device__ __forceinline__ uint32_t walk_offset(const Operand &op, bool kc, int kt, int i, GivenTid tid) {
     using E = Elem<BF16>;
     constexpr uint32_t sz = sizeof(typename E::T);
-    const int lane = tid & (kWave - 1);
-    const int b = i * ProdLay::kWaves + __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int lane = tid() & (kWave - 1);
+    const int b = i * ProdLay::kWaves + __builtin_amdgcn_readfirstlane(tid() / kWave);
     int mn, k;
     if (kc) {
         mn = b * 16 + (lane >> 2);
@@ -1292,12 +1307,12 @@ template <bool BF16, bool QKC>
 __device__ __forceinline__ void pack_tile_kloop(const PackTile<BF16> &cur, const PackTile<BF16> &nxt,
                                                 const DmaSlices<BF16, 256, ProdLay::kWaves> &lp,
                                                 const DmaSlices<BF16, 256, ProdLay::kWaves> &lq, char *smem,
-                                                f32x16_t (&acc)[kFM][kFN], int tid) {
+                                                f32x16_t (&acc)[kFM][kFN], GivenTid tid) {
     using L = ProdLay;
     using E = Elem<BF16>;
     constexpr int TN = L::kTileN, S = L::kStages;
     constexpr int SIDE = QKC ? ID_Q : ID_P;
-    const int wid = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int wid = __builtin_amdgcn_readfirstlane(tid() / kWave);
     const int wm0 = L::m0(wid), wn0 = L::n0(wid);
     const int w0 = SIDE == ID_Q ? wn0 : wm0;
 #pragma unroll
@@ -1309,7 +1324,7 @@ __device__ __forceinline__ void pack_tile_kloop(const PackTile<BF16> &cur, const
     constexpr int PL = L::kPLoads, QL = L::kQLoads, NLD = PL + QL;
     const uint32_t lds0 = lds_addr(smem);
     Frags<BF16> fa, fb;
-    read_frags<BF16, true, QKC, TN>(fa, smem, smem + L::kPBytes, wm0, wn0, 0, tid);
+    read_frags<BF16, true, QKC, TN, GivenTid>(fa, smem, smem + L::kPBytes, wm0, wn0, 0, tid);
     constexpr int NID = (SIDE == ID_Q ? TN : L::kTileM) / E::BK;
     const int iters = cur.iters;
     constexpr int kSteps = kFM * kFN, kFrag = kFM + kFN;
@@ -1331,7 +1346,7 @@ __device__ __forceinline__ void pack_tile_kloop(const PackTile<BF16> &cur, const
 #pragma unroll
         for (int i = 0; i < kSteps; ++i) {
             mma_step<BF16>(fa, acc, i);
-            if (i < kFrag) read_frag<BF16, true, QKC, TN>(fb, cb, cb + L::kPBytes, wm0, wn0, 1, i, tid);
+            if (i < kFrag) read_frag<BF16, true, QKC, TN, GivenTid>(fb, cb, cb + L::kPBytes, wm0, wn0, 1, i, tid);
             if (i % eQ == eQ - 1) {
                 if constexpr (TL >= 1)
                     lq.issue_at(late_dst, i / eQ, walk_offset<BF16>(nxt.Q, QKC, late, i / eQ, tid),
@@ -1341,7 +1356,7 @@ __device__ __forceinline__ void pack_tile_kloop(const PackTile<BF16> &cur, const
             }
             __builtin_amdgcn_sched_barrier(0);
         }
-        if constexpr (JID >= 0) mma_identity_at<BF16, SIDE, JID>(fa, acc, w0, 0, tid);
+        if constexpr (JID >= 0) mma_identity_at<BF16, SIDE, JID, GivenTid>(fa, acc, w0, 0, tid);
         wait_vm_lgkm0<(S - 2) * NLD>();
         lds_barrier();
         const char *nb = smem + ((js + 1) % S) * L::kStageBytes;
@@ -1350,7 +1365,7 @@ __device__ __forceinline__ void pack_tile_kloop(const PackTile<BF16> &cur, const
 #pragma unroll
         for (int i = 0; i < kSteps; ++i) {
             mma_step<BF16>(fb, acc, i);
-            if (i < kFrag) read_frag<BF16, true, QKC, TN>(fa, nb, nb + L::kPBytes, wm0, wn0, 0, i, tid);
+            if (i < kFrag) read_frag<BF16, true, QKC, TN, GivenTid>(fa, nb, nb + L::kPBytes, wm0, wn0, 0, i, tid);
             if (i % eP == eP - 1) {
                 if constexpr (TL >= 0)
                     lp.issue_at(dst, i / eP, walk_offset<BF16>(nxt.P, true, refill, i / eP, tid),
@@ -1360,7 +1375,7 @@ __device__ __forceinline__ void pack_tile_kloop(const PackTile<BF16> &cur, const
             }
             __builtin_amdgcn_sched_barrier(0);
         }
-        if constexpr (JID >= 0) mma_identity_at<BF16, SIDE, JID>(fb, acc, w0, 1, tid);
+        if constexpr (JID >= 0) mma_identity_at<BF16, SIDE, JID, GivenTid>(fb, acc, w0, 1, tid);
     };
     using NoTail = std::integral_constant<int, -1>;
     static_for(std::make_integer_sequence<int, NID>{},
@@ -1411,7 +1426,7 @@ void ns_product_pack_kernel(NsBatch b) {
         // registers across the whole walk.
         int lane;
         asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane));
-        const int tid = wid0 * kWave + lane;
+        const GivenTid tid{(unsigned)(wid0 * kWave + lane)};
         const int vn = vb + G;
         const bool more = vn < total;
         if (more)
@@ -1419,12 +1434,12 @@ void ns_product_pack_kernel(NsBatch b) {
         else
             nxt.none();
         pack_tile_kloop<BF16, QKC>(cur, nxt, lp, lq, smem, acc, tid);
-        pack_from_registers(cur.pa, acc, tid);
+        pack_from_registers<GivenTid>(cur.pa, acc, tid);
         if (!more) break;
         vb = vn;
         cur = nxt;
-        lp.template setup<true>(cur.P, tid);
-        lq.template setup<QKC>(cur.Q, tid);
+        lp.template setup<true, GivenTid>(cur.P, tid);
+        lq.template setup<QKC, GivenTid>(cur.Q, tid);
     }
     wait_vm_lgkm0<0>();  // the zero-fill loads past the last tile write LDS too
 }
