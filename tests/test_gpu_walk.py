@@ -59,13 +59,13 @@ def build(shapes, mw, seed, polar):
     return mats, host
 
 
-@pytest.mark.parametrize("mw", [16, 5])
-def test_walk_bits_equal_stored_u_bits(mw):
+@pytest.mark.parametrize("mw,k", [(16, 1), (5, 1), (5, 2)])
+def test_walk_bits_equal_stored_u_bits(mw, k):
     shapes = WALK + PLAIN
-    p = sm.Params(workers=mw, beta=0.9, eta=1e-3, ns_iters=1, mom_dtype=sm.BF16, ns_dtype=sm.BF16)
+    p = sm.Params(workers=mw, beta=0.9, eta=1e-3, ns_iters=k, mom_dtype=sm.BF16, ns_dtype=sm.BF16)
     walk, host = build(shapes, mw, 7000, polar=False)
     ref, _ = build(shapes, mw, 7000, polar=True)
-    announce(f"  {mw} workers, {len(shapes)} matrices: walk run")
+    announce(f"  {mw} workers, {len(shapes)} matrices, k = {k}: walk run")
     sm.signmuon_step(walk, p, sm.workspace_tensor(walk, p, DEV))
     announce("  reference run (U stored: one tile per block)")
     sm.signmuon_step(ref, p, sm.workspace_tensor(ref, p, DEV))
@@ -81,6 +81,8 @@ def test_walk_bits_equal_stored_u_bits(mw):
         # the stored U (reference run) against the oracle at sampled entries,
         # and the walk's bits against the oracle's signs there
         u = to_host(b.polar_out)
+        if k != 1:
+            continue  # the sampled oracle values below are the k = 1 formula
         for w in (0, mw - 1):
             m_ref = np.zeros((R, C), np.uint16)
             oracle.momentum(host[j][0][w], m_ref, 0.9)
@@ -131,3 +133,19 @@ def test_walk_on_gpt2_small_matches_plain_kernel_over_two_steps():
             np.testing.assert_array_equal(to_host(a.packed), to_host(b.packed), err_msg=f"packed {j} t {t}")
             np.testing.assert_array_equal(to_host(a.vote_out), to_host(b.vote_out), err_msg=f"vote {j} t {t}")
             np.testing.assert_array_equal(to_host(a.weight), to_host(b.weight), err_msg=f"W {j} t {t}")
+
+
+def test_walk_with_more_matrices_than_one_launch_holds():
+    """60 walk-eligible matrices (wide and tall): each group splits into
+    launches of at most 48 matrices; bits, vote and W as with stored U."""
+    shapes = [(384, 1024), (1024, 384), (640, 704)] * 20
+    mw = 2
+    p = sm.Params(workers=mw, beta=0.9, eta=1e-3, ns_iters=1, mom_dtype=sm.BF16, ns_dtype=sm.BF16)
+    walk, _ = build(shapes, mw, 8100, polar=False)
+    ref, _ = build(shapes, mw, 8100, polar=True)
+    sm.signmuon_step(walk, p, sm.workspace_tensor(walk, p, DEV))
+    sm.signmuon_step(ref, p, sm.workspace_tensor(ref, p, DEV))
+    torch.cuda.synchronize()
+    for j, (a, b) in enumerate(zip(walk, ref)):
+        np.testing.assert_array_equal(to_host(a.packed), to_host(b.packed), err_msg=f"packed {j} {shapes[j]}")
+        np.testing.assert_array_equal(to_host(a.weight), to_host(b.weight), err_msg=f"W {j} {shapes[j]}")
