@@ -37,10 +37,17 @@ def state(shapes, mw, seed, int8):
     return mats
 
 
-@pytest.mark.parametrize("payload", ["bits", "int8"])
-@pytest.mark.parametrize("k", [0, 1, 3])
-def test_captured_step_replays_like_eager_steps(payload, k):
-    shapes, mw = [(256, 640), (640, 256), (100, 130)], 4
+# The default shapes run the one-tile-per-block kernels; the "walk" set
+# (bf16, packed signs, k loop of at least 12 slices) runs the final product's
+# persistent tile walk, wide and tall, with several tiles per workgroup.
+SHAPES = {"default": ([(256, 640), (640, 256), (100, 130)], 4),
+          "walk": ([(384, 1024), (1024, 384), (768, 3072)], 8)}
+
+
+@pytest.mark.parametrize("payload,k,shapes", [(p, k, "default") for p in ("bits", "int8") for k in (0, 1, 3)]
+                         + [("bits", 1, "walk"), ("bits", 2, "walk")])
+def test_captured_step_replays_like_eager_steps(payload, k, shapes):
+    shapes, mw = SHAPES[shapes]
     int8 = payload == "int8"
     p = sm.Params(workers=mw, beta=0.9, eta=1e-3, ns_iters=k, mom_dtype=sm.BF16, ns_dtype=sm.BF16,
                   payload=sm.PAYLOAD_INT8 if int8 else sm.PAYLOAD_BITS)
