@@ -1186,15 +1186,15 @@ void ns_product_kernel(NsBatch b) {
 
 // ---------------------------------------------------------------------------
 // Persistent final product with sign + pack from the accumulators, for a
-// launch in which every matrix packs that way (no U output, C % 64 == 0,
-// 16-byte operands). One workgroup per CU walks the tiles vb = blockIdx.x,
-// vb + gridDim.x, ... in the same XCD-contiguous order as the one-tile-per-
-// block kernel. The direct-to-LDS pipeline runs on across tile boundaries:
-// the loads that a tile's last iterations would issue past its own k range
-// fetch the first slices of the workgroup's next tile instead, and the
-// epilogue, which touches no LDS, runs while they are in flight. A tile
-// therefore starts with its pipeline full and its first fragments in
-// registers, and its descriptor is decoded while the previous tile computes.
+// bf16 launch in which every matrix packs that way (no U output, C % 64 ==
+// 0, 16-byte operands). One workgroup per CU walks the tiles vb =
+// blockIdx.x, vb + gridDim.x, ... in the same XCD-contiguous order as the
+// one-tile-per-block kernel. The direct-to-LDS pipeline runs on across tile
+// boundaries: the loads that a tile's last iterations would issue past its
+// own k range fetch the first slices of the workgroup's next tile instead,
+// and the epilogue, which touches no LDS, runs while they are in flight. A
+// tile therefore starts with its pipeline full; the next tile's descriptor
+// is decoded (scalar loads) at the start of the current one.
 // ---------------------------------------------------------------------------
 template <bool BF16>
 struct PackTile {
@@ -1270,16 +1270,14 @@ __device__ __forceinline__ uint32_t walk_offset(const Operand &op, bool kc, int 
     constexpr uint32_t sz = sizeof(typename E::T);
     const int lane = tid() & (kWave - 1);
     const int b = i * ProdLay::kWaves + __builtin_amdgcn_readfirstlane(tid() / kWave);
+    static_assert(BF16, "the walk's layouts are the bf16 ones");
     int mn, k;
-    if (kc) {
+    if (kc) {  // 16 rows of 64 bytes, 16-byte chunks swizzled
         mn = b * 16 + (lane >> 2);
         k = ((lane & 3) ^ ((lane >> 4) & 3)) * E::EPC;
-    } else if (BF16) {
+    } else {   // 8 blocks of 4 (k) x 16 (mn)
         k = (b >> 1) * 4 + ((lane & 7) >> 1);
         mn = ((b & 1) * 8 + (lane >> 3)) * 16 + (lane & 1) * 8;
-    } else {
-        k = b;
-        mn = lane * 4;
     }
     const int kk = kt * E::BK + k;
     const bool ok = mn < op.rows && kk < op.K;
@@ -1389,6 +1387,7 @@ __device__ __forceinline__ void pack_tile_kloop(const PackTile<BF16> &cur, const
 template <bool BF16, bool QKC>
 __global__ __launch_bounds__(ProdLay::kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void ns_product_pack_kernel(NsBatch b) {
+    static_assert(BF16, "the walk is built for bf16 operands");
     using L = ProdLay;
     constexpr int S = L::kStages, PL = L::kPLoads, QL = L::kQLoads, NLD = PL + QL;
     __shared__ __attribute__((aligned(16))) char smem[L::kLdsBytes];
