@@ -1069,9 +1069,14 @@ __device__ __forceinline__ int write_lane(int dst, uint32_t val, int lane) {
     return dst;
 }
 
-template <class Tid = HwTid>
-__device__ __forceinline__ void pack_from_registers(const ProductArgs &pa, const f32x16_t (&acc)[kFM][kFN],
-                                                    Tid tid = Tid{}) {
+// Gathers the wave's sign words (u = gamma * acc, bit = (u >= 0)) into
+// lo / hi: word id of the wave sits in lane id % 64, slot id / 64. Then
+// store(slot, row, first column, word) for each word of the lane inside the
+// matrix.
+template <class Tid, class Store>
+__device__ __forceinline__ void sign_words_from_registers(const ProductArgs &pa,
+                                                          const f32x16_t (&acc)[kFM][kFN], Tid tid,
+                                                          Store &&store) {
     const float gamma = -0.5f * pa.s.get();
     const int lane = tid() & (kWave - 1), wid = tid() / kWave;
     const int m0 = pa.ti * kNsTileM + ProdLay::m0(wid), n0 = pa.tj * kNsProdTileN + ProdLay::n0(wid);
@@ -1106,8 +1111,41 @@ __device__ __forceinline__ void pack_from_registers(const ProductArgs &pa, const
         const int gm = m0 + f * 32 + 8 * (rr >> 2) + (rr & 3) + 4 * hrow;
         const int gn0 = n0 + 64 * gp;
         const uint64_t word = (uint64_t)(uint32_t)lo[sl] | ((uint64_t)(uint32_t)hi[sl] << 32);
-        if (gm < pa.R && gn0 < pa.C) pa.pk[((int64_t)gm * pa.C + gn0) >> 6] = word;
+        if (gm < pa.R && gn0 < pa.C) store(gm, gn0, word);
     }
+}
+
+template <class Tid = HwTid>
+__device__ __forceinline__ void pack_from_registers(const ProductArgs &pa, const f32x16_t (&acc)[kFM][kFN],
+                                                    Tid tid = Tid{}) {
+    sign_words_from_registers(pa, acc, tid, [&](int gm, int gn0, uint64_t word) {
+        pa.pk[((int64_t)gm * pa.C + gn0) >> 6] = word;
+    });
+}
+
+// The same signs as int8 (+1 / -1), straight from the sign words: table entry
+// b holds the 8 bytes of the 8 bits of b (LSB first), so the 64 columns of a
+// word go out as four 16-byte stores (C % 64 == 0, 16-byte aligned rows).
+template <class Tid>
+__device__ __forceinline__ void int8_from_registers(const ProductArgs &pa, const f32x16_t (&acc)[kFM][kFN],
+                                                    Tid tid, const uint2 *table) {
+    sign_words_from_registers(pa, acc, tid, [&](int gm, int gn0, uint64_t word) {
+        uint4 *dst = reinterpret_cast<uint4 *>(pa.i8 + (int64_t)gm * pa.C + gn0);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const uint32_t bits = (uint32_t)(word >> (16 * q));
+            const uint2 a = table[bits & 0xffu], b = table[(bits >> 8) & 0xffu];
+            dst[q] = make_uint4(a.x, a.y, b.x, b.y);
+        }
+    });
+}
+
+// Entry e of the int8 table: byte j is +1 where bit j of e is set, else -1.
+__device__ __forceinline__ uint2 int8_table_entry(int e) {
+    uint32_t w[2] = {0u, 0u};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) w[j >> 2] |= (((e >> j) & 1) ? 0x01u : 0xffu) << (8 * (j & 3));
+    return make_uint2(w[0], w[1]);
 }
 
 template <bool BF16, bool QKC, int EPI>
@@ -1185,9 +1223,9 @@ void ns_product_kernel(NsBatch b) {
 }
 
 // ---------------------------------------------------------------------------
-// Persistent final product with sign + pack from the accumulators, for a
-// bf16 launch in which every matrix packs that way (no U output, C % 64 ==
-// 0, 16-byte operands). One workgroup per CU walks the tiles vb =
+// Persistent final product with the signs (packed, or int8) straight from
+// the accumulators, for a bf16 launch in which every matrix takes them that
+// way (no U output, C % 64 == 0, 16-byte operands). One workgroup per CU walks the tiles vb =
 // blockIdx.x, vb + gridDim.x, ... in the same XCD-contiguous order as the
 // one-tile-per-block kernel. The direct-to-LDS pipeline runs on across tile
 // boundaries: the loads that a tile's last iterations would issue past its
@@ -1210,7 +1248,8 @@ struct PackTile {
         return j >= kt_n ? kt_n : (t < kt_n ? t : t - kt_n);
     }
 
-    __device__ __forceinline__ void decode(const NsBatch &b, int sv, int lt) {
+    // i8: the signs go to M.i8 as int8, else packed to M.packed.
+    __device__ __forceinline__ void decode(const NsBatch &b, int sv, int lt, bool i8) {
         using T = typename Elem<BF16>::T;
         constexpr int BK = Elem<BF16>::BK;
         const int w = lt / b.tiles_per_worker_all;
@@ -1227,8 +1266,8 @@ struct PackTile {
         const char *a = static_cast<const char *>(M.a) + (int64_t)w * r * r * (int64_t)sizeof(T);
         pa.out = nullptr;
         pa.u_out = nullptr;
-        pa.i8 = nullptr;
-        pa.pk = M.packed + (int64_t)w * ((n + 63) >> 6);
+        pa.i8 = i8 ? M.i8 + (int64_t)w * n : nullptr;
+        pa.pk = i8 ? nullptr : M.packed + (int64_t)w * ((n + 63) >> 6);
         pa.R = R;
         pa.C = C;
         pa.ti = ti;
@@ -1383,11 +1422,14 @@ __device__ __forceinline__ void pack_tile_kloop(const PackTile<BF16> &cur, const
                [&](auto tl) { iteration(iters - S + decltype(tl)::value, NoTail{}, tl); });
 }
 
-// QKC: every matrix of the launch is tall (true) or wide (false).
-template <bool BF16, bool QKC>
+// QKC: every matrix of the launch is tall (true) or wide (false). EPI:
+// EPI_FINAL (packed signs) or EPI_FINAL_I8 (int8 signs).
+template <bool BF16, bool QKC, int EPI>
 __global__ __launch_bounds__(ProdLay::kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void ns_product_pack_kernel(NsBatch b) {
     static_assert(BF16, "the walk is built for bf16 operands");
+    static_assert(EPI == EPI_FINAL || EPI == EPI_FINAL_I8, "sign epilogues only");
+    constexpr bool kI8 = EPI == EPI_FINAL_I8;
     using L = ProdLay;
     constexpr int S = L::kStages, PL = L::kPLoads, QL = L::kQLoads, NLD = PL + QL;
     __shared__ __attribute__((aligned(16))) char smem[L::kLdsBytes];
@@ -1395,14 +1437,16 @@ void ns_product_pack_kernel(NsBatch b) {
     // walk (read back per tile: a register copy would be spilled, and its
     // reload would wait for every load in flight).
     __shared__ int starts[kWave];
+    __shared__ uint2 i8_table[kI8 ? 256 : 1];
     const int sv = ns_start_of_lane();
     if (threadIdx.x < kWave) starts[threadIdx.x] = sv;
+    if (kI8 && threadIdx.x < 256) i8_table[threadIdx.x] = int8_table_entry((int)threadIdx.x);
     const int wid0 = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
     const int total = b.total_tiles, G = gridDim.x;
     int vb = blockIdx.x;
     PackTile<BF16> cur, nxt;
     DmaSlices<BF16, 256, L::kWaves> lp, lq;
-    cur.decode(b, sv, xcd_remap(vb, total));
+    cur.decode(b, sv, xcd_remap(vb, total), kI8);
     lp.template setup<true>(cur.P);
     lq.template setup<QKC>(cur.Q);
     // The first tile fills the pipeline itself: slices 0 .. S - 2 and the P
@@ -1429,11 +1473,14 @@ void ns_product_pack_kernel(NsBatch b) {
         const int vn = vb + G;
         const bool more = vn < total;
         if (more)
-            nxt.decode(b, starts[lane], xcd_remap(vn, total));
+            nxt.decode(b, starts[lane], xcd_remap(vn, total), kI8);
         else
             nxt.none();
         pack_tile_kloop<BF16, QKC>(cur, nxt, lp, lq, smem, acc, tid);
-        pack_from_registers<GivenTid>(cur.pa, acc, tid);
+        if constexpr (kI8)
+            int8_from_registers(cur.pa, acc, tid, i8_table);
+        else
+            pack_from_registers<GivenTid>(cur.pa, acc, tid);
         if (!more) break;
         vb = vn;
         cur = nxt;
@@ -1470,12 +1517,17 @@ void launch_ns_product(const NsBatch &b, bool ns_bf16, NsEpilogue epi, hipStream
 #undef SM_PROD
 }
 
-void launch_ns_product_pack(const NsBatch &b, bool tall, int grid_blocks, hipStream_t s) {
+void launch_ns_product_pack(const NsBatch &b, bool tall, bool i8, int grid_blocks, hipStream_t s) {
     dim3 grid(grid_blocks), block(ProdLay::kThreads);
-    if (tall)
-        hipLaunchKernelGGL((ns_product_pack_kernel<true, true>), grid, block, 0, s, b);
-    else
-        hipLaunchKernelGGL((ns_product_pack_kernel<true, false>), grid, block, 0, s, b);
+#define SM_WALK(TALL, E) hipLaunchKernelGGL((ns_product_pack_kernel<true, TALL, E>), grid, block, 0, s, b)
+    if (i8) {
+        if (tall) SM_WALK(true, EPI_FINAL_I8);
+        else SM_WALK(false, EPI_FINAL_I8);
+    } else {
+        if (tall) SM_WALK(true, EPI_FINAL);
+        else SM_WALK(false, EPI_FINAL);
+    }
+#undef SM_WALK
 }
 
 }  // namespace sm

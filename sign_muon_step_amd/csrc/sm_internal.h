@@ -123,14 +123,14 @@ inline int32_t ns_product_tiles(int64_t R, int64_t C) {
 // ns_bf16 selects the operand storage type; epi the epilogue.
 void launch_ns_gram(const NsBatch &b, bool ns_bf16, hipStream_t s);
 void launch_ns_product(const NsBatch &b, bool ns_bf16, NsEpilogue epi, hipStream_t s);
-// The final product with bf16 operands when every matrix of b packs its
-// signs from the accumulators (packed set, out and i8 null, C % 64 == 0, C
-// and min(R, C) multiples of 8, each worker's matrix under 2 GiB, and
-// ceil(min(R, C) / 32) a multiple of 4 and at least 12) and every matrix is
-// tall (R > C) or every one wide: grid_blocks workgroups (one per CU, at most
-// b.total_tiles) walk the tiles with the load pipeline running across tile
-// boundaries.
-void launch_ns_product_pack(const NsBatch &b, bool tall, int grid_blocks, hipStream_t s);
+// The final product with bf16 operands when every matrix of b takes its
+// signs straight from the accumulators, packed (packed set) or as int8 (i8,
+// i8 set), with no U output (out null), C % 64 == 0, C and min(R, C)
+// multiples of 8, each worker's matrix under 2 GiB, and ceil(min(R, C) / 32)
+// a multiple of 4 and at least 12, and every matrix is tall (R > C) or every
+// one wide: grid_blocks workgroups (one per CU, at most b.total_tiles) walk
+// the tiles with the load pipeline running across tile boundaries.
+void launch_ns_product_pack(const NsBatch &b, bool tall, bool i8, int grid_blocks, hipStream_t s);
 
 // ---------------------------------------------------------------------------
 // Sign + pack of a stored U, and scale + sign + pack for k = 0.

@@ -40,7 +40,7 @@ def _name_the_case(request):
     torch.cuda.synchronize()
 
 
-def build(shapes, mw, seed, polar):
+def build(shapes, mw, seed, polar, int8=False):
     def grad(jm):
         j, m = jm
         return synthetic.random_matrix(seed + 100 * j + m, shapes[j], 1e-3)
@@ -52,10 +52,12 @@ def build(shapes, mw, seed, polar):
         host.append((g, w0))
         mats.append(sm.Matrix(
             grad=to_dev(g), momentum=torch.zeros((mw, R, C), dtype=torch.bfloat16, device=DEV),
-            packed=torch.zeros((mw, sm.signmuon_packed_words(R * C)), dtype=torch.int64, device=DEV),
+            packed=None if int8 else torch.zeros((mw, sm.signmuon_packed_words(R * C)), dtype=torch.int64,
+                                                 device=DEV),
             weight=to_dev(w0),
             polar_out=torch.zeros((mw, R, C), dtype=torch.float32, device=DEV) if polar else None,
-            vote_out=torch.zeros((R, C), dtype=torch.int8, device=DEV)))
+            vote_out=torch.zeros((R, C), dtype=torch.int8, device=DEV),
+            signs_i8=torch.zeros((mw, R, C), dtype=torch.int8, device=DEV) if int8 else None))
     return mats, host
 
 
@@ -149,3 +151,28 @@ def test_walk_with_more_matrices_than_one_launch_holds():
     for j, (a, b) in enumerate(zip(walk, ref)):
         np.testing.assert_array_equal(to_host(a.packed), to_host(b.packed), err_msg=f"packed {j} {shapes[j]}")
         np.testing.assert_array_equal(to_host(a.weight), to_host(b.weight), err_msg=f"W {j} {shapes[j]}")
+
+
+@pytest.mark.parametrize("mw,k", [(16, 1), (3, 2)])
+def test_walk_int8_signs_equal_stored_u_int8_signs(mw, k):
+    """The int8 payload: the walk expands each sign word into 64 bytes of
+    +1 / -1; they must equal the int8 signs of the one-tile-per-block kernel
+    that also stores U, and 2 bit - 1 of the oracle's signs where clear."""
+    shapes = WALK + PLAIN
+    p = sm.Params(workers=mw, beta=0.9, eta=1e-3, ns_iters=k, mom_dtype=sm.BF16, ns_dtype=sm.BF16,
+                  payload=sm.PAYLOAD_INT8)
+    walk, host = build(shapes, mw, 9100, polar=False, int8=True)
+    ref, _ = build(shapes, mw, 9100, polar=True, int8=True)
+    announce(f"  int8, {mw} workers, k = {k}: walk run, then stored-U run")
+    sm.signmuon_step(walk, p, sm.workspace_tensor(walk, p, DEV))
+    sm.signmuon_step(ref, p, sm.workspace_tensor(ref, p, DEV))
+    torch.cuda.synchronize()
+    for j, (a, b) in enumerate(zip(walk, ref)):
+        sw = to_host(a.signs_i8)
+        np.testing.assert_array_equal(sw, to_host(b.signs_i8), err_msg=f"int8 signs {shapes[j]}")
+        assert set(np.unique(sw).tolist()) <= {-1, 1}
+        np.testing.assert_array_equal(to_host(a.vote_out), to_host(b.vote_out), err_msg=f"vote {shapes[j]}")
+        np.testing.assert_array_equal(to_host(a.weight), to_host(b.weight), err_msg=f"W {shapes[j]}")
+        # U of the stored-U run decides the sign of every int8 entry
+        u = to_host(b.polar_out)
+        np.testing.assert_array_equal(sw, np.where(u >= 0, 1, -1).astype(np.int8), err_msg=f"rule {shapes[j]}")
