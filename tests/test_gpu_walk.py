@@ -176,3 +176,42 @@ def test_walk_int8_signs_equal_stored_u_int8_signs(mw, k):
         # U of the stored-U run decides the sign of every int8 entry
         u = to_host(b.polar_out)
         np.testing.assert_array_equal(sw, np.where(u >= 0, 1, -1).astype(np.int8), err_msg=f"rule {shapes[j]}")
+
+
+def test_walk_degenerate_workers_match_oracle():
+    """Workers whose gradient is zero (U = 0: every sign +1), holds a NaN (U
+    is NaN: every sign -1) or an Inf (s = 0, and 0 * Inf is NaN: every sign
+    -1), next to ordinary workers, through the walk: every packed word of
+    the degenerate workers equals the oracle's, and the whole output equals
+    the stored-U kernel's."""
+    shapes = [(384, 1024), (1024, 384), (768, 768)]
+    mw = 3
+    p = sm.Params(workers=mw, beta=0.9, eta=1e-3, ns_iters=1, mom_dtype=sm.BF16, ns_dtype=sm.BF16)
+    bad = {0: (0, "zero"), 1: (1, "nan"), 2: (2, "inf")}  # matrix -> (worker, kind)
+    runs = []
+    for polar in (False, True):
+        mats, host = build(shapes, mw, 9500, polar=polar)
+        for j, (w, kind) in bad.items():
+            g = host[j][0]
+            if kind == "zero":
+                g[w] = 0.0
+            else:
+                g[w].ravel()[12345 % g[w].size] = np.nan if kind == "nan" else np.inf
+            mats[j].grad.copy_(torch.from_numpy(g))
+        sm.signmuon_step(mats, p, sm.workspace_tensor(mats, p, DEV))
+        torch.cuda.synchronize()
+        runs.append((mats, host))
+    (walk, host), (ref, _) = runs
+    for j, (w, kind) in bad.items():
+        R, C = shapes[j]
+        pw = to_host(walk[j].packed)
+        np.testing.assert_array_equal(pw, to_host(ref[j].packed), err_msg=f"packed {shapes[j]}")
+        np.testing.assert_array_equal(to_host(walk[j].weight), to_host(ref[j].weight), err_msg=f"W {shapes[j]}")
+        m = np.zeros((mw, R, C), np.uint16)
+        w0 = host[j][1].copy()
+        packed_ref, _, _ = oracle.step_matrix(host[j][0], m, w0, 0.9, 1e-3, 1, oracle.BF16)
+        announce(f"  {shapes[j]} worker {w} ({kind}): GPU words {np.unique(pw[w])[:3]}, "
+                 f"oracle words {np.unique(packed_ref[w])[:3]}")
+        np.testing.assert_array_equal(pw[w], packed_ref[w], err_msg=f"{kind} worker")
+        want = np.uint64(0xFFFFFFFFFFFFFFFF) if kind == "zero" else np.uint64(0)
+        assert (pw[w] == want).all()
