@@ -74,6 +74,8 @@ struct MatPlan {
     size_t pw_off;          // spectral: power vectors [2][Mw][r] (floats from the section)
     size_t pwp_off;         // spectral: block sums [2][Mw][pw_bpw] (doubles from the section)
     int32_t pw_bpw;         // spectral: power-step blocks per worker
+    int32_t gram_split;     // k chunks per Gram tile (0: the Gram kernel stores A itself)
+    size_t gpart_off;       // split Gram: partial tiles [Mw][Gram tiles][split][256][256] fp32
     bool fused_pack;        // the last product packs the signs itself (bits payload)
     bool fused_i8;          // the last product writes the int8 signs itself (int8 payload)
     bool u_scratch;         // U goes through workspace scratch
@@ -83,7 +85,7 @@ struct Plan {
     std::vector<MatPlan> m;
     int32_t units = 0, post_unit_base = 0, partials = 0;
     size_t off_partials = 0, off_scales = 0, off_nnz = 0, off_gram = 0, off_iter[2] = {0, 0};
-    size_t off_vns = 0, off_u = 0, off_pw = 0, off_pwp = 0, total = 0;
+    size_t off_vns = 0, off_u = 0, off_pw = 0, off_pwp = 0, off_gpart = 0, total = 0;
     bool spectral = false;
     bool i8 = false;  // int8 payload
 };
@@ -111,7 +113,7 @@ int make_plan(const signmuon_matrix *mats, int32_t n_mats, const signmuon_params
     const bool post = step && p->post_polar_iters > 0;
     size_t pw = 0, pwp = 0;
     pl.m.assign(n_mats, MatPlan{});
-    size_t gram = 0, iter = 0, post_gram = 0, post_iter = 0, vns = 0, u = 0;
+    size_t gram = 0, iter = 0, post_gram = 0, post_iter = 0, vns = 0, u = 0, gpart = 0;
     int64_t partials = 0;
     for (int32_t i = 0; i < n_mats; ++i) {
         const signmuon_matrix &s = mats[i];
@@ -130,6 +132,11 @@ int make_plan(const signmuon_matrix *mats, int32_t n_mats, const signmuon_params
         pl.units += (int32_t)mw;
         q.gram_off = gram;
         gram += align_up((size_t)(mw * q.r * q.r) * ns, kSectionAlign);
+        q.gram_split = sm::ns_gram_split(q.R, q.C, p->ns_dtype == SIGNMUON_BF16);
+        q.gpart_off = gpart;
+        if (q.gram_split > 0)
+            gpart += (size_t)mw * sm::ns_gram_tiles(q.R, q.C) * q.gram_split * sm::kNsTileM * sm::kNsTileM *
+                     sizeof(float);
         q.iter_off = iter;
         iter += align_up((size_t)(mw * q.n) * ns, kSectionAlign);
         q.post_gram_off = post_gram;
@@ -171,6 +178,8 @@ int make_plan(const signmuon_matrix *mats, int32_t n_mats, const signmuon_params
     pl.off_gram = off;
     const bool need_gram = p->ns_iters > 0 || post || pl.spectral;
     off += need_gram ? (gram > post_gram ? gram : post_gram) : 0;
+    pl.off_gpart = off;
+    off += need_gram ? align_up(gpart, kSectionAlign) : 0;
     size_t iter_need = 0;
     if (p->ns_iters >= 2) iter_need = iter;
     if (post && p->post_polar_iters >= 2 && post_iter > iter_need) iter_need = post_iter;
@@ -267,6 +276,7 @@ int device_cus() {
 // stage round); wide and tall matrices go in separate launches. Everything else, and every other
 // product, uses the one-tile-per-block kernel.
 enum ProdGroup { PG_PLAIN = 0, PG_WALK_WIDE = 1, PG_WALK_TALL = 2 };
+constexpr int PG_SPLIT = 1;  // the Gram pass's second group: split k
 
 int product_group(const MatPlan &q, const sm::NsMat &d, bool bf16) {
     if (!bf16 || d.out || !(d.packed || d.i8)) return PG_PLAIN;
@@ -315,7 +325,9 @@ int ns_pass(const signmuon_matrix *mats, int32_t n_mats, const signmuon_params *
     };
     const sm::NsEpilogue epi = !last ? sm::EPI_ITER
                                      : (muon ? sm::EPI_WUPD : (step && pl.i8 ? sm::EPI_FINAL_I8 : sm::EPI_FINAL));
-    // The matrices of each launch group, in order.
+    // The matrices of each launch group, in order: for the product, the
+    // one-tile-per-block kernel and the walk's wide and tall launches; for the
+    // Gram, the whole-k kernel and the split one (PG_SPLIT, then the reduce).
     std::vector<int32_t> groups[3];
     for (int32_t i = 0; i < n_mats; ++i) {
         int g = PG_PLAIN;
@@ -323,6 +335,8 @@ int ns_pass(const signmuon_matrix *mats, int32_t n_mats, const signmuon_params *
             sm::NsMat d;
             describe(i, d);
             g = product_group(pl.m[i], d, bf16);
+        } else if (pass == 0 && pl.m[i].gram_split > 0) {
+            g = PG_SPLIT;
         }
         groups[g].push_back(i);
     }
@@ -336,18 +350,37 @@ int ns_pass(const signmuon_matrix *mats, int32_t n_mats, const signmuon_params *
             b.use_scales = use_scales;
             b.scales = scales;
             b.eta = p->eta;  // the W-update epilogue
-            int64_t tiles = 0;
+            const bool split = pass == 0 && g == PG_SPLIT;
+            // split Gram: Gram tiles x split blocks per worker; the reduce
+            // then runs 16 blocks per Gram tile
+            auto number_tiles = [&](int per_tile) {
+                int64_t tiles = 0;
+                for (int32_t i = 0; i < cn; ++i) {
+                    sm::NsMat &d = b.mat[i];
+                    d.tile_begin = (int32_t)tiles;
+                    b.starts.v[i] = d.tile_begin;
+                    tiles += (int64_t)d.tiles_per_worker * (per_tile ? per_tile : d.split);
+                }
+                b.tiles_per_worker_all = (int32_t)tiles;
+                b.total_tiles = (int32_t)(tiles * p->workers);
+                return tiles * p->workers <= INT32_MAX;
+            };
             for (int32_t i = 0; i < cn; ++i) {
                 sm::NsMat &d = b.mat[i];
                 describe(idx[c0 + i], d);
-                d.tile_begin = (int32_t)tiles;
-                b.starts.v[i] = d.tile_begin;
-                tiles += d.tiles_per_worker;
+                if (split) {
+                    const MatPlan &q = pl.m[idx[c0 + i]];
+                    d.split = q.gram_split;
+                    d.out = ws_at<char>(ws, pl.off_gpart + q.gpart_off);
+                }
             }
-            if (tiles * p->workers > INT32_MAX) return SIGNMUON_ERANGE;
-            b.tiles_per_worker_all = (int32_t)tiles;
-            b.total_tiles = (int32_t)(tiles * p->workers);
-            if (pass == 0)
+            if (!number_tiles(split ? 0 : 1)) return SIGNMUON_ERANGE;
+            if (split) {
+                sm::launch_ns_gram_split(b, bf16, st);
+                if (int rc = tr.after(SIGNMUON_K_GRAM)) return rc;
+                if (!number_tiles(sm::kGramReduceParts)) return SIGNMUON_ERANGE;
+                sm::launch_gram_reduce(b, bf16, st);
+            } else if (pass == 0)
                 sm::launch_ns_gram(b, bf16, st);
             else if (g == PG_PLAIN)
                 sm::launch_ns_product(b, bf16, epi, st);

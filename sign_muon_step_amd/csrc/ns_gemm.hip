@@ -925,7 +925,25 @@ __device__ __forceinline__ void gram_tile(const Operand &P, const Operand &Q, ch
         gram_epilogue<BF16, false>(acc, smem, ti, tj, r, sc, a);
 }
 
-template <bool BF16>
+// One k chunk of a split Gram tile: the unscaled fp32 sum, stored whole
+// (256 x 256, row-major) at its place in M.out.
+template <bool BF16, bool KC>
+__device__ __forceinline__ void gram_partial_tile(const Operand &P, const Operand &Q, char *smem,
+                                                  const NsMat &M, int w, int tile, int chunk) {
+    f32x16_t acc[kFM][kFN];
+    tile_mainloop<GramLay, BF16, KC, KC>(P, Q, smem, acc);
+    const int r = M.R <= M.C ? M.R : M.C;
+    const int T_ = (r + kNsTileM - 1) / kNsTileM;
+    float *part = static_cast<float *>(M.out) +
+                  ((int64_t)(w * (T_ * (T_ + 1) / 2) + tile) * M.split + chunk) * (kNsTileM * kNsTileM);
+    gram_epilogue<false, true>(acc, smem, 0, 0, kNsTileM, LateScale{1.0f, 0}, part);
+}
+
+// SPLIT: each tile's k range is cut into M.split chunks, one block each;
+// a block writes its chunk's unscaled fp32 sum as a full 256 x 256 tile to
+// M.out (worker stride tiles * split tiles, tile t's chunks consecutive) and
+// gram_reduce_kernel adds the chunks in order, scales and stores A.
+template <bool BF16, bool SPLIT = false>
 __global__ __launch_bounds__(GramLay::kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void ns_gram_kernel(NsBatch b) {
     using T = typename Elem<BF16>::T;
@@ -936,9 +954,15 @@ void ns_gram_kernel(NsBatch b) {
     const int lw = lt - w * b.tiles_per_worker_all;
     const NsMat M = load_ns_mat(find_ns_mat(sv, lw));
     int t = lw - M.tile_begin;
+    int chunk = 0;
+    if constexpr (SPLIT) {
+        chunk = t % M.split;
+        t /= M.split;
+    }
     const bool wide = M.R <= M.C;
     const int r = wide ? M.R : M.C, c = wide ? M.C : M.R;
     const int T_ = (r + kNsTileM - 1) / kNsTileM;
+    const int tile = t;
     int ti = 0;
     while (t >= T_ - ti) {
         t -= T_ - ti;
@@ -951,16 +975,83 @@ void ns_gram_kernel(NsBatch b) {
     const bool vec = (M.C % Elem<BF16>::EPC) == 0 && n * (int64_t)sizeof(T) < ((int64_t)1 << 31);
     const LateScale sc{b.scales[M.unit_begin + w].y, b.use_scales};
     void *a = static_cast<char *>(M.a) + (int64_t)w * r * r * (int64_t)sizeof(T);
+    int k0 = 0, kn = c;
+    if constexpr (SPLIT) {
+        // chunk of whole k slices: ceil(slices / split) slices each
+        constexpr int BK = Elem<BF16>::BK;
+        const int per = ((c + BK - 1) / BK + M.split - 1) / M.split * BK;
+        k0 = chunk * per;
+        kn = c - k0 < per ? c - k0 : per;
+    }
     if (wide) {
         // Y = X (r x c, k-contiguous rows)
-        Operand P{y + (int64_t)ti * kNsTileM * M.C * (int64_t)sizeof(T), M.C, r - ti * kNsTileM, c, vec};
-        Operand Q{y + (int64_t)tj * kNsTileM * M.C * (int64_t)sizeof(T), M.C, r - tj * kNsTileM, c, vec};
-        gram_tile<BF16, true>(P, Q, smem, ti, tj, r, sc, a);
+        const char *base = y + (int64_t)k0 * (int64_t)sizeof(T);
+        Operand P{base + (int64_t)ti * kNsTileM * M.C * (int64_t)sizeof(T), M.C, r - ti * kNsTileM, kn, vec};
+        Operand Q{base + (int64_t)tj * kNsTileM * M.C * (int64_t)sizeof(T), M.C, r - tj * kNsTileM, kn, vec};
+        if constexpr (SPLIT)
+            gram_partial_tile<BF16, true>(P, Q, smem, M, w, tile, chunk);
+        else
+            gram_tile<BF16, true>(P, Q, smem, ti, tj, r, sc, a);
     } else {
         // Y = X^T: element (i, k) of Y is X[k][i]: mn-contiguous, ld = C
-        Operand P{y + (int64_t)ti * kNsTileM * (int64_t)sizeof(T), M.C, r - ti * kNsTileM, c, vec};
-        Operand Q{y + (int64_t)tj * kNsTileM * (int64_t)sizeof(T), M.C, r - tj * kNsTileM, c, vec};
-        gram_tile<BF16, false>(P, Q, smem, ti, tj, r, sc, a);
+        const char *base = y + (int64_t)k0 * M.C * (int64_t)sizeof(T);
+        Operand P{base + (int64_t)ti * kNsTileM * (int64_t)sizeof(T), M.C, r - ti * kNsTileM, kn, vec};
+        Operand Q{base + (int64_t)tj * kNsTileM * (int64_t)sizeof(T), M.C, r - tj * kNsTileM, kn, vec};
+        if constexpr (SPLIT)
+            gram_partial_tile<BF16, false>(P, Q, smem, M, w, tile, chunk);
+        else
+            gram_tile<BF16, false>(P, Q, smem, ti, tj, r, sc, a);
+    }
+}
+
+// Sums the split Gram's chunks of 16 rows of one 256 x 256 tile per block,
+// in chunk order, then stores A = scale * sum in the storage type (the tile
+// and, above the diagonal, its mirror). 256 threads: 4 rows of 64 threads x
+// 4 columns per pass.
+template <bool BF16>
+__global__ __launch_bounds__(256) void gram_reduce_kernel(NsBatch b) {
+    constexpr int kRows = kNsTileM / kGramReduceParts;
+    const int sv = ns_start_of_lane();
+    const int lt = blockIdx.x;  // one block per (worker, tile, 16 rows)
+    const int w = lt / b.tiles_per_worker_all;
+    const int lw = lt - w * b.tiles_per_worker_all;
+    const NsMat M = load_ns_mat(find_ns_mat(sv, lw));
+    const int rows0 = (lw - M.tile_begin) % kGramReduceParts * kRows;  // this block's rows
+    int t = (lw - M.tile_begin) / kGramReduceParts;
+    const int r = M.R <= M.C ? M.R : M.C;
+    const int T_ = (r + kNsTileM - 1) / kNsTileM;
+    const int tile = t;
+    int ti = 0;
+    while (t >= T_ - ti) {
+        t -= T_ - ti;
+        ++ti;
+    }
+    const int tj = ti + t;
+    const int tiles = T_ * (T_ + 1) / 2;
+    const float *part = static_cast<const float *>(M.out) +
+                        ((int64_t)(w * tiles + tile) * M.split) * (kNsTileM * kNsTileM);
+    void *a = static_cast<char *>(M.a) + (int64_t)w * r * r * (int64_t)sizeof(typename Elem<BF16>::T);
+    const float scale = b.use_scales ? b.scales[M.unit_begin + w].y : 1.0f;
+    const int c4 = (threadIdx.x & 63) * 4;
+    for (int row = rows0 + (threadIdx.x >> 6); row < rows0 + kRows; row += 4) {
+        const int gi = ti * kNsTileM + row, gj = tj * kNsTileM + c4;
+        if (gi >= r || gj >= r) continue;
+        float4 sum = *reinterpret_cast<const float4 *>(part + row * kNsTileM + c4);
+        for (int s = 1; s < M.split; ++s) {
+            const float4 v = *reinterpret_cast<const float4 *>(part + (int64_t)s * kNsTileM * kNsTileM +
+                                                               row * kNsTileM + c4);
+            sum.x += v.x;
+            sum.y += v.y;
+            sum.z += v.z;
+            sum.w += v.w;
+        }
+        const float v[4] = {sum.x * scale, sum.y * scale, sum.z * scale, sum.w * scale};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            if (gj + e >= r) break;
+            store_val<BF16>(a, (int64_t)gi * r + gj + e, v[e]);
+            if (ti < tj) store_val<BF16>(a, (int64_t)(gj + e) * r + gi, v[e]);
+        }
     }
 }
 
@@ -1498,6 +1589,22 @@ void launch_ns_gram(const NsBatch &b, bool ns_bf16, hipStream_t s) {
         hipLaunchKernelGGL(ns_gram_kernel<true>, grid, block, 0, s, b);
     else
         hipLaunchKernelGGL(ns_gram_kernel<false>, grid, block, 0, s, b);
+}
+
+void launch_ns_gram_split(const NsBatch &b, bool ns_bf16, hipStream_t s) {
+    dim3 grid(b.total_tiles), block(GramLay::kThreads);
+    if (ns_bf16)
+        hipLaunchKernelGGL((ns_gram_kernel<true, true>), grid, block, 0, s, b);
+    else
+        hipLaunchKernelGGL((ns_gram_kernel<false, true>), grid, block, 0, s, b);
+}
+
+void launch_gram_reduce(const NsBatch &b, bool ns_bf16, hipStream_t s) {
+    dim3 grid(b.total_tiles), block(256);
+    if (ns_bf16)
+        hipLaunchKernelGGL(gram_reduce_kernel<true>, grid, block, 0, s, b);
+    else
+        hipLaunchKernelGGL(gram_reduce_kernel<false>, grid, block, 0, s, b);
 }
 
 void launch_ns_product(const NsBatch &b, bool ns_bf16, NsEpilogue epi, hipStream_t s) {

@@ -84,7 +84,7 @@ struct NsMat {
     int32_t tile_begin;  // first tile of this matrix within one worker's tiles
     int32_t tiles_per_worker;
     int32_t unit_begin;  // index of (this matrix, worker 0) in scales
-    int32_t pad_;
+    int32_t split;       // split Gram: k chunks per tile (partial tiles in out)
 };
 
 // Tiles are numbered worker-major: worker w's tiles of every matrix of the
@@ -122,6 +122,27 @@ inline int32_t ns_product_tiles(int64_t R, int64_t C) {
 
 // ns_bf16 selects the operand storage type; epi the epilogue.
 void launch_ns_gram(const NsBatch &b, bool ns_bf16, hipStream_t s);
+// The Gram matrices of few-tile matrices with a long k range, in two
+// launches: launch_ns_gram_split (tiles_per_worker = Gram tiles x split, one
+// block per k chunk of a tile) writes unscaled fp32 partial tiles to each
+// matrix's out ([Mw][Gram tiles][split][256][256]); launch_gram_reduce
+// (tiles_per_worker = Gram tiles x 16, one block per 16 rows of a tile)
+// adds them in chunk order, applies s^2 when use_scales, and stores A and its
+// mirror.
+constexpr int kGramReduceParts = 16;  // reduce blocks per Gram tile (16 rows each)
+void launch_ns_gram_split(const NsBatch &b, bool ns_bf16, hipStream_t s);
+void launch_gram_reduce(const NsBatch &b, bool ns_bf16, hipStream_t s);
+// K chunks per Gram tile of an R x C matrix (0: not split, the Gram kernel
+// stores A itself): for matrices with at most 3 Gram tiles per worker and at
+// least 32 k slices (BK k each), slices / 16 chunks, at most 8, so that the
+// few tiles spread over more blocks. A function of the shape alone, so that
+// results do not depend on which matrices share a launch.
+inline int32_t ns_gram_split(int64_t R, int64_t C, bool ns_bf16) {
+    if (ns_gram_tiles(R, C) > 3) return 0;
+    const int64_t c = R > C ? R : C, bk = ns_bf16 ? 32 : 16;
+    const int64_t s = (c + bk - 1) / bk / 16;
+    return (int32_t)(s < 2 ? 0 : (s > 8 ? 8 : s));
+}
 void launch_ns_product(const NsBatch &b, bool ns_bf16, NsEpilogue epi, hipStream_t s);
 // The final product with bf16 operands when every matrix of b takes its
 // signs straight from the accumulators, packed (packed set) or as int8 (i8,
