@@ -269,19 +269,25 @@ int device_cus() {
     return n;
 }
 
-// Launch groups of the final product. The persistent kernel takes bf16
-// matrices whose signs (packed or int8) come straight from the accumulators
-// and whose k loop suits its tile walk (16-byte operands, k slices a
-// multiple of the 4 pipeline stages and at least the 256 identity k plus one
-// stage round); wide and tall matrices go in separate launches. Everything else, and every other
+// Launch groups of a product. The persistent kernel takes bf16 matrices
+// whose k loop suits its tile walk (16-byte operands, k slices a multiple of
+// the 4 pipeline stages and at least the 256 identity k plus one stage
+// round), for the next iterate or the final signs (packed or int8) straight
+// from the accumulators; wide and tall matrices go in separate launches. Everything else, and every other
 // product, uses the one-tile-per-block kernel.
 enum ProdGroup { PG_PLAIN = 0, PG_WALK_WIDE = 1, PG_WALK_TALL = 2 };
 constexpr int PG_SPLIT = 1;  // the Gram pass's second group: split k
 
-int product_group(const MatPlan &q, const sm::NsMat &d, bool bf16) {
-    if (!bf16 || d.out || !(d.packed || d.i8)) return PG_PLAIN;
+int product_group(const MatPlan &q, const sm::NsMat &d, bool bf16, sm::NsEpilogue epi) {
+    if (!bf16) return PG_PLAIN;
+    if (epi == sm::EPI_FINAL || epi == sm::EPI_FINAL_I8) {
+        // signs straight from the accumulators: no U output
+        if (d.out || !(d.packed || d.i8) || q.C % 64) return PG_PLAIN;
+    } else if (epi != sm::EPI_ITER) {
+        return PG_PLAIN;  // the W update stays on the one-tile-per-block kernel
+    }
     const int64_t kt_n = (q.r + 31) / 32;  // 32-wide bf16 k slices
-    if (q.C % 64 || q.r % 8 || q.n * 2 >= ((int64_t)1 << 31)) return PG_PLAIN;
+    if (q.C % 8 || q.r % 8 || q.n * 2 >= ((int64_t)1 << 31)) return PG_PLAIN;
     if (kt_n % 4 || kt_n < 256 / 32 + 4) return PG_PLAIN;
     return q.R > q.C ? PG_WALK_TALL : PG_WALK_WIDE;
 }
@@ -331,10 +337,10 @@ int ns_pass(const signmuon_matrix *mats, int32_t n_mats, const signmuon_params *
     std::vector<int32_t> groups[3];
     for (int32_t i = 0; i < n_mats; ++i) {
         int g = PG_PLAIN;
-        if (pass == 1 && (epi == sm::EPI_FINAL || epi == sm::EPI_FINAL_I8)) {
+        if (pass == 1) {
             sm::NsMat d;
             describe(i, d);
-            g = product_group(pl.m[i], d, bf16);
+            g = product_group(pl.m[i], d, bf16, epi);
         } else if (pass == 0 && pl.m[i].gram_split > 0) {
             g = PG_SPLIT;
         }
@@ -385,8 +391,7 @@ int ns_pass(const signmuon_matrix *mats, int32_t n_mats, const signmuon_params *
             else if (g == PG_PLAIN)
                 sm::launch_ns_product(b, bf16, epi, st);
             else
-                sm::launch_ns_product_pack(b, g == PG_WALK_TALL, epi == sm::EPI_FINAL_I8,
-                                           std::min(b.total_tiles, device_cus()), st);
+                sm::launch_ns_product_pack(b, g == PG_WALK_TALL, epi, std::min(b.total_tiles, device_cus()), st);
             if (int rc = tr.after(pass == 0 ? SIGNMUON_K_GRAM : SIGNMUON_K_PRODUCT)) return rc;
         }
     }

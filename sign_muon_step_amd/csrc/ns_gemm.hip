@@ -1231,6 +1231,48 @@ __device__ __forceinline__ void int8_from_registers(const ProductArgs &pa, const
     });
 }
 
+// Epilogue of the walk for the next bf16 iterate (EPI_ITER), staged 8 rows
+// at a time through the wave's own 8 x kStageStride floats outside the stage
+// buffers, so that the next tile's loads keep landing meanwhile. Register
+// 4q + t of block (f, g) holds row 8q + 4h + t (h = lane / 32) of the block;
+// the arithmetic is that of product_epilogue (u = gamma * acc, one RNE
+// rounding to bf16). (The W update is not walked: its loads of W, waited for
+// one pass at a time, would serialise the epilogue.)
+template <int EPI, bool FAST, class Tid>
+__device__ __forceinline__ void walk_staged_epilogue(const ProductArgs &pa, const f32x16_t (&acc)[kFM][kFN],
+                                                     Tid tid, float *estage) {
+    const float gamma = -0.5f * pa.s.get();
+    const int lane = tid() & (kWave - 1), wid = tid() / kWave;
+    const int m0 = pa.ti * kNsTileM + ProdLay::m0(wid), n0 = pa.tj * kNsProdTileN + ProdLay::n0(wid);
+    float *st = estage + wid * 8 * kStageStride;
+    const int R = pa.R, C = pa.C;
+#pragma unroll
+    for (int f = 0; f < kFM; ++f)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+#pragma unroll
+            for (int g = 0; g < kFN; ++g)
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+                    st[(4 * (lane >> 5) + t) * kStageStride + 32 * g + (lane & 31)] = acc[f][g][4 * q + t] * 1.0f;
+            wave_lds_fence();
+#pragma unroll
+            for (int it = 0; it < 8 / kRowsPerInstr; ++it) {
+                const int row = it * kRowsPerInstr + lane / kLanesPerRow, c4 = (lane % kLanesPerRow) * 4;
+                const int gm = m0 + f * 32 + 8 * q + row, gn = n0 + c4;
+                const int64_t idx = (int64_t)gm * C + gn;
+                const float4 v4 = *reinterpret_cast<const float4 *>(st + row * kStageStride + c4);
+                const float v[4] = {v4.x, v4.y, v4.z, v4.w};
+                float u[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) u[e] = (FAST || (gm < R && gn + e < C)) ? gamma * v[e] : 0.f;
+                static_assert(EPI == EPI_ITER, "the staged walk epilogue writes the next iterate");
+                store4<true, FAST>(pa.out, idx, u, gm < R, C - gn);
+            }
+            wave_lds_fence();
+        }
+}
+
 // Entry e of the int8 table: byte j is +1 where bit j of e is set, else -1.
 __device__ __forceinline__ uint2 int8_table_entry(int e) {
     uint32_t w[2] = {0u, 0u};
@@ -1314,9 +1356,10 @@ void ns_product_kernel(NsBatch b) {
 }
 
 // ---------------------------------------------------------------------------
-// Persistent final product with the signs (packed, or int8) straight from
-// the accumulators, for a bf16 launch in which every matrix takes them that
-// way (no U output, C % 64 == 0, 16-byte operands). One workgroup per CU walks the tiles vb =
+// Persistent product for a bf16 launch: the final product with the signs
+// (packed, or int8) straight from the accumulators (no U output, C % 64 ==
+// 0), or an intermediate product whose output (the next iterate) is staged
+// through LDS outside the stage buffers; 16-byte operands. One workgroup per CU walks the tiles vb =
 // blockIdx.x, vb + gridDim.x, ... in the same XCD-contiguous order as the
 // one-tile-per-block kernel. The direct-to-LDS pipeline runs on across tile
 // boundaries: the loads that a tile's last iterations would issue past its
@@ -1339,8 +1382,10 @@ struct PackTile {
         return j >= kt_n ? kt_n : (t < kt_n ? t : t - kt_n);
     }
 
-    // i8: the signs go to M.i8 as int8, else packed to M.packed.
-    __device__ __forceinline__ void decode(const NsBatch &b, int sv, int lt, bool i8) {
+    // EPI: what the tile's epilogue writes (packed signs to M.packed, int8
+    // signs to M.i8, or the next iterate to M.out).
+    template <int EPI>
+    __device__ __forceinline__ void decode(const NsBatch &b, int sv, int lt) {
         using T = typename Elem<BF16>::T;
         constexpr int BK = Elem<BF16>::BK;
         const int w = lt / b.tiles_per_worker_all;
@@ -1355,10 +1400,10 @@ struct PackTile {
         const int64_t n = (int64_t)R * C;
         const char *x = static_cast<const char *>(M.x) + (int64_t)w * n * (int64_t)sizeof(T);
         const char *a = static_cast<const char *>(M.a) + (int64_t)w * r * r * (int64_t)sizeof(T);
-        pa.out = nullptr;
+        pa.out = EPI == EPI_ITER ? static_cast<char *>(M.out) + (int64_t)w * n * (int64_t)sizeof(T) : nullptr;
         pa.u_out = nullptr;
-        pa.i8 = i8 ? M.i8 + (int64_t)w * n : nullptr;
-        pa.pk = i8 ? nullptr : M.packed + (int64_t)w * ((n + 63) >> 6);
+        pa.i8 = EPI == EPI_FINAL_I8 ? M.i8 + (int64_t)w * n : nullptr;
+        pa.pk = EPI == EPI_FINAL ? M.packed + (int64_t)w * ((n + 63) >> 6) : nullptr;
         pa.R = R;
         pa.C = C;
         pa.ti = ti;
@@ -1514,13 +1559,15 @@ __device__ __forceinline__ void pack_tile_kloop(const PackTile<BF16> &cur, const
 }
 
 // QKC: every matrix of the launch is tall (true) or wide (false). EPI:
-// EPI_FINAL (packed signs) or EPI_FINAL_I8 (int8 signs).
+// EPI_FINAL (packed signs), EPI_FINAL_I8 (int8 signs) or EPI_ITER (the next
+// iterate).
 template <bool BF16, bool QKC, int EPI>
 __global__ __launch_bounds__(ProdLay::kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void ns_product_pack_kernel(NsBatch b) {
     static_assert(BF16, "the walk is built for bf16 operands");
-    static_assert(EPI == EPI_FINAL || EPI == EPI_FINAL_I8, "sign epilogues only");
     constexpr bool kI8 = EPI == EPI_FINAL_I8;
+    static_assert(EPI == EPI_FINAL || EPI == EPI_FINAL_I8 || EPI == EPI_ITER, "walked epilogues");
+    constexpr bool kStaged = EPI == EPI_ITER;
     using L = ProdLay;
     constexpr int S = L::kStages, PL = L::kPLoads, QL = L::kQLoads, NLD = PL + QL;
     __shared__ __attribute__((aligned(16))) char smem[L::kLdsBytes];
@@ -1529,6 +1576,7 @@ void ns_product_pack_kernel(NsBatch b) {
     // reload would wait for every load in flight).
     __shared__ int starts[kWave];
     __shared__ uint2 i8_table[kI8 ? 256 : 1];
+    __shared__ __attribute__((aligned(16))) float estage[kStaged ? L::kWaves * 8 * kStageStride : 1];
     const int sv = ns_start_of_lane();
     if (threadIdx.x < kWave) starts[threadIdx.x] = sv;
     if (kI8 && threadIdx.x < 256) i8_table[threadIdx.x] = int8_table_entry((int)threadIdx.x);
@@ -1537,7 +1585,7 @@ void ns_product_pack_kernel(NsBatch b) {
     int vb = blockIdx.x;
     PackTile<BF16> cur, nxt;
     DmaSlices<BF16, 256, L::kWaves> lp, lq;
-    cur.decode(b, sv, xcd_remap(vb, total), kI8);
+    cur.template decode<EPI>(b, sv, xcd_remap(vb, total));
     lp.template setup<true>(cur.P);
     lq.template setup<QKC>(cur.Q);
     // The first tile fills the pipeline itself: slices 0 .. S - 2 and the P
@@ -1564,14 +1612,20 @@ void ns_product_pack_kernel(NsBatch b) {
         const int vn = vb + G;
         const bool more = vn < total;
         if (more)
-            nxt.decode(b, starts[lane], xcd_remap(vn, total), kI8);
+            nxt.template decode<EPI>(b, starts[lane], xcd_remap(vn, total));
         else
             nxt.none();
         pack_tile_kloop<BF16, QKC>(cur, nxt, lp, lq, smem, acc, tid);
-        if constexpr (kI8)
+        if constexpr (kI8) {
             int8_from_registers(cur.pa, acc, tid, i8_table);
-        else
+        } else if constexpr (kStaged) {
+            if ((cur.pa.ti + 1) * kNsTileM <= cur.pa.R && (cur.pa.tj + 1) * kNsProdTileN <= cur.pa.C)
+                walk_staged_epilogue<EPI, true>(cur.pa, acc, tid, estage);
+            else
+                walk_staged_epilogue<EPI, false>(cur.pa, acc, tid, estage);
+        } else {
             pack_from_registers<GivenTid>(cur.pa, acc, tid);
+        }
         if (!more) break;
         vb = vn;
         cur = nxt;
@@ -1624,16 +1678,18 @@ void launch_ns_product(const NsBatch &b, bool ns_bf16, NsEpilogue epi, hipStream
 #undef SM_PROD
 }
 
-void launch_ns_product_pack(const NsBatch &b, bool tall, bool i8, int grid_blocks, hipStream_t s) {
+void launch_ns_product_pack(const NsBatch &b, bool tall, NsEpilogue epi, int grid_blocks, hipStream_t s) {
     dim3 grid(grid_blocks), block(ProdLay::kThreads);
 #define SM_WALK(TALL, E) hipLaunchKernelGGL((ns_product_pack_kernel<true, TALL, E>), grid, block, 0, s, b)
-    if (i8) {
-        if (tall) SM_WALK(true, EPI_FINAL_I8);
-        else SM_WALK(false, EPI_FINAL_I8);
-    } else {
-        if (tall) SM_WALK(true, EPI_FINAL);
-        else SM_WALK(false, EPI_FINAL);
-    }
+#define SM_WALK2(E) \
+    do {                            \
+        if (tall) SM_WALK(true, E);  \
+        else SM_WALK(false, E);      \
+    } while (0)
+    if (epi == EPI_FINAL_I8) SM_WALK2(EPI_FINAL_I8);
+    else if (epi == EPI_ITER) SM_WALK2(EPI_ITER);
+    else SM_WALK2(EPI_FINAL);
+#undef SM_WALK2
 #undef SM_WALK
 }
 

@@ -144,14 +144,15 @@ inline int32_t ns_gram_split(int64_t R, int64_t C, bool ns_bf16) {
     return (int32_t)(s < 2 ? 0 : (s > 8 ? 8 : s));
 }
 void launch_ns_product(const NsBatch &b, bool ns_bf16, NsEpilogue epi, hipStream_t s);
-// The final product with bf16 operands when every matrix of b takes its
-// signs straight from the accumulators, packed (packed set) or as int8 (i8,
-// i8 set), with no U output (out null), C % 64 == 0, C and min(R, C)
-// multiples of 8, each worker's matrix under 2 GiB, and ceil(min(R, C) / 32)
-// a multiple of 4 and at least 12, and every matrix is tall (R > C) or every
-// one wide: grid_blocks workgroups (one per CU, at most b.total_tiles) walk
-// the tiles with the load pipeline running across tile boundaries.
-void launch_ns_product_pack(const NsBatch &b, bool tall, bool i8, int grid_blocks, hipStream_t s);
+// A product with bf16 operands as a persistent tile walk: grid_blocks
+// workgroups (one per CU, at most b.total_tiles) walk the tiles with the
+// load pipeline running across tile boundaries. Every matrix of b is tall
+// (R > C) or every one wide; C and min(R, C) are multiples of 8, each
+// worker's matrix is under 2 GiB, and ceil(min(R, C) / 32) is a multiple of
+// 4 and at least 12. epi: EPI_FINAL (packed set, out null, C % 64 == 0),
+// EPI_FINAL_I8 (i8 set, out null, C % 64 == 0) or EPI_ITER (out: the next
+// iterate, as for launch_ns_product).
+void launch_ns_product_pack(const NsBatch &b, bool tall, NsEpilogue epi, int grid_blocks, hipStream_t s);
 
 // ---------------------------------------------------------------------------
 // Sign + pack of a stored U, and scale + sign + pack for k = 0.

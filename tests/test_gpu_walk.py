@@ -215,3 +215,31 @@ def test_walk_degenerate_workers_match_oracle():
         np.testing.assert_array_equal(pw[w], packed_ref[w], err_msg=f"{kind} worker")
         want = np.uint64(0xFFFFFFFFFFFFFFFF) if kind == "zero" else np.uint64(0)
         assert (pw[w] == want).all()
+
+
+def test_walk_iterates_do_not_depend_on_the_batch():
+    """k = 3: the intermediate products write the next iterate from the walk
+    (staged through LDS beside the stage buffers). A matrix's U must be the
+    same bit for bit alone (one tile per workgroup) and among 40 others
+    (several tiles per workgroup, wide and tall launches), and within the
+    Newton-Schulz tolerance of the oracle's."""
+    mw, k = 4, 3
+    target = (768, 1024)
+    others = [(640, 1216), (1216, 640), (384, 1024), (1024, 384)] * 10
+    p = sm.Params(workers=mw, beta=0.9, eta=1e-3, ns_iters=k, mom_dtype=sm.BF16, ns_dtype=sm.BF16)
+    alone, host = build([target], mw, 9700, polar=True)
+    sm.signmuon_step(alone, p, sm.workspace_tensor(alone, p, DEV))
+    batch, _ = build([target] + others, mw, 9700, polar=True)  # same seeds for the target
+    announce(f"  target alone, then among {len(others)} others")
+    sm.signmuon_step(batch, p, sm.workspace_tensor(batch, p, DEV))
+    torch.cuda.synchronize()
+    u = to_host(alone[0].polar_out)
+    np.testing.assert_array_equal(u, to_host(batch[0].polar_out))
+    np.testing.assert_array_equal(to_host(alone[0].packed), to_host(batch[0].packed))
+    m_ref = np.zeros((mw,) + target, np.uint16)
+    oracle.momentum(host[0][0], m_ref, 0.9)
+    _, x0 = oracle.normalise(m_ref[1])
+    u_ref = oracle.newton_schulz(x0, k, oracle.BF16)
+    err = np.linalg.norm(u[1] - u_ref) / np.linalg.norm(u_ref)
+    announce(f"  {target} worker 1, k = {k}: rel err {err:.2e}")
+    assert err <= 2e-2
