@@ -24,6 +24,14 @@
 // steps 2-3, and "Communication efficiency"); or (Muon step, post-vote polar
 // step) it applies W <- fmaf(-eta, Y, W).
 //
+// Kernels: ns_gram_kernel (one block per Gram tile; for matrices with at
+// most 3 Gram tiles per worker, one block per k chunk of a tile, writing fp32
+// partial tiles that gram_reduce_kernel adds in order, scales and stores);
+// ns_product_kernel (one block per output tile, every epilogue); and
+// ns_product_pack_kernel, the bf16 products as a persistent walk of one
+// workgroup per CU whose direct-to-LDS loads run on across tile boundaries
+// (final signs packed or int8 from the accumulators, or the next iterate).
+//
 // Every GEMM is C[m][n] = sum_k P[m][k] Q[n][k] on a 256 x TN output tile
 // computed by waves of 128 x 64, two waves per SIMD (one wave's LDS reads and
 // waits overlap the other's matrix instructions). Both kernels use TN = 256:
