@@ -346,6 +346,17 @@ int ns_pass(const signmuon_matrix *mats, int32_t n_mats, const signmuon_params *
         }
         groups[g].push_back(i);
     }
+    // The Gram's tiles take time in proportion to their k range and blocks
+    // are handed out in order: longest k first (stable), so that the short
+    // tiles fill the end of the launch. Each tile is computed on its own, so
+    // the order changes no result.
+    if (pass == 0)
+        for (auto &idx : groups)
+            std::stable_sort(idx.begin(), idx.end(), [&](int32_t x, int32_t y) {
+                const int64_t cx = pl.m[x].R > pl.m[x].C ? pl.m[x].R : pl.m[x].C;
+                const int64_t cy = pl.m[y].R > pl.m[y].C ? pl.m[y].R : pl.m[y].C;
+                return cx > cy;
+            });
     for (int g = 0; g < 3; ++g) {
         const std::vector<int32_t> &idx = groups[g];
         for (size_t c0 = 0; c0 < idx.size(); c0 += sm::kMaxMatsPerLaunch) {
