@@ -269,33 +269,34 @@ int device_cus() {
     return n;
 }
 
-// Launch groups of a product. The persistent kernel takes bf16 matrices
-// whose k loop suits its tile walk (16-byte operands, k slices a multiple of
-// the 4 pipeline stages and at least the 256 identity k plus one stage
-// round), for the next iterate or the final signs (packed or int8) straight
-// from the accumulators; wide and tall matrices go in separate launches. Everything else, and every other
-// product, uses the one-tile-per-block kernel.
-enum ProdGroup { PG_PLAIN = 0, PG_WALK_WIDE = 1, PG_WALK_TALL = 2 };
-constexpr int PG_SPLIT = 1;  // the Gram pass's second group: split k
+// Launch groups of one Newton-Schulz pass. Product: LG_DIRECT (one block per
+// tile) or the persistent walk, whose wide and tall matrices go in separate
+// launches (LG_WALK_WIDE, LG_WALK_TALL). Gram: LG_DIRECT (whole k range) or
+// LG_GRAM_SPLIT (split k, then the reduce).
+enum LaunchGroup { LG_DIRECT = 0, LG_WALK_WIDE = 1, LG_WALK_TALL = 2, LG_GRAM_SPLIT = 1 };
 
+// The walk takes bf16 matrices whose k loop suits it (16-byte operands, k
+// slices a multiple of the 4 pipeline stages and at least the 256 identity
+// k plus one stage round), for the next iterate or the final signs (packed
+// or int8) straight from the accumulators.
 int product_group(const MatPlan &q, const sm::NsMat &d, bool bf16, sm::NsEpilogue epi) {
-    if (!bf16) return PG_PLAIN;
+    if (!bf16) return LG_DIRECT;
     if (epi == sm::EPI_FINAL || epi == sm::EPI_FINAL_I8) {
         // signs straight from the accumulators: no U output
-        if (d.out || !(d.packed || d.i8) || q.C % 64) return PG_PLAIN;
+        if (d.out || !(d.packed || d.i8) || q.C % 64) return LG_DIRECT;
     } else if (epi != sm::EPI_ITER) {
-        return PG_PLAIN;  // the W update stays on the one-tile-per-block kernel
+        return LG_DIRECT;  // the W update stays on the one-tile-per-block kernel
     }
     const int64_t kt_n = (q.r + 31) / 32;  // 32-wide bf16 k slices
-    if (q.C % 8 || q.r % 8 || q.n * 2 >= ((int64_t)1 << 31)) return PG_PLAIN;
-    if (kt_n % 4 || kt_n < 256 / 32 + 4) return PG_PLAIN;
-    return q.R > q.C ? PG_WALK_TALL : PG_WALK_WIDE;
+    if (q.C % 8 || q.r % 8 || q.n * 2 >= ((int64_t)1 << 31)) return LG_DIRECT;
+    if (kt_n % 4 || kt_n < 256 / 32 + 4) return LG_DIRECT;
+    return q.R > q.C ? LG_WALK_TALL : LG_WALK_WIDE;
 }
 
 // One Newton-Schulz launch pass over every (matrix, worker): iteration j's
 // Gram matrix (pass 0) or product (pass 1). use_scales folds s^2 (Gram) or s
 // (product) of iteration 0 in. The last product's epilogue writes U
-// (polar_out or scratch) and, for step, the fused packed signs.
+// (polar_out or scratch) and, for step, the signs (packed or int8).
 int ns_pass(const signmuon_matrix *mats, int32_t n_mats, const signmuon_params *p, const Plan &pl,
             void *ws, bool step, int j, int pass, bool use_scales, hipStream_t st, Tracer &tr,
             bool muon = false) {
@@ -331,18 +332,16 @@ int ns_pass(const signmuon_matrix *mats, int32_t n_mats, const signmuon_params *
     };
     const sm::NsEpilogue epi = !last ? sm::EPI_ITER
                                      : (muon ? sm::EPI_WUPD : (step && pl.i8 ? sm::EPI_FINAL_I8 : sm::EPI_FINAL));
-    // The matrices of each launch group, in order: for the product, the
-    // one-tile-per-block kernel and the walk's wide and tall launches; for the
-    // Gram, the whole-k kernel and the split one (PG_SPLIT, then the reduce).
+    // The matrices of each launch group, in order.
     std::vector<int32_t> groups[3];
     for (int32_t i = 0; i < n_mats; ++i) {
-        int g = PG_PLAIN;
+        int g = LG_DIRECT;
         if (pass == 1) {
             sm::NsMat d;
             describe(i, d);
             g = product_group(pl.m[i], d, bf16, epi);
         } else if (pass == 0 && pl.m[i].gram_split > 0) {
-            g = PG_SPLIT;
+            g = LG_GRAM_SPLIT;
         }
         groups[g].push_back(i);
     }
@@ -367,7 +366,7 @@ int ns_pass(const signmuon_matrix *mats, int32_t n_mats, const signmuon_params *
             b.use_scales = use_scales;
             b.scales = scales;
             b.eta = p->eta;  // the W-update epilogue
-            const bool split = pass == 0 && g == PG_SPLIT;
+            const bool split = pass == 0 && g == LG_GRAM_SPLIT;
             // split Gram: Gram tiles x split blocks per worker; the reduce
             // then runs 16 blocks per Gram tile
             auto number_tiles = [&](int per_tile) {
@@ -399,10 +398,10 @@ int ns_pass(const signmuon_matrix *mats, int32_t n_mats, const signmuon_params *
                 sm::launch_gram_reduce(b, bf16, st);
             } else if (pass == 0)
                 sm::launch_ns_gram(b, bf16, st);
-            else if (g == PG_PLAIN)
+            else if (g == LG_DIRECT)
                 sm::launch_ns_product(b, bf16, epi, st);
             else
-                sm::launch_ns_product_pack(b, g == PG_WALK_TALL, epi, std::min(b.total_tiles, device_cus()), st);
+                sm::launch_ns_product_pack(b, g == LG_WALK_TALL, epi, std::min(b.total_tiles, device_cus()), st);
             if (int rc = tr.after(pass == 0 ? SIGNMUON_K_GRAM : SIGNMUON_K_PRODUCT)) return rc;
         }
     }
