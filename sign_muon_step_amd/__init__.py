@@ -305,7 +305,9 @@ class Prepared:
         self.n = len(mats)
         self.ws = _ptr(workspace)
         self.nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-        self._keep = (list(mats), workspace)
+        # the tensors themselves: a field of a Matrix reassigned later must not
+        # free a buffer whose pointer is marshalled here
+        self._keep = ([t for m in mats for _, t in _buffers(m) if t is not None], workspace)
 
     def _args(self, stream):
         return self.arr, self.n, ctypes.byref(self.p), self.ws, self.nbytes, _stream(stream)
@@ -324,20 +326,47 @@ class Prepared:
         _check(library().signmuon_muon_step(*self._args(stream)))
 
 
+def _expect_room(t: Optional[torch.Tensor], name: str, dtypes, numel: int) -> None:
+    """For the single-stage calls: element type, and at least `numel` elements
+    (the kernels touch exactly that many; a shorter buffer would be accessed
+    out of bounds). Sizes are checked only for a valid n and worker count; the
+    library rejects the others."""
+    if t is None:
+        return
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name}: dtype {t.dtype}, expected {' or '.join(map(str, dtypes))}")
+    if numel > 0 and t.numel() < numel:
+        raise ValueError(f"{name}: {t.numel()} elements, at least {numel} needed")
+
+
+def _words(n: int) -> int:
+    return (n + 63) // 64 if n > 0 else 0
+
+
 def signmuon_sign_pack(u: torch.Tensor, n: int, workers: int, packed: torch.Tensor,
                        stream=None) -> None:
+    k = workers if workers > 0 else 0
+    _expect_room(u, "u", (torch.float32, torch.bfloat16), k * max(n, 0))
+    _expect_room(packed, "packed", (torch.int64,), k * _words(n))
     _check(library().signmuon_sign_pack(_ptr(u), _dtype_code(u), n, workers, _ptr(packed),
                                         _stream(stream)))
 
 
 def signmuon_vote_update(packed: torch.Tensor, workers: int, n: int, weight: Optional[torch.Tensor],
                          eta: float, vote_out: Optional[torch.Tensor] = None, stream=None) -> None:
+    k = workers if workers > 0 else 0
+    _expect_room(packed, "packed", (torch.int64,), k * _words(n))
+    _expect_room(weight, "weight", (torch.float32,), max(n, 0))
+    _expect_room(vote_out, "vote_out", (torch.int8,), max(n, 0))
     _check(library().signmuon_vote_update(_ptr(packed), workers, n, _ptr(weight), eta,
                                           _ptr(vote_out), _stream(stream)))
 
 
 def signmuon_sign_int8(u: torch.Tensor, n: int, workers: int, signs: torch.Tensor,
                        stream=None) -> None:
+    k = workers if workers > 0 else 0
+    _expect_room(u, "u", (torch.float32, torch.bfloat16), k * max(n, 0))
+    _expect_room(signs, "signs", (torch.int8,), k * max(n, 0))
     _check(library().signmuon_sign_int8(_ptr(u), _dtype_code(u), n, workers, _ptr(signs),
                                         _stream(stream)))
 
@@ -345,6 +374,10 @@ def signmuon_sign_int8(u: torch.Tensor, n: int, workers: int, signs: torch.Tenso
 def signmuon_vote_update_int8(signs: torch.Tensor, workers: int, n: int,
                               weight: Optional[torch.Tensor], eta: float,
                               vote_out: Optional[torch.Tensor] = None, stream=None) -> None:
+    k = workers if workers > 0 else 0
+    _expect_room(signs, "signs", (torch.int8,), k * max(n, 0))
+    _expect_room(weight, "weight", (torch.float32,), max(n, 0))
+    _expect_room(vote_out, "vote_out", (torch.int8,), max(n, 0))
     _check(library().signmuon_vote_update_int8(_ptr(signs), workers, n, _ptr(weight), eta,
                                                _ptr(vote_out), _stream(stream)))
 

@@ -58,3 +58,25 @@ def test_host_memory_is_refused():
         call(cpu_matrix())
     with pytest.raises(ValueError, match="GPU memory"):
         sm.signmuon_sign_pack(torch.zeros(64), 64, 1, torch.zeros(1, dtype=torch.int64))
+
+
+def test_single_stage_calls_refuse_short_buffers():
+    # checked before the library sees a pointer; the buffers are CPU tensors, so
+    # a buffer that passes the size check is then refused as host memory
+    u = torch.zeros(2 * 100)
+    with pytest.raises(ValueError, match="packed"):
+        sm.signmuon_sign_pack(u, 100, 2, torch.zeros(3, dtype=torch.int64))
+    with pytest.raises(ValueError, match="u:"):
+        sm.signmuon_sign_pack(torch.zeros(199), 100, 2, torch.zeros(4, dtype=torch.int64))
+    with pytest.raises(ValueError, match="signs"):
+        sm.signmuon_sign_int8(u, 100, 2, torch.zeros(199, dtype=torch.int8))
+    with pytest.raises(ValueError, match="weight"):
+        sm.signmuon_vote_update(torch.zeros(4, dtype=torch.int64), 2, 100, torch.zeros(99), 1e-3)
+    with pytest.raises(ValueError, match="vote_out"):
+        sm.signmuon_vote_update_int8(torch.zeros(200, dtype=torch.int8), 2, 100, None, 1e-3,
+                                     torch.zeros(99, dtype=torch.int8))
+    with pytest.raises(TypeError, match="packed"):
+        sm.signmuon_vote_update(torch.zeros(4, dtype=torch.int32), 2, 100, None, 1e-3)
+    with pytest.raises(ValueError, match="GPU memory"):
+        sm.signmuon_sign_pack(u, 100, 2, torch.zeros(4, dtype=torch.int64))
+
