@@ -234,10 +234,11 @@ __global__ __launch_bounds__(256) void finalize_scales_kernel(MomBatch b) {
 // 2-3): word w of a worker holds entries 64w..64w+63, bit j = (u >= 0) for
 // entry 64w + j. In little-endian byte order, byte c of a worker's words is
 // then the 8 signs of entries 8c..8c+7 (bit t = entry 8c + t), so each lane
-// packs whole 8-entry chunks: one 16-byte load (bf16) or two (fp32), one byte
-// stored. A block's chunks are interleaved by thread, so every wave load
-// covers 1 KiB (bf16) of consecutive entries and every store 64 consecutive
-// bytes. Entries past n, up to the end of the last word, pack as 0. With an
+// packs whole 8-entry chunks: one 16-byte load (bf16) or two (fp32) give one
+// byte, stored by its lane (bf16) or gathered with its 7 neighbours into one
+// 8-byte word store (fp32). A block's chunks are interleaved by thread, so
+// every wave load covers 1 KiB (bf16) of consecutive entries and every wave
+// store 64 consecutive bytes. Entries past n, up to the end of the last word, pack as 0. With an
 // int8 target the chunk's 8 signs are stored as +1 / -1 bytes instead (one
 // 8-byte store per chunk).
 // ---------------------------------------------------------------------------
