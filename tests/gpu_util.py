@@ -72,3 +72,15 @@ def sign_stats(u_gpu: np.ndarray, u_ref: np.ndarray):
     n = int(keep.sum())
     bad = int((~same & keep).sum())
     return (1.0 if n == 0 else 1.0 - bad / n), bad, n
+
+
+def bit_sign_stats(packed_words: np.ndarray, u_ref: np.ndarray):
+    """sign_stats for packed bits (LSB-first words, bit 1 = +1) against a
+    reference U: agreement over the entries with |U| >= 1e-6 max|U|."""
+    n = u_ref.size
+    bits = np.unpackbits(packed_words.view(np.uint8), bitorder="little")[:n].astype(bool)
+    ref = u_ref.ravel()
+    keep = np.abs(ref) >= 1e-6 * float(np.abs(ref).max())
+    bad = int((bits != (ref >= 0))[keep].sum())
+    cnt = int(keep.sum())
+    return (1.0 if cnt == 0 else 1.0 - bad / cnt), bad, cnt
