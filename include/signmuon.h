@@ -17,8 +17,9 @@
  *  - A matrix is R x C, row-major and contiguous; n = R * C >= 1.
  *  - Per-worker arrays are stacked: [Mw][R][C], worker m at offset m * n.
  *  - All data pointers are DEVICE pointers owned by the caller. The library
- *    allocates no memory, frees nothing and keeps no state between calls;
- *    every call may be made from any host thread.
+ *    allocates no memory, frees nothing and keeps no state between calls
+ *    (except signmuon_step_noalloc's static scratch, below); every call may be
+ *    made from any host thread.
  *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
  *    the call returns without waiting for it. The library never synchronises.
  *    The compute entry points enqueue only kernel launches (no allocation, no
@@ -50,7 +51,7 @@
 extern "C" {
 #endif
 
-#define SIGNMUON_ABI_VERSION 3
+#define SIGNMUON_ABI_VERSION 4
 
 /* Status codes. */
 enum {
@@ -60,7 +61,9 @@ enum {
     SIGNMUON_EALIGN = -3,     /* a device pointer is not 16-byte aligned */
     SIGNMUON_EWORKSPACE = -4, /* workspace missing or smaller than required */
     SIGNMUON_EHIP = -5,       /* a HIP call failed */
-    SIGNMUON_ERANGE = -6      /* a size exceeds what the kernels index */
+    SIGNMUON_ERANGE = -6,     /* a size exceeds what the kernels index */
+    SIGNMUON_ESCRATCH = -7    /* signmuon_step_noalloc: the step's workspace exceeds
+                                 SIGNMUON_STATIC_SCRATCH_BYTES */
 };
 
 typedef enum { SIGNMUON_F32 = 0, SIGNMUON_BF16 = 1 } signmuon_dtype;
@@ -237,6 +240,27 @@ int signmuon_step(const signmuon_matrix *mats, int32_t n_mats, const signmuon_pa
  */
 int signmuon_muon_step(const signmuon_matrix *mats, int32_t n_mats, const signmuon_params *p,
                        void *workspace, size_t workspace_bytes, signmuon_stream stream);
+
+/*
+ * signmuon_step_noalloc -- signmuon_step for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation): the same launches and results, with the workspace
+ * taken from a static device array inside the library instead of a caller's
+ * buffer. The array holds SIGNMUON_STATIC_SCRATCH_BYTES per GPU; it is
+ * reserved on each GPU the library runs on and held until the process ends,
+ * and its device address is looked up on the first call on each device.
+ * Arguments, ownership and errors are those of signmuon_step, plus
+ * SIGNMUON_ESCRATCH when signmuon_workspace_bytes(mats, n_mats, p) exceeds
+ * the array (checked before any HIP call; nothing is enqueued). The call
+ * allocates nothing. No part of the array needs to start at zero: every part
+ * a step reads, it has written first in the same stream order. All calls on
+ * one GPU share its array, so two calls whose work overlaps in time on the
+ * same GPU (different streams or host threads without ordering) race and
+ * give undefined results; order them on one stream.
+ */
+#define SIGNMUON_STATIC_SCRATCH_BYTES (128u << 20)
+int signmuon_step_noalloc(const signmuon_matrix *mats, int32_t n_mats, const signmuon_params *p,
+                          signmuon_stream stream);
 
 /* Kernel kinds reported by signmuon_step_traced, one per launch. */
 enum {

@@ -21,10 +21,13 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libsignmuon.so")
 
 F32, BF16 = 0, 1
-ABI_VERSION = 3
+ABI_VERSION = 4
+# device bytes of the static scratch behind signmuon_step_noalloc
+STATIC_SCRATCH_BYTES = 128 << 20
 
 STATUS = {0: "SIGNMUON_OK", -1: "SIGNMUON_EINVAL", -2: "SIGNMUON_EDTYPE", -3: "SIGNMUON_EALIGN",
-          -4: "SIGNMUON_EWORKSPACE", -5: "SIGNMUON_EHIP", -6: "SIGNMUON_ERANGE"}
+          -4: "SIGNMUON_EWORKSPACE", -5: "SIGNMUON_EHIP", -6: "SIGNMUON_ERANGE",
+          -7: "SIGNMUON_ESCRATCH"}
 
 
 class SignmuonError(RuntimeError):
@@ -76,6 +79,8 @@ def library() -> ctypes.CDLL:
     lib.signmuon_momentum_ns.argtypes = [mp, i32, pp, vp, ctypes.c_size_t, vp]
     lib.signmuon_step.restype = ctypes.c_int
     lib.signmuon_step.argtypes = [mp, i32, pp, vp, ctypes.c_size_t, vp]
+    lib.signmuon_step_noalloc.restype = ctypes.c_int
+    lib.signmuon_step_noalloc.argtypes = [mp, i32, pp, vp]
     lib.signmuon_muon_step.restype = ctypes.c_int
     lib.signmuon_muon_step.argtypes = [mp, i32, pp, vp, ctypes.c_size_t, vp]
     lib.signmuon_step_traced.restype = ctypes.c_int
@@ -256,6 +261,14 @@ def signmuon_step(mats: Sequence[Matrix], params: Params, workspace: Optional[to
     nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(library().signmuon_step(arr, len(mats), ctypes.byref(p), _ptr(workspace), nbytes,
                                    _stream(stream)))
+
+
+def signmuon_step_noalloc(mats: Sequence[Matrix], params: Params, stream=None) -> None:
+    """signmuon_step with the library's static device scratch as workspace
+    (no allocation anywhere); raises SignmuonError (SIGNMUON_ESCRATCH) when
+    the step needs more than STATIC_SCRATCH_BYTES."""
+    arr, p = _marshal(mats, params)
+    _check(library().signmuon_step_noalloc(arr, len(mats), ctypes.byref(p), _stream(stream)))
 
 
 def signmuon_muon_step(mats: Sequence[Matrix], params: Params, workspace: Optional[torch.Tensor],

@@ -8,10 +8,18 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "signmuon.h"
 #include "sm_internal.h"
+
+// Device scratch of signmuon_step_noalloc: the workspace of an allocation-
+// free step lives here, one copy per GPU, held until the process ends. Host
+// code never passes this name to a kernel or a copy (on the host it only
+// stands for the symbol): it uses the device address hipGetSymbolAddress
+// returns for the current device (noalloc_scratch below).
+static __device__ __align__(256) char scratch[SIGNMUON_STATIC_SCRATCH_BYTES];
 
 namespace {
 
@@ -667,6 +675,31 @@ int check_workspace(const Plan &pl, void *ws, size_t ws_bytes) {
     return SIGNMUON_OK;
 }
 
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept.
+constexpr int kMaxScratchDevices = 64;
+std::atomic<void *> g_scratch_ptr[kMaxScratchDevices];
+std::mutex g_scratch_mu;
+
+int noalloc_scratch(void **out) {
+    int dev = 0;
+    if (hipError_t e = hipGetDevice(&dev); e != hipSuccess) return hip_status(e);
+    if (dev < 0 || dev >= kMaxScratchDevices) return SIGNMUON_ERANGE;
+    void *p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            if (hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)); e != hipSuccess)
+                return hip_status(e);
+            if (!p) return hip_status(hipErrorInvalidSymbol);
+            g_scratch_ptr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return SIGNMUON_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -684,6 +717,9 @@ const char *signmuon_strerror(int status) {
     case SIGNMUON_EWORKSPACE: return "workspace missing or too small";
     case SIGNMUON_EHIP: return g_hip_err[0] ? g_hip_err : "HIP error";
     case SIGNMUON_ERANGE: return "size beyond the kernels' limits";
+    case SIGNMUON_ESCRATCH:
+        return "the step needs more workspace than the static scratch of signmuon_step_noalloc holds "
+               "(SIGNMUON_STATIC_SCRATCH_BYTES); call signmuon_step with a workspace instead";
     default: return "unknown status";
     }
 }
@@ -759,6 +795,19 @@ int signmuon_muon_step(const signmuon_matrix *mats, int32_t n_mats, const signmu
 int signmuon_step(const signmuon_matrix *mats, int32_t n_mats, const signmuon_params *p,
                   void *workspace, size_t workspace_bytes, signmuon_stream stream) {
     return signmuon_step_traced(mats, n_mats, p, workspace, workspace_bytes, stream, nullptr);
+}
+
+int signmuon_step_noalloc(const signmuon_matrix *mats, int32_t n_mats, const signmuon_params *p,
+                          signmuon_stream stream) {
+    // The sizes are checked before any HIP call, so an oversized step is
+    // refused with nothing enqueued and no device touched.
+    Plan pl;
+    if (int rc = make_plan(mats, n_mats, p, true, pl)) return rc;
+    if (int rc = check_step_pointers(mats, n_mats, true, pl.i8)) return rc;
+    if (pl.total > (size_t)SIGNMUON_STATIC_SCRATCH_BYTES) return SIGNMUON_ESCRATCH;
+    void *ws = nullptr;
+    if (int rc = noalloc_scratch(&ws)) return rc;
+    return signmuon_step_traced(mats, n_mats, p, ws, SIGNMUON_STATIC_SCRATCH_BYTES, stream, nullptr);
 }
 
 int signmuon_sign_pack(const void *u, signmuon_dtype u_dtype, int64_t n, int32_t workers,
