@@ -107,6 +107,148 @@ def work_per_kind(wl):
     }
 
 
+def kernel_table(wl, per_kind_ms):
+    """Per kernel kind: ms per step and, for the kinds with an algorithmic
+    work count, the achieved rate and its fraction of the peak."""
+    work = work_per_kind(wl)
+    mfma_peak = PEAK_BF16_TFLOPS if wl.ns_dtype == "bf16" else PEAK_FP32_TFLOPS
+    kernels = {}
+    for name, ms in per_kind_ms.items():
+        entry = {"ms": round(ms, 5)}
+        if name in work and work[name][1] > 0:
+            bound, amount = work[name]
+            if bound == "hbm":
+                ach = amount / (ms * 1e-3) / 1e9
+                entry.update(bound="hbm", achieved=round(ach, 1), unit="GB/s",
+                             frac=round(ach / PEAK_HBM_GBS, 4), algorithmic_bytes=int(amount))
+            else:
+                ach = amount / (ms * 1e-3) / 1e12
+                entry.update(bound="mfma", achieved=round(ach, 1), unit="TFLOP/s",
+                             frac=round(ach / mfma_peak, 4), algorithmic_flops=int(amount))
+        kernels[name] = entry
+    return kernels
+
+
+def build_state(sm, wl, dev, threads=16):
+    """Device buffers of a workload (step 0 gradients from the seeded
+    generator, zero momentum, initial W), as the benchmark passes them: packed
+    signs and W, no U and no vote output."""
+    import torch
+
+    import synthetic
+    mom_t = torch.bfloat16 if wl.mom_dtype == "bf16" else torch.float32
+    mats = []
+
+    def draw(jm):
+        j, m = jm
+        return jm, synthetic.gradient(wl, j, m, 0)
+
+    grads = [torch.empty((wl.workers, R, C), dtype=torch.float32, device=dev) for R, C in wl.shapes]
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        for (j, m), g in ex.map(draw, [(j, m) for j in range(len(wl.shapes)) for m in range(wl.workers)]):
+            grads[j][m].copy_(torch.from_numpy(g))
+    for j, (R, C) in enumerate(wl.shapes):
+        mats.append(sm.Matrix(
+            grad=grads[j],
+            momentum=torch.zeros((wl.workers, R, C), dtype=mom_t, device=dev),
+            packed=torch.zeros((wl.workers, sm.signmuon_packed_words(R * C)), dtype=torch.int64,
+                               device=dev),
+            weight=torch.from_numpy(synthetic.initial_weight(wl, j)).to(dev)))
+    return mats
+
+
+def params_of(sm, wl):
+    code = {"f32": sm.F32, "bf16": sm.BF16}
+    return sm.Params(workers=wl.workers, beta=wl.beta, eta=wl.eta, ns_iters=wl.ns_iters,
+                     post_polar_iters=wl.post_polar_iters, grad_dtype=code[wl.grad_dtype],
+                     mom_dtype=code[wl.mom_dtype], ns_dtype=code[wl.ns_dtype],
+                     norm=sm.NORM_SPECTRAL if wl.norm == "spectral" else sm.NORM_FROBENIUS,
+                     power_iters=wl.power_iters)
+
+
+# The other configurations of the measurement plan, each timed in the same run
+# (they are parity cases; the benchmarked line is the GPT-2 small one):
+# (workload, warmup steps, timed steps).
+OTHER_CONFIGS = (("square256_mw4_k1", 5, 20), ("resnet50_4shapes_mw4_k1", 5, 20),
+                 ("resnet50_4shapes_mw4_k5", 3, 10), ("gpt2s_mw16_k5_t3", 2, 5),
+                 ("block4096_mw16_k5", 1, 3))
+
+
+def time_other_configs(sm, hip, dev, configs=OTHER_CONFIGS):
+    """Each configuration as whole traced steps on its own buffers: ms per step
+    (wall clock over the timed steps), params/s and the per-kernel table."""
+    import torch
+
+    import synthetic
+    out = {}
+    for name, warmup, steps in configs:
+        wl = synthetic.WORKLOADS[name]
+        t0 = time.perf_counter()
+        mats = build_state(sm, wl, dev)
+        params = params_of(sm, wl)
+        ws = sm.workspace_tensor(mats, params, dev)
+        step = sm.Prepared(mats, params, ws)
+        for _ in range(warmup):
+            step.step()
+        traces = [sm.Trace([hip.event() for _ in range(128)]) for _ in range(steps)]
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        for tr in traces:
+            step.step_traced(tr)
+        torch.cuda.synchronize()
+        ms = 1e3 * (time.perf_counter() - t1) / steps
+        per_kind, _ = traced_kernel_ms(sm, hip, traces)
+        for tr in traces:
+            for e in list(tr._events):
+                hip.destroy(e)
+        kernels = kernel_table(wl, per_kind)
+        gram, prod = per_kind.get("ns_gram", 0.0), per_kind.get("ns_product", 0.0)
+        peak = PEAK_BF16_TFLOPS if wl.ns_dtype == "bf16" else PEAK_FP32_TFLOPS
+        ns_util = (100.0 * wl.ns_flops() / ((gram + prod) * 1e-3) / (peak * 1e12)
+                   if gram + prod > 0 else None)
+        out[name] = {"description": wl.description, "params": wl.params, "workers": wl.workers,
+                     "ns_iters": wl.ns_iters, "ns_dtype": wl.ns_dtype, "steps": steps,
+                     "ms_per_step": round(ms, 4), "params_per_s": round(wl.params / (ms * 1e-3), 1),
+                     "steps_per_s": round(1e3 / ms, 2),
+                     "ns_mfma_util_pct": None if ns_util is None else round(ns_util, 2),
+                     "kernels_ms_per_step": kernels}
+        log(f"[bench] {name}: {ms:.3f} ms per step ({time.perf_counter() - t0:.1f} s with set-up)")
+        del mats, ws, step
+        torch.cuda.empty_cache()
+    return out
+
+
+def time_standalone_pack(sm, wl, hip, dev, reps=10):
+    """signmuon_sign_pack on a [workers][n] U of the workload's size (n = all
+    its parameters), bf16 and fp32, timed between HIP events; algorithmic
+    bytes: U read once, the packed bits written once."""
+    import torch
+    stream = torch.cuda.current_stream().cuda_stream
+    n, mw = wl.params, wl.workers
+    out = {}
+    for name, dt, code, size in (("bf16", torch.bfloat16, sm.BF16, 2), ("fp32", torch.float32, sm.F32, 4)):
+        u = torch.randn((mw, n), dtype=dt, device=dev)
+        packed = torch.empty((mw, sm.signmuon_packed_words(n)), dtype=torch.int64, device=dev)
+        ev = [hip.event() for _ in range(2)]
+        sm.signmuon_sign_pack(u, n, mw, packed)
+        hip.record(ev[0], stream)
+        for _ in range(reps):
+            sm.signmuon_sign_pack(u, n, mw, packed)
+        hip.record(ev[1], stream)
+        hip.sync(ev[1])
+        ms = hip.elapsed_ms(ev[0], ev[1]) / reps
+        for e in ev:
+            hip.destroy(e)
+        nbytes = mw * n * (size + 1 / 8)
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        out[name] = {"ms": round(ms, 5), "bound": "hbm", "achieved": round(gbs, 1), "unit": "GB/s",
+                     "frac": round(gbs / PEAK_HBM_GBS, 4), "algorithmic_bytes": int(nbytes),
+                     "workers": mw, "n": n}
+        del u, packed
+    torch.cuda.empty_cache()
+    return out
+
+
 def time_int8_payload(sm, mats, wl, code, hip, dev, reps=10):
     """The whole step with the int8 payload on the workload's matrices: the
     last Newton-Schulz product writes each worker's signs as int8, and one
@@ -248,7 +390,7 @@ def cpu_model():
     return None
 
 
-def cpu_baseline(wl, js=(0, 1, 2, 3)):
+def cpu_baseline(wl, js=(0, 1, 2, 3), others=True):
     """The oracle, single-threaded, on a bounded sample of the workload: the
     matrices js (for GPT-2 small, the four matrices of one transformer layer)
     with all workers, one full step each (momentum, normalisation,
@@ -276,13 +418,83 @@ def cpu_baseline(wl, js=(0, 1, 2, 3)):
                        power_iters=wl.power_iters)
         total_s += time.perf_counter() - t0
         params += R * C
+    other = cpu_baseline_other(wl, js, total_s) if others else None
     os.sched_setaffinity(0, saved)
     shapes = ", ".join(f"{wl.shapes[j][0]}x{wl.shapes[j][1]}" for j in js)
-    return {"value": params / total_s, "unit": "params/s", "cores": 1, "kind": "oracle",
-            "cpu_model": cpu_model(), "host_threads": len(saved), "pinned_core": core,
-            "sample": f"{wl.name} matrices {js[0]}-{js[-1]} ({shapes}; {params} params), all "
-                      f"{wl.workers} workers, one full step each: {total_s:.1f} s single-threaded "
-                      f"on this host's CPU"}
+    out = {"value": params / total_s, "unit": "params/s", "cores": 1, "kind": "oracle",
+           "cpu_model": cpu_model(), "host_threads": len(saved), "pinned_core": core,
+           "sample": f"{wl.name} matrices {js[0]}-{js[-1]} ({shapes}; {params} params), all "
+                     f"{wl.workers} workers, one full step each: {total_s:.1f} s single-threaded "
+                     f"on this host's CPU"}
+    if other is not None:
+        out["other_configs"] = other
+    return out
+
+
+def oracle_multiply_adds(wl):
+    """Multiply-adds of the oracle's Newton-Schulz for one whole step (it
+    forms the whole Gram matrix: 2 r^2 c per worker, matrix and iteration)."""
+    return sum(2 * min(R, C) ** 2 * max(R, C) for R, C in wl.shapes) * wl.workers * wl.ns_iters
+
+
+def cpu_baseline_other(wl_main, js_main, main_s):
+    """The oracle (one core, the caller pins it) on the other configurations:
+    whole steps where they take seconds (the 256x256 and ResNet-50 k = 1
+    workloads), and, for the three that would take minutes to hours,
+    extrapolations from measured samples, labelled as such."""
+    import numpy as np
+
+    import oracle
+    import synthetic
+
+    def full_step(name):
+        wl = synthetic.WORKLOADS[name]
+        ns = oracle.BF16 if wl.ns_dtype == "bf16" else oracle.F32
+        t = 0.0
+        for j, (R, C) in enumerate(wl.shapes):
+            g = synthetic.gradients(wl, j, 0)
+            m = np.zeros((wl.workers, R, C), np.uint16 if wl.mom_dtype == "bf16" else np.float32)
+            w = synthetic.initial_weight(wl, j)
+            t0 = time.perf_counter()
+            oracle.step_matrix(g, m, w, wl.beta, wl.eta, wl.ns_iters, ns)
+            t += time.perf_counter() - t0
+        return {"params_per_s": wl.params / t, "seconds_per_step": round(t, 3), "kind": "measured",
+                "sample": f"one whole step ({len(wl.shapes)} matrices, {wl.workers} workers)"}
+
+    out = {n: full_step(n) for n in ("square256_mw4_k1", "resnet50_4shapes_mw4_k1")}
+    # GPT-2 shapes with 16 workers and 5 iterations: the main sample's layer of
+    # the same shapes (all 8 workers, k = 1) scaled by layers, workers and k
+    for name in ("gpt2s_mw16_k5_t3",):
+        wl = synthetic.WORKLOADS[name]
+        layers = len(wl.shapes) / len(js_main)
+        t = main_s * layers * (wl.workers / wl_main.workers) * (wl.ns_iters / wl_main.ns_iters)
+        out[name] = {"params_per_s": wl.params / t, "seconds_per_step": round(t, 1),
+                     "kind": "extrapolated",
+                     "sample": f"the measured {wl_main.name} layer ({main_s:.1f} s for the same four "
+                               f"shapes, {wl_main.workers} workers, k = {wl_main.ns_iters}) scaled "
+                               f"linearly by {layers:.0f} layers, {wl.workers} workers and "
+                               f"k = {wl.ns_iters}"}
+    # the transformer block: one worker's Newton-Schulz on a 512 x 4096 slab of
+    # its gradient (k = 1), scaled by the oracle's multiply-adds
+    wl = synthetic.WORKLOADS["block4096_mw16_k5"]
+    g = synthetic.gradient(wl, 0, 0, 0)[:512]
+    m = np.zeros(g.shape, np.uint16)
+    t0 = time.perf_counter()
+    oracle.momentum(g, m, wl.beta)
+    x0 = oracle.normalise(m)[1]
+    oracle.newton_schulz(x0, 1, oracle.BF16)
+    dt = time.perf_counter() - t0
+    rate = 2 * 512 * 512 * 4096 / dt
+    t = oracle_multiply_adds(wl) / rate
+    out[wl.name] = {"params_per_s": wl.params / t, "seconds_per_step": round(t, 1),
+                    "kind": "extrapolated",
+                    "sample": f"one worker's momentum and Newton-Schulz (k = 1) on a 512x4096 slab "
+                              f"of a 4096x4096 gradient: {dt:.1f} s, {rate / 1e9:.2f} G multiply-adds/s; "
+                              f"the whole step's {oracle_multiply_adds(wl):.3g} Newton-Schulz "
+                              f"multiply-adds at that rate"}
+    for v in out.values():
+        v["params_per_s"] = round(v["params_per_s"], 1)
+    return out
 
 
 def library_source_hash():
@@ -406,20 +618,7 @@ def main():
 
     work = work_per_kind(wl)
     mfma_peak = PEAK_BF16_TFLOPS if wl.ns_dtype == "bf16" else PEAK_FP32_TFLOPS
-    kernels = {}
-    for name, ms in per_kind_ms.items():
-        entry = {"ms": round(ms, 5)}
-        if name in work and work[name][1] > 0:
-            bound, amount = work[name]
-            if bound == "hbm":
-                ach = amount / (ms * 1e-3) / 1e9
-                entry.update(bound="hbm", achieved=round(ach, 1), unit="GB/s",
-                             frac=round(ach / PEAK_HBM_GBS, 4), algorithmic_bytes=int(amount))
-            else:
-                ach = amount / (ms * 1e-3) / 1e12
-                entry.update(bound="mfma", achieved=round(ach, 1), unit="TFLOP/s",
-                             frac=round(ach / mfma_peak, 4), algorithmic_flops=int(amount))
-        kernels[name] = entry
+    kernels = kernel_table(wl, per_kind_ms)
     dominant = max((k for k in kernels if "bound" in kernels[k]), key=lambda k: kernels[k]["ms"])
     d = kernels[dominant]
     roofline = {"bound": d["bound"], "achieved": d["achieved"],
@@ -431,17 +630,23 @@ def main():
     ns_util = 100.0 * ns_flops / (ns_ms * 1e-3) / (mfma_peak * 1e12) if ns_ms > 0 else None
     vote_gbs = kernels.get("vote_update", {}).get("achieved")
 
-    int8 = comparison = None
+    int8 = comparison = others = pack = None
     if not args.no_extras:
         log("[bench] timing the step with the int8 payload")
         int8 = time_int8_payload(sm, mats, wl, code, hip, dev)
         log("[bench] timing the comparison steps (Muon, one worker; majority-vote signum)")
         comparison = time_comparison_steps(sm, mats, wl, code, hip, dev)
+        log("[bench] timing the other configurations")
+        del step, ws, mats
+        torch.cuda.empty_cache()
+        others = time_other_configs(sm, hip, dev)
+        log("[bench] timing the standalone sign + pack")
+        pack = time_standalone_pack(sm, wl, hip, dev)
 
     base = None
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample")
-        base = cpu_baseline(wl)
+        base = cpu_baseline(wl, others=not args.no_extras)
 
     params_per_s = wl.params / (ms_per_step * 1e-3)
     out = {
@@ -464,6 +669,8 @@ def main():
         "launches_per_step": launches,
         "int8_payload": int8,
         "comparison_steps": comparison,
+        "other_configs": others,
+        "standalone_sign_pack": pack,
         "roofline": roofline,
         "cpu_baseline": base,
     }

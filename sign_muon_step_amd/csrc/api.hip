@@ -84,6 +84,7 @@ struct MatPlan {
     int32_t pw_bpw;         // spectral: power-step blocks per worker
     int32_t gram_split;     // k chunks per Gram tile (0: the Gram kernel stores A itself)
     size_t gpart_off;       // split Gram: partial tiles [Mw][Gram tiles][split][256][256] fp32
+    bool fused_k0;          // k = 0: the momentum kernel packs the signs (bits payload)
     bool fused_pack;        // the last product packs the signs itself (bits payload)
     bool fused_i8;          // the last product writes the int8 signs itself (int8 payload)
     bool u_scratch;         // U goes through workspace scratch
@@ -94,6 +95,8 @@ struct Plan {
     int32_t units = 0, post_unit_base = 0, partials = 0;
     size_t off_partials = 0, off_scales = 0, off_nnz = 0, off_gram = 0, off_iter[2] = {0, 0};
     size_t off_vns = 0, off_u = 0, off_pw = 0, off_pwp = 0, off_gpart = 0, total = 0;
+    size_t off_fix = 0;  // k = 0 packed by the momentum kernel: per-unit flags
+    bool any_k0 = false;
     bool spectral = false;
     bool i8 = false;  // int8 payload
 };
@@ -153,6 +156,12 @@ int make_plan(const signmuon_matrix *mats, int32_t n_mats, const signmuon_params
         post_iter += align_up((size_t)q.n * ns, kSectionAlign);
         q.vns_off = vns;
         if (post) vns += align_up((size_t)q.n * ns, kSectionAlign);
+        // k = 0 (Frobenius scale, no U output): the momentum kernel packs
+        // sign(M), the signs of M / ||M||_F unless finalize_scales flags the
+        // unit (a NaN or Inf entry; the fix-up kernel then redoes it)
+        q.fused_k0 = step && !pl.i8 && p->ns_iters == 0 && !pl.spectral && s.polar_out == nullptr &&
+                     (q.n % 64) == 0;
+        pl.any_k0 = pl.any_k0 || q.fused_k0;
         q.fused_pack = step && !pl.i8 && p->ns_iters > 0 && (q.C % 64) == 0;
         q.fused_i8 = pl.i8 && p->ns_iters > 0;
         q.u_scratch = step && p->ns_iters > 0 && !q.fused_pack && !q.fused_i8 && s.polar_out == nullptr;
@@ -177,6 +186,8 @@ int make_plan(const signmuon_matrix *mats, int32_t n_mats, const signmuon_params
     off += align_up((size_t)partials * sizeof(double), kSectionAlign);
     pl.off_scales = off;
     off += align_up((size_t)scale_count * sizeof(float2), kSectionAlign);
+    pl.off_fix = off;
+    off += pl.any_k0 ? align_up((size_t)pl.units * sizeof(int32_t), kSectionAlign) : 0;
     pl.off_nnz = off;
     off += align_up((size_t)n_mats * sizeof(uint32_t), kSectionAlign);
     pl.off_pw = off;
@@ -238,12 +249,16 @@ int run_momentum(const signmuon_matrix *mats, int32_t n_mats, const signmuon_par
         b.m_bf16 = p->mom_dtype == SIGNMUON_BF16;
         b.partials = ws_at<double>(ws, pl.off_partials);
         b.scales = ws_at<float2>(ws, pl.off_scales);
+        b.pack_fix = pl.any_k0 ? ws_at<int32_t>(ws, pl.off_fix) : nullptr;
+        bool packs = false;
         int64_t blocks = 0;
         for (int32_t j = 0; j < cn; ++j) {
             const MatPlan &q = pl.m[c0 + j];
             sm::MomMat &d = b.mat[j];
             d.g = mats[c0 + j].grad;
             d.m = mats[c0 + j].momentum;
+            d.packed = q.fused_k0 ? mats[c0 + j].packed : nullptr;
+            packs = packs || q.fused_k0;
             d.n = q.n;
             d.block_begin = (int32_t)blocks;
             b.starts.v[j] = d.block_begin;
@@ -258,6 +273,10 @@ int run_momentum(const signmuon_matrix *mats, int32_t n_mats, const signmuon_par
         if (int rc = tr.after(SIGNMUON_K_MOMENTUM)) return rc;
         sm::launch_finalize_scales(b, st);
         if (int rc = tr.after(SIGNMUON_K_SCALES)) return rc;
+        if (packs) {
+            sm::launch_pack_fixup(b, b.m_bf16, st);
+            if (int rc = tr.after(SIGNMUON_K_PACK)) return rc;
+        }
     }
     return SIGNMUON_OK;
 }
@@ -279,9 +298,23 @@ int device_cus() {
 
 // Launch groups of one Newton-Schulz pass. Product: LG_DIRECT (one block per
 // tile) or the persistent walk, whose wide and tall matrices go in separate
-// launches (LG_WALK_WIDE, LG_WALK_TALL). Gram: LG_DIRECT (whole k range) or
-// LG_GRAM_SPLIT (split k, then the reduce).
-enum LaunchGroup { LG_DIRECT = 0, LG_WALK_WIDE = 1, LG_WALK_TALL = 2, LG_GRAM_SPLIT = 1 };
+// launches (LG_WALK_WIDE, LG_WALK_TALL). Gram: LG_DIRECT (one block per tile,
+// whole k range), LG_GRAM_SPLIT (split k, then the reduce) or LG_GRAM_WALK
+// (the persistent walk, wide and tall matrices in one launch).
+enum LaunchGroup { LG_DIRECT = 0, LG_WALK_WIDE = 1, LG_WALK_TALL = 2, LG_GRAM_SPLIT = 1, LG_GRAM_WALK = 2 };
+
+// The Gram walk takes bf16 matrices that are not split, with 16-byte rows of
+// X and of A, and a k loop of whole stage rounds (the 4 pipeline stages) at
+// least two rounds long.
+int gram_group(const MatPlan &q, bool bf16) {
+    if (q.gram_split > 0) return LG_GRAM_SPLIT;
+    if (!bf16) return LG_DIRECT;
+    const int64_t c = q.R > q.C ? q.R : q.C;
+    const int64_t kt_n = (c + 31) / 32;  // 32-wide bf16 k slices
+    if (q.C % 8 || q.r % 8 || q.n * 2 >= ((int64_t)1 << 31)) return LG_DIRECT;
+    if (kt_n % 4 || kt_n < 8) return LG_DIRECT;
+    return LG_GRAM_WALK;
+}
 
 // The walk takes bf16 matrices whose k loop suits it (16-byte operands, k
 // slices a multiple of the 4 pipeline stages and at least the 256 identity
@@ -348,8 +381,8 @@ int ns_pass(const signmuon_matrix *mats, int32_t n_mats, const signmuon_params *
             sm::NsMat d;
             describe(i, d);
             g = product_group(pl.m[i], d, bf16, epi);
-        } else if (pass == 0 && pl.m[i].gram_split > 0) {
-            g = LG_GRAM_SPLIT;
+        } else {
+            g = gram_group(pl.m[i], bf16);
         }
         groups[g].push_back(i);
     }
@@ -375,19 +408,22 @@ int ns_pass(const signmuon_matrix *mats, int32_t n_mats, const signmuon_params *
             b.scales = scales;
             b.eta = p->eta;  // the W-update epilogue
             const bool split = pass == 0 && g == LG_GRAM_SPLIT;
+            const bool gram_walk = pass == 0 && g == LG_GRAM_WALK;
             // split Gram: Gram tiles x split blocks per worker; the reduce
-            // then runs 16 blocks per Gram tile
+            // then runs 16 blocks per Gram tile. The Gram walk numbers its
+            // tiles matrix-major (all workers of a matrix, then the next).
             auto number_tiles = [&](int per_tile) {
                 int64_t tiles = 0;
+                const int64_t per_mat = gram_walk ? p->workers : 1;
                 for (int32_t i = 0; i < cn; ++i) {
                     sm::NsMat &d = b.mat[i];
                     d.tile_begin = (int32_t)tiles;
                     b.starts.v[i] = d.tile_begin;
-                    tiles += (int64_t)d.tiles_per_worker * (per_tile ? per_tile : d.split);
+                    tiles += (int64_t)d.tiles_per_worker * (per_tile ? per_tile : d.split) * per_mat;
                 }
-                b.tiles_per_worker_all = (int32_t)tiles;
-                b.total_tiles = (int32_t)(tiles * p->workers);
-                return tiles * p->workers <= INT32_MAX;
+                b.tiles_per_worker_all = (int32_t)(tiles / per_mat);
+                b.total_tiles = (int32_t)(gram_walk ? tiles : tiles * p->workers);
+                return tiles * (gram_walk ? 1 : p->workers) <= INT32_MAX;
             };
             for (int32_t i = 0; i < cn; ++i) {
                 sm::NsMat &d = b.mat[i];
@@ -404,7 +440,9 @@ int ns_pass(const signmuon_matrix *mats, int32_t n_mats, const signmuon_params *
                 if (int rc = tr.after(SIGNMUON_K_GRAM)) return rc;
                 if (!number_tiles(sm::kGramReduceParts)) return SIGNMUON_ERANGE;
                 sm::launch_gram_reduce(b, bf16, st);
-            } else if (pass == 0)
+            } else if (gram_walk)
+                sm::launch_ns_gram_walk(b, std::min(b.total_tiles, device_cus()), st);
+            else if (pass == 0)
                 sm::launch_ns_gram(b, bf16, st);
             else if (g == LG_DIRECT)
                 sm::launch_ns_product(b, bf16, epi, st);
@@ -493,7 +531,8 @@ int run_pack(const signmuon_matrix *mats, int32_t n_mats, const signmuon_params 
     const bool k0 = p->ns_iters == 0;
     std::vector<int32_t> sel;
     for (int32_t i = 0; i < n_mats; ++i)
-        if (k0 || (step && !pl.m[i].fused_pack && !pl.m[i].fused_i8)) sel.push_back(i);
+        if ((k0 && !pl.m[i].fused_k0) || (!k0 && step && !pl.m[i].fused_pack && !pl.m[i].fused_i8))
+            sel.push_back(i);
     for (size_t c0 = 0; c0 < sel.size(); c0 += sm::kMaxMatsPerLaunch) {
         const size_t cn = sel.size() - c0 < (size_t)sm::kMaxMatsPerLaunch ? sel.size() - c0
                                                                           : (size_t)sm::kMaxMatsPerLaunch;
@@ -519,7 +558,8 @@ int run_pack(const signmuon_matrix *mats, int32_t n_mats, const signmuon_params 
             d.i8 = step && pl.i8 ? s.signs_i8 : nullptr;
             d.n = q.n;
             d.unit_begin = q.unit_begin;
-            d.blocks_per_worker = (int32_t)((q.nw + sm::kPackWordsPerBlock - 1) / sm::kPackWordsPerBlock);
+            const int64_t wpb = sm::pack_words_per_block(b.u_bf16 != 0);
+            d.blocks_per_worker = (int32_t)((q.nw + wpb - 1) / wpb);
             d.block_begin = (int32_t)blocks;
             b.starts.v[i] = d.block_begin;
             blocks += (int64_t)p->workers * d.blocks_per_worker;
@@ -817,7 +857,8 @@ int signmuon_sign_pack(const void *u, signmuon_dtype u_dtype, int64_t n, int32_t
     if (!aligned16(u) || !aligned16(packed)) return SIGNMUON_EALIGN;
     if (n > kMaxN) return SIGNMUON_ERANGE;
     const int64_t nw = (n + 63) / 64;
-    const int64_t bpw = (nw + sm::kPackWordsPerBlock - 1) / sm::kPackWordsPerBlock;
+    const int64_t wpb = sm::pack_words_per_block(u_dtype == SIGNMUON_BF16);
+    const int64_t bpw = (nw + wpb - 1) / wpb;
     if (bpw * workers > INT32_MAX) return SIGNMUON_ERANGE;
     sm::PackBatch b{};
     b.nmat = 1;

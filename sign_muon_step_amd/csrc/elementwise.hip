@@ -92,11 +92,18 @@ __device__ __forceinline__ void unpack8(const Raw8 &r, float (&x)[8]) {
     }
 }
 
+// Sign byte (bit t = (v_t >= 0)) of 8 stored values (the k = 0 signs packed
+// by the momentum kernel).
+struct Signs8 {
+    uint32_t byte = 0;
+    __device__ __forceinline__ void add(int t, float v) { byte |= (uint32_t)(v >= 0.0f) << t; }
+};
+
 // y = fmaf(beta, m, g) for 8 entries, stored in the momentum's type; returns
-// the sum of squares of the stored values.
+// the sum of squares of the stored values, and their signs in sg.
 template <bool MB>
 __device__ __forceinline__ double update8(float beta, const float (&g)[8], const float (&m)[8], void *mp,
-                                          int64_t e) {
+                                          int64_t e, Signs8 &sg) {
     double ss = 0.0;
     if (MB) {
         u32x4_t out;
@@ -106,9 +113,12 @@ __device__ __forceinline__ double update8(float beta, const float (&g)[8], const
                                               __builtin_fmaf(beta, m[2 * i + 1], g[2 * i + 1]));
             const uint32_t lo = both & 0xffffu, hi = both >> 16;
             out[i] = both;
-            const double s0 = bf16_bits_to_f32(lo), s1 = bf16_bits_to_f32(hi);
+            const float f0 = bf16_bits_to_f32(lo), f1 = bf16_bits_to_f32(hi);
+            const double s0 = f0, s1 = f1;
             ss += s0 * s0;
             ss += s1 * s1;
+            sg.add(2 * i, f0);
+            sg.add(2 * i + 1, f1);
         }
         store16_nt(static_cast<uint16_t *>(mp) + e, out);
     } else {
@@ -119,6 +129,7 @@ __device__ __forceinline__ double update8(float beta, const float (&g)[8], const
             y[i >> 2][i & 3] = __float_as_uint(v);
             const double d = v;
             ss += d * d;
+            sg.add(i, v);
         }
         float *q = static_cast<float *>(mp) + e;
         store16_nt(q, y[0]);
@@ -147,6 +158,12 @@ __device__ __forceinline__ double momentum_one(const MomBatch &b, const void *gp
     return d * d;
 }
 
+// With M.packed (k = 0, n % 64 == 0) the kernel also packs the signs of the
+// stored M -- bit t of byte c is (M[8c + t] >= 0), the sign-pack layout. For
+// k = 0 the factor is U = M / ||M||_F, whose signs are those of M whenever
+// ||M||_F is finite (also when it is 0: M is then all +-0, every bit 1);
+// finalize_scales flags the units where it is not (a NaN or Inf entry), and
+// launch_pack_fixup recomputes those.
 template <bool GB, bool MB>
 __global__ __launch_bounds__(kMomThreads) void momentum_kernel(MomBatch b) {
     const int blk = blockIdx.x;
@@ -158,6 +175,7 @@ __global__ __launch_bounds__(kMomThreads) void momentum_kernel(MomBatch b) {
     const size_t gsz = GB ? 2 : 4, msz = MB ? 2 : 4;
     const void *gp = static_cast<const char *>(M.g) + (size_t)w * (size_t)n * gsz;
     void *mp = static_cast<char *>(M.m) + (size_t)w * (size_t)n * msz;
+    uint8_t *pk = M.packed ? reinterpret_cast<uint8_t *>(M.packed) + (size_t)w * (size_t)(n >> 3) : nullptr;
     const int64_t begin = (int64_t)chunk * kMomChunk;
     double ss = 0.0;
     if ((n & 7) == 0) {
@@ -182,7 +200,9 @@ __global__ __launch_bounds__(kMomThreads) void momentum_kernel(MomBatch b) {
                 float g[8], m[8];
                 unpack8<GB>(graw[r], g);
                 unpack8<MB>(mraw[r], m);
-                ss += update8<MB>(b.beta, g, m, mp, e);
+                Signs8 sg;
+                ss += update8<MB>(b.beta, g, m, mp, e, sg);
+                if (pk) pk[e >> 3] = (uint8_t)sg.byte;
             }
         }
     } else {
@@ -226,6 +246,39 @@ __global__ __launch_bounds__(256) void finalize_scales_kernel(MomBatch b) {
             s2 = (float)(1.0 / ss);
         }
         b.scales[M.unit_begin + w] = make_float2(s, s2);
+        // the momentum kernel packed sign(M): the signs of M / ||M||_F unless
+        // the sum of squares is NaN or Inf (then s = 0 and U = 0 * M)
+        if (M.packed) b.pack_fix[M.unit_begin + w] = (ss - ss == 0.0) ? 0 : 1;
+    }
+}
+
+// k = 0, packed by the momentum kernel: the units flagged in pack_fix (a NaN
+// or Inf in M, so s = 0) get the signs of U = s M recomputed from the stored
+// M (bit = (s * M >= 0), the sign_pack arithmetic: +1 for finite entries, -1
+// for NaN and Inf), one 64-entry word per thread. kFixBlocks blocks per unit
+// (blockIdx.x = unit * kFixBlocks + part); a block of an unflagged unit reads
+// its flag and returns.
+constexpr int kFixBlocks = 4;
+
+template <bool MB>
+__global__ __launch_bounds__(256) void pack_fixup_kernel(MomBatch b) {
+    const int u = blockIdx.x / kFixBlocks, part = blockIdx.x % kFixBlocks;
+    const MomMat &M = b.mat[u / b.workers];
+    const int w = u % b.workers;
+    if (!M.packed || !b.pack_fix[M.unit_begin + w]) return;
+    const float s = b.scales[M.unit_begin + w].x;
+    const int64_t words = M.n >> 6;
+    const char *mp = static_cast<const char *>(M.m) + (size_t)w * (size_t)M.n * (MB ? 2 : 4);
+    uint64_t *pk = M.packed + (size_t)w * (size_t)words;
+    for (int64_t q = (int64_t)part * 256 + threadIdx.x; q < words; q += kFixBlocks * 256) {
+        uint64_t word = 0;
+        for (int t = 0; t < 64; ++t) {
+            const int64_t e = q * 64 + t;
+            const float v = MB ? bf16_bits_to_f32(reinterpret_cast<const uint16_t *>(mp)[e])
+                               : reinterpret_cast<const float *>(mp)[e];
+            word |= (uint64_t)(s * v >= 0.0f) << t;
+        }
+        pk[q] = word;
     }
 }
 
@@ -264,57 +317,67 @@ __global__ __launch_bounds__(256) void sign_pack_kernel(PackBatch b) {
     // n % 8 == 0: every chunk is whole and 16-byte aligned (bf16) or
     // 32-byte aligned (fp32) given a 16-byte aligned base.
     const bool vec = (n & 7) == 0;
-    const int64_t c0 = (int64_t)wb * kPackChunksPerBlock + threadIdx.x;
-    float v[kPackChunksPerThread][8];
+    constexpr int CPT = pack_chunks_per_thread(UB);
+    const int64_t c0 = (int64_t)wb * (256 * CPT) + threadIdx.x;
+    // Every chunk's raw 16-byte pieces are loaded first (all in flight
+    // together, 128 bytes of U per thread) and unpacked one chunk at a time,
+    // so the registers hold raw words rather than CPT x 8 floats.
+    u32x4_t raw[CPT][UB ? 1 : 2];
 #pragma unroll
-    for (int i = 0; i < kPackChunksPerThread; ++i) {
+    for (int i = 0; i < CPT; ++i) {
+        const int64_t e0 = (c0 + i * 256) * 8;
+        if (vec && e0 < n) {  // read once: nontemporal
+            raw[i][0] = load16_nt(u + e0 * usz);
+            if (!UB) raw[i][UB ? 0 : 1] = load16_nt(u + e0 * usz + 16);
+        }
+    }
+    // chunk i as 8 values (0 past n)
+    auto values = [&](int i, float (&v)[8]) {
         const int64_t e0 = (c0 + i * 256) * 8;
         if (vec && e0 < n) {
-            if (UB) {  // read once: nontemporal
-                const u32x4_t q = load16_nt(u + e0 * 2);
-                const uint32_t h[4] = {q[0], q[1], q[2], q[3]};
+            if (UB) {
 #pragma unroll
                 for (int t = 0; t < 4; ++t) {
-                    v[i][2 * t] = bf16_bits_to_f32(h[t] & 0xffffu);
-                    v[i][2 * t + 1] = bf16_bits_to_f32(h[t] >> 16);
+                    v[2 * t] = bf16_bits_to_f32(raw[i][0][t] & 0xffffu);
+                    v[2 * t + 1] = bf16_bits_to_f32(raw[i][0][t] >> 16);
                 }
             } else {
-                const u32x4_t a = load16_nt(u + e0 * 4);
-                const u32x4_t c = load16_nt(u + e0 * 4 + 16);
 #pragma unroll
                 for (int t = 0; t < 4; ++t) {
-                    v[i][t] = __uint_as_float(a[t]);
-                    v[i][4 + t] = __uint_as_float(c[t]);
+                    v[t] = __uint_as_float(raw[i][0][t]);
+                    v[4 + t] = __uint_as_float(raw[i][UB ? 0 : 1][t]);
                 }
             }
         } else {
 #pragma unroll
             for (int t = 0; t < 8; ++t) {
                 const int64_t e = e0 + t;
-                v[i][t] = e < n ? (UB ? bf16_bits_to_f32(reinterpret_cast<const uint16_t *>(u)[e])
-                                      : reinterpret_cast<const float *>(u)[e])
-                                : 0.0f;
+                v[t] = e < n ? (UB ? bf16_bits_to_f32(reinterpret_cast<const uint16_t *>(u)[e])
+                                   : reinterpret_cast<const float *>(u)[e])
+                             : 0.0f;
             }
         }
-    }
+    };
     const int lane = threadIdx.x & (kWave - 1);
 #pragma unroll
-    for (int i = 0; i < kPackChunksPerThread; ++i) {
+    for (int i = 0; i < CPT; ++i) {
         const int64_t c = c0 + i * 256, e0 = c * 8;
         if (UB && c >= nbytes) continue;
+        float v[8];
+        values(i, v);
         uint32_t byte = 0;
         if (e0 + 8 <= n) {  // a whole chunk: no per-entry bound (5 % faster for bf16 U)
 #pragma unroll
             for (int t = 0; t < 8; ++t) {
-                const float x = b.scales ? s * v[i][t] : v[i][t];
-                v[i][t] = x;
+                const float x = b.scales ? s * v[t] : v[t];
+                v[t] = x;
                 byte |= (uint32_t)(x >= 0.0f) << t;
             }
         } else {
 #pragma unroll
             for (int t = 0; t < 8; ++t) {
-                const float x = b.scales ? s * v[i][t] : v[i][t];
-                v[i][t] = x;
+                const float x = b.scales ? s * v[t] : v[t];
+                v[t] = x;
                 byte |= (uint32_t)(e0 + t < n && x >= 0.0f) << t;
             }
         }
@@ -353,12 +416,12 @@ __global__ __launch_bounds__(256) void sign_pack_kernel(PackBatch b) {
         }
         if (uo) {
             if (vec && e0 < n) {
-                *reinterpret_cast<float4 *>(uo + e0) = make_float4(v[i][0], v[i][1], v[i][2], v[i][3]);
-                *reinterpret_cast<float4 *>(uo + e0 + 4) = make_float4(v[i][4], v[i][5], v[i][6], v[i][7]);
+                *reinterpret_cast<float4 *>(uo + e0) = make_float4(v[0], v[1], v[2], v[3]);
+                *reinterpret_cast<float4 *>(uo + e0 + 4) = make_float4(v[4], v[5], v[6], v[7]);
             } else {
 #pragma unroll
                 for (int t = 0; t < 8; ++t)
-                    if (e0 + t < n) uo[e0 + t] = v[i][t];
+                    if (e0 + t < n) uo[e0 + t] = v[t];
             }
         }
     }
@@ -641,6 +704,14 @@ void launch_momentum(const MomBatch &b, hipStream_t s) {
 void launch_finalize_scales(const MomBatch &b, hipStream_t s) {
     int units = b.nmat * b.workers;
     hipLaunchKernelGGL(finalize_scales_kernel, dim3((units + 3) / 4), dim3(256), 0, s, b);
+}
+
+void launch_pack_fixup(const MomBatch &b, bool m_bf16, hipStream_t s) {
+    const dim3 grid(b.nmat * b.workers * kFixBlocks);
+    if (m_bf16)
+        hipLaunchKernelGGL(pack_fixup_kernel<true>, grid, dim3(256), 0, s, b);
+    else
+        hipLaunchKernelGGL(pack_fixup_kernel<false>, grid, dim3(256), 0, s, b);
 }
 
 void launch_sign_pack(const PackBatch &b, hipStream_t s) {

@@ -1643,6 +1643,282 @@ void ns_product_pack_kernel(NsBatch b) {
     wait_vm_lgkm0<0>();  // the zero-fill loads past the last tile write LDS too
 }
 
+// ---------------------------------------------------------------------------
+// Persistent Gram for a bf16 launch: one workgroup per CU walks Gram tiles of
+// wide and tall matrices alike (a launch of one orientation would leave its
+// last round of tiles mostly empty when a shape has few tiles per CU). The
+// launch numbers its tiles matrix-major -- matrix (longest k first), then
+// worker, then the tile within the worker's upper triangle -- so that tiles
+// that share a panel of Y sit next to each other and tile costs (k slices)
+// never increase along the order. Round rho hands positions rho * G ..
+// rho * G + G - 1 (G workgroups) out in a snake: XCD-contiguous positions in
+// even rounds, reversed in odd ones, which evens out the work per CU when
+// the costs fall along the order. As in the product walk, the loads a tile's
+// last iterations would issue past its k range fetch the first slices of
+// the workgroup's next tile (whatever its orientation: the load offsets come
+// from the next tile's scalar description), and the epilogue, staged 8 rows
+// at a time through LDS beside the stage buffers, runs while they land.
+// Each tile's k loop, MFMA order and epilogue arithmetic are those of
+// ns_gram_kernel, so A is the same bit for bit.
+// ---------------------------------------------------------------------------
+struct GramWalkTile {
+    Operand P, Q;   // row panels ti and tj of Y (X when wide, X^T when tall)
+    char *a;        // this worker's Gram matrix [r][r]
+    LateScale sc;   // s^2 of the first iteration (applied in the epilogue)
+    int tall;       // Y = X^T: both panels mn-contiguous
+    int ti, tj, r;
+    int kt_n;       // k slices of the tile
+
+    __device__ __forceinline__ int slice(int j) const { return j < kt_n ? j : kt_n; }
+
+    __device__ __forceinline__ void decode(const NsBatch &b, int sv, int L) {
+        constexpr int64_t sz = 2;  // bf16
+        const NsMat M = load_ns_mat_scalar(find_ns_mat(sv, L));
+        const int rem = L - M.tile_begin;
+        const int w = rem / M.tiles_per_worker;
+        int t = rem - w * M.tiles_per_worker;
+        tall = M.R > M.C;
+        r = tall ? M.C : M.R;
+        const int c = tall ? M.R : M.C;
+        const int T_ = (r + kNsTileM - 1) / kNsTileM;
+        int i = 0;
+        while (t >= T_ - i) {
+            t -= T_ - i;
+            ++i;
+        }
+        ti = i;
+        tj = i + t;
+        const char *y = static_cast<const char *>(M.x) + (int64_t)w * M.R * M.C * sz;
+        a = static_cast<char *>(M.a) + (int64_t)w * r * r * sz;
+        sc = LateScale{load_scale_scalar(b.scales, M.unit_begin + w, 1), b.use_scales};
+        if (!tall) {  // Y = X: k-contiguous rows
+            P = Operand{y + (int64_t)ti * kNsTileM * M.C * sz, M.C, r - ti * kNsTileM, c, true};
+            Q = Operand{y + (int64_t)tj * kNsTileM * M.C * sz, M.C, r - tj * kNsTileM, c, true};
+        } else {      // Y = X^T: element (i, k) at X[k][i], mn-contiguous
+            P = Operand{y + (int64_t)ti * kNsTileM * sz, M.C, r - ti * kNsTileM, c, true};
+            Q = Operand{y + (int64_t)tj * kNsTileM * sz, M.C, r - tj * kNsTileM, c, true};
+        }
+        kt_n = (c + Elem<true>::BK - 1) / Elem<true>::BK;
+    }
+
+    // No further tile: an empty buffer, so its loads read zeros.
+    __device__ __forceinline__ void none() {
+        P = Q = Operand{nullptr, 0, 0, 0, true};
+        a = nullptr;
+        sc = LateScale{1.0f, 0};
+        tall = 0;
+        ti = tj = r = 0;
+        kt_n = 1;
+    }
+};
+
+// The k loop of one Gram tile of the walk (KC: both panels k-contiguous,
+// i.e. a wide X), with the same per-iteration schedule as pack_tile_kloop
+// (no identity term, no rotation): its last S iterations load nxt's first
+// slices. Every tile's slice count is a multiple of S and at least 2 S (the
+// launcher checks), so iteration j uses LDS stage j % S and nxt's slice s
+// lands in stage s.
+template <bool KC>
+__device__ __forceinline__ void gram_walk_kloop(const GramWalkTile &cur, const GramWalkTile &nxt,
+                                                const DmaSlices<true, 256, GramLay::kWaves> &lp,
+                                                const DmaSlices<true, 256, GramLay::kWaves> &lq, char *smem,
+                                                f32x16_t (&acc)[kFM][kFN], GivenTid tid) {
+    using L = GramLay;
+    constexpr int TN = L::kTileN, S = L::kStages;
+    const int wid = __builtin_amdgcn_readfirstlane(tid() / kWave);
+    const int wm0 = L::m0(wid), wn0 = L::n0(wid);
+#pragma unroll
+    for (int f = 0; f < kFM; ++f)
+#pragma unroll
+        for (int gg = 0; gg < kFN; ++gg)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[f][gg][r] = 0.f;
+    constexpr int PL = L::kPLoads, QL = L::kQLoads, NLD = PL + QL;
+    const uint32_t lds0 = lds_addr(smem);
+    Frags<true> fa, fb;
+    read_frags<true, KC, KC, TN, GivenTid>(fa, smem, smem + L::kPBytes, wm0, wn0, 0, tid);
+    const int iters = cur.kt_n;
+    const bool nkc = !nxt.tall;
+    constexpr int kSteps = kFM * kFN, kFrag = kFM + kFN;
+    constexpr int eQ = kSteps / QL, eP = kSteps / PL;
+    static_assert(kFrag <= kSteps && eQ * QL == kSteps && eP * PL == kSteps, "interleave");
+    auto iteration = [&](int j, auto tl) {
+        constexpr int TL = decltype(tl)::value;
+        const int js = TL >= 0 ? TL : j % S;
+        const char *cb = smem + js * L::kStageBytes;
+        const uint32_t late_dst = lds0 + ((js + S - 1) % S) * L::kStageBytes + L::kPBytes;
+        const int late = TL >= 1 ? nxt.slice(TL - 1) : cur.slice(j + S - 1);
+#pragma unroll
+        for (int i = 0; i < kSteps; ++i) {
+            mma_step<true>(fa, acc, i);
+            if (i < kFrag) read_frag<true, KC, KC, TN, GivenTid>(fb, cb, cb + L::kPBytes, wm0, wn0, 1, i, tid);
+            if (i % eQ == eQ - 1) {
+                if constexpr (TL >= 1)
+                    lq.issue_at(late_dst, i / eQ, walk_offset<true>(nxt.Q, nkc, late, i / eQ, tid),
+                                walk_rsrc<true>(nxt.Q, nkc));
+                else
+                    lq.issue_one(late, late_dst, i / eQ);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        wait_vm_lgkm0<(S - 2) * NLD>();
+        lds_barrier();
+        const char *nb = smem + ((js + 1) % S) * L::kStageBytes;
+        const uint32_t dst = lds0 + js * L::kStageBytes;
+        const int refill = TL >= 0 ? nxt.slice(TL) : cur.slice(j + S);
+#pragma unroll
+        for (int i = 0; i < kSteps; ++i) {
+            mma_step<true>(fb, acc, i);
+            if (i < kFrag) read_frag<true, KC, KC, TN, GivenTid>(fa, nb, nb + L::kPBytes, wm0, wn0, 0, i, tid);
+            if (i % eP == eP - 1) {
+                if constexpr (TL >= 0)
+                    lp.issue_at(dst, i / eP, walk_offset<true>(nxt.P, nkc, refill, i / eP, tid),
+                                walk_rsrc<true>(nxt.P, nkc));
+                else
+                    lp.issue_one(refill, dst, i / eP);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    using NoTail = std::integral_constant<int, -1>;
+    for (int j = 0; j < iters - S; ++j) iteration(j, NoTail{});
+    static_for(std::make_integer_sequence<int, S>{},
+               [&](auto tl) { iteration(iters - S + decltype(tl)::value, tl); });
+}
+
+// Epilogue of a walked Gram tile: A = scale * acc rounded to bf16, the tile
+// and (above the diagonal) its mirror, 8 rows of the wave's 128 x 64 result
+// at a time through the wave's 8 x kStageStride floats outside the stage
+// buffers. Register 4q + t of block (f, g) holds row 8q + 4h + t (h = lane /
+// 32) of the block. Direct rows: 8 lanes per row, 8 columns (16 bytes) each.
+// Mirror: lane l reads staged column l, i.e. 8 consecutive entries of
+// mirrored row n0 + l, and stores them as 16 bytes. FAST: the tile lies
+// inside the matrix and r % 8 == 0.
+template <bool FAST>
+__device__ __forceinline__ void gram_walk_epilogue(const GramWalkTile &g, const f32x16_t (&acc)[kFM][kFN],
+                                                   GivenTid tid, float *estage) {
+    const float scale = g.sc.get();
+    const int lane = tid() & (kWave - 1), wid = tid() / kWave;
+    const int m0 = g.ti * kNsTileM + GramLay::m0(wid), n0 = g.tj * kNsTileM + GramLay::n0(wid);
+    float *st = estage + wid * 8 * kStageStride;
+    uint16_t *a = reinterpret_cast<uint16_t *>(g.a);
+    const int r = g.r;
+    const bool mirror = g.ti < g.tj;
+#pragma unroll
+    for (int f = 0; f < kFM; ++f)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+#pragma unroll
+            for (int gg = 0; gg < kFN; ++gg)
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+                    st[(4 * (lane >> 5) + t) * kStageStride + 32 * gg + (lane & 31)] = acc[f][gg][4 * q + t] * scale;
+            wave_lds_fence();
+            {
+                const int row = lane >> 3, c8 = (lane & 7) * 8;
+                const int gi = m0 + f * 32 + 8 * q + row, gj = n0 + c8;
+                const float4 lo = *reinterpret_cast<const float4 *>(st + row * kStageStride + c8);
+                const float4 hi = *reinterpret_cast<const float4 *>(st + row * kStageStride + c8 + 4);
+                const float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+                if (FAST) {
+                    *reinterpret_cast<uint4 *>(a + (int64_t)gi * r + gj) =
+                        make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                                   pack_bf16x2(v[6], v[7]));
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        if (gi < r && gj + e < r) a[(int64_t)gi * r + gj + e] = (uint16_t)f32_to_bf16_bits(v[e]);
+                }
+            }
+            if (mirror) {
+                const int gj = n0 + lane, gi = m0 + f * 32 + 8 * q;
+                float v[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v[e] = st[e * kStageStride + lane];
+                if (FAST) {
+                    *reinterpret_cast<uint4 *>(a + (int64_t)gj * r + gi) =
+                        make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                                   pack_bf16x2(v[6], v[7]));
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        if (gj < r && gi + e < r) a[(int64_t)gj * r + gi + e] = (uint16_t)f32_to_bf16_bits(v[e]);
+                }
+            }
+            wave_lds_fence();
+        }
+}
+
+// Logical tile of workgroup position pos in round rho (snake order).
+__device__ __forceinline__ int gram_walk_tile(int rho, int pos, int G) {
+    return rho * G + ((rho & 1) ? G - 1 - pos : pos);
+}
+
+__global__ __launch_bounds__(GramLay::kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void ns_gram_walk_kernel(NsBatch b) {
+    using L = GramLay;
+    constexpr int S = L::kStages, PL = L::kPLoads, QL = L::kQLoads, NLD = PL + QL;
+    __shared__ __attribute__((aligned(16))) char smem[L::kLdsBytes];
+    __shared__ int starts[kWave];  // the matrix start table (see ns_product_pack_kernel)
+    __shared__ __attribute__((aligned(16))) float estage[L::kWaves * 8 * kStageStride];
+    const int sv = ns_start_of_lane();
+    if (threadIdx.x < kWave) starts[threadIdx.x] = sv;
+    const int wid0 = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
+    const int total = b.total_tiles, G = gridDim.x;
+    const int pos = xcd_remap(blockIdx.x, G);  // XCD-contiguous positions
+    int rho = 0;
+    GramWalkTile cur, nxt;
+    DmaSlices<true, 256, L::kWaves> lp, lq;
+    cur.decode(b, sv, gram_walk_tile(0, pos, G));  // G <= total: round 0 is full
+    if (cur.tall) {
+        lp.template setup<false>(cur.P);
+        lq.template setup<false>(cur.Q);
+    } else {
+        lp.template setup<true>(cur.P);
+        lq.template setup<true>(cur.Q);
+    }
+    const uint32_t lds0 = lds_addr(smem);
+#pragma unroll
+    for (int st = 0; st < S - 1; ++st) {
+        lp.issue(cur.slice(st), lds0 + st * L::kStageBytes);
+        lq.issue(cur.slice(st), lds0 + st * L::kStageBytes + L::kPBytes);
+    }
+    lp.issue(cur.slice(S - 1), lds0 + (S - 1) * L::kStageBytes);
+    wait_vm_lgkm0<(S - 2) * NLD + PL>();  // slice 0 landed
+    lds_barrier();
+    f32x16_t acc[kFM][kFN];
+    for (;;) {
+        int lane;
+        asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane));
+        const GivenTid tid{(unsigned)(wid0 * kWave + lane)};
+        const int ln = gram_walk_tile(rho + 1, pos, G);
+        const bool more = ln < total;
+        if (more)
+            nxt.decode(b, starts[lane], ln);
+        else
+            nxt.none();
+        if (cur.tall)
+            gram_walk_kloop<false>(cur, nxt, lp, lq, smem, acc, tid);
+        else
+            gram_walk_kloop<true>(cur, nxt, lp, lq, smem, acc, tid);
+        if ((cur.ti + 1) * kNsTileM <= cur.r && (cur.tj + 1) * kNsTileM <= cur.r)
+            gram_walk_epilogue<true>(cur, acc, tid, estage);
+        else
+            gram_walk_epilogue<false>(cur, acc, tid, estage);
+        if (!more) break;
+        ++rho;
+        cur = nxt;
+        if (cur.tall) {
+            lp.template setup<false, GivenTid>(cur.P, tid);
+            lq.template setup<false, GivenTid>(cur.Q, tid);
+        } else {
+            lp.template setup<true, GivenTid>(cur.P, tid);
+            lq.template setup<true, GivenTid>(cur.Q, tid);
+        }
+    }
+    wait_vm_lgkm0<0>();  // the zero-fill loads past the last tile write LDS too
+}
+
 }  // namespace
 
 void launch_ns_gram(const NsBatch &b, bool ns_bf16, hipStream_t s) {
@@ -1684,6 +1960,11 @@ void launch_ns_product(const NsBatch &b, bool ns_bf16, NsEpilogue epi, hipStream
         else SM_PROD(false, EPI_WUPD);
     }
 #undef SM_PROD
+}
+
+void launch_ns_gram_walk(const NsBatch &b, int grid_blocks, hipStream_t s) {
+    dim3 grid(grid_blocks), block(GramLay::kThreads);
+    hipLaunchKernelGGL(ns_gram_walk_kernel, grid, block, 0, s, b);
 }
 
 void launch_ns_product_pack(const NsBatch &b, bool tall, NsEpilogue epi, int grid_blocks, hipStream_t s) {

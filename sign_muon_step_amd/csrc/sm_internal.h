@@ -41,6 +41,8 @@ constexpr int kMomChunk = kMomThreads * kMomElemsPerThread;
 struct MomMat {
     const void *g;          // [Mw][n] gradient
     void *m;                // [Mw][n] momentum, in place
+    uint64_t *packed;       // k = 0: [Mw][n / 64] signs of the stored M (n % 64 == 0,
+                            // n % 8 == 0 path), or nullptr
     int64_t n;
     int32_t block_begin;    // first block of this matrix within the launch
     int32_t blocks_per_worker;
@@ -58,11 +60,19 @@ struct MomBatch {
     int32_t m_bf16;
     double *partials;       // sum of squares of the stored momentum, per block
     float2 *scales;         // per unit: {s = 1/||M||_F, s^2} (0 when ||M|| = 0)
+    int32_t *pack_fix;      // per unit: 1 where the signs of U = s M differ from those of
+                            // M, i.e. ||M||_F is NaN or Inf (set by finalize_scales for
+                            // matrices with packed)
     Starts starts;         // first block (tile) of each matrix
 };
 
 void launch_momentum(const MomBatch &b, hipStream_t s);
 void launch_finalize_scales(const MomBatch &b, hipStream_t s);
+// k = 0 with signs packed by the momentum kernel: for each unit flagged in
+// b.pack_fix, the signs of s M again from the stored M and its scale (the
+// sign_pack arithmetic), over the whole unit; a few blocks per unit, which
+// return at once for an unflagged one.
+void launch_pack_fixup(const MomBatch &b, bool m_bf16, hipStream_t s);
 
 // ---------------------------------------------------------------------------
 // Newton-Schulz GEMMs (matrix cores).
@@ -143,6 +153,14 @@ inline int32_t ns_gram_split(int64_t R, int64_t C, bool ns_bf16) {
     const int64_t s = (c + bk - 1) / bk / 16;
     return (int32_t)(s < 2 ? 0 : (s > 8 ? 8 : s));
 }
+// The bf16 Gram matrices as a persistent walk: grid_blocks workgroups (one
+// per CU, at most b.total_tiles) walk the tiles of wide and tall matrices in
+// one launch. Tiles are numbered matrix-major: tile_begin of matrix i is the
+// number of tiles (all workers) of matrices 0 .. i - 1, tiles_per_worker its
+// Gram tiles of one worker; the matrices are listed longest k first. Every
+// matrix has C and min(R, C) multiples of 8, each worker's matrix is under
+// 2 GiB, and ceil(max(R, C) / 32) is a multiple of 4 and at least 8.
+void launch_ns_gram_walk(const NsBatch &b, int grid_blocks, hipStream_t s);
 void launch_ns_product(const NsBatch &b, bool ns_bf16, NsEpilogue epi, hipStream_t s);
 // A product with bf16 operands as a persistent tile walk: grid_blocks
 // workgroups (one per CU, at most b.total_tiles) walk the tiles with the
@@ -179,11 +197,11 @@ struct PackBatch {
     Starts starts;         // first block (tile) of each matrix
 };
 
-// 256 threads, each packing kPackChunksPerThread chunks of 8 entries (one
-// byte of packed words each).
-constexpr int kPackChunksPerThread = 4;
-constexpr int kPackChunksPerBlock = 256 * kPackChunksPerThread;
-constexpr int kPackWordsPerBlock = kPackChunksPerBlock / 8;
+// 256 threads, each packing pack_chunks_per_thread chunks of 8 entries (one
+// byte of packed words each): 8 for bf16 U (16 bytes per chunk), 4 for fp32
+// U (32 bytes), so 128 bytes of U per thread are in flight together.
+constexpr int pack_chunks_per_thread(bool u_bf16) { return u_bf16 ? 8 : 4; }
+constexpr int pack_words_per_block(bool u_bf16) { return 256 * pack_chunks_per_thread(u_bf16) / 8; }
 
 void launch_sign_pack(const PackBatch &b, hipStream_t s);
 

@@ -114,3 +114,48 @@ def test_majority_vote_signum_is_the_k0_step(mom, mw):
     np.testing.assert_array_equal(to_host(mat.packed), packed)
     np.testing.assert_array_equal(to_host(mat.vote_out), vote)
     np.testing.assert_array_equal(to_host(mat.weight), w_ref)
+
+
+@pytest.mark.parametrize("mom", ["f32", "bf16"])
+@pytest.mark.parametrize("mw", [1, 4, 8])
+def test_signum_signs_packed_by_the_momentum_kernel(mom, mw):
+    """k = 0 with no U output: the momentum kernel packs the signs of the
+    stored M itself (n % 64 == 0), a ragged matrix in the same call takes the
+    separate pack. Two steps; degenerate workers next to ordinary ones: a
+    zero gradient (U = 0: every bit 1), a NaN and an Inf entry (||M||_F is not
+    finite, s = 0: U = 0 * M, +1 for finite entries and -1 for the NaN and
+    Inf), and an extreme dynamic range (one entry near 1e38 next to -1e-10
+    ones, whose U = M / ||M||_F is about -1e-48). Momentum, packed signs, vote
+    and W bit-exact against the oracle's whole step."""
+    shapes = [(192, 320), (64, 576), (37, 53)]
+    np_m, _, code = dtype_of(mom)
+    rng = np.random.default_rng(90 + mw)
+    host = []
+    for j, (R, C) in enumerate(shapes):
+        g = np.stack([synthetic.random_matrix(900 + 10 * j + i, (R, C), 1e-3, "normal") for i in range(mw)])
+        if j == 0 and mw >= 4:
+            g[1] = 0.0
+            g[2].ravel()[rng.integers(R * C)] = np.nan
+            g[3, 5, 7] = -np.inf
+        if j == 1 and mw >= 4:
+            g[1] = -1e-10
+            g[1, 3, 3] = 1e38
+        host.append((g, synthetic.random_matrix(950 + j, (R, C), 0.02, "normal")))
+    mats = [make_matrix(g, np.zeros(g.shape, np_m), w, polar=False) for g, w in host]
+    m_ref = [np.zeros(g.shape, np_m) for g, _ in host]
+    w_ref = [w.copy() for _, w in host]
+    p = sm.Params(workers=mw, beta=0.9, eta=1e-3, ns_iters=0, mom_dtype=code, ns_dtype=code)
+    ws = sm.workspace_tensor(mats, p, DEV)
+    for t in range(2):
+        if t == 1:  # new gradients, same degenerate pattern's finite workers
+            for j, (g, _) in enumerate(host):
+                mats[j].grad.copy_(to_dev(g * np.float32(0.5)))
+                host[j] = (g * np.float32(0.5), host[j][1])
+        sm.signmuon_step(mats, p, ws)
+        torch.cuda.synchronize()
+        for j, (g, _) in enumerate(host):
+            packed, vote, _ = oracle.step_matrix(g, m_ref[j], w_ref[j], 0.9, 1e-3, 0, ORC_DT[mom])
+            np.testing.assert_array_equal(to_host(mats[j].momentum), m_ref[j], err_msg=f"M {j} step {t}")
+            np.testing.assert_array_equal(to_host(mats[j].packed), packed, err_msg=f"packed {j} step {t}")
+            np.testing.assert_array_equal(to_host(mats[j].vote_out), vote, err_msg=f"vote {j} step {t}")
+            np.testing.assert_array_equal(to_host(mats[j].weight), w_ref[j], err_msg=f"W {j} step {t}")
