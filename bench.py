@@ -369,7 +369,9 @@ def time_comparison_steps(sm, mats, wl, code, hip, dev, reps=10):
         for e in list(tr._events):
             hip.destroy(e)
     mw, n = wl.workers, wl.params
-    nbytes = mw * n * (s_g + 2 * s_m) + mw * n * (s_m + 1 / 8) + n * (mw / 8 + 8)
+    # momentum (G read, M read and written) with the signs packed in the same pass, then the
+    # vote (the packed bits read, W read and written)
+    nbytes = mw * n * (s_g + 2 * s_m + 1 / 8) + n * (mw / 8 + 8)
     gbs = nbytes / (ms * 1e-3) / 1e9
     out["signum"] = {"workers": mw, "ms_per_step": round(ms, 5),
                      "params_per_s": round(n / (ms * 1e-3), 1),
