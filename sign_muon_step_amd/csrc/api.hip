@@ -428,6 +428,7 @@ int ns_pass(const signmuon_matrix *mats, int32_t n_mats, const signmuon_params *
             for (int32_t i = 0; i < cn; ++i) {
                 sm::NsMat &d = b.mat[i];
                 describe(idx[c0 + i], d);
+                if (gram_walk) d.tiles_per_worker = sm::ns_gram_walk_tiles(pl.m[idx[c0 + i]].R, pl.m[idx[c0 + i]].C);
                 if (split) {
                     const MatPlan &q = pl.m[idx[c0 + i]];
                     d.split = q.gram_split;

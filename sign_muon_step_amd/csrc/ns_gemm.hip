@@ -504,7 +504,7 @@ __device__ __forceinline__ void mma_identity(const Frags<BF16> &fr, f32x16_t (&a
             if (b == blk)
 #pragma unroll
                 for (int o = 0; o < NO; ++o) {
-                    if (SIDE == ID_P)
+                    if constexpr (SIDE == ID_P)
                         acc[b][o] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(id, fr.q[o], acc[b][o], 0, 0, 0);
                     else
                         acc[o][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr.p[o], id, acc[o][b], 0, 0, 0);
@@ -518,7 +518,7 @@ __device__ __forceinline__ void mma_identity(const Frags<BF16> &fr, f32x16_t (&a
                 for (int st = 0; st < 4; ++st)
 #pragma unroll
                     for (int o = 0; o < NO; ++o) {
-                        if (SIDE == ID_P)
+                        if constexpr (SIDE == ID_P)
                             acc[b][o] = __builtin_amdgcn_mfma_f32_32x32x2f32(id[st], fr.q[o][st], acc[b][o], 0, 0, 0);
                         else
                             acc[o][b] = __builtin_amdgcn_mfma_f32_32x32x2f32(fr.p[o][st], id[st], acc[o][b], 0, 0, 0);
@@ -547,7 +547,7 @@ __device__ __forceinline__ void mma_identity_at(const Frags<BF16> &fr, f32x16_t 
         for (int e = 0; e < 8; ++e) id[e] = active ? one[e] : (__bf16)0.0f;
 #pragma unroll
         for (int o = 0; o < NO; ++o) {
-            if (SIDE == ID_P)
+            if constexpr (SIDE == ID_P)
                 acc[b][o] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(id, fr.q[o], acc[b][o], 0, 0, 0);
             else
                 acc[o][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr.p[o], id, acc[o][b], 0, 0, 0);
@@ -561,7 +561,7 @@ __device__ __forceinline__ void mma_identity_at(const Frags<BF16> &fr, f32x16_t 
         for (int st = 0; st < 4; ++st)
 #pragma unroll
             for (int o = 0; o < NO; ++o) {
-                if (SIDE == ID_P)
+                if constexpr (SIDE == ID_P)
                     acc[b][o] = __builtin_amdgcn_mfma_f32_32x32x2f32(id[st], fr.q[o][st], acc[b][o], 0, 0, 0);
                 else
                     acc[o][b] = __builtin_amdgcn_mfma_f32_32x32x2f32(fr.p[o][st], id[st], acc[o][b], 0, 0, 0);
@@ -1658,14 +1658,45 @@ void ns_product_pack_kernel(NsBatch b) {
 // the workgroup's next tile (whatever its orientation: the load offsets come
 // from the next tile's scalar description), and the epilogue, staged 8 rows
 // at a time through LDS beside the stage buffers, runs while they land.
-// Each tile's k loop, MFMA order and epilogue arithmetic are those of
-// ns_gram_kernel, so A is the same bit for bit.
+// A tile loads two 256-row groups of Y (P: group ti, Q: group tj), eight
+// 64-row panels ("slots" 0-3 of P, 4-7 of Q), and each wave computes two
+// 64 x 64 blocks of A that share their column panel: rows from slots a1 and
+// a2, columns from slot b (a 128 x 64 result, as in ns_gram_kernel). The
+// upper triangle is covered block by block: a cross tile (ti < tj) takes the
+// 16 blocks of groups ti x tj; the ten blocks inside one group (four on the
+// diagonal, six above it) take five waves, so a pair tile holds all of one
+// group's (waves 0-4, P) and three or two waves of another's (waves 5-7, Q),
+// and three groups need two tiles where whole diagonal tiles would need three
+// (a fifth fewer MFMAs at r = 768). Every block's entries come out of the same
+// MFMA chain over the same k order as in ns_gram_kernel (the products of bf16
+// values are exact, and an entry and its mirror add the same products), so A
+// is the same bit for bit.
 // ---------------------------------------------------------------------------
+enum GramWalkKind { GW_CROSS = 0, GW_PAIR3 = 1, GW_PAIR2 = 2, GW_SINGLE = 3 };
+
+// Slots of wave wid in a tile of the given kind: a1 | a2 << 4 | b << 8, and
+// bit 12 set when the wave's blocks are part of A (idle waves compute on
+// whatever their slots hold and store nothing). One group's ten blocks as
+// five waves (a1, a2; b): (0, 2; 0) (1, 3; 1) (2, 3; 2) (3, 0; 3) (0, 2; 1).
+__device__ __forceinline__ int gram_wave_slots(int kind, int wid) {
+    if (kind == GW_CROSS) return (2 * (wid >> 2)) | ((2 * (wid >> 2) + 1) << 4) | ((4 + (wid & 3)) << 8) | (1 << 12);
+    constexpr uint64_t kGroupWaves = 0x120ull << 48 | 0x303ull << 36 | 0x232ull << 24 | 0x131ull << 12 | 0x020ull;
+    int w = wid, add = 0, live = 1;
+    if (wid >= 5) {
+        w = (kind == GW_PAIR3 ? 0 : 3) + wid - 5;
+        add = 0x444;
+        live = kind == GW_PAIR3 || (kind == GW_PAIR2 && wid < 7);
+        if (!live) w = 0;
+    }
+    return ((int)(kGroupWaves >> (12 * w)) & 0xfff) + add + (live << 12);
+}
+
 struct GramWalkTile {
-    Operand P, Q;   // row panels ti and tj of Y (X when wide, X^T when tall)
+    Operand P, Q;   // row groups ti and tj of Y (X when wide, X^T when tall)
     char *a;        // this worker's Gram matrix [r][r]
     LateScale sc;   // s^2 of the first iteration (applied in the epilogue)
     int tall;       // Y = X^T: both panels mn-contiguous
+    int kind;       // GramWalkKind
     int ti, tj, r;
     int kt_n;       // k slices of the tile
 
@@ -1680,14 +1711,29 @@ struct GramWalkTile {
         tall = M.R > M.C;
         r = tall ? M.C : M.R;
         const int c = tall ? M.R : M.C;
+        // A worker's tiles: the in-group tiles first (pairs of groups 3u, 3u + 1
+        // and 3u + 2, 3u + 1, then the groups left over alone), then the
+        // cross tiles in row-major order of the upper triangle of groups.
         const int T_ = (r + kNsTileM - 1) / kNsTileM;
-        int i = 0;
-        while (t >= T_ - i) {
-            t -= T_ - i;
-            ++i;
+        const int trip = T_ / 3, nd = 2 * trip + T_ % 3;
+        if (t < 2 * trip) {
+            tj = 3 * (t >> 1) + 1;
+            ti = tj + ((t & 1) ? 1 : -1);
+            kind = (t & 1) ? GW_PAIR2 : GW_PAIR3;
+        } else if (t < nd) {
+            ti = tj = 3 * trip + t - 2 * trip;
+            kind = GW_SINGLE;
+        } else {
+            t -= nd;
+            int i = 0;
+            while (t >= T_ - 1 - i) {
+                t -= T_ - 1 - i;
+                ++i;
+            }
+            ti = i;
+            tj = i + 1 + t;
+            kind = GW_CROSS;
         }
-        ti = i;
-        tj = i + t;
         const char *y = static_cast<const char *>(M.x) + (int64_t)w * M.R * M.C * sz;
         a = static_cast<char *>(M.a) + (int64_t)w * r * r * sz;
         sc = LateScale{load_scale_scalar(b.scales, M.unit_begin + w, 1), b.use_scales};
@@ -1698,6 +1744,7 @@ struct GramWalkTile {
             P = Operand{y + (int64_t)ti * kNsTileM * sz, M.C, r - ti * kNsTileM, c, true};
             Q = Operand{y + (int64_t)tj * kNsTileM * sz, M.C, r - tj * kNsTileM, c, true};
         }
+        if (kind == GW_SINGLE) Q = Operand{nullptr, 0, 0, 0, true};  // nothing to load: zeros
         kt_n = (c + Elem<true>::BK - 1) / Elem<true>::BK;
     }
 
@@ -1707,10 +1754,31 @@ struct GramWalkTile {
         a = nullptr;
         sc = LateScale{1.0f, 0};
         tall = 0;
+        kind = GW_SINGLE;
         ti = tj = r = 0;
         kt_n = 1;
     }
 };
+
+// LDS byte offset of slot s (a 64-row panel; 0-3 in P, 4-7 in Q) within a
+// stage: both layouts are linear in 64-row steps, and Q follows P.
+template <bool KC>
+__device__ __forceinline__ uint32_t gram_slot_off(int s) {
+    return KC ? (uint32_t)s * (64 * kRowBytes) : (uint32_t)(s & 3) * 512u + (uint32_t)(s >> 2) * GramLay::kPBytes;
+}
+
+// Fragment j of one half for a wave whose P blocks come from the slots at
+// LDS offsets o1 (m-blocks 0, 1) and o2 (2, 3) and its Q blocks from ob.
+template <bool KC>
+__device__ __forceinline__ void gram_read_frag(Frags<true> &fr, const char *cb, uint32_t o1, uint32_t o2,
+                                               uint32_t ob, int half, int j, GivenTid tid) {
+    if (j < 2)
+        fr.p[j] = frag_bf16<KC, 256, GivenTid>(cb + o1, 32 * j, half, tid);
+    else if (j < kFM)
+        fr.p[j] = frag_bf16<KC, 256, GivenTid>(cb + o2, 32 * (j - 2), half, tid);
+    else
+        fr.q[j - kFM] = frag_bf16<KC, 256, GivenTid>(cb + ob, 32 * (j - kFM), half, tid);
+}
 
 // The k loop of one Gram tile of the walk (KC: both panels k-contiguous,
 // i.e. a wide X), with the same per-iteration schedule as pack_tile_kloop
@@ -1724,9 +1792,11 @@ __device__ __forceinline__ void gram_walk_kloop(const GramWalkTile &cur, const G
                                                 const DmaSlices<true, 256, GramLay::kWaves> &lq, char *smem,
                                                 f32x16_t (&acc)[kFM][kFN], GivenTid tid) {
     using L = GramLay;
-    constexpr int TN = L::kTileN, S = L::kStages;
+    constexpr int S = L::kStages;
     const int wid = __builtin_amdgcn_readfirstlane(tid() / kWave);
-    const int wm0 = L::m0(wid), wn0 = L::n0(wid);
+    const int sl = __builtin_amdgcn_readfirstlane(gram_wave_slots(cur.kind, wid));
+    const uint32_t o1 = gram_slot_off<KC>(sl & 15), o2 = gram_slot_off<KC>((sl >> 4) & 15),
+                   ob = gram_slot_off<KC>((sl >> 8) & 15);
 #pragma unroll
     for (int f = 0; f < kFM; ++f)
 #pragma unroll
@@ -1736,7 +1806,8 @@ __device__ __forceinline__ void gram_walk_kloop(const GramWalkTile &cur, const G
     constexpr int PL = L::kPLoads, QL = L::kQLoads, NLD = PL + QL;
     const uint32_t lds0 = lds_addr(smem);
     Frags<true> fa, fb;
-    read_frags<true, KC, KC, TN, GivenTid>(fa, smem, smem + L::kPBytes, wm0, wn0, 0, tid);
+#pragma unroll
+    for (int j = 0; j < kFM + kFN; ++j) gram_read_frag<KC>(fa, smem, o1, o2, ob, 0, j, tid);
     const int iters = cur.kt_n;
     const bool nkc = !nxt.tall;
     constexpr int kSteps = kFM * kFN, kFrag = kFM + kFN;
@@ -1751,7 +1822,7 @@ __device__ __forceinline__ void gram_walk_kloop(const GramWalkTile &cur, const G
 #pragma unroll
         for (int i = 0; i < kSteps; ++i) {
             mma_step<true>(fa, acc, i);
-            if (i < kFrag) read_frag<true, KC, KC, TN, GivenTid>(fb, cb, cb + L::kPBytes, wm0, wn0, 1, i, tid);
+            if (i < kFrag) gram_read_frag<KC>(fb, cb, o1, o2, ob, 1, i, tid);
             if (i % eQ == eQ - 1) {
                 if constexpr (TL >= 1)
                     lq.issue_at(late_dst, i / eQ, walk_offset<true>(nxt.Q, nkc, late, i / eQ, tid),
@@ -1769,7 +1840,7 @@ __device__ __forceinline__ void gram_walk_kloop(const GramWalkTile &cur, const G
 #pragma unroll
         for (int i = 0; i < kSteps; ++i) {
             mma_step<true>(fb, acc, i);
-            if (i < kFrag) read_frag<true, KC, KC, TN, GivenTid>(fa, nb, nb + L::kPBytes, wm0, wn0, 0, i, tid);
+            if (i < kFrag) gram_read_frag<KC>(fa, nb, o1, o2, ob, 0, i, tid);
             if (i % eP == eP - 1) {
                 if constexpr (TL >= 0)
                     lp.issue_at(dst, i / eP, walk_offset<true>(nxt.P, nkc, refill, i / eP, tid),
@@ -1786,28 +1857,34 @@ __device__ __forceinline__ void gram_walk_kloop(const GramWalkTile &cur, const G
                [&](auto tl) { iteration(iters - S + decltype(tl)::value, tl); });
 }
 
-// Epilogue of a walked Gram tile: A = scale * acc rounded to bf16, the tile
-// and (above the diagonal) its mirror, 8 rows of the wave's 128 x 64 result
-// at a time through the wave's 8 x kStageStride floats outside the stage
-// buffers. Register 4q + t of block (f, g) holds row 8q + 4h + t (h = lane /
-// 32) of the block. Direct rows: 8 lanes per row, 8 columns (16 bytes) each.
-// Mirror: lane l reads staged column l, i.e. 8 consecutive entries of
-// mirrored row n0 + l, and stores them as 16 bytes. FAST: the tile lies
-// inside the matrix and r % 8 == 0.
+// Epilogue of a walked Gram tile: A = scale * acc rounded to bf16, each of
+// the wave's two 64 x 64 blocks and (off the diagonal) its mirror, 8 rows of
+// the wave's 128 x 64 result at a time through the wave's 8 x kStageStride
+// floats outside the stage buffers. Register 4q + t of block (f, g) holds
+// row 8q + 4h + t (h = lane / 32) of the block. Direct rows: 8 lanes per
+// row, 8 columns (16 bytes) each. Mirror: lane l reads staged column l, i.e.
+// 8 consecutive entries of mirrored row n0 + l, and stores them as 16 bytes.
+// A diagonal block holds both triangles and is stored once. FAST: the tile's
+// groups lie inside the matrix and r % 8 == 0.
 template <bool FAST>
 __device__ __forceinline__ void gram_walk_epilogue(const GramWalkTile &g, const f32x16_t (&acc)[kFM][kFN],
                                                    GivenTid tid, float *estage) {
     const float scale = g.sc.get();
     const int lane = tid() & (kWave - 1), wid = tid() / kWave;
-    const int m0 = g.ti * kNsTileM + GramLay::m0(wid), n0 = g.tj * kNsTileM + GramLay::n0(wid);
+    const int sl = __builtin_amdgcn_readfirstlane(gram_wave_slots(g.kind, wid));
+    if (!((sl >> 12) & 1)) return;  // an idle wave of a pair or single tile
+    auto row_of = [&](int slot) { return (slot < 4 ? g.ti : g.tj) * kNsTileM + 64 * (slot & 3); };
+    const int s1 = sl & 15, s2 = (sl >> 4) & 15, sb = (sl >> 8) & 15;
+    const int m1 = row_of(s1), m2 = row_of(s2), n0 = row_of(sb);
     float *st = estage + wid * 8 * kStageStride;
     uint16_t *a = reinterpret_cast<uint16_t *>(g.a);
     const int r = g.r;
-    const bool mirror = g.ti < g.tj;
 #pragma unroll
     for (int f = 0; f < kFM; ++f)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
+            const int mb = (f < 2 ? m1 : m2) + 32 * (f & 1);  // first row of 32-row block f
+            const bool mirror = (f < 2 ? s1 : s2) != sb;
 #pragma unroll
             for (int gg = 0; gg < kFN; ++gg)
 #pragma unroll
@@ -1816,7 +1893,7 @@ __device__ __forceinline__ void gram_walk_epilogue(const GramWalkTile &g, const 
             wave_lds_fence();
             {
                 const int row = lane >> 3, c8 = (lane & 7) * 8;
-                const int gi = m0 + f * 32 + 8 * q + row, gj = n0 + c8;
+                const int gi = mb + 8 * q + row, gj = n0 + c8;
                 const float4 lo = *reinterpret_cast<const float4 *>(st + row * kStageStride + c8);
                 const float4 hi = *reinterpret_cast<const float4 *>(st + row * kStageStride + c8 + 4);
                 const float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
@@ -1831,7 +1908,7 @@ __device__ __forceinline__ void gram_walk_epilogue(const GramWalkTile &g, const 
                 }
             }
             if (mirror) {
-                const int gj = n0 + lane, gi = m0 + f * 32 + 8 * q;
+                const int gj = n0 + lane, gi = mb + 8 * q;
                 float v[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) v[e] = st[e * kStageStride + lane];

@@ -125,6 +125,15 @@ inline int32_t ns_gram_tiles(int64_t R, int64_t C) {
     int64_t t = (r + kNsTileM - 1) / kNsTileM;
     return (int32_t)(t * (t + 1) / 2);
 }
+// Tiles one worker of an R x C matrix takes in the persistent Gram walk, which
+// covers the upper triangle in 64 x 64 blocks: one tile per pair of distinct
+// 256-row groups, and two tiles per three groups for the blocks inside a group
+// (ten per group: five waves of two blocks), one for each group left over.
+inline int32_t ns_gram_walk_tiles(int64_t R, int64_t C) {
+    int64_t r = R < C ? R : C;
+    int64_t g = (r + kNsTileM - 1) / kNsTileM;
+    return (int32_t)(g * (g - 1) / 2 + 2 * (g / 3) + g % 3);
+}
 inline int32_t ns_product_tiles(int64_t R, int64_t C) {
     // output rows = R, cols = C in both orientations
     return (int32_t)(((R + kNsTileM - 1) / kNsTileM) * ((C + kNsProdTileN - 1) / kNsProdTileN));
