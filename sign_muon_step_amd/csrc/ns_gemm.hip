@@ -529,8 +529,10 @@ __device__ __forceinline__ void mma_identity(const Frags<BF16> &fr, f32x16_t (&a
 // Identity term of iteration J of a rotated k loop (the tile's own 256 k
 // come first, see tile_mainloop): the slice covers k = J * BK .. + BK - 1 of
 // the tile, i.e. rows (ID_P) or columns (ID_Q) w0 + 32 b + roff .. of the
-// wave's extent WS on that side when J * BK lies in [w0, w0 + WS); other
-// waves multiply a zero fragment, so the sequence has no branch.
+// wave's extent WS on that side when J * BK lies in [w0, w0 + WS). Other
+// waves have no term at this slice and skip it (a wave-uniform branch: their
+// fragment would be all zeros, and adding exact zeros to an accumulator that
+// starts at +0 changes no bit).
 template <bool BF16, int SIDE, int J, class Tid = HwTid>
 __device__ __forceinline__ void mma_identity_at(const Frags<BF16> &fr, f32x16_t (&acc)[kFM][kFN], int w0,
                                                 int half, Tid tid = Tid{}) {
@@ -539,12 +541,9 @@ __device__ __forceinline__ void mma_identity_at(const Frags<BF16> &fr, f32x16_t 
     constexpr int NO = SIDE == ID_Q ? kFM : kFN;
     constexpr int kb = J * RS;
     constexpr int b = (kb % WS) / 32, roff = kb % 32;
-    const bool active = kb / WS == w0 / WS;
+    if (__builtin_amdgcn_readfirstlane(kb / WS == w0 / WS ? 1 : 0) == 0) return;
     if constexpr (BF16) {
-        const bf16x8_t one = id_frag_bf16<Tid>(roff, half, tid);
-        bf16x8_t id;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) id[e] = active ? one[e] : (__bf16)0.0f;
+        const bf16x8_t id = id_frag_bf16<Tid>(roff, half, tid);
 #pragma unroll
         for (int o = 0; o < NO; ++o) {
             if constexpr (SIDE == ID_P)
@@ -553,10 +552,7 @@ __device__ __forceinline__ void mma_identity_at(const Frags<BF16> &fr, f32x16_t 
                 acc[o][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr.p[o], id, acc[o][b], 0, 0, 0);
         }
     } else {
-        const f32x4_t one = id_frag_f32<Tid>(roff, half, tid);
-        f32x4_t id;
-#pragma unroll
-        for (int st = 0; st < 4; ++st) id[st] = active ? one[st] : 0.0f;
+        const f32x4_t id = id_frag_f32<Tid>(roff, half, tid);
 #pragma unroll
         for (int st = 0; st < 4; ++st)
 #pragma unroll
