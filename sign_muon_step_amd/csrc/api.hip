@@ -484,6 +484,18 @@ int run_spectral(const signmuon_matrix *mats, int32_t n_mats, const signmuon_par
         }
         if (blocks > INT32_MAX) return SIGNMUON_ERANGE;
         b.total_blocks = (int32_t)blocks;
+        // One workgroup per (matrix, worker) runs every step, the scale and
+        // the rescale when each Gram matrix suits it and there are enough
+        // units to fill the device; otherwise one launch per step.
+        bool fused = (int64_t)cn * p->workers >= device_cus() / 2;
+        for (int32_t i = 0; i < cn; ++i)
+            fused = fused && pl.m[c0 + i].r % 8 == 0 && pl.m[c0 + i].r <= sm::max_fused_pow_r(bf16);
+        if (fused) {
+            b.it = p->power_iters;
+            sm::launch_power_fused(b, bf16, rescale, st);
+            if (int rc = tr.after(SIGNMUON_K_POWER)) return rc;
+            continue;
+        }
         for (int it = 0; it < p->power_iters; ++it) {
             b.it = it;
             sm::launch_power_step(b, bf16, st);

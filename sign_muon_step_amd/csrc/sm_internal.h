@@ -274,6 +274,8 @@ void launch_vote_update_int8(const VoteI8Batch &b, hipStream_t s);
 // ---------------------------------------------------------------------------
 constexpr int kPowRowsPerBlock = 32;  // rows of A per power-step block (8 per wave)
 constexpr int kMaxPowR = 8192;         // the power vector of a Gram lives in LDS
+// The one-workgroup power iteration: two 16-byte column chunks per lane at most.
+inline int max_fused_pow_r(bool bf16) { return bf16 ? 1024 : 512; }
 
 struct PowMat {
     const void *a;   // worker 0's Gram matrix [r][r] (ns type); worker stride r*r
@@ -301,6 +303,9 @@ void launch_power_step(const PowBatch &b, bool bf16, hipStream_t s);
 void launch_power_finalize(const PowBatch &b, hipStream_t s);
 // bpw of the batch: rescale_blocks_per_worker
 void launch_gram_rescale(const PowBatch &b, bool bf16, hipStream_t s);
+// All it = p power steps, the scales and (rescale) A <- round(s^2 A) with one
+// workgroup per (matrix, worker); every r % 8 == 0 and r <= max_fused_pow_r.
+void launch_power_fused(const PowBatch &b, bool bf16, bool rescale, hipStream_t s);
 
 // Post-vote polar step helpers.
 void launch_zero_u32(uint32_t *p, int32_t count, hipStream_t s);

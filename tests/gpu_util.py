@@ -50,6 +50,29 @@ def make_matrix(g: np.ndarray, m: np.ndarray, w: np.ndarray = None, *, polar=Tru
         vote_out=torch.zeros((R, C), dtype=torch.int8, device=DEV) if vote else None)
 
 
+def traced_step_kinds(mats, params: sm.Params, capacity: int = 256):
+    """Run signmuon_step_traced once; the kernel kind of each launch, in order
+    (names from sm.KERNEL_KINDS)."""
+    import ctypes
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    events = []
+    for _ in range(capacity):
+        e = ctypes.c_void_p()
+        assert hip.hipEventCreate(ctypes.byref(e)) == 0
+        events.append(e.value)
+    try:
+        tr = sm.Trace(events)
+        sm.signmuon_step_traced(mats, params, sm.workspace_tensor(mats, params, DEV), tr)
+        torch.cuda.synchronize()
+        assert tr.launches < capacity
+        return [sm.KERNEL_KINDS[k] for k in tr.kinds()]
+    finally:
+        for e in events:
+            hip.hipEventDestroy(e)
+
+
 def run(entry: str, mats, params: sm.Params):
     ws = sm.workspace_tensor(mats, params, DEV)
     getattr(sm, entry)(mats, params, ws)

@@ -15,7 +15,8 @@ import torch
 import oracle
 import sign_muon_step_amd as sm
 import synthetic
-from gpu_util import DEV, announce, dtype_of, make_matrix, rel_fro, run, sign_stats, to_dev, to_host
+from gpu_util import (DEV, announce, dtype_of, make_matrix, rel_fro, run, sign_stats, to_dev, to_host,
+                      traced_step_kinds)
 
 pytestmark = pytest.mark.gpu
 
@@ -144,3 +145,42 @@ def test_spectral_gpt2_shape_full_size():
         announce(f"    worker {w}: rel err {err:.2e}, sign agreement {agree:.6f} ({bad} of {n} differ)")
         assert err < NS_TOL["bf16"]
         assert agree >= 0.999
+
+
+@pytest.mark.parametrize("ns", ["f32", "bf16"])
+@pytest.mark.parametrize("k", [0, 1])
+def test_spectral_power_iteration_in_one_launch(ns, k):
+    """A batch of at least half a device of (matrix, worker) units, every r a
+    multiple of 8 and at most 1024 (bf16) or 512 (fp32), takes the power
+    iteration with one
+    workgroup per unit: all p steps, the scales and (k >= 1) the rescale of
+    A in a single launch, the steps reading the upper part of A only. U of
+    the first and last worker of each distinct shape against the oracle; the
+    packed signs of every worker equal those of its stored U."""
+    shapes = [(64, 200), (200, 64), (128, 320), (256, 256), (200, 448), (448, 200)] * 4
+    mw, p = 8, 4
+    np_m = np.float32 if ns == "f32" else np.uint16
+    g = [grads(60 + j, mw, R, C) for j, (R, C) in enumerate(shapes)]
+    mats = [make_matrix(g[j], np.zeros(g[j].shape, np_m), np.zeros(s_, np.float32))
+            for j, s_ in enumerate(shapes)]
+    kinds = traced_step_kinds(mats, params(mw, k, ns, p))
+    announce(f"  {len(shapes)} matrices x {mw} workers, k = {k}: launches {kinds}")
+    assert kinds.count("power") == 1
+    for j in range(len(shapes)):
+        u, packed = to_host(mats[j].polar_out), to_host(mats[j].packed)
+        for w in range(mw):
+            np.testing.assert_array_equal(packed[w], oracle.sign_pack(u[w]))
+    for j in range(6):
+        m_ref = momentum_after(g[j], ns)
+        np.testing.assert_array_equal(to_host(mats[j].momentum), m_ref)
+        u = to_host(mats[j].polar_out)
+        for w in (0, mw - 1):
+            if k == 0:
+                ref = oracle.spectral_x0_a0(m_ref[w], ORC_DT[ns], p)[1]
+                tol = 1e-5
+            else:
+                ref = oracle_u(m_ref[w:w + 1], k, ns, p)[0]
+                tol = NS_TOL[ns]
+            err = rel_fro(u[w], ref)
+            announce(f"    {shapes[j]} worker {w}: rel err {err:.2e} (bound {tol:.0e})")
+            assert err < tol
