@@ -687,6 +687,72 @@ __global__ __launch_bounds__(256) void vote_update_int8_kernel(VoteI8Batch b) {
     }
 }
 
+
+// Sign + pack when the packed bits are the only output and n % 8 == 0 (the
+// same blocks as sign_pack_kernel: 2048 chunks of 8 entries per block for
+// bf16 U, 1024 for fp32). Every load is one 16-byte piece of U, consecutive
+// across the lanes (8 bf16 entries: one packed byte; 4 fp32 entries: half a
+// byte), and the bits go through 2 KiB of LDS, so that the block writes its
+// packed bytes as 8-byte words: byte stores of 64 bytes per wave instruction
+// cost more than all the loads.
+template <bool UB>
+__global__ __launch_bounds__(256) void sign_pack_words_kernel(PackBatch b) {
+    constexpr int EPP = UB ? 8 : 4;        // entries per 16-byte piece
+    constexpr int PPT = 8;                 // pieces per thread
+    constexpr int OUT = 256 * PPT * EPP / 8;  // packed bytes per block
+    __shared__ __attribute__((aligned(16))) uint8_t bits[256 * PPT];  // per piece: a byte (bf16) or a nibble (fp32)
+    const int blk = blockIdx.x;
+    const PackMat &M = b.mat[find_mat(b, blk)];
+    const int local = blk - M.block_begin;
+    const int w = local / M.blocks_per_worker;
+    const int wb = local - w * M.blocks_per_worker;
+    const int64_t n = M.n;
+    const int64_t nbytes = ((n + 63) >> 6) * 8;
+    const float s = b.scales ? b.scales[M.unit_begin + w].x : 1.0f;
+    const char *u = static_cast<const char *>(M.u) + (size_t)w * (size_t)n * (UB ? 2 : 4);
+    uint8_t *pk = reinterpret_cast<uint8_t *>(M.packed) + (size_t)w * (size_t)nbytes;
+    const int64_t q0 = (int64_t)wb * (256 * PPT);  // first piece of the block
+    u32x4_t raw[PPT];
+#pragma unroll
+    for (int i = 0; i < PPT; ++i) {
+        const int64_t e0 = (q0 + i * 256 + threadIdx.x) * EPP;
+        if (e0 < n) raw[i] = load16_nt(u + e0 * (UB ? 2 : 4));
+    }
+#pragma unroll
+    for (int i = 0; i < PPT; ++i) {
+        const int64_t e0 = (q0 + i * 256 + threadIdx.x) * EPP;
+        uint32_t v = 0;
+        if (e0 < n) {  // n % 8 == 0: the piece is whole
+#pragma unroll
+            for (int t = 0; t < EPP; ++t) {
+                const float x = UB ? bf16_bits_to_f32(t & 1 ? raw[i][t >> 1] >> 16 : raw[i][t >> 1] & 0xffffu)
+                                   : __uint_as_float(raw[i][t]);
+                v |= (uint32_t)((b.scales ? s * x : x) >= 0.0f) << t;
+            }
+        }
+        bits[i * 256 + threadIdx.x] = (uint8_t)v;
+    }
+    __syncthreads();
+    // thread t writes packed bytes 8t .. 8t + 7 of the block
+    if (threadIdx.x * 8 < OUT) {
+        const int64_t c = (int64_t)wb * OUT + threadIdx.x * 8;
+        if (c < nbytes) {  // nbytes % 8 == 0: the word is whole
+            const uint32_t *b32 = reinterpret_cast<const uint32_t *>(bits);
+            uint32_t lo, hi;
+            if (UB) {  // one byte per piece already
+                lo = b32[threadIdx.x * 2];
+                hi = b32[threadIdx.x * 2 + 1];
+            } else {   // two nibbles (pieces 2j, 2j + 1, one per byte) per packed byte j
+                auto pair = [](uint32_t x) {  // bytes n0 n1 n2 n3 -> (n0 | n1 << 4) | (n2 | n3 << 4) << 8
+                    return (x & 0xfu) | ((x >> 4) & 0xf0u) | ((x >> 8) & 0xf00u) | ((x >> 12) & 0xf000u);
+                };
+                lo = pair(b32[threadIdx.x * 4]) | pair(b32[threadIdx.x * 4 + 1]) << 16;
+                hi = pair(b32[threadIdx.x * 4 + 2]) | pair(b32[threadIdx.x * 4 + 3]) << 16;
+            }
+            *reinterpret_cast<uint2 *>(pk + c) = make_uint2(lo, hi);
+        }
+    }
+}
 }  // namespace
 
 void launch_momentum(const MomBatch &b, hipStream_t s) {
@@ -716,6 +782,16 @@ void launch_pack_fixup(const MomBatch &b, bool m_bf16, hipStream_t s) {
 
 void launch_sign_pack(const PackBatch &b, hipStream_t s) {
     dim3 grid(b.total_blocks), block(256);
+    bool words = true;  // packed bits the only output, whole chunks
+    for (int i = 0; i < b.nmat; ++i)
+        words = words && b.mat[i].packed && !b.mat[i].u_out && !b.mat[i].i8 && (b.mat[i].n & 7) == 0;
+    if (words) {
+        if (b.u_bf16)
+            hipLaunchKernelGGL(sign_pack_words_kernel<true>, grid, block, 0, s, b);
+        else
+            hipLaunchKernelGGL(sign_pack_words_kernel<false>, grid, block, 0, s, b);
+        return;
+    }
     if (b.u_bf16)
         hipLaunchKernelGGL(sign_pack_kernel<true>, grid, block, 0, s, b);
     else
