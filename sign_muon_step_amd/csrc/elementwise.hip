@@ -177,6 +177,9 @@ __global__ __launch_bounds__(kMomThreads) void momentum_kernel(MomBatch b) {
     void *mp = static_cast<char *>(M.m) + (size_t)w * (size_t)n * msz;
     uint8_t *pk = M.packed ? reinterpret_cast<uint8_t *>(M.packed) + (size_t)w * (size_t)(n >> 3) : nullptr;
     const int64_t begin = (int64_t)chunk * kMomChunk;
+    // the block's sign bytes (k = 0, packed here): staged, then stored as
+    // 8-byte words (one byte per lane would be 64 bytes per wave store)
+    __shared__ __attribute__((aligned(16))) uint8_t sbytes[kMomChunk / 8];
     double ss = 0.0;
     if ((n & 7) == 0) {
         // 8 consecutive entries per thread and round; n % 8 == 0 keeps every
@@ -202,7 +205,7 @@ __global__ __launch_bounds__(kMomThreads) void momentum_kernel(MomBatch b) {
                 unpack8<MB>(mraw[r], m);
                 Signs8 sg;
                 ss += update8<MB>(b.beta, g, m, mp, e, sg);
-                if (pk) pk[e >> 3] = (uint8_t)sg.byte;
+                if (pk) sbytes[(e - begin) >> 3] = (uint8_t)sg.byte;
             }
         }
     } else {
@@ -220,6 +223,11 @@ __global__ __launch_bounds__(kMomThreads) void momentum_kernel(MomBatch b) {
         double t = 0.0;
         for (int i = 0; i < kMomThreads / kWave; ++i) t += wsum[i];
         b.partials[M.partial_begin + local] = t;
+    }
+    if (pk) {  // n % 64 == 0: the block's byte count is a multiple of 8
+        const int64_t nb = (n - begin < kMomChunk ? n - begin : kMomChunk) >> 3;
+        for (int64_t o = (int64_t)threadIdx.x * 8; o < nb; o += (int64_t)kMomThreads * 8)
+            *reinterpret_cast<uint2 *>(pk + (begin >> 3) + o) = *reinterpret_cast<const uint2 *>(sbytes + o);
     }
 }
 
