@@ -120,20 +120,23 @@ def test_majority_vote_signum_is_the_k0_step(mom, mw):
 @pytest.mark.parametrize("mw", [1, 4, 8])
 def test_signum_signs_packed_by_the_momentum_kernel(mom, mw):
     """k = 0 with no U output: the momentum kernel packs the signs of the
-    stored M itself (n % 64 == 0), a ragged matrix in the same call takes the
-    separate pack. Two steps; degenerate workers next to ordinary ones: a
-    zero gradient (U = 0: every bit 1), a NaN and an Inf entry (||M||_F is not
-    finite, s = 0: U = 0 * M, +1 for finite entries and -1 for the NaN and
-    Inf), and an extreme dynamic range (one entry near 1e38 next to -1e-10
-    ones, whose U = M / ||M||_F is about -1e-48). Momentum, packed signs, vote
-    and W bit-exact against the oracle's whole step."""
-    shapes = [(192, 320), (64, 576), (37, 53)]
+    stored M itself (n % 64 == 0); the other matrices in the same call take
+    the separate pack of s * M (n % 8 == 0 but not 64: the 16-byte-piece
+    kernel; n % 8 != 0: the per-chunk kernel). Two steps; degenerate workers
+    next to ordinary ones: a zero gradient (U = 0: every bit 1), a NaN and an
+    Inf entry (||M||_F is not finite, s = 0: U = 0 * M, +1 for finite entries
+    and -1 for the NaN and Inf) in the first and the last matrix, and an
+    extreme dynamic range (one entry near 1e38 next to -1e-10 ones, whose
+    U = M / ||M||_F is about -1e-48) in a matrix the momentum kernel packs.
+    Momentum, packed signs, vote and W bit-exact against the oracle's whole
+    step."""
+    shapes = [(192, 320), (64, 576), (37, 53), (40, 52)]
     np_m, _, code = dtype_of(mom)
     rng = np.random.default_rng(90 + mw)
     host = []
     for j, (R, C) in enumerate(shapes):
         g = np.stack([synthetic.random_matrix(900 + 10 * j + i, (R, C), 1e-3, "normal") for i in range(mw)])
-        if j == 0 and mw >= 4:
+        if j in (0, 3) and mw >= 4:
             g[1] = 0.0
             g[2].ravel()[rng.integers(R * C)] = np.nan
             g[3, 5, 7] = -np.inf

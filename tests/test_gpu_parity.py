@@ -96,7 +96,11 @@ def test_zero_gradient_gives_all_plus_signs():
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("udt", ["f32", "bf16"])
 @pytest.mark.parametrize("n,workers", [(1, 1), (63, 2), (64, 1), (65, 3), (4097, 2), (100003, 5),
-                                       (2048 * 33 + 7, 1)])
+                                       (2048 * 33 + 7, 1),
+                                       # n % 8 == 0: the 16-byte-piece kernel, words staged in LDS;
+                                       # one chunk, a partial last word, several blocks (8192 fp32 /
+                                       # 16384 bf16 entries each) with a partial last block
+                                       (8, 3), (72, 2), (8192 + 24, 2), (16384 * 3 + 8, 2), (100000, 3)])
 def test_sign_pack_bitexact(udt, n, workers):
     rng = np.random.default_rng(n)
     u = rng.standard_normal((workers, n)).astype(np.float32)
