@@ -1157,28 +1157,25 @@ __device__ __forceinline__ void product_epilogue(const ProductArgs &pa, f32x16_t
 // register rr of block (f, g) holds row R0 (lanes 0-31) and row R0 + 4
 // (lanes 32-63) over the block's 32 columns; blocks 2 gp and 2 gp + 1 give
 // the 64 columns of one packed word (C % 64 == 0). Word id of the wave goes
-// to lane id % 64, slot id / 64; each lane then stores its kSlots words.
+// to lane id % 64, slot id / 64; each lane then stores its kSignSlots words.
 // dst in lane `lane` <- val (a uniform value); the other lanes keep dst.
 __device__ __forceinline__ int write_lane(int dst, uint32_t val, int lane) {
     asm("v_writelane_b32 %0, %1, %2" : "+v"(dst) : "s"(val), "i"(lane));
     return dst;
 }
 
+constexpr int kSignSlots = kWaveM * kWordsPerRow / kWave;  // sign words per lane
+
 // Gathers the wave's sign words (u = gamma * acc, bit = (u >= 0)) into
-// lo / hi: word id of the wave sits in lane id % 64, slot id / 64. Then
-// store(slot, row, first column, word) for each word of the lane inside the
-// matrix.
-template <class Tid, class Store>
-__device__ __forceinline__ void sign_words_from_registers(const ProductArgs &pa,
-                                                          const f32x16_t (&acc)[kFM][kFN], Tid tid,
-                                                          Store &&store) {
+// lo / hi (32-bit halves): word id of the wave sits in lane id % 64, slot
+// id / 64.
+template <class Tid>
+__device__ __forceinline__ void gather_sign_words(const ProductArgs &pa, const f32x16_t (&acc)[kFM][kFN], Tid tid,
+                                                  int (&lo)[kSignSlots], int (&hi)[kSignSlots]) {
     const float gamma = -0.5f * pa.s.get();
-    const int lane = tid() & (kWave - 1), wid = tid() / kWave;
-    const int m0 = pa.ti * kNsTileM + ProdLay::m0(wid), n0 = pa.tj * kNsProdTileN + ProdLay::n0(wid);
-    constexpr int kSlots = kWaveM * kWordsPerRow / kWave;
-    int lo[kSlots], hi[kSlots];  // 32-bit halves of each lane's words
+    (void)tid;
 #pragma unroll
-    for (int sl = 0; sl < kSlots; ++sl) lo[sl] = hi[sl] = 0;
+    for (int sl = 0; sl < kSignSlots; ++sl) lo[sl] = hi[sl] = 0;
 #pragma unroll
     for (int f = 0; f < kFM; ++f) {
 #pragma unroll
@@ -1198,41 +1195,60 @@ __device__ __forceinline__ void sign_words_from_registers(const ProductArgs &pa,
                 __builtin_amdgcn_sched_barrier(0);
             }
     }
-#pragma unroll
-    for (int sl = 0; sl < kSlots; ++sl) {
-        const int id = sl * 64 + lane;
-        const int hrow = id & 1, gp = (id >> 1) % kWordsPerRow, fr = (id >> 1) / kWordsPerRow;
-        const int rr = fr & 15, f = fr >> 4;
-        const int gm = m0 + f * 32 + 8 * (rr >> 2) + (rr & 3) + 4 * hrow;
-        const int gn0 = n0 + 64 * gp;
-        const uint64_t word = (uint64_t)(uint32_t)lo[sl] | ((uint64_t)(uint32_t)hi[sl] << 32);
-        if (gm < pa.R && gn0 < pa.C) store(gm, gn0, word);
-    }
+}
+
+// Matrix row and first column of word id of wave wid's tile part.
+__device__ __forceinline__ void sign_word_origin(const ProductArgs &pa, int wid, int id, int &gm, int &gn0) {
+    const int m0 = pa.ti * kNsTileM + ProdLay::m0(wid), n0 = pa.tj * kNsProdTileN + ProdLay::n0(wid);
+    const int hrow = id & 1, gp = (id >> 1) % kWordsPerRow, fr = (id >> 1) / kWordsPerRow;
+    const int rr = fr & 15, f = fr >> 4;
+    gm = m0 + f * 32 + 8 * (rr >> 2) + (rr & 3) + 4 * hrow;
+    gn0 = n0 + 64 * gp;
 }
 
 template <class Tid = HwTid>
 __device__ __forceinline__ void pack_from_registers(const ProductArgs &pa, const f32x16_t (&acc)[kFM][kFN],
                                                     Tid tid = Tid{}) {
-    sign_words_from_registers(pa, acc, tid, [&](int gm, int gn0, uint64_t word) {
-        pa.pk[((int64_t)gm * pa.C + gn0) >> 6] = word;
-    });
+    int lo[kSignSlots], hi[kSignSlots];
+    gather_sign_words(pa, acc, tid, lo, hi);
+    const int lane = tid() & (kWave - 1), wid = tid() / kWave;
+#pragma unroll
+    for (int sl = 0; sl < kSignSlots; ++sl) {
+        int gm, gn0;
+        sign_word_origin(pa, wid, sl * 64 + lane, gm, gn0);
+        const uint64_t word = (uint64_t)(uint32_t)lo[sl] | ((uint64_t)(uint32_t)hi[sl] << 32);
+        if (gm < pa.R && gn0 < pa.C) pa.pk[((int64_t)gm * pa.C + gn0) >> 6] = word;
+    }
 }
 
 // The same signs as int8 (+1 / -1), straight from the sign words: table entry
-// b holds the 8 bytes of the 8 bits of b (LSB first), so the 64 columns of a
-// word go out as four 16-byte stores (C % 64 == 0, 16-byte aligned rows).
+// b holds the 8 bytes of the 8 bits of b (LSB first), so a word's 64 columns
+// are four 16-byte pieces (C % 64 == 0, 16-byte aligned rows). The four lanes
+// of a quad take the quad's four words in turn (a quad_perm broadcast), and
+// lane 4k + p writes piece p: each store instruction covers 16 rows with 64
+// contiguous bytes each, where one lane per row would scatter 16 bytes into
+// each of 64 rows.
 template <class Tid>
 __device__ __forceinline__ void int8_from_registers(const ProductArgs &pa, const f32x16_t (&acc)[kFM][kFN],
                                                     Tid tid, const uint2 *table) {
-    sign_words_from_registers(pa, acc, tid, [&](int gm, int gn0, uint64_t word) {
-        uint4 *dst = reinterpret_cast<uint4 *>(pa.i8 + (int64_t)gm * pa.C + gn0);
+    int lo[kSignSlots], hi[kSignSlots];
+    gather_sign_words(pa, acc, tid, lo, hi);
+    const int lane = tid() & (kWave - 1), wid = tid() / kWave;
+    const int p = lane & 3;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const uint32_t bits = (uint32_t)(word >> (16 * q));
-            const uint2 a = table[bits & 0xffu], b = table[(bits >> 8) & 0xffu];
-            dst[q] = make_uint4(a.x, a.y, b.x, b.y);
-        }
-    });
+    for (int sl = 0; sl < kSignSlots; ++sl)
+        static_for(std::make_integer_sequence<int, 4>{}, [&](auto jc) {
+            constexpr int j = decltype(jc)::value;
+            constexpr int kQuad = j * 0x55;  // quad_perm: every lane of the quad reads its lane j
+            const uint32_t wl = (uint32_t)__builtin_amdgcn_update_dpp(0, lo[sl], kQuad, 0xf, 0xf, false);
+            const uint32_t wh = (uint32_t)__builtin_amdgcn_update_dpp(0, hi[sl], kQuad, 0xf, 0xf, false);
+            int gm, gn0;
+            sign_word_origin(pa, wid, sl * 64 + (lane & ~3) + j, gm, gn0);
+            const uint32_t bits = ((p < 2 ? wl : wh) >> (16 * (p & 1))) & 0xffffu;
+            const uint2 a = table[bits & 0xffu], b = table[bits >> 8];
+            if (gm < pa.R && gn0 < pa.C)
+                *reinterpret_cast<uint4 *>(pa.i8 + (int64_t)gm * pa.C + gn0 + 16 * p) = make_uint4(a.x, a.y, b.x, b.y);
+        });
 }
 
 // Epilogue of the walk for the next bf16 iterate (EPI_ITER), staged 8 rows
