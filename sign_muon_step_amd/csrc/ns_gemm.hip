@@ -1878,6 +1878,57 @@ __device__ __forceinline__ void gram_walk_kloop(const GramWalkTile &cur, const G
 // 8 consecutive entries of mirrored row n0 + l, and stores them as 16 bytes.
 // A diagonal block holds both triangles and is stored once. FAST: the tile's
 // groups lie inside the matrix and r % 8 == 0.
+// 4 x 4 transpose of 16-byte pieces within each quad of lanes: lane 4k + r
+// holds x[c] = T[r][c] before and x[c] = T[c][r] after (two exchanges, with
+// the lane at distance 1 and then 2; each lane sends the piece its partner
+// needs).
+__device__ __forceinline__ uint4 dpp_quad(uint4 v, int ctrl_is_swap2) {
+    // quad_perm [1, 0, 3, 2] (swap with lane ^ 1) or [2, 3, 0, 1] (lane ^ 2)
+    if (ctrl_is_swap2)
+        return make_uint4((uint32_t)__builtin_amdgcn_update_dpp(0, (int)v.x, 0x4e, 0xf, 0xf, false),
+                          (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v.y, 0x4e, 0xf, 0xf, false),
+                          (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v.z, 0x4e, 0xf, 0xf, false),
+                          (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v.w, 0x4e, 0xf, 0xf, false));
+    return make_uint4((uint32_t)__builtin_amdgcn_update_dpp(0, (int)v.x, 0xb1, 0xf, 0xf, false),
+                      (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v.y, 0xb1, 0xf, 0xf, false),
+                      (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v.z, 0xb1, 0xf, 0xf, false),
+                      (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v.w, 0xb1, 0xf, 0xf, false));
+}
+
+__device__ __forceinline__ uint4 sel4(bool c, uint4 a, uint4 b) {  // c ? a : b, per component
+    return make_uint4(c ? a.x : b.x, c ? a.y : b.y, c ? a.z : b.z, c ? a.w : b.w);
+}
+
+__device__ __forceinline__ void quad_transpose(uint4 (&x)[4], int lane) {
+    const bool odd = lane & 1, high = lane & 2;
+#pragma unroll
+    for (int c = 0; c < 4; c += 2) {  // pieces c, c + 1 across lane ^ 1
+        const uint4 x0 = x[c], x1 = x[c + 1];
+        const uint4 got = dpp_quad(sel4(odd, x0, x1), 0);
+        x[c] = sel4(odd, got, x0);
+        x[c + 1] = sel4(odd, x1, got);
+    }
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {  // pieces c, c + 2 across lane ^ 2
+        const uint4 x0 = x[c], x2 = x[c + 2];
+        const uint4 got = dpp_quad(sel4(high, x0, x2), 1);
+        x[c] = sel4(high, got, x0);
+        x[c + 2] = sel4(high, x2, got);
+    }
+}
+
+// Epilogue of a walked Gram tile: A = scale * acc rounded to bf16, each of
+// the wave's two 64 x 64 blocks and (off the diagonal) its mirror, 8 rows of
+// the wave's 128 x 64 result at a time through the wave's 8 x kStageStride
+// floats outside the stage buffers. Register 4q + t of block (f, g) holds
+// row 8q + 4h + t (h = lane / 32) of the block. Direct rows: 8 lanes per
+// row, 8 columns (16 bytes) each. Mirror: lane l reads staged column l, i.e.
+// 8 consecutive entries of mirrored row n0 + l (16 bytes); FAST keeps the
+// four such pieces of a 32-row block, transposes them within each quad of
+// lanes and writes 16 mirrored rows x 64 contiguous bytes per store (one
+// lane per row would scatter 16 bytes into each of 64 rows). A diagonal
+// block holds both triangles and is stored once. FAST: the tile's groups
+// lie inside the matrix and r % 8 == 0.
 template <bool FAST>
 __device__ __forceinline__ void gram_walk_epilogue(const GramWalkTile &g, const f32x16_t (&acc)[kFM][kFN],
                                                    GivenTid tid, float *estage) {
@@ -1892,11 +1943,12 @@ __device__ __forceinline__ void gram_walk_epilogue(const GramWalkTile &g, const 
     uint16_t *a = reinterpret_cast<uint16_t *>(g.a);
     const int r = g.r;
 #pragma unroll
-    for (int f = 0; f < kFM; ++f)
+    for (int f = 0; f < kFM; ++f) {
+        const int mb = (f < 2 ? m1 : m2) + 32 * (f & 1);  // first row of 32-row block f
+        const bool mirror = (f < 2 ? s1 : s2) != sb;
+        uint4 mp[4];  // FAST mirror: this lane's pieces of mirrored row n0 + lane, q = 0..3
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            const int mb = (f < 2 ? m1 : m2) + 32 * (f & 1);  // first row of 32-row block f
-            const bool mirror = (f < 2 ? s1 : s2) != sb;
 #pragma unroll
             for (int gg = 0; gg < kFN; ++gg)
 #pragma unroll
@@ -1925,9 +1977,8 @@ __device__ __forceinline__ void gram_walk_epilogue(const GramWalkTile &g, const 
 #pragma unroll
                 for (int e = 0; e < 8; ++e) v[e] = st[e * kStageStride + lane];
                 if (FAST) {
-                    *reinterpret_cast<uint4 *>(a + (int64_t)gj * r + gi) =
-                        make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
-                                   pack_bf16x2(v[6], v[7]));
+                    mp[q] = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                                       pack_bf16x2(v[6], v[7]));
                 } else {
 #pragma unroll
                     for (int e = 0; e < 8; ++e)
@@ -1936,6 +1987,15 @@ __device__ __forceinline__ void gram_walk_epilogue(const GramWalkTile &g, const 
             }
             wave_lds_fence();
         }
+        if (FAST && mirror) {
+            // lane 4k + p now takes piece p of mirrored rows n0 + 4k + j, j = 0..3
+            quad_transpose(mp, lane);
+            const int p = lane & 3, k4 = lane & ~3;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                *reinterpret_cast<uint4 *>(a + (int64_t)(n0 + k4 + j) * r + mb + 8 * p) = mp[j];
+        }
+    }
 }
 
 // Logical tile of workgroup position pos in round rho (snake order).
