@@ -159,8 +159,8 @@ void launch_gram_reduce(const NsBatch &b, bool ns_bf16, hipStream_t s);
 inline int32_t ns_gram_split(int64_t R, int64_t C, bool ns_bf16) {
     if (ns_gram_tiles(R, C) > 3) return 0;
     const int64_t c = R > C ? R : C, bk = ns_bf16 ? 32 : 16;
-    const int64_t s = (c + bk - 1) / bk / 16;
-    return (int32_t)(s < 2 ? 0 : (s > 8 ? 8 : s));
+    const int64_t s = ((c + bk - 1) / bk + 23) / 24;  // chunks of about 24 k slices
+    return (int32_t)(s < 2 ? 0 : (s > 16 ? 16 : s));
 }
 // The bf16 Gram matrices as a persistent walk: grid_blocks workgroups (one
 // per CU, at most b.total_tiles) walk the tiles of wide and tall matrices in
