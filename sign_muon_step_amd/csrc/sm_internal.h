@@ -275,7 +275,7 @@ void launch_vote_update_int8(const VoteI8Batch &b, hipStream_t s);
 constexpr int kPowRowsPerBlock = 32;  // rows of A per power-step block (8 per wave)
 constexpr int kMaxPowR = 8192;         // the power vector of a Gram lives in LDS
 // The one-workgroup power iteration: two 16-byte column chunks per lane at most.
-inline int max_fused_pow_r(bool bf16) { return bf16 ? 1024 : 512; }
+inline int max_fused_pow_r(bool bf16) { return bf16 ? 1016 : 504; }  // (r + 8) / EPC <= 128
 
 struct PowMat {
     const void *a;   // worker 0's Gram matrix [r][r] (ns type); worker stride r*r

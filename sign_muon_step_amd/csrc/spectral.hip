@@ -226,132 +226,180 @@ __global__ __launch_bounds__(kThreads) void gram_rescale_kernel(PowBatch b) {
 // steps, the scale and (for the first Newton-Schulz iteration) the rescale
 // of A, in one launch over every unit. A is stored symmetric (each
 // off-diagonal entry with its mirror), so a step reads the upper part only.
-// Rows go in groups of 8 (rows j0 .. j0 + 7), one group per wave at a time.
-// For row j of a group:
-//   row sum:     sum over c >= j0 of A[j][c] v[c]   (whole 16-byte chunks;
-//                the few c < j of the group's own chunk are the stored
-//                lower entries of the diagonal block)
-//   column sums: A[j][c] v[j] added to column c for every c >= j0 + 8.
-// A pair (j, c) with c < j0 is then covered by row c's column sums (c's
-// group ends at or before j0), and no pair twice: w[c] = row sum of c + the
-// eight waves' column sums of c, in wave order. Lane l owns the 16-byte
-// column chunks l, l + 64, ... and keeps their column sums in registers over
-// the wave's groups. Every sum runs in a fixed order, so results do not
-// depend on timing. The working set of the units in flight is their upper
-// triangles (about 0.6 MB at r = 768), which the Infinity Cache holds
-// across the p steps, where one launch per step over every unit streams all
-// of A from HBM each time.
+// Rows go in groups of 8: group g is rows 8g .. 8g + 7, and it reads the
+// 16-byte chunks from its 8 x 8 diagonal block to the row end. For row j of
+// group g:
+//   row sum:     sum over c >= 8g of A[j][c] v[c]  (the few c < j of the
+//                diagonal block are its stored lower entries)
+//   column sums: A[j][c] v[j] added to column c for every c >= 8g + 8.
+// A pair (j, c) with c < 8g is then covered by row c's column sums, and no
+// pair twice: w[c] = row sum of c + the column sums of c.
+// Group g's chunk count falls by one diagonal block per group, so groups g
+// and G - 1 - g (G = r / 8) together have r / EPC + 8 / EPC chunks whatever
+// g is: a wave takes such a pair at a time, its chunk list spread over the
+// lanes (position p in slot p / 64 of lane p % 64), and few lanes idle.
+// Lane sums go to the 16 row sums by one butterfly and to the column sums
+// in LDS, one array per wave for each side of the pair (lanes of one load
+// never share a column chunk within a side). Every sum runs in a fixed
+// order, so results do not depend on timing. The working set of the units
+// in flight is their upper triangles (about 0.6 MB at r = 768), which the
+// Infinity Cache holds across the p steps, where one launch per step over
+// every unit streams all of A from HBM each time.
 // ---------------------------------------------------------------------------
 constexpr int kFusedThreads = 512, kFusedWaves = kFusedThreads / kWave;
 
-template <bool BF16, int T>  // T: chunk slots per lane, T * 64 * EPC >= r
+typedef uint32_t v4u32 __attribute__((ext_vector_type(4)));
+constexpr uint32_t kOOB = 0x80000000u;  // buffer offset past every extent: loads read zeros, stores drop
+
+template <bool BF16, int T>  // T: chunk slots per lane, T * 64 >= (r + 8) / EPC
 __global__ __launch_bounds__(kFusedThreads) void power_fused_kernel(PowBatch b, int rescale) {
     constexpr int EPC = BF16 ? 8 : 4;                // entries per 16-byte chunk
-    extern __shared__ float lds[];                   // v [r], row sums / w [r], column sums [waves][r]
+    constexpr uint32_t ES = BF16 ? 2 : 4;            // bytes per entry
+    constexpr int DQ = 8 / EPC;                      // chunks per row of an 8 x 8 block
+    extern __shared__ float lds[];                   // v [r], row sums / w [r], column sums [2][waves][r]
     __shared__ double red[kFusedWaves];
     __shared__ double tot;
     const int mi = blockIdx.x / b.workers, w = blockIdx.x - mi * b.workers;
     const PowMat &M = b.mat[mi];
-    const int r = M.r;  // r % 8 == 0, r <= T * 64 * EPC (the launcher checks)
-    float *v = lds, *rowsum = lds + r, *colsum = lds + 2 * r;
+    const int r = M.r;  // r % 8 == 0, (r + 8) / EPC <= T * 64 (the launcher checks)
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-    char *a = static_cast<char *>(const_cast<void *>(M.a)) + (int64_t)w * r * r * (BF16 ? 2 : 4);
-    const int nch = r / EPC;  // chunks per row
+    float *v = lds, *rowsum = lds + r;
+    float *col_a = lds + (2 + wave) * r, *col_b = lds + (2 + kFusedWaves + wave) * r;
+    char *a = static_cast<char *>(const_cast<void *>(M.a)) + (int64_t)w * r * r * ES;
+    // A buffer over this unit's A: a position that a pair does not fill, and
+    // any pair past the last, takes the offset kOOB and reads zeros. Every
+    // pair thus issues the same loads with no branch around them, and the
+    // compiler can wait for one pair's loads while the next pair's stay in
+    // flight.
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(a, 0, (int)((uint32_t)r * r * ES), 0x00020000);
+    const int nch = r / EPC, G = r / 8, npairs = (G + 1) / 2;
     const float v0 = (float)(1.0 / sqrt((double)r));
     for (int c = threadIdx.x; c < r; c += kFusedThreads) v[c] = v0;
     __syncthreads();
-    double n2 = 0.0;
-    for (int it = 0; it < b.it; ++it) {
-        float col[T][EPC];
+    // Pair k: groups k and G - 1 - k (the same group once when G is odd).
+    // Position p: chunk DQ k + p of group k for p < La, else chunk
+    // DQ (G - 1 - k) + p - La of the other group.
+    struct Pos {
+        int row0, q;
+        bool first, ok;
+    };
+    auto where = [&](int k, int t) {
+        const int ga = k, gb = G - 1 - k;
+        const int la = nch - DQ * ga, lb = gb > ga ? nch - DQ * gb : 0;
+        const int p = lane + kWave * t;
+        Pos o;
+        o.first = p < la;
+        o.ok = k < npairs && p < la + lb;
+        o.row0 = 8 * (o.first ? ga : gb);
+        o.q = o.first ? DQ * ga + p : DQ * gb + (p - la);
+        return o;
+    };
+    auto issue = [&](int k, v4u32 (&h)[T][8]) {
 #pragma unroll
-        for (int t = 0; t < T; ++t)
+        for (int t = 0; t < T; ++t) {
+            const Pos o = where(k, t);
+            const uint32_t off = ((uint32_t)o.row0 * r + (uint32_t)o.q * EPC) * ES;
 #pragma unroll
-            for (int e = 0; e < EPC; ++e) col[t][e] = 0.f;
-        // Row groups j0 = 8 wave, 8 wave + 64, ...: the next group's chunks are
-        // loaded while the current one is summed.
-        auto load_group = [&](int j0, uint4 (&h)[T][8]) {
-            const int qa = j0 / EPC;
+            for (int i = 0; i < 8; ++i)
+                h[t][i] = __builtin_amdgcn_raw_buffer_load_b128(rs, o.ok ? off + (uint32_t)i * r * ES : kOOB, 0, 0);
+        }
+    };
+    // Pair k (k < npairs): its 16 row sums to LDS, its column sums added to
+    // the wave's arrays.
+    auto consume = [&](int k, const v4u32 (&h)[T][8]) {
+        const int ga = k, gb = G - 1 - k;
+        const bool two = gb > ga;
+        const int np = nch - DQ * ga + (two ? nch - DQ * gb : 0);
+        float va[8], vb[8], ra[8], rb[8];
 #pragma unroll
-            for (int t = 0; t < T; ++t) {
-                const int q = lane + kWave * t;
-                const bool ok = j0 < r && q >= qa && q < nch;
-#pragma unroll
-                for (int i = 0; i < 8; ++i)
-                    h[t][i] = ok ? *reinterpret_cast<const uint4 *>(
-                                       a + ((int64_t)(j0 + i) * r + (int64_t)q * EPC) * (BF16 ? 2 : 4))
-                                 : make_uint4(0, 0, 0, 0);
-            }
-        };
-        uint4 hc[T][8];
-        load_group(8 * wave, hc);
-        for (int j0 = 8 * wave; j0 < r; j0 += 8 * kFusedWaves) {
-            uint4 hn[T][8];
-            load_group(j0 + 8 * kFusedWaves, hn);
-            const int qa = j0 / EPC, qb = (j0 + 8) / EPC;  // first chunk read; first with column sums
-            float vj[8], row[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                vj[i] = v[j0 + i];
-                row[i] = 0.f;
-            }
-#pragma unroll
-            for (int t = 0; t < T; ++t) {
-                const int q = lane + kWave * t;
-                if (kWave * t + kWave <= qa || kWave * t >= nch) continue;  // uniform: no chunk of this slot
-                if (q < qa || q >= nch) continue;
-                float vc[EPC];
-#pragma unroll
-                for (int e = 0; e < EPC; ++e) vc[e] = v[q * EPC + e];
-                // the group's own chunk (q < qb) adds nothing to the column sums:
-                // multiplied by 0 (a non-finite A gives s = 0 either way)
-                const bool cols = q >= qb;
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    float x[EPC];
-                    if constexpr (BF16) {
-                        const uint32_t hw[4] = {hc[t][i].x, hc[t][i].y, hc[t][i].z, hc[t][i].w};
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            x[2 * e] = bf16_bits_to_f32(hw[e] & 0xffffu);
-                            x[2 * e + 1] = bf16_bits_to_f32(hw[e] >> 16);
-                        }
-                    } else {
-                        x[0] = __uint_as_float(hc[t][i].x);
-                        x[1] = __uint_as_float(hc[t][i].y);
-                        x[2] = __uint_as_float(hc[t][i].z);
-                        x[3] = __uint_as_float(hc[t][i].w);
-                    }
-                    const float cs = cols ? vj[i] : 0.f;
-#pragma unroll
-                    for (int e = 0; e < EPC; ++e) {
-                        row[i] = __builtin_fmaf(x[e], vc[e], row[i]);
-                        col[t][e] = __builtin_fmaf(x[e], cs, col[t][e]);
-                    }
-                }
-            }
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const float s = wave_sum_f32(row[i]);
-                if (lane == 0) rowsum[j0 + i] = s;
-            }
-#pragma unroll
-            for (int t = 0; t < T; ++t)
-#pragma unroll
-                for (int i = 0; i < 8; ++i) hc[t][i] = hn[t][i];
+        for (int i = 0; i < 8; ++i) {
+            va[i] = v[8 * ga + i];
+            vb[i] = two ? v[8 * gb + i] : 0.f;
+            ra[i] = rb[i] = 0.f;
         }
 #pragma unroll
         for (int t = 0; t < T; ++t) {
-            const int q = lane + kWave * t;
-            if (q < nch)
+            if (kWave * t >= np) continue;  // uniform: no position in this slot
+            const Pos o = where(k, t);
+            if (!o.ok) continue;
+            float vc[EPC], cs[EPC];
 #pragma unroll
-                for (int e = 0; e < EPC; ++e) colsum[wave * r + q * EPC + e] = col[t][e];
+            for (int e = 0; e < EPC; ++e) {
+                vc[e] = v[o.q * EPC + e];
+                cs[e] = 0.f;
+            }
+            // the group's diagonal chunks add nothing to the column sums:
+            // multiplied by 0 (a non-finite A gives s = 0 either way)
+            const bool cols = o.q >= o.row0 / EPC + DQ;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                float x[EPC];
+                if constexpr (BF16) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        x[2 * e] = bf16_bits_to_f32(h[t][i][e] & 0xffffu);
+                        x[2 * e + 1] = bf16_bits_to_f32(h[t][i][e] >> 16);
+                    }
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) x[e] = __uint_as_float(h[t][i][e]);
+                }
+                float d = 0.f;
+#pragma unroll
+                for (int e = 0; e < EPC; ++e) d = __builtin_fmaf(x[e], vc[e], d);
+                ra[i] += o.first ? d : 0.f;
+                rb[i] += o.first ? 0.f : d;
+                const float vj = cols ? (o.first ? va[i] : vb[i]) : 0.f;
+#pragma unroll
+                for (int e = 0; e < EPC; ++e) cs[e] = __builtin_fmaf(x[e], vj, cs[e]);
+            }
+            float *cp = (o.first ? col_a : col_b) + o.q * EPC;
+#pragma unroll
+            for (int e = 0; e < EPC; ++e) cp[e] += cs[e];
+        }
+        // 16 sums over the wave: each exchange halves the values a lane
+        // keeps, so lane l ends with the whole sum of value
+        // 8 l5 + 4 l4 + 2 l3 + l2 (l5 .. l2: bits of l).
+        float s[16];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            s[i] = ra[i];
+            s[8 + i] = rb[i];
+        }
+#pragma unroll
+        for (int half = 8, bit = 32; half >= 1; half >>= 1, bit >>= 1) {
+            const bool hi = (lane & bit) != 0;
+#pragma unroll
+            for (int m = 0; m < half; ++m) {
+                const float keep = hi ? s[half + m] : s[m], send = hi ? s[m] : s[half + m];
+                s[m] = keep + __shfl_xor(send, bit, kWave);
+            }
+        }
+        s[0] += __shfl_xor(s[0], 2, kWave);
+        s[0] += __shfl_xor(s[0], 1, kWave);
+        const int idx = lane >> 2;  // 8 l5 + 4 l4 + 2 l3 + l2
+        if ((lane & 3) == 0 && (idx < 8 || two)) rowsum[idx < 8 ? 8 * ga + idx : 8 * gb + idx - 8] = s[0];
+    };
+    double n2 = 0.0;
+    for (int it = 0; it < b.it; ++it) {
+        for (int c = lane; c < r; c += kWave) col_a[c] = col_b[c] = 0.f;  // this wave's arrays
+        // The wave's pairs k = wave, wave + 8, ... two at a time in two
+        // register sets: a pair's loads are issued before the pair ahead of
+        // it is summed.
+        v4u32 ha[T][8], hb[T][8];
+        issue(wave, ha);
+        for (int k = wave; k < npairs; k += 2 * kFusedWaves) {
+            issue(k + kFusedWaves, hb);
+            consume(k, ha);
+            issue(k + 2 * kFusedWaves, ha);
+            if (k + kFusedWaves < npairs) consume(k + kFusedWaves, hb);
         }
         __syncthreads();  // every read of v done; row and column sums complete
         double sq = 0.0;
         for (int c = threadIdx.x; c < r; c += kFusedThreads) {
             float wc = rowsum[c];
 #pragma unroll
-            for (int k = 0; k < kFusedWaves; ++k) wc += colsum[k * r + c];
+            for (int k = 0; k < 2 * kFusedWaves; ++k) wc += lds[(2 + k) * r + c];
             rowsum[c] = wc;
             sq += (double)wc * wc;
         }
@@ -378,34 +426,30 @@ __global__ __launch_bounds__(kFusedThreads) void power_fused_kernel(PowBatch b, 
     }
     if (threadIdx.x == 0) b.scales[M.unit_begin + w] = make_float2(s, s2);
     if (!rescale) return;
-    // A <- round(s^2 * A), 16 bytes per access (r % 8 == 0), eight accesses of
-    // each thread in flight at a time
+    // A <- round(s^2 * A), 16 bytes per access (r % 8 == 0), kIn accesses of
+    // each thread in flight at a time; accesses past the end take kOOB.
     constexpr int kIn = 8;
-    const int64_t nq = (int64_t)r * r / EPC;
-    uint4 *p = reinterpret_cast<uint4 *>(a);
-    for (int64_t i0 = threadIdx.x; i0 < nq; i0 += (int64_t)kIn * kFusedThreads) {
-        uint4 h[kIn];
+    const uint32_t nq = (uint32_t)r * r / EPC;
+    for (uint32_t i0 = threadIdx.x; i0 < nq; i0 += (uint32_t)kIn * kFusedThreads) {
+        v4u32 h[kIn];
 #pragma unroll
         for (int u = 0; u < kIn; ++u) {
-            const int64_t i = i0 + (int64_t)u * kFusedThreads;
-            h[u] = i < nq ? p[i] : make_uint4(0, 0, 0, 0);
+            const uint32_t i = i0 + (uint32_t)u * kFusedThreads;
+            h[u] = __builtin_amdgcn_raw_buffer_load_b128(rs, i < nq ? i * 16u : kOOB, 0, 0);
         }
 #pragma unroll
         for (int u = 0; u < kIn; ++u) {
-            const int64_t i = i0 + (int64_t)u * kFusedThreads;
-            if (i >= nq) break;
+            const uint32_t i = i0 + (uint32_t)u * kFusedThreads;
+            v4u32 o;
             if constexpr (BF16) {
-                uint32_t hw[4] = {h[u].x, h[u].y, h[u].z, h[u].w};
 #pragma unroll
                 for (int t = 0; t < 4; ++t)
-                    hw[t] = pack_bf16x2(s2 * bf16_bits_to_f32(hw[t] & 0xffffu), s2 * bf16_bits_to_f32(hw[t] >> 16));
-                p[i] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+                    o[t] = pack_bf16x2(s2 * bf16_bits_to_f32(h[u][t] & 0xffffu), s2 * bf16_bits_to_f32(h[u][t] >> 16));
             } else {
-                p[i] = make_uint4(__float_as_uint(s2 * __uint_as_float(h[u].x)),
-                                  __float_as_uint(s2 * __uint_as_float(h[u].y)),
-                                  __float_as_uint(s2 * __uint_as_float(h[u].z)),
-                                  __float_as_uint(s2 * __uint_as_float(h[u].w)));
+#pragma unroll
+                for (int t = 0; t < 4; ++t) o[t] = __float_as_uint(s2 * __uint_as_float(h[u][t]));
             }
+            __builtin_amdgcn_raw_buffer_store_b128(o, rs, i < nq ? i * 16u : kOOB, 0, 0);
         }
     }
 }
@@ -434,9 +478,10 @@ void launch_power_finalize(const PowBatch &b, hipStream_t s) {
 void launch_power_fused(const PowBatch &b, bool bf16, bool rescale, hipStream_t s) {
     int rmax = 0;
     for (int i = 0; i < b.nmat; ++i) rmax = b.mat[i].r > rmax ? b.mat[i].r : rmax;
-    const size_t lds = (size_t)rmax * (2 + kFusedWaves) * sizeof(float);
+    const size_t lds = (size_t)rmax * (2 + 2 * kFusedWaves) * sizeof(float);
     dim3 grid(b.nmat * b.workers), block(kFusedThreads);
-    const int slots = (rmax / (bf16 ? 8 : 4) + kWave - 1) / kWave;  // chunk slots per lane
+    const int epc = bf16 ? 8 : 4;
+    const int slots = ((rmax + 8) / epc + kWave - 1) / kWave;  // chunk slots per lane for a pair of row groups
     const int rs = rescale ? 1 : 0;
 #define SM_FUSED(BF, TS) hipLaunchKernelGGL((power_fused_kernel<BF, TS>), grid, block, lds, s, b, rs)
     if (bf16) {

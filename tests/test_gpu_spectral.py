@@ -151,7 +151,7 @@ def test_spectral_gpt2_shape_full_size():
 @pytest.mark.parametrize("k", [0, 1])
 def test_spectral_power_iteration_in_one_launch(ns, k):
     """A batch of at least half a device of (matrix, worker) units, every r a
-    multiple of 8 and at most 1024 (bf16) or 512 (fp32), takes the power
+    multiple of 8 and at most 1016 (bf16) or 504 (fp32), takes the power
     iteration with one
     workgroup per unit: all p steps, the scales and (k >= 1) the rescale of
     A in a single launch, the steps reading the upper part of A only. U of
@@ -184,3 +184,32 @@ def test_spectral_power_iteration_in_one_launch(ns, k):
             err = rel_fro(u[w], ref)
             announce(f"    {shapes[j]} worker {w}: rel err {err:.2e} (bound {tol:.0e})")
             assert err < tol
+
+
+@pytest.mark.parametrize("ns", ["f32", "bf16"])
+def test_spectral_one_launch_at_its_widest(ns):
+    """The one-launch power iteration at r up to its limit (1016 in bf16, 504
+    in fp32), where a pair of row groups spreads over two chunks per lane,
+    and at r = 768 (the GPT-2 shapes): 16 matrices x 8 workers, k = 1. U of
+    the first and last worker of each distinct shape against the oracle."""
+    shapes = ([(768, 1536), (1016, 1016), (1536, 768), (512, 600)] if ns == "bf16"
+              else [(504, 504), (256, 512), (480, 256), (264, 256)])
+    mw, p, k = 8, 6, 1
+    np_m = np.float32 if ns == "f32" else np.uint16
+    g = list(POOL.map(lambda j: grads(90 + j, mw, *shapes[j]), range(len(shapes))))
+    mats = [make_matrix(g[j % 4], np.zeros(g[j % 4].shape, np_m), np.zeros(shapes[j % 4], np.float32))
+            for j in range(16)]
+    kinds = traced_step_kinds(mats, params(mw, k, ns, p))
+    announce(f"  16 matrices x {mw} workers, k = {k}: launches {kinds}")
+    assert kinds.count("power") == 1
+    for j in range(4):
+        m_ref = momentum_after(g[j], ns)
+        for jj in (j, j + 12):
+            np.testing.assert_array_equal(to_host(mats[jj].momentum), m_ref)
+        u, u_last = to_host(mats[j].polar_out), to_host(mats[j + 12].polar_out)
+        np.testing.assert_array_equal(u, u_last)
+        refs = oracle_u(m_ref[[0, mw - 1]], k, ns, p)
+        for w, ref in zip((0, mw - 1), refs):
+            err = rel_fro(u[w], ref)
+            announce(f"    {shapes[j]} worker {w}: rel err {err:.2e} (bound {NS_TOL[ns]:.0e})")
+            assert err < NS_TOL[ns]
