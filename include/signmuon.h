@@ -271,7 +271,7 @@ enum {
     SIGNMUON_K_PACK = 5,     /* standalone sign + pack */
     SIGNMUON_K_VOTE = 6,     /* majority vote + update */
     SIGNMUON_K_AUX = 7,      /* post-vote polar step bookkeeping */
-    SIGNMUON_K_POWER = 8,    /* spectral normalisation: power step, scale, Gram rescale */
+    SIGNMUON_K_POWER = 8,    /* spectral normalisation: power steps and scale */
     SIGNMUON_K_VOTE_I8 = 9   /* vote from the int8 payload + update */
 };
 

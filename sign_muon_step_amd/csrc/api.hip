@@ -407,6 +407,7 @@ int ns_pass(const signmuon_matrix *mats, int32_t n_mats, const signmuon_params *
             b.use_scales = use_scales;
             b.scales = scales;
             b.eta = p->eta;  // the W-update epilogue
+            b.id_scaled = pass == 1 && use_scales && pl.spectral ? 1 : 0;
             const bool split = pass == 0 && g == LG_GRAM_SPLIT;
             const bool gram_walk = pass == 0 && g == LG_GRAM_WALK;
             // split Gram: Gram tiles x split blocks per worker; the reduce
@@ -456,11 +457,11 @@ int ns_pass(const signmuon_matrix *mats, int32_t n_mats, const signmuon_params *
 }
 
 // Spectral normalisation (see signmuon_params.power_iters): the unscaled Gram
-// matrix of the stored momentum, power_iters power steps on it, the scales
-// {s, s^2}, and (rescale) A_0 = round(s^2 A_raw) in place for the first
-// product.
+// matrix of the stored momentum, power_iters power steps on it and the
+// scales {s, s^2}. A stays unscaled: the first product applies s^2 itself
+// (NsBatch::id_scaled).
 int run_spectral(const signmuon_matrix *mats, int32_t n_mats, const signmuon_params *p,
-                 const Plan &pl, void *ws, bool rescale, hipStream_t st, Tracer &tr) {
+                 const Plan &pl, void *ws, hipStream_t st, Tracer &tr) {
     if (int rc = ns_pass(mats, n_mats, p, pl, ws, false, 0, 0, false, st, tr)) return rc;
     const bool bf16 = p->ns_dtype == SIGNMUON_BF16;
     for (int32_t c0 = 0; c0 < n_mats; c0 += sm::kMaxMatsPerLaunch) {
@@ -484,15 +485,15 @@ int run_spectral(const signmuon_matrix *mats, int32_t n_mats, const signmuon_par
         }
         if (blocks > INT32_MAX) return SIGNMUON_ERANGE;
         b.total_blocks = (int32_t)blocks;
-        // One workgroup per (matrix, worker) runs every step, the scale and
-        // the rescale when each Gram matrix suits it and there are enough
-        // units to fill the device; otherwise one launch per step.
+        // One workgroup per (matrix, worker) runs every step and the scale
+        // when each Gram matrix suits it and there are enough units to fill
+        // the device; otherwise one launch per step.
         bool fused = (int64_t)cn * p->workers >= device_cus() / 2;
         for (int32_t i = 0; i < cn; ++i)
             fused = fused && pl.m[c0 + i].r % 8 == 0 && pl.m[c0 + i].r <= sm::max_fused_pow_r(bf16);
         if (fused) {
             b.it = p->power_iters;
-            sm::launch_power_fused(b, bf16, rescale, st);
+            sm::launch_power_fused(b, bf16, st);
             if (int rc = tr.after(SIGNMUON_K_POWER)) return rc;
             continue;
         }
@@ -504,19 +505,6 @@ int run_spectral(const signmuon_matrix *mats, int32_t n_mats, const signmuon_par
         b.it = p->power_iters - 1;
         sm::launch_power_finalize(b, st);
         if (int rc = tr.after(SIGNMUON_K_POWER)) return rc;
-        if (rescale) {
-            int64_t rblocks = 0;
-            for (int32_t i = 0; i < cn; ++i) {
-                const MatPlan &q = pl.m[c0 + i];
-                b.mat[i].bpw = sm::rescale_blocks_per_worker(q.r);
-                b.starts.v[i] = (int32_t)rblocks;
-                rblocks += (int64_t)p->workers * b.mat[i].bpw;
-            }
-            if (rblocks > INT32_MAX) return SIGNMUON_ERANGE;
-            b.total_blocks = (int32_t)rblocks;
-            sm::launch_gram_rescale(b, bf16, st);
-            if (int rc = tr.after(SIGNMUON_K_POWER)) return rc;
-        }
     }
     return SIGNMUON_OK;
 }
@@ -528,7 +516,7 @@ int run_newton_schulz(const signmuon_matrix *mats, int32_t n_mats, const signmuo
                       bool muon = false) {
     for (int j = 0; j < p->ns_iters; ++j) {
         if (j == 0 && pl.spectral) {
-            if (int rc = run_spectral(mats, n_mats, p, pl, ws, true, st, tr)) return rc;
+            if (int rc = run_spectral(mats, n_mats, p, pl, ws, st, tr)) return rc;
         } else {
             if (int rc = ns_pass(mats, n_mats, p, pl, ws, step, j, 0, j == 0, st, tr)) return rc;
         }
@@ -794,7 +782,7 @@ int signmuon_momentum_ns(const signmuon_matrix *mats, int32_t n_mats, const sign
     if (int rc = run_momentum(mats, n_mats, p, pl, workspace, st, tr)) return rc;
     if (p->ns_iters == 0) {
         if (pl.spectral)
-            if (int rc = run_spectral(mats, n_mats, p, pl, workspace, false, st, tr)) return rc;
+            if (int rc = run_spectral(mats, n_mats, p, pl, workspace, st, tr)) return rc;
         return run_pack(mats, n_mats, p, pl, workspace, false, st, tr);
     }
     return run_newton_schulz(mats, n_mats, p, pl, workspace, false, st, tr);
@@ -817,7 +805,7 @@ int signmuon_step_traced(const signmuon_matrix *mats, int32_t n_mats, const sign
     if (p->ns_iters > 0) {
         if (int rc = run_newton_schulz(mats, n_mats, p, pl, workspace, true, st, tr)) return rc;
     } else if (pl.spectral) {
-        if (int rc = run_spectral(mats, n_mats, p, pl, workspace, false, st, tr)) return rc;
+        if (int rc = run_spectral(mats, n_mats, p, pl, workspace, st, tr)) return rc;
     }
     if (int rc = run_pack(mats, n_mats, p, pl, workspace, true, st, tr)) return rc;
     if (int rc = run_vote(mats, n_mats, p, pl, workspace, st, tr)) return rc;

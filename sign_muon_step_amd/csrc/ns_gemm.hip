@@ -465,52 +465,80 @@ __device__ __forceinline__ void mma_step(const Frags<BF16> &fr, f32x16_t (&acc)[
 // and the products are exact in fp32.
 enum IdSide { ID_NONE = 0, ID_P = 1, ID_Q = 2 };
 
-// One-hot -3 fragment: lane l, k index kl (within the 32-row block) holds -3
-// where kl equals the lane's row (l & 31).
+// Coefficient of the identity term: -3, or, in the first iteration under
+// spectral scaling, -3 / s^2. There A enters unscaled and the accumulators
+// are multiplied by s^2 before the epilogue, so that s^2 (A - 3 / s^2 I) X
+// stands for (s^2 A - 3 I) X without a rescaled copy of A. A bf16 fragment
+// holds the coefficient as the sum hi + lo of two bf16 values (relative
+// error below 2^-17; lo = 0 for -3, and its MFMA is issued only when lo is
+// not 0), an fp32 fragment whole. Every field is wave-uniform.
+struct IdCoef {
+    uint32_t hi, lo;  // bf16 bits
+    float f;
+};
+constexpr IdCoef kIdMinus3{0xc040u, 0u, -3.0f};
+
+// s2: the unit's s^2. It is 0 when lambda is 0 or not finite; then s = 0 as
+// well, and -3 keeps the accumulators as finite as they were.
+__device__ __forceinline__ IdCoef id_coef_spectral(float s2) {
+    const float c = s2 > 0.f ? -3.0f / s2 : -3.0f;
+    const uint32_t hi = f32_to_bf16_bits(c);
+    const uint32_t lo = f32_to_bf16_bits(c - __uint_as_float(hi << 16));  // c - hi is exact
+    return IdCoef{(uint32_t)__builtin_amdgcn_readfirstlane((int)hi),
+                  (uint32_t)__builtin_amdgcn_readfirstlane((int)lo),
+                  __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(c)))};
+}
+
+// One-hot fragment of the bf16 value with bits h: lane l, k index kl (within
+// the 32-row block) holds it where kl equals the lane's row (l & 31).
 template <class Tid = HwTid>
-__device__ __forceinline__ bf16x8_t id_frag_bf16(int roff, int kk, Tid tid = Tid{}) {
+__device__ __forceinline__ bf16x8_t id_frag_bf16(int roff, int kk, uint32_t h, Tid tid = Tid{}) {
     const int lane = tid() & (kWave - 1);
-    const int j = (lane & 31) - roff - 16 * kk - 8 * (lane >> 5);  // element holding -3
+    const int j = (lane & 31) - roff - 16 * kk - 8 * (lane >> 5);  // element holding h
     uint32_t w[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-        w[e] = (j == 2 * e ? 0xc040u : 0u) | (j == 2 * e + 1 ? 0xc0400000u : 0u);
+        w[e] = (j == 2 * e ? h : 0u) | (j == 2 * e + 1 ? h << 16 : 0u);
     return __builtin_bit_cast(bf16x8_t, make_uint4(w[0], w[1], w[2], w[3]));
 }
 
 template <class Tid = HwTid>
-__device__ __forceinline__ f32x4_t id_frag_f32(int roff, int cp, Tid tid = Tid{}) {
+__device__ __forceinline__ f32x4_t id_frag_f32(int roff, int cp, float c, Tid tid = Tid{}) {
     const int lane = tid() & (kWave - 1);
     const int j = (lane & 31) - roff - 8 * cp - 4 * (lane >> 5);
     f32x4_t v;
 #pragma unroll
-    for (int st = 0; st < 4; ++st) v[st] = j == st ? -3.0f : 0.0f;
+    for (int st = 0; st < 4; ++st) v[st] = j == st ? c : 0.0f;
     return v;
 }
 
 // d = slice index minus the wave's first identity slice.
 template <bool BF16, int SIDE>
 __device__ __forceinline__ void mma_identity(const Frags<BF16> &fr, f32x16_t (&acc)[kFM][kFN], int d,
-                                             int half) {
+                                             int half, const IdCoef &ic) {
     constexpr int RS = Elem<BF16>::BK;  // k rows per slice
     constexpr int WS = SIDE == ID_Q ? kWaveN : kWaveM;  // wave extent on the identity side
     constexpr int NB = WS / 32, NO = SIDE == ID_Q ? kFM : kFN;
     if (SIDE == ID_NONE || d < 0 || d >= WS / RS) return;
     const int blk = d * RS / 32, roff = (d * RS) % 32;
     if constexpr (BF16) {
-        const bf16x8_t id = id_frag_bf16(roff, half);
+        for (int part = 0; part < 2; ++part) {
+            const uint32_t h = part == 0 ? ic.hi : ic.lo;
+            if (part == 1 && h == 0u) break;
+            const bf16x8_t id = id_frag_bf16(roff, half, h);
 #pragma unroll
-        for (int b = 0; b < NB; ++b)
-            if (b == blk)
+            for (int b = 0; b < NB; ++b)
+                if (b == blk)
 #pragma unroll
-                for (int o = 0; o < NO; ++o) {
-                    if constexpr (SIDE == ID_P)
-                        acc[b][o] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(id, fr.q[o], acc[b][o], 0, 0, 0);
-                    else
-                        acc[o][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr.p[o], id, acc[o][b], 0, 0, 0);
-                }
+                    for (int o = 0; o < NO; ++o) {
+                        if constexpr (SIDE == ID_P)
+                            acc[b][o] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(id, fr.q[o], acc[b][o], 0, 0, 0);
+                        else
+                            acc[o][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr.p[o], id, acc[o][b], 0, 0, 0);
+                    }
+        }
     } else {
-        const f32x4_t id = id_frag_f32(roff, half);
+        const f32x4_t id = id_frag_f32(roff, half, ic.f);
 #pragma unroll
         for (int b = 0; b < NB; ++b)
             if (b == blk)
@@ -535,7 +563,7 @@ __device__ __forceinline__ void mma_identity(const Frags<BF16> &fr, f32x16_t (&a
 // starts at +0 changes no bit).
 template <bool BF16, int SIDE, int J, class Tid = HwTid>
 __device__ __forceinline__ void mma_identity_at(const Frags<BF16> &fr, f32x16_t (&acc)[kFM][kFN], int w0,
-                                                int half, Tid tid = Tid{}) {
+                                                int half, const IdCoef &ic, Tid tid = Tid{}) {
     constexpr int RS = Elem<BF16>::BK;
     constexpr int WS = SIDE == ID_Q ? kWaveN : kWaveM;
     constexpr int NO = SIDE == ID_Q ? kFM : kFN;
@@ -543,7 +571,7 @@ __device__ __forceinline__ void mma_identity_at(const Frags<BF16> &fr, f32x16_t 
     constexpr int b = (kb % WS) / 32, roff = kb % 32;
     if (__builtin_amdgcn_readfirstlane(kb / WS == w0 / WS ? 1 : 0) == 0) return;
     if constexpr (BF16) {
-        const bf16x8_t id = id_frag_bf16<Tid>(roff, half, tid);
+        const bf16x8_t id = id_frag_bf16<Tid>(roff, half, ic.hi, tid);
 #pragma unroll
         for (int o = 0; o < NO; ++o) {
             if constexpr (SIDE == ID_P)
@@ -551,8 +579,18 @@ __device__ __forceinline__ void mma_identity_at(const Frags<BF16> &fr, f32x16_t 
             else
                 acc[o][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr.p[o], id, acc[o][b], 0, 0, 0);
         }
+        if (ic.lo != 0u) {
+            const bf16x8_t il = id_frag_bf16<Tid>(roff, half, ic.lo, tid);
+#pragma unroll
+            for (int o = 0; o < NO; ++o) {
+                if constexpr (SIDE == ID_P)
+                    acc[b][o] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(il, fr.q[o], acc[b][o], 0, 0, 0);
+                else
+                    acc[o][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr.p[o], il, acc[o][b], 0, 0, 0);
+            }
+        }
     } else {
-        const f32x4_t id = id_frag_f32<Tid>(roff, half, tid);
+        const f32x4_t id = id_frag_f32<Tid>(roff, half, ic.f, tid);
 #pragma unroll
         for (int st = 0; st < 4; ++st)
 #pragma unroll
@@ -584,7 +622,8 @@ __device__ __forceinline__ uint32_t lds_addr(const char *p) {
 // term; unused for ID_NONE.
 template <class L, bool BF16, bool PKC, bool QKC, int SIDE = ID_NONE>
 __device__ __forceinline__ void tile_mainloop(const Operand &P, const Operand &Q, char *smem,
-                                              f32x16_t (&acc)[kFM][kFN], int id_origin = 0) {
+                                              f32x16_t (&acc)[kFM][kFN], int id_origin = 0,
+                                              IdCoef ic = kIdMinus3) {
     using E = Elem<BF16>;
     constexpr int TN = L::kTileN, S = L::kStages;
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -654,7 +693,7 @@ __device__ __forceinline__ void tile_mainloop(const Operand &P, const Operand &Q
                 if (i % eQ == eQ - 1) lq.issue_one(late, late_dst, i / eQ);
                 __builtin_amdgcn_sched_barrier(0);
             }
-            if constexpr (JID >= 0) mma_identity_at<BF16, SIDE, JID>(fa, acc, w0, 0);
+            if constexpr (JID >= 0) mma_identity_at<BF16, SIDE, JID>(fa, acc, w0, 0, ic);
             wait_vm_lgkm0<(S - 2) * NLD>();
             lds_barrier();
             const char *nxt = smem + ((j + 1) % S) * L::kStageBytes;
@@ -667,7 +706,7 @@ __device__ __forceinline__ void tile_mainloop(const Operand &P, const Operand &Q
                 if (i % eP == eP - 1) lp.issue_one(refill, dst, i / eP);
                 __builtin_amdgcn_sched_barrier(0);
             }
-            if constexpr (JID >= 0) mma_identity_at<BF16, SIDE, JID>(fb, acc, w0, 1);
+            if constexpr (JID >= 0) mma_identity_at<BF16, SIDE, JID>(fb, acc, w0, 1, ic);
         };
         static_for(std::make_integer_sequence<int, NID>{}, [&](auto jid) { iteration(decltype(jid)::value, jid); });
         for (int j = NID; j < iters; ++j) iteration(j, std::integral_constant<int, -1>{});
@@ -684,10 +723,10 @@ __device__ __forceinline__ void tile_mainloop(const Operand &P, const Operand &Q
             Frags<BF16> fa;
             read_frags<BF16, PKC, QKC, TN>(fa, smem, smem + L::kPBytes, wm0, wn0, 0);
             mma_half<BF16>(fa, acc);
-            mma_identity<BF16, SIDE>(fa, acc, kt - id0, 0);
+            mma_identity<BF16, SIDE>(fa, acc, kt - id0, 0, ic);
             read_frags<BF16, PKC, QKC, TN>(fa, smem, smem + L::kPBytes, wm0, wn0, 1);
             mma_half<BF16>(fa, acc);
-            mma_identity<BF16, SIDE>(fa, acc, kt - id0, 1);
+            mma_identity<BF16, SIDE>(fa, acc, kt - id0, 1, ic);
             __syncthreads();
         }
     }
@@ -1070,7 +1109,20 @@ struct ProductArgs {
     int R, C, ti, tj;
     LateScale s;     // -0.5 s is the epilogue's factor gamma
     float eta;
+    IdCoef idc;      // coefficient of the identity term
+    float s2;        // spectral0: the accumulators' factor before the epilogue
+    int spectral0;   // first product under spectral scaling (A unscaled)
 };
+
+// First product under spectral scaling: acc *= s^2 (see IdCoef).
+__device__ __forceinline__ void scale_acc(f32x16_t (&acc)[kFM][kFN], float s2) {
+#pragma unroll
+    for (int f = 0; f < kFM; ++f)
+#pragma unroll
+        for (int g = 0; g < kFN; ++g)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[f][g][r] *= s2;
+}
 
 // Epilogue of the product, 32 rows of the wave's tile at a time through
 // LDS: u = gamma * acc row-major (4 columns per lane), stored as
@@ -1308,9 +1360,10 @@ __device__ __forceinline__ void product_tile(const Operand &P, const Operand &Q,
     // wide (Q = X, mn-contiguous): -3 X enters on the P side at the output
     // rows; tall (Q = A): on the Q side at the output columns.
     if constexpr (QKC)
-        tile_mainloop<ProdLay, BF16, true, QKC, ID_Q>(P, Q, smem, acc, pa.tj * kNsProdTileN);
+        tile_mainloop<ProdLay, BF16, true, QKC, ID_Q>(P, Q, smem, acc, pa.tj * kNsProdTileN, pa.idc);
     else
-        tile_mainloop<ProdLay, BF16, true, QKC, ID_P>(P, Q, smem, acc, pa.ti * kNsTileM);
+        tile_mainloop<ProdLay, BF16, true, QKC, ID_P>(P, Q, smem, acc, pa.ti * kNsTileM, pa.idc);
+    if (pa.spectral0) scale_acc(acc, pa.s2);
     if (EPI == EPI_FINAL && pa.pk && !pa.out) {
         pack_from_registers(pa, acc);
         return;
@@ -1350,8 +1403,12 @@ void ns_product_kernel(NsBatch b) {
     pa.C = C;
     pa.ti = ti;
     pa.tj = tj;
-    pa.s = LateScale{b.scales[M.unit_begin + w].x, b.use_scales};
+    const float2 sc = b.scales[M.unit_begin + w];
+    pa.s = LateScale{sc.x, b.use_scales};
     pa.eta = b.eta;
+    pa.spectral0 = b.id_scaled;
+    pa.s2 = sc.y;
+    pa.idc = b.id_scaled ? id_coef_spectral(sc.y) : kIdMinus3;
     if (EPI == EPI_ITER)
         pa.out = static_cast<char *>(M.out) + (int64_t)w * n * (int64_t)sizeof(T);
     else if (EPI == EPI_FINAL || EPI == EPI_FINAL_I8)
@@ -1403,8 +1460,9 @@ struct PackTile {
     }
 
     // EPI: what the tile's epilogue writes (packed signs to M.packed, int8
-    // signs to M.i8, or the next iterate to M.out).
-    template <int EPI>
+    // signs to M.i8, or the next iterate to M.out). SPEC: the first product
+    // under spectral scaling (NsBatch::id_scaled).
+    template <int EPI, bool SPEC>
     __device__ __forceinline__ void decode(const NsBatch &b, int sv, int lt) {
         using T = typename Elem<BF16>::T;
         constexpr int BK = Elem<BF16>::BK;
@@ -1430,6 +1488,11 @@ struct PackTile {
         pa.tj = tj;
         pa.s = LateScale{load_scale_scalar(b.scales, M.unit_begin + w, 0), b.use_scales};
         pa.eta = 0.f;
+        pa.spectral0 = SPEC;
+        if constexpr (SPEC) {
+            pa.s2 = load_scale_scalar(b.scales, M.unit_begin + w, 1);
+            pa.idc = id_coef_spectral(pa.s2);
+        }
         if (!tall) {
             // out[m][n] = sum_k A[m][k] X[k][n]; -3 X on the P side at the output rows
             P = Operand{a + (int64_t)ti * kNsTileM * r * (int64_t)sizeof(T), r, R - ti * kNsTileM, r, true};
@@ -1496,7 +1559,7 @@ __device__ __forceinline__ v4u32 walk_rsrc(const Operand &op, bool kc) {
 // (the tail, unrolled) are the only ones that load for nxt. The first
 // fragments are read at the tile's start (slice 0 has landed and the
 // barrier that handed it over has passed).
-template <bool BF16, bool QKC>
+template <bool BF16, bool QKC, bool SPEC>
 __device__ __forceinline__ void pack_tile_kloop(const PackTile<BF16> &cur, const PackTile<BF16> &nxt,
                                                 const DmaSlices<BF16, 256, ProdLay::kWaves> &lp,
                                                 const DmaSlices<BF16, 256, ProdLay::kWaves> &lq, char *smem,
@@ -1508,6 +1571,7 @@ __device__ __forceinline__ void pack_tile_kloop(const PackTile<BF16> &cur, const
     const int wid = __builtin_amdgcn_readfirstlane(tid() / kWave);
     const int wm0 = L::m0(wid), wn0 = L::n0(wid);
     const int w0 = SIDE == ID_Q ? wn0 : wm0;
+    const IdCoef ic = SPEC ? cur.pa.idc : kIdMinus3;
 #pragma unroll
     for (int f = 0; f < kFM; ++f)
 #pragma unroll
@@ -1549,7 +1613,7 @@ __device__ __forceinline__ void pack_tile_kloop(const PackTile<BF16> &cur, const
             }
             __builtin_amdgcn_sched_barrier(0);
         }
-        if constexpr (JID >= 0) mma_identity_at<BF16, SIDE, JID, GivenTid>(fa, acc, w0, 0, tid);
+        if constexpr (JID >= 0) mma_identity_at<BF16, SIDE, JID, GivenTid>(fa, acc, w0, 0, ic, tid);
         wait_vm_lgkm0<(S - 2) * NLD>();
         lds_barrier();
         const char *nb = smem + ((js + 1) % S) * L::kStageBytes;
@@ -1568,7 +1632,7 @@ __device__ __forceinline__ void pack_tile_kloop(const PackTile<BF16> &cur, const
             }
             __builtin_amdgcn_sched_barrier(0);
         }
-        if constexpr (JID >= 0) mma_identity_at<BF16, SIDE, JID, GivenTid>(fb, acc, w0, 1, tid);
+        if constexpr (JID >= 0) mma_identity_at<BF16, SIDE, JID, GivenTid>(fb, acc, w0, 1, ic, tid);
     };
     using NoTail = std::integral_constant<int, -1>;
     static_for(std::make_integer_sequence<int, NID>{},
@@ -1580,8 +1644,8 @@ __device__ __forceinline__ void pack_tile_kloop(const PackTile<BF16> &cur, const
 
 // QKC: every matrix of the launch is tall (true) or wide (false). EPI:
 // EPI_FINAL (packed signs), EPI_FINAL_I8 (int8 signs) or EPI_ITER (the next
-// iterate).
-template <bool BF16, bool QKC, int EPI>
+// iterate). SPEC: the first product under spectral scaling (b.id_scaled).
+template <bool BF16, bool QKC, int EPI, bool SPEC>
 __global__ __launch_bounds__(ProdLay::kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void ns_product_pack_kernel(NsBatch b) {
     static_assert(BF16, "the walk is built for bf16 operands");
@@ -1605,7 +1669,7 @@ void ns_product_pack_kernel(NsBatch b) {
     int vb = blockIdx.x;
     PackTile<BF16> cur, nxt;
     DmaSlices<BF16, 256, L::kWaves> lp, lq;
-    cur.template decode<EPI>(b, sv, xcd_remap(vb, total));
+    cur.template decode<EPI, SPEC>(b, sv, xcd_remap(vb, total));
     lp.template setup<true>(cur.P);
     lq.template setup<QKC>(cur.Q);
     // The first tile fills the pipeline itself: slices 0 .. S - 2 and the P
@@ -1632,10 +1696,11 @@ void ns_product_pack_kernel(NsBatch b) {
         const int vn = vb + G;
         const bool more = vn < total;
         if (more)
-            nxt.template decode<EPI>(b, starts[lane], xcd_remap(vn, total));
+            nxt.template decode<EPI, SPEC>(b, starts[lane], xcd_remap(vn, total));
         else
             nxt.none();
-        pack_tile_kloop<BF16, QKC>(cur, nxt, lp, lq, smem, acc, tid);
+        pack_tile_kloop<BF16, QKC, SPEC>(cur, nxt, lp, lq, smem, acc, tid);
+        if constexpr (SPEC) scale_acc(acc, cur.pa.s2);
         if constexpr (kI8) {
             int8_from_registers(cur.pa, acc, tid, i8_table);
         } else if constexpr (kStaged) {
@@ -2118,11 +2183,16 @@ void launch_ns_gram_walk(const NsBatch &b, int grid_blocks, hipStream_t s) {
 
 void launch_ns_product_pack(const NsBatch &b, bool tall, NsEpilogue epi, int grid_blocks, hipStream_t s) {
     dim3 grid(grid_blocks), block(ProdLay::kThreads);
-#define SM_WALK(TALL, E) hipLaunchKernelGGL((ns_product_pack_kernel<true, TALL, E>), grid, block, 0, s, b)
-#define SM_WALK2(E) \
-    do {                            \
-        if (tall) SM_WALK(true, E);  \
-        else SM_WALK(false, E);      \
+#define SM_WALK(TALL, E, SP) hipLaunchKernelGGL((ns_product_pack_kernel<true, TALL, E, SP>), grid, block, 0, s, b)
+#define SM_WALK2(E)                               \
+    do {                                          \
+        if (b.id_scaled) {                        \
+            if (tall) SM_WALK(true, E, true);     \
+            else SM_WALK(false, E, true);         \
+        } else {                                  \
+            if (tall) SM_WALK(true, E, false);    \
+            else SM_WALK(false, E, false);        \
+        }                                         \
     } while (0)
     if (epi == EPI_FINAL_I8) SM_WALK2(EPI_FINAL_I8);
     else if (epi == EPI_ITER) SM_WALK2(EPI_ITER);

@@ -110,7 +110,9 @@ struct NsBatch {
     const float2 *scales; // per unit {s, s^2}; must cover every unit of the batch even
                           // when use_scales = 0 (the kernels read it unconditionally)
     float eta;            // EPI_WUPD step size
-    int32_t pad_;
+    int32_t id_scaled;    // first product under spectral scaling: A is the unscaled Gram
+                          // matrix; the identity coefficient is -3 / s^2 and the
+                          // accumulators are multiplied by s^2 before the epilogue
     Starts starts;         // first block (tile) of each matrix
 };
 
@@ -298,14 +300,11 @@ struct PowBatch {
 };
 
 int32_t power_blocks_per_worker(int64_t r);
-int32_t rescale_blocks_per_worker(int64_t r);
 void launch_power_step(const PowBatch &b, bool bf16, hipStream_t s);
 void launch_power_finalize(const PowBatch &b, hipStream_t s);
-// bpw of the batch: rescale_blocks_per_worker
-void launch_gram_rescale(const PowBatch &b, bool bf16, hipStream_t s);
-// All it = p power steps, the scales and (rescale) A <- round(s^2 A) with one
-// workgroup per (matrix, worker); every r % 8 == 0 and r <= max_fused_pow_r.
-void launch_power_fused(const PowBatch &b, bool bf16, bool rescale, hipStream_t s);
+// All it = p power steps and the scales with one workgroup per (matrix,
+// worker); every r % 8 == 0 and r <= max_fused_pow_r.
+void launch_power_fused(const PowBatch &b, bool bf16, hipStream_t s);
 
 // Post-vote polar step helpers.
 void launch_zero_u32(uint32_t *p, int32_t count, hipStream_t s);

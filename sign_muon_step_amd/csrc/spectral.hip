@@ -1,6 +1,6 @@
 // spectral.hip -- spectral normalisation of the Newton-Schulz input for
-// gfx950: power iteration on each worker's Gram matrix, the scale it gives,
-// and the rescaling of the stored Gram matrix.
+// gfx950: power iteration on each worker's Gram matrix and the scale it
+// gives.
 //
 // Method: "SignMuon: Communication-Efficient Distributed Muon Optimization"
 // (gist.science, paper 2605.16311, technical summary), §4 "nanoGPT" (the
@@ -9,8 +9,10 @@
 // stored Gram matrix of the stored momentum (the Newton-Schulz orientation),
 // lambda is the last ||A v|| of p power-iteration steps from the all-ones
 // vector (w = A v, lambda = ||w||, v = w / lambda), s = 1 / sqrt(lambda), and
-// the first iteration uses A_0 = round(fp32(1 / lambda) * A_raw) with
-// X_0 = s M. lambda = 0 gives s = 0 (U = 0).
+// the first iteration uses A_0 = s^2 A_raw with s^2 = fp32(1 / lambda) and
+// X_0 = s M. lambda = 0 gives s = 0 (U = 0). A_raw is not rescaled in memory:
+// the first product multiplies its fp32 accumulators of (A_raw - 3 / s^2 I) M
+// by s^2 (ns_gemm.hip, IdCoef).
 #include "sm_internal.h"
 
 namespace sm {
@@ -177,54 +179,9 @@ __global__ __launch_bounds__(kThreads) void power_finalize_kernel(PowBatch b) {
     }
 }
 
-// A <- round(s^2 * A) in place for every (matrix, worker) Gram matrix; 8
-// entries per thread. Blocks: per matrix, workers x rescale_bpw.
-template <bool BF16>
-__global__ __launch_bounds__(kThreads) void gram_rescale_kernel(PowBatch b) {
-    const int blk = blockIdx.x;
-    const int mi = find_start(b.starts, blk);
-    const PowMat &M = b.mat[mi];
-    const int local = blk - b.starts.v[mi];
-    const int w = local / M.bpw, cb = local - w * M.bpw;
-    const int64_t rr = (int64_t)M.r * M.r;
-    const float s2 = b.scales[M.unit_begin + w].y;
-    const int64_t e0 = ((int64_t)cb * kThreads + threadIdx.x) * 8;
-    char *a = static_cast<char *>(const_cast<void *>(M.a)) + (int64_t)w * rr * (BF16 ? 2 : 4);
-    if ((rr & 7) == 0 && e0 + 8 <= rr) {  // 16-byte aligned: one (bf16) or two (fp32) vector accesses
-        if (BF16) {
-            uint4 *p = reinterpret_cast<uint4 *>(a + e0 * 2);
-            const uint4 q = *p;
-            uint32_t h[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-            for (int t = 0; t < 4; ++t)
-                h[t] = pack_bf16x2(s2 * bf16_bits_to_f32(h[t] & 0xffffu), s2 * bf16_bits_to_f32(h[t] >> 16));
-            *p = make_uint4(h[0], h[1], h[2], h[3]);
-        } else {
-            float4 *p = reinterpret_cast<float4 *>(a + e0 * 4);
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                float4 v = p[t];
-                v.x *= s2; v.y *= s2; v.z *= s2; v.w *= s2;
-                p[t] = v;
-            }
-        }
-        return;
-    }
-    for (int64_t e = e0; e < e0 + 8 && e < rr; ++e) {
-        if (BF16) {
-            uint16_t *p = reinterpret_cast<uint16_t *>(a) + e;
-            *p = (uint16_t)f32_to_bf16_bits(s2 * bf16_bits_to_f32(*p));
-        } else {
-            float *p = reinterpret_cast<float *>(a) + e;
-            *p = s2 * *p;
-        }
-    }
-}
-
 // ---------------------------------------------------------------------------
 // The whole power iteration of one (matrix, worker) in one workgroup: the p
-// steps, the scale and (for the first Newton-Schulz iteration) the rescale
-// of A, in one launch over every unit. A is stored symmetric (each
+// steps and the scale, in one launch over every unit. A is stored symmetric (each
 // off-diagonal entry with its mirror), so a step reads the upper part only.
 // Rows go in groups of 8: group g is rows 8g .. 8g + 7, and it reads the
 // 16-byte chunks from its 8 x 8 diagonal block to the row end. For row j of
@@ -252,7 +209,7 @@ typedef uint32_t v4u32 __attribute__((ext_vector_type(4)));
 constexpr uint32_t kOOB = 0x80000000u;  // buffer offset past every extent: loads read zeros, stores drop
 
 template <bool BF16, int T>  // T: chunk slots per lane, T * 64 >= (r + 8) / EPC
-__global__ __launch_bounds__(kFusedThreads) void power_fused_kernel(PowBatch b, int rescale) {
+__global__ __launch_bounds__(kFusedThreads) void power_fused_kernel(PowBatch b) {
     constexpr int EPC = BF16 ? 8 : 4;                // entries per 16-byte chunk
     constexpr uint32_t ES = BF16 ? 2 : 4;            // bytes per entry
     constexpr int DQ = 8 / EPC;                      // chunks per row of an 8 x 8 block
@@ -425,39 +382,11 @@ __global__ __launch_bounds__(kFusedThreads) void power_fused_kernel(PowBatch b, 
         s2 = (float)(1.0 / lambda);
     }
     if (threadIdx.x == 0) b.scales[M.unit_begin + w] = make_float2(s, s2);
-    if (!rescale) return;
-    // A <- round(s^2 * A), 16 bytes per access (r % 8 == 0), kIn accesses of
-    // each thread in flight at a time; accesses past the end take kOOB.
-    constexpr int kIn = 8;
-    const uint32_t nq = (uint32_t)r * r / EPC;
-    for (uint32_t i0 = threadIdx.x; i0 < nq; i0 += (uint32_t)kIn * kFusedThreads) {
-        v4u32 h[kIn];
-#pragma unroll
-        for (int u = 0; u < kIn; ++u) {
-            const uint32_t i = i0 + (uint32_t)u * kFusedThreads;
-            h[u] = __builtin_amdgcn_raw_buffer_load_b128(rs, i < nq ? i * 16u : kOOB, 0, 0);
-        }
-#pragma unroll
-        for (int u = 0; u < kIn; ++u) {
-            const uint32_t i = i0 + (uint32_t)u * kFusedThreads;
-            v4u32 o;
-            if constexpr (BF16) {
-#pragma unroll
-                for (int t = 0; t < 4; ++t)
-                    o[t] = pack_bf16x2(s2 * bf16_bits_to_f32(h[u][t] & 0xffffu), s2 * bf16_bits_to_f32(h[u][t] >> 16));
-            } else {
-#pragma unroll
-                for (int t = 0; t < 4; ++t) o[t] = __float_as_uint(s2 * __uint_as_float(h[u][t]));
-            }
-            __builtin_amdgcn_raw_buffer_store_b128(o, rs, i < nq ? i * 16u : kOOB, 0, 0);
-        }
-    }
 }
 
 }  // namespace
 
 int32_t power_blocks_per_worker(int64_t r) { return (int32_t)((r + kPowRowsPerBlock - 1) / kPowRowsPerBlock); }
-int32_t rescale_blocks_per_worker(int64_t r) { return (int32_t)((r * r + kThreads * 8 - 1) / (kThreads * 8)); }
 
 void launch_power_step(const PowBatch &b, bool bf16, hipStream_t s) {
     dim3 grid(b.total_blocks), block(kThreads);
@@ -475,15 +404,14 @@ void launch_power_finalize(const PowBatch &b, hipStream_t s) {
     hipLaunchKernelGGL(power_finalize_kernel, dim3((units + 3) / 4), dim3(kThreads), 0, s, b);
 }
 
-void launch_power_fused(const PowBatch &b, bool bf16, bool rescale, hipStream_t s) {
+void launch_power_fused(const PowBatch &b, bool bf16, hipStream_t s) {
     int rmax = 0;
     for (int i = 0; i < b.nmat; ++i) rmax = b.mat[i].r > rmax ? b.mat[i].r : rmax;
     const size_t lds = (size_t)rmax * (2 + 2 * kFusedWaves) * sizeof(float);
     dim3 grid(b.nmat * b.workers), block(kFusedThreads);
     const int epc = bf16 ? 8 : 4;
     const int slots = ((rmax + 8) / epc + kWave - 1) / kWave;  // chunk slots per lane for a pair of row groups
-    const int rs = rescale ? 1 : 0;
-#define SM_FUSED(BF, TS) hipLaunchKernelGGL((power_fused_kernel<BF, TS>), grid, block, lds, s, b, rs)
+#define SM_FUSED(BF, TS) hipLaunchKernelGGL((power_fused_kernel<BF, TS>), grid, block, lds, s, b)
     if (bf16) {
         if (slots <= 1) SM_FUSED(true, 1);
         else SM_FUSED(true, 2);
@@ -492,14 +420,6 @@ void launch_power_fused(const PowBatch &b, bool bf16, bool rescale, hipStream_t 
         else SM_FUSED(false, 2);
     }
 #undef SM_FUSED
-}
-
-void launch_gram_rescale(const PowBatch &b, bool bf16, hipStream_t s) {
-    dim3 grid(b.total_blocks), block(kThreads);
-    if (bf16)
-        hipLaunchKernelGGL(gram_rescale_kernel<true>, grid, block, 0, s, b);
-    else
-        hipLaunchKernelGGL(gram_rescale_kernel<false>, grid, block, 0, s, b);
 }
 
 }  // namespace sm

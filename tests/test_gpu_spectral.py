@@ -153,8 +153,9 @@ def test_spectral_power_iteration_in_one_launch(ns, k):
     """A batch of at least half a device of (matrix, worker) units, every r a
     multiple of 8 and at most 1016 (bf16) or 504 (fp32), takes the power
     iteration with one
-    workgroup per unit: all p steps, the scales and (k >= 1) the rescale of
-    A in a single launch, the steps reading the upper part of A only. U of
+    workgroup per unit: all p steps and the scales in a single launch, the
+    steps reading the upper part of A only (A stays unscaled; the first
+    product applies s^2 to its accumulators). U of
     the first and last worker of each distinct shape against the oracle; the
     packed signs of every worker equal those of its stored U."""
     shapes = [(64, 200), (200, 64), (128, 320), (256, 256), (200, 448), (448, 200)] * 4
