@@ -154,14 +154,17 @@ constexpr int kGramReduceParts = 16;  // reduce blocks per Gram tile (16 rows ea
 void launch_ns_gram_split(const NsBatch &b, bool ns_bf16, hipStream_t s);
 void launch_gram_reduce(const NsBatch &b, bool ns_bf16, hipStream_t s);
 // K chunks per Gram tile of an R x C matrix (0: not split, the Gram kernel
-// stores A itself): for matrices with at most 3 Gram tiles per worker and at
-// least 32 k slices (BK k each), slices / 16 chunks, at most 8, so that the
-// few tiles spread over more blocks. A function of the shape alone, so that
-// results do not depend on which matrices share a launch.
+// stores A itself): for matrices with at most 3 Gram tiles per worker, so
+// that the few tiles spread over more blocks. A chunk is a quarter of the k
+// slices (BK k each), but at least 4 and at most 24 slices; at most 16
+// chunks, and a single chunk means no split. A function of the shape alone,
+// so that results do not depend on which matrices share a launch.
 inline int32_t ns_gram_split(int64_t R, int64_t C, bool ns_bf16) {
     if (ns_gram_tiles(R, C) > 3) return 0;
     const int64_t c = R > C ? R : C, bk = ns_bf16 ? 32 : 16;
-    const int64_t s = ((c + bk - 1) / bk + 23) / 24;  // chunks of about 24 k slices
+    const int64_t slices = (c + bk - 1) / bk;
+    const int64_t len = slices / 4 < 4 ? 4 : (slices / 4 > 24 ? 24 : slices / 4);
+    const int64_t s = (slices + len - 1) / len;
     return (int32_t)(s < 2 ? 0 : (s > 16 ? 16 : s));
 }
 // The bf16 Gram matrices as a persistent walk: grid_blocks workgroups (one
