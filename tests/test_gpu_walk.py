@@ -100,6 +100,53 @@ def test_walk_bits_equal_stored_u_bits(mw, k):
         assert agree >= 0.999
 
 
+
+@pytest.mark.parametrize("mw,k,plain", [(16, 1, 2), (5, 2, 3)])
+def test_walk_bits_equal_stored_u_bits_spectral(mw, k, plain):
+    """Spectral scaling (8 power steps). The Gram matrix stays unscaled and the
+    first product takes the identity coefficient -3 / s^2 and multiplies its
+    accumulators by s^2: in the walk a compile-time flag, in the one-tile-per-
+    block product (the stored-U run) a run-time one, with the same MFMAs in
+    the same order, so the packed bits, the vote and W must be equal. 16
+    workers with r % 8 == 0 throughout run the one-launch power iteration;
+    5 workers with a 300-row matrix run the per-step launches, and k = 2 adds
+    an intermediate walk product (the next iterate) under the flag. U of
+    workers 0 and mw - 1 against the oracle's spectral Newton-Schulz, and the
+    walk's bits against the oracle's signs."""
+    shapes = WALK + PLAIN[:plain]
+    power = 8
+    p = sm.Params(workers=mw, beta=0.9, eta=1e-3, ns_iters=k, mom_dtype=sm.BF16, ns_dtype=sm.BF16,
+                  norm=sm.NORM_SPECTRAL, power_iters=power)
+    walk, host = build(shapes, mw, 7300, polar=False)
+    ref, _ = build(shapes, mw, 7300, polar=True)
+    announce(f"  {mw} workers, {len(shapes)} matrices, k = {k}, spectral: walk run")
+    sm.signmuon_step(walk, p, sm.workspace_tensor(walk, p, DEV))
+    announce("  reference run (U stored: one tile per block)")
+    sm.signmuon_step(ref, p, sm.workspace_tensor(ref, p, DEV))
+    torch.cuda.synchronize()
+    for j, (a, b) in enumerate(zip(walk, ref)):
+        np.testing.assert_array_equal(to_host(a.momentum), to_host(b.momentum), err_msg=f"M {shapes[j]}")
+        np.testing.assert_array_equal(to_host(a.packed), to_host(b.packed), err_msg=f"packed {shapes[j]}")
+        np.testing.assert_array_equal(to_host(a.vote_out), to_host(b.vote_out), err_msg=f"vote {shapes[j]}")
+        np.testing.assert_array_equal(to_host(a.weight), to_host(b.weight), err_msg=f"W {shapes[j]}")
+    cases = [(j, w) for j in range(len(shapes)) for w in (0, mw - 1)]
+
+    def oracle_u(jw):
+        j, w = jw
+        m_ref = np.zeros(shapes[j], np.uint16)
+        oracle.momentum(host[j][0][w], m_ref, 0.9)
+        _, x0, a0 = oracle.spectral_x0_a0(m_ref, oracle.BF16, power)
+        return oracle.newton_schulz_a0(x0, a0, k, oracle.BF16)
+
+    for (j, w), u_ref in zip(cases, POOL.map(oracle_u, cases)):
+        u = to_host(ref[j].polar_out)[w]
+        err = rel_fro(u, u_ref)
+        agree, bad, cnt = bit_sign_stats(to_host(walk[j].packed)[w], u_ref)
+        announce(f"  {shapes[j]} worker {w}: rel_fro {err:.2e}, walk bits vs oracle signs "
+                 f"{agree:.6f} ({bad} of {cnt} differ)")
+        assert err <= 2e-2
+        assert agree >= 0.999
+
 def test_walk_on_gpt2_small_matches_plain_kernel_over_two_steps():
     """The benchmarked batch itself (48 GPT-2 small matrices, 8 workers): two
     steps, every packed word, the vote and W equal to the stored-U run's."""
