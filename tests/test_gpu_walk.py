@@ -100,7 +100,6 @@ def test_walk_bits_equal_stored_u_bits(mw, k):
         assert agree >= 0.999
 
 
-
 @pytest.mark.parametrize("mw,k,plain", [(16, 1, 2), (5, 2, 3)])
 def test_walk_bits_equal_stored_u_bits_spectral(mw, k, plain):
     """Spectral scaling (8 power steps). The Gram matrix stays unscaled and the
@@ -146,6 +145,7 @@ def test_walk_bits_equal_stored_u_bits_spectral(mw, k, plain):
                  f"{agree:.6f} ({bad} of {cnt} differ)")
         assert err <= 2e-2
         assert agree >= 0.999
+
 
 def test_walk_on_gpt2_small_matches_plain_kernel_over_two_steps():
     """The benchmarked batch itself (48 GPT-2 small matrices, 8 workers): two
@@ -196,14 +196,16 @@ def test_walk_with_more_matrices_than_one_launch_holds():
         np.testing.assert_array_equal(to_host(a.weight), to_host(b.weight), err_msg=f"W {j} {shapes[j]}")
 
 
-@pytest.mark.parametrize("mw,k", [(16, 1), (3, 2)])
-def test_walk_int8_signs_equal_stored_u_int8_signs(mw, k):
+@pytest.mark.parametrize("mw,k,spectral", [(16, 1, False), (3, 2, False), (16, 1, True)])
+def test_walk_int8_signs_equal_stored_u_int8_signs(mw, k, spectral):
     """The int8 payload: the walk expands each sign word into 64 bytes of
     +1 / -1; they must equal the int8 signs of the one-tile-per-block kernel
-    that also stores U, and 2 bit - 1 of the oracle's signs where clear."""
+    that also stores U, and 2 bit - 1 of the oracle's signs where clear. Also
+    under spectral scaling (the first product with the unscaled Gram matrix)."""
     shapes = WALK + PLAIN
     p = sm.Params(workers=mw, beta=0.9, eta=1e-3, ns_iters=k, mom_dtype=sm.BF16, ns_dtype=sm.BF16,
-                  payload=sm.PAYLOAD_INT8)
+                  payload=sm.PAYLOAD_INT8, norm=sm.NORM_SPECTRAL if spectral else sm.NORM_FROBENIUS,
+                  power_iters=6 if spectral else 0)
     walk, host = build(shapes, mw, 9100, polar=False, int8=True)
     ref, _ = build(shapes, mw, 9100, polar=True, int8=True)
     announce(f"  int8, {mw} workers, k = {k}: walk run, then stored-U run")
@@ -221,15 +223,21 @@ def test_walk_int8_signs_equal_stored_u_int8_signs(mw, k):
         np.testing.assert_array_equal(sw, np.where(u >= 0, 1, -1).astype(np.int8), err_msg=f"rule {shapes[j]}")
 
 
-def test_walk_degenerate_workers_match_oracle():
+@pytest.mark.parametrize("spectral", [False, True])
+def test_walk_degenerate_workers_match_oracle(spectral):
     """Workers whose gradient is zero (U = 0: every sign +1), holds a NaN (U
     is NaN: every sign -1) or an Inf (s = 0, and 0 * Inf is NaN: every sign
     -1), next to ordinary workers, through the walk: every packed word of
     the degenerate workers equals the oracle's, and the whole output equals
-    the stored-U kernel's."""
+    the stored-U kernel's. Under spectral scaling lambda is 0 or not finite
+    for them, so s = s^2 = 0 and the first product's identity coefficient is
+    -3."""
     shapes = [(384, 1024), (1024, 384), (768, 768)]
     mw = 3
-    p = sm.Params(workers=mw, beta=0.9, eta=1e-3, ns_iters=1, mom_dtype=sm.BF16, ns_dtype=sm.BF16)
+    norm = sm.NORM_SPECTRAL if spectral else sm.NORM_FROBENIUS
+    power = 5 if spectral else 0
+    p = sm.Params(workers=mw, beta=0.9, eta=1e-3, ns_iters=1, mom_dtype=sm.BF16, ns_dtype=sm.BF16,
+                  norm=norm, power_iters=power)
     bad = {0: (0, "zero"), 1: (1, "nan"), 2: (2, "inf")}  # matrix -> (worker, kind)
     runs = []
     for polar in (False, True):
@@ -252,7 +260,9 @@ def test_walk_degenerate_workers_match_oracle():
         np.testing.assert_array_equal(to_host(walk[j].weight), to_host(ref[j].weight), err_msg=f"W {shapes[j]}")
         m = np.zeros((mw, R, C), np.uint16)
         w0 = host[j][1].copy()
-        packed_ref, _, _ = oracle.step_matrix(host[j][0], m, w0, 0.9, 1e-3, 1, oracle.BF16)
+        packed_ref, _, _ = oracle.step_matrix(host[j][0], m, w0, 0.9, 1e-3, 1, oracle.BF16,
+                                              norm=oracle.NORM_SPECTRAL if spectral else oracle.NORM_FROB,
+                                              power_iters=power)
         announce(f"  {shapes[j]} worker {w} ({kind}): GPU words {np.unique(pw[w])[:3]}, "
                  f"oracle words {np.unique(packed_ref[w])[:3]}")
         np.testing.assert_array_equal(pw[w], packed_ref[w], err_msg=f"{kind} worker")
