@@ -167,11 +167,12 @@ def params_of(sm, wl):
 
 
 # The other configurations of the measurement plan, each timed in the same run
-# (they are parity cases; the benchmarked line is the GPT-2 small one):
-# (workload, warmup steps, timed steps).
+# (they are parity cases; the benchmarked line is the GPT-2 small one), and
+# the benchmarked workload with spectral scaling (its `power` kind is the
+# power iteration): (workload, warmup steps, timed steps).
 OTHER_CONFIGS = (("square256_mw4_k1", 5, 20), ("resnet50_4shapes_mw4_k1", 5, 20),
                  ("resnet50_4shapes_mw4_k5", 3, 10), ("gpt2s_mw16_k5_t3", 2, 5),
-                 ("block4096_mw16_k5", 1, 3))
+                 ("block4096_mw16_k5", 1, 3), ("gpt2s_mw8_k1_spectral", 3, 10))
 
 
 def time_other_configs(sm, hip, dev, configs=OTHER_CONFIGS):
