@@ -1,6 +1,7 @@
 """signmuon_step captured in a HIP graph: the library enqueues only kernel
 launches on the caller's stream (no allocation, no memset, no host
-synchronisation), so a captured step can be replayed. Two copies of the same
+synchronisation), so a captured step can be replayed (Frobenius and spectral
+scaling). Two copies of the same
 state advance side by side, one by graph replays and one by eager calls, with
 eager work and synchronisations between the replays; after every replay the
 momentum, the packed signs, the vote and W of both copies must be equal bit
@@ -39,18 +40,26 @@ def state(shapes, mw, seed, int8):
 
 # The default shapes run the one-tile-per-block kernels; the "walk" set
 # (bf16, packed signs, k loop of at least 12 slices) runs the final product's
-# persistent tile walk, wide and tall, with several tiles per workgroup.
+# persistent tile walk, wide and tall, with several tiles per workgroup; the
+# "units" set has 128 (matrix, worker) units, so that spectral scaling runs
+# its power iteration in one launch.
 SHAPES = {"default": ([(256, 640), (640, 256), (100, 130)], 4),
-          "walk": ([(384, 1024), (1024, 384), (768, 3072)], 8)}
+          "walk": ([(384, 1024), (1024, 384), (768, 3072)], 8),
+          "units": ([(256, 512), (512, 256)] * 8, 8)}
 
 
-@pytest.mark.parametrize("payload,k,shapes", [(p, k, "default") for p in ("bits", "int8") for k in (0, 1, 3)]
-                         + [("bits", 1, "walk"), ("bits", 2, "walk")])
-def test_captured_step_replays_like_eager_steps(payload, k, shapes):
+@pytest.mark.parametrize("payload,k,shapes,norm",
+                         [(p, k, "default", "frobenius") for p in ("bits", "int8") for k in (0, 1, 3)]
+                         + [("bits", 1, "walk", "frobenius"), ("bits", 2, "walk", "frobenius"),
+                            ("bits", 1, "walk", "spectral"), ("int8", 2, "default", "spectral"),
+                            ("bits", 1, "units", "spectral")])
+def test_captured_step_replays_like_eager_steps(payload, k, shapes, norm):
     shapes, mw = SHAPES[shapes]
     int8 = payload == "int8"
+    spectral = norm == "spectral"
     p = sm.Params(workers=mw, beta=0.9, eta=1e-3, ns_iters=k, mom_dtype=sm.BF16, ns_dtype=sm.BF16,
-                  payload=sm.PAYLOAD_INT8 if int8 else sm.PAYLOAD_BITS)
+                  payload=sm.PAYLOAD_INT8 if int8 else sm.PAYLOAD_BITS,
+                  norm=sm.NORM_SPECTRAL if spectral else sm.NORM_FROBENIUS, power_iters=6 if spectral else 0)
     graphed, eager = state(shapes, mw, 50, int8), state(shapes, mw, 50, int8)
     ws_g, ws_e = sm.workspace_tensor(graphed, p, DEV), sm.workspace_tensor(eager, p, DEV)
     torch.cuda.synchronize()
